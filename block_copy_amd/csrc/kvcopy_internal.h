@@ -1,0 +1,60 @@
+// kvcopy_internal.h -- pieces shared by the planner, the runtime and the
+// copy kernel of libkvcopy.  Not part of the public ABI (include/kvcopy.h).
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+namespace kvc {
+
+// One entry of the chunk worklist the kernel consumes: a piece of one merged
+// range, at most chunk_bytes long (a multiple of 16 except for the last
+// piece of a range, which may end in an 8-byte word).
+struct ChunkRec {
+    uint64_t src;
+    uint64_t dst;
+    uint32_t bytes;
+    uint32_t reserved;
+};
+static_assert(sizeof(ChunkRec) == 24, "ChunkRec is 24 bytes");
+
+// ---- planner (plan.cpp) ----------------------------------------------------
+
+// Drops zero sizes and (if `merge`) merges list-consecutive ranges that are
+// adjacent in both source and destination.  Checks 8-byte alignment and
+// address wrap-around.  Output arrays need room for n entries and may alias
+// the inputs.  Returns KVCOPY_OK, KVCOPY_EALIGN or KVCOPY_EINVAL.
+int merge_ranges(const uint64_t *src, const uint64_t *dst, const uint64_t *size, uint64_t n,
+                 bool merge, uint64_t *osrc, uint64_t *odst, uint64_t *osize, uint64_t *m_out,
+                 uint64_t *total_out);
+
+// KVCOPY_EOVERLAP if any two destination ranges overlap or a destination
+// overlaps a source range, else KVCOPY_OK.  O(m log m).
+int check_overlap(const uint64_t *src, const uint64_t *dst, const uint64_t *size, uint64_t m);
+
+// begin[i] = sum over j < i of ceil(size[j] / chunk); begin has m + 1 entries.
+// Returns begin[m].
+uint64_t chunk_prefix(const uint64_t *size, uint64_t m, uint32_t chunk, uint64_t *begin);
+
+// Writes the worklist: range i's chunks go to out[begin[i] .. begin[i+1]).
+void emit_chunks(const uint64_t *src, const uint64_t *dst, const uint64_t *size,
+                 const uint64_t *begin, uint64_t m, uint32_t chunk, ChunkRec *out);
+
+// True when KVCOPY_VALIDATE=1 in the environment; any value other than
+// unset, "0" or "1" makes *bad true (strict parsing).
+bool env_validate(bool *bad);
+
+// ---- kernel launch (kvcopy_kernel.hip) -------------------------------------
+
+constexpr uint32_t kWavesPerWG = 4;
+constexpr uint32_t kThreadsPerWG = 64 * kWavesPerWG;
+
+// Launches the copy kernel: `grid` workgroups, wavefronts take chunks
+// round-robin.  recs must be device-readable (device memory or mapped host
+// memory).  Returns the launch status.
+hipError_t launch_copy(const ChunkRec *recs, uint32_t n_chunks, uint32_t grid, int dir,
+                       hipStream_t stream);
+
+}  // namespace kvc

@@ -1,0 +1,141 @@
+// kvcopy_kernel.hip -- the persistent, workgroup-capped copy kernel (gfx950).
+//
+// Work unit: one chunk of the worklist (at most chunk_bytes, never crossing a
+// range; FreeToken issue #751 "gather missed experts with a few TMA
+// bulk-copy CTAs", section "What we changed").  Chunks are dealt round-robin
+// to wavefronts: wavefront w of a grid of W takes chunks w, w + W, w + 2W, ...
+// That is the persistent loop of the vLLM PR #42212 report ("Triton fast path
+// for small CPU->GPU swap_blocks_batch"), section "key source snippet", where
+// program p takes jobs p, p + P, ...; here the job is a byte-bounded chunk
+// instead of a whole descriptor, so a 1 MiB row is shared by many wavefronts
+// while small rows are not left waiting.  The grid is capped by max_wgs
+// (PegaFlow issue #408, "Follow-up", item 1: a bounded grid).
+//
+// Data path (CDNA4): each lane moves 16-byte vectors with nontemporal
+// buffer_load_dwordx4 / buffer_store_dwordx4, lanes interleaved so that one
+// wavefront instruction covers 1 KiB of contiguous bytes.  A wavefront
+// issues the loads for up to 16 KiB (16 vectors per lane, 64 VGPRs) before
+// the first store, so a single wavefront keeps up to 16 KiB of reads in
+// flight; the next chunk's worklist entry is fetched with scalar loads
+// (counted by lgkmcnt, not vmcnt) while the current chunk's vector traffic
+// is in flight.  Addresses only need 8-byte alignment: gfx950 serves
+// 8-byte-aligned dwordx4 accesses directly, so no head peeling or register
+// shifting is needed when src and dst differ mod 16.  A range whose size is
+// an odd multiple of 8 ends in one 8-byte word, moved by lane 0.
+#include <hip/hip_runtime.h>
+
+#include "kvcopy.h"
+#include "kvcopy_internal.h"
+
+namespace kvc {
+namespace {
+
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+#define KVC_GLOBAL __attribute__((address_space(1)))
+
+// Raw buffer resources.  The fourth descriptor word is the gfx9-family raw
+// buffer format (32-bit data format, no swizzle, no stride).  A buffer access
+// at an offset at or beyond num_records is dropped (stores) or reads zero
+// (loads); every vector access here is either wholly inside or wholly
+// outside its range, so the lanes past the end of a short row need no exec
+// masking.  Without per-row branches the compiler keeps all loads of a pass
+// in flight and waits with vmcnt(N) before each store, never vmcnt(0).
+constexpr int kRsrcWord3 = 0x00020000;
+constexpr int kNontemporal = 2;                    // cache-policy bit "nt" on gfx940+
+constexpr uint32_t kRowBytes = 64u * 16u;          // one wavefront instruction: 1 KiB
+constexpr int kMaxRows = 16;                       // 16 KiB per pass, 64 VGPRs of data
+constexpr uint32_t kPassBytes = kRowBytes * kMaxRows;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(uint64_t base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(base), 0, (int)bytes,
+                                             kRsrcWord3);
+}
+
+// R rows of 1 KiB: all loads first, then all stores.
+template <int R>
+__device__ __forceinline__ void copy_rows(__amdgpu_buffer_rsrc_t rs, __amdgpu_buffer_rsrc_t rd,
+                                          uint32_t voff)
+{
+    v4u v[R];
+#pragma unroll
+    for (int j = 0; j < R; ++j)
+        v[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(voff + j * kRowBytes), 0,
+                                                     kNontemporal);
+#pragma unroll
+    for (int j = 0; j < R; ++j)
+        __builtin_amdgcn_raw_buffer_store_b128(v[j], rd, (int)(voff + j * kRowBytes), 0,
+                                               kNontemporal);
+}
+
+// One wavefront copies one chunk.  src, dst and bytes are wave-uniform.
+__device__ __forceinline__ void copy_chunk(uint64_t src, uint64_t dst, uint32_t bytes,
+                                           uint32_t lane)
+{
+    const uint32_t body = bytes & ~15u;
+    const uint32_t voff = lane * 16u;
+    for (uint32_t off = 0; off < body; off += kPassBytes) {
+        const uint32_t pb = body - off < kPassBytes ? body - off : kPassBytes;
+        const __amdgpu_buffer_rsrc_t rs = rsrc(src + off, pb);
+        const __amdgpu_buffer_rsrc_t rd = rsrc(dst + off, pb);
+        switch ((pb + kRowBytes - 1) / kRowBytes) {
+        case 1: copy_rows<1>(rs, rd, voff); break;
+        case 2: copy_rows<2>(rs, rd, voff); break;
+        case 3: copy_rows<3>(rs, rd, voff); break;
+        case 4: copy_rows<4>(rs, rd, voff); break;
+        case 5: copy_rows<5>(rs, rd, voff); break;
+        case 6: copy_rows<6>(rs, rd, voff); break;
+        case 7: copy_rows<7>(rs, rd, voff); break;
+        case 8: copy_rows<8>(rs, rd, voff); break;
+        case 9: copy_rows<9>(rs, rd, voff); break;
+        case 10: copy_rows<10>(rs, rd, voff); break;
+        case 11: copy_rows<11>(rs, rd, voff); break;
+        case 12: copy_rows<12>(rs, rd, voff); break;
+        case 13: copy_rows<13>(rs, rd, voff); break;
+        case 14: copy_rows<14>(rs, rd, voff); break;
+        case 15: copy_rows<15>(rs, rd, voff); break;
+        default: copy_rows<16>(rs, rd, voff); break;
+        }
+    }
+    if ((bytes & 8u) && lane == 0) {   // a range that ends in an odd 8-byte word
+        const uint64_t w =
+            __builtin_nontemporal_load(reinterpret_cast<KVC_GLOBAL const uint64_t *>(src + body));
+        __builtin_nontemporal_store(w, reinterpret_cast<KVC_GLOBAL uint64_t *>(dst + body));
+    }
+}
+
+__global__ __launch_bounds__(kThreadsPerWG) void kvcopy_chunks_kernel(
+    const ChunkRec *__restrict__ recs, uint32_t n_chunks)
+{
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t stride = gridDim.x * kWavesPerWG;
+    uint32_t k = __builtin_amdgcn_readfirstlane(blockIdx.x * kWavesPerWG + (threadIdx.x >> 6));
+    if (k >= n_chunks)
+        return;
+    ChunkRec cur = recs[k];
+    for (;;) {
+        const uint32_t next = k + stride;
+        const bool more = next < n_chunks;
+        ChunkRec nxt;
+        if (more)
+            nxt = recs[next];            // scalar prefetch of the next worklist entry
+        copy_chunk(cur.src, cur.dst, cur.bytes, lane);
+        if (!more)
+            break;
+        cur = nxt;
+        k = next;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_copy(const ChunkRec *recs, uint32_t n_chunks, uint32_t grid, int dir,
+                       hipStream_t stream)
+{
+    (void)dir;
+    void *args[] = {(void *)&recs, (void *)&n_chunks};
+    return hipLaunchKernel(reinterpret_cast<const void *>(&kvcopy_chunks_kernel), dim3(grid),
+                           dim3(kThreadsPerWG), args, 0, stream);
+}
+
+}  // namespace kvc

@@ -1,0 +1,213 @@
+// plan.cpp -- host-side planning of a batch: validate, coalesce, chunk.
+//
+// Coalescing: PegaFlow issue #408 ("Kernel transfer backend causes decode
+// TPOT tail spikes under concurrent KV transfers"), section "Relevant
+// implementation" -- adjacent ranges are merged before submission.  The rule
+// used: one pass in list order; zero sizes dropped; a range joins the one
+// built so far when it continues it in both source and destination.
+//
+// Chunking: FreeToken issue #751 ("gather missed experts with a few TMA
+// bulk-copy CTAs"), section "What we changed" -- the call's bytes are cut
+// into chunks of at most 16 KiB, each inside one row, and spread over a few
+// workers so that one 1 MiB row does not leave the workers of small rows idle.
+// Here the chunk numbers of range i start at the exclusive prefix sum of the
+// per-range chunk counts, so every range's worklist entries can be written
+// independently.
+#include <stdlib.h>
+#include <string.h>
+
+#include <algorithm>
+#include <vector>
+
+#include "kvcopy.h"
+#include "kvcopy_internal.h"
+
+namespace kvc {
+
+int merge_ranges(const uint64_t *src, const uint64_t *dst, const uint64_t *size, uint64_t n,
+                 bool merge, uint64_t *osrc, uint64_t *odst, uint64_t *osize, uint64_t *m_out,
+                 uint64_t *total_out)
+{
+    uint64_t bits = 0, total = 0, m = 0;
+    bool wrap = false;
+    // Current open range (not yet written) so that in-place use is safe.
+    uint64_t cs = 0, cd = 0, cn = 0;
+    for (uint64_t i = 0; i < n; ++i) {
+        const uint64_t s = src[i], d = dst[i], z = size[i];
+        bits |= s | d | z;
+        if (z == 0)
+            continue;
+        wrap |= (s + z < s) | (d + z < d);
+        total += z;
+        if (cn != 0 && merge && cs + cn == s && cd + cn == d) {
+            cn += z;
+            continue;
+        }
+        if (cn != 0) {
+            osrc[m] = cs;
+            odst[m] = cd;
+            osize[m] = cn;
+            ++m;
+        }
+        cs = s;
+        cd = d;
+        cn = z;
+    }
+    if (cn != 0) {
+        osrc[m] = cs;
+        odst[m] = cd;
+        osize[m] = cn;
+        ++m;
+    }
+    *m_out = m;
+    *total_out = total;
+    if (bits & 7u)
+        return KVCOPY_EALIGN;
+    if (wrap)
+        return KVCOPY_EINVAL;
+    return KVCOPY_OK;
+}
+
+int check_overlap(const uint64_t *src, const uint64_t *dst, const uint64_t *size, uint64_t m)
+{
+    std::vector<std::pair<uint64_t, uint64_t>> d(m);
+    for (uint64_t i = 0; i < m; ++i)
+        d[i] = {dst[i], dst[i] + size[i]};
+    std::sort(d.begin(), d.end());
+    for (uint64_t i = 1; i < m; ++i)
+        if (d[i].first < d[i - 1].second)
+            return KVCOPY_EOVERLAP;
+    // Destinations are now disjoint and sorted: a source overlaps one iff the
+    // last destination starting before the source's end reaches past its start.
+    for (uint64_t i = 0; i < m; ++i) {
+        const uint64_t lo = src[i], hi = src[i] + size[i];
+        auto it = std::lower_bound(d.begin(), d.end(), std::make_pair(hi, (uint64_t)0));
+        if (it != d.begin() && std::prev(it)->second > lo)
+            return KVCOPY_EOVERLAP;
+    }
+    return KVCOPY_OK;
+}
+
+uint64_t chunk_prefix(const uint64_t *size, uint64_t m, uint32_t chunk, uint64_t *begin)
+{
+    uint64_t acc = 0;
+    for (uint64_t i = 0; i < m; ++i) {
+        begin[i] = acc;
+        acc += size[i] / chunk + (size[i] % chunk != 0);
+    }
+    begin[m] = acc;
+    return acc;
+}
+
+void emit_chunks(const uint64_t *src, const uint64_t *dst, const uint64_t *size,
+                 const uint64_t *begin, uint64_t m, uint32_t chunk, ChunkRec *out)
+{
+    for (uint64_t i = 0; i < m; ++i) {
+        ChunkRec *r = out + begin[i];
+        const uint64_t s = src[i], d = dst[i], z = size[i];
+        if (z <= chunk) {   // the common case: one chunk per range
+            r->src = s;
+            r->dst = d;
+            r->bytes = (uint32_t)z;
+            r->reserved = 0;
+            continue;
+        }
+        for (uint64_t off = 0; off < z; off += chunk, ++r) {
+            const uint64_t left = z - off;
+            r->src = s + off;
+            r->dst = d + off;
+            r->bytes = (uint32_t)(left < chunk ? left : chunk);
+            r->reserved = 0;
+        }
+    }
+}
+
+bool env_validate(bool *bad)
+{
+    const char *v = getenv("KVCOPY_VALIDATE");
+    *bad = false;
+    if (v == nullptr || strcmp(v, "0") == 0)
+        return false;
+    if (strcmp(v, "1") == 0)
+        return true;
+    *bad = true;
+    return false;
+}
+
+}  // namespace kvc
+
+using namespace kvc;
+
+extern "C" int kvcopy_coalesce(const uint64_t *src, const uint64_t *dst, const uint64_t *sizes,
+                               uint64_t n, uint64_t *out_src, uint64_t *out_dst,
+                               uint64_t *out_sizes, uint64_t *out_n)
+{
+    if (out_n == nullptr)
+        return KVCOPY_EINVAL;
+    if (n == 0) {
+        *out_n = 0;
+        return KVCOPY_OK;
+    }
+    if (!src || !dst || !sizes || !out_src || !out_dst || !out_sizes)
+        return KVCOPY_EINVAL;
+    // Same pass as the batch planner; alignment is not this call's concern.
+    uint64_t m = 0, total = 0;
+    (void)merge_ranges(src, dst, sizes, n, true, out_src, out_dst, out_sizes, &m, &total);
+    *out_n = m;
+    return KVCOPY_OK;
+}
+
+extern "C" int kvcopy_plan(const uint64_t *src, const uint64_t *dst, const uint64_t *sizes,
+                           uint64_t n, uint32_t chunk_bytes, kvcopy_plan_t *out)
+{
+    if (out == nullptr)
+        return KVCOPY_EINVAL;
+    memset(out, 0, sizeof(*out));
+    if (chunk_bytes == 0)
+        chunk_bytes = KVCOPY_CHUNK_DEFAULT;
+    if ((chunk_bytes & 15u) || chunk_bytes > KVCOPY_CHUNK_MAX)
+        return KVCOPY_EINVAL;
+    if (n > KVCOPY_MAX_DESCS || (n > 0 && (!src || !dst || !sizes)))
+        return KVCOPY_EINVAL;
+    bool bad_env = false;
+    const bool validate = env_validate(&bad_env);
+    if (bad_env)
+        return KVCOPY_EINVAL;
+
+    // One allocation holds src, dst, size (n each) and chunk_begin (n + 1).
+    uint64_t *buf = (uint64_t *)malloc(sizeof(uint64_t) * (4 * n + 1));
+    if (buf == nullptr)
+        return KVCOPY_ENOMEM;
+    uint64_t *ms = buf, *md = buf + n, *mz = buf + 2 * n, *mb = buf + 3 * n;
+    uint64_t m = 0, total = 0;
+    int rc = merge_ranges(src, dst, sizes, n, true, ms, md, mz, &m, &total);
+    if (rc == KVCOPY_OK && validate)
+        rc = check_overlap(ms, md, mz, m);
+    if (rc != KVCOPY_OK) {
+        free(buf);
+        return rc;
+    }
+    const uint64_t chunks = chunk_prefix(mz, m, chunk_bytes, mb);
+    if (chunks > KVCOPY_MAX_CHUNKS) {
+        free(buf);
+        return KVCOPY_EINVAL;
+    }
+    out->n_in = n;
+    out->n_merged = m;
+    out->n_chunks = chunks;
+    out->total_bytes = total;
+    out->chunk_bytes = chunk_bytes;
+    out->src = ms;
+    out->dst = md;
+    out->size = mz;
+    out->chunk_begin = mb;
+    return KVCOPY_OK;
+}
+
+extern "C" void kvcopy_plan_free(kvcopy_plan_t *plan)
+{
+    if (plan == nullptr)
+        return;
+    free((void *)plan->src);   // the arrays share one allocation starting at src
+    memset(plan, 0, sizeof(*plan));
+}

@@ -1,0 +1,237 @@
+"""ctypes binding of libkvcopy.so (include/kvcopy.h): argument marshalling only.
+
+Every step of the copy runs inside the library (host planner + gfx950
+kernel).  This module never computes a result itself and has no fallback:
+if the library is missing or cannot be loaded, importing it raises.
+
+Descriptor arrays may be NumPy arrays, CPU torch tensors or sequences of
+ints; they are passed as contiguous uint64 buffers.  Streams are HIP stream
+handles as integers (``torch.cuda.current_stream().cuda_stream`` on ROCm) or
+None for the null stream.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import numpy as np
+
+H2D, D2H, D2D = 0, 1, 2
+OK, EINVAL, EALIGN, EOVERLAP, ENOMEM, EHIP = 0, -1, -2, -3, -4, -5
+WGS_ALL = 0
+CHUNK_DEFAULT = 16384
+CHUNK_MAX = 1 << 20
+F_VALIDATE, F_NO_COALESCE, F_DESC_MAPPED = 0x1, 0x2, 0x4
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvcopy.so")
+
+# Every symbol include/kvcopy.h declares.
+EXPORTS = ("kvcopy_coalesce", "kvcopy_plan", "kvcopy_plan_free", "kvcopy_batch",
+           "kvcopy_batch_ex", "kvcopy_strerror", "kvcopy_last_hip_error",
+           "kvcopy_host_alloc_mapped", "kvcopy_host_free")
+
+
+class KvcopyError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        msg = f"{where}: {kvcopy_strerror(code)} ({code})"
+        if code == EHIP:
+            msg += f", hipError {kvcopy_last_hip_error()}"
+        super().__init__(msg)
+
+
+class _Plan(ctypes.Structure):
+    _fields_ = [("n_in", ctypes.c_uint64), ("n_merged", ctypes.c_uint64),
+                ("n_chunks", ctypes.c_uint64), ("total_bytes", ctypes.c_uint64),
+                ("chunk_bytes", ctypes.c_uint32), ("reserved", ctypes.c_uint32),
+                ("src", ctypes.POINTER(ctypes.c_uint64)), ("dst", ctypes.POINTER(ctypes.c_uint64)),
+                ("size", ctypes.POINTER(ctypes.c_uint64)),
+                ("chunk_begin", ctypes.POINTER(ctypes.c_uint64))]
+
+
+class Opts(ctypes.Structure):
+    """kvcopy_opts_t."""
+    _fields_ = [("struct_size", ctypes.c_uint32), ("chunk_bytes", ctypes.c_uint32),
+                ("flags", ctypes.c_uint32), ("reserved", ctypes.c_uint32),
+                ("kernel_begin", ctypes.c_void_p), ("kernel_end", ctypes.c_void_p)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"libkvcopy.so not built ({LIB_PATH}); run "
+                          "`python -c 'import __graft_entry__ as g; g.build()'`")
+    lib = ctypes.CDLL(LIB_PATH)
+    u64p = ctypes.POINTER(ctypes.c_uint64)
+    lib.kvcopy_coalesce.restype = ctypes.c_int
+    lib.kvcopy_coalesce.argtypes = [u64p, u64p, u64p, ctypes.c_uint64, u64p, u64p, u64p, u64p]
+    lib.kvcopy_plan.restype = ctypes.c_int
+    lib.kvcopy_plan.argtypes = [u64p, u64p, u64p, ctypes.c_uint64, ctypes.c_uint32,
+                                ctypes.POINTER(_Plan)]
+    lib.kvcopy_plan_free.restype = None
+    lib.kvcopy_plan_free.argtypes = [ctypes.POINTER(_Plan)]
+    lib.kvcopy_batch.restype = ctypes.c_int
+    lib.kvcopy_batch.argtypes = [u64p, u64p, u64p, ctypes.c_uint64, ctypes.c_int, ctypes.c_int,
+                                 ctypes.c_void_p]
+    lib.kvcopy_batch_ex.restype = ctypes.c_int
+    lib.kvcopy_batch_ex.argtypes = [u64p, u64p, u64p, ctypes.c_uint64, ctypes.c_int,
+                                    ctypes.c_int, ctypes.c_void_p, ctypes.POINTER(Opts)]
+    lib.kvcopy_strerror.restype = ctypes.c_char_p
+    lib.kvcopy_strerror.argtypes = [ctypes.c_int]
+    lib.kvcopy_last_hip_error.restype = ctypes.c_int
+    lib.kvcopy_last_hip_error.argtypes = []
+    lib.kvcopy_host_alloc_mapped.restype = ctypes.c_int
+    lib.kvcopy_host_alloc_mapped.argtypes = [ctypes.c_uint64, ctypes.POINTER(ctypes.c_void_p)]
+    lib.kvcopy_host_free.restype = ctypes.c_int
+    lib.kvcopy_host_free.argtypes = [ctypes.c_void_p]
+    return lib
+
+
+lib = _load()
+
+
+def _u64(a):
+    """(keep-alive array, uint64* pointer) for an int sequence / ndarray / CPU tensor."""
+    if a is None:
+        return None, None
+    if hasattr(a, "numpy") and hasattr(a, "device"):       # torch tensor
+        if a.device.type != "cpu":
+            raise ValueError("descriptor arrays must be host (CPU) arrays")
+        a = a.numpy()
+    arr = np.asarray(a)
+    if arr.dtype != np.uint64:
+        arr = arr.astype(np.uint64)
+    arr = np.ascontiguousarray(arr)
+    return arr, arr.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64))
+
+
+def _n(*arrays):
+    lens = {len(x) for x in arrays if x is not None}
+    if len(lens) > 1:
+        raise ValueError("src, dst and sizes must have the same length")
+    return lens.pop() if lens else 0
+
+
+def kvcopy_strerror(code: int) -> str:
+    return lib.kvcopy_strerror(int(code)).decode()
+
+
+def kvcopy_last_hip_error() -> int:
+    return int(lib.kvcopy_last_hip_error())
+
+
+def kvcopy_coalesce(src, dst, sizes, raw: bool = False):
+    """Merged (src, dst, sizes) uint64 arrays.  raw=True returns (code, arrays)."""
+    s, sp = _u64(src)
+    d, dp = _u64(dst)
+    z, zp = _u64(sizes)
+    n = _n(s, d, z)
+    os_ = np.empty(n, np.uint64)
+    od = np.empty(n, np.uint64)
+    oz = np.empty(n, np.uint64)
+    m = ctypes.c_uint64(0)
+    p = lambda x: x.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64))  # noqa: E731
+    rc = lib.kvcopy_coalesce(sp, dp, zp, n, p(os_), p(od), p(oz), ctypes.byref(m))
+    out = (os_[:m.value], od[:m.value], oz[:m.value])
+    if raw:
+        return rc, out
+    if rc != OK:
+        raise KvcopyError(rc, "kvcopy_coalesce")
+    return out
+
+
+@dataclass
+class Plan:
+    n_in: int
+    n_merged: int
+    n_chunks: int
+    total_bytes: int
+    chunk_bytes: int
+    src: np.ndarray
+    dst: np.ndarray
+    size: np.ndarray
+    chunk_begin: np.ndarray
+
+
+def kvcopy_plan(src, dst, sizes, chunk_bytes: int = 0) -> Plan:
+    """Validated, coalesced and chunked plan (copied out of the library)."""
+    s, sp = _u64(src)
+    d, dp = _u64(dst)
+    z, zp = _u64(sizes)
+    n = _n(s, d, z)
+    plan = _Plan()
+    rc = lib.kvcopy_plan(sp, dp, zp, n, int(chunk_bytes), ctypes.byref(plan))
+    if rc != OK:
+        raise KvcopyError(rc, "kvcopy_plan")
+    try:
+        m = plan.n_merged
+
+        def grab(ptr, k):
+            return np.ctypeslib.as_array(ptr, shape=(k,)).copy() if k else np.zeros(0, np.uint64)
+        return Plan(plan.n_in, m, plan.n_chunks, plan.total_bytes, plan.chunk_bytes,
+                    grab(plan.src, m), grab(plan.dst, m), grab(plan.size, m),
+                    grab(plan.chunk_begin, m + 1))
+    finally:
+        lib.kvcopy_plan_free(ctypes.byref(plan))
+
+
+def kvcopy_batch(src_addrs, dst_addrs, sizes, dir: int, max_wgs: int = WGS_ALL,
+                 stream=None, *, chunk_bytes: int = 0, flags: int = 0,
+                 kernel_begin=None, kernel_end=None, check: bool = True) -> int:
+    """Enqueue the batch on `stream` (see include/kvcopy.h).
+
+    With any option given, calls kvcopy_batch_ex.  kernel_begin/kernel_end
+    are raw hipEvent_t handles (ints).  Raises KvcopyError on failure unless
+    check=False, in which case the status code is returned.
+    """
+    s, sp = _u64(src_addrs)
+    d, dp = _u64(dst_addrs)
+    z, zp = _u64(sizes)
+    n = _n(s, d, z)
+    st = ctypes.c_void_p(int(stream) if stream else 0)
+    if chunk_bytes or flags or kernel_begin or kernel_end:
+        o = Opts(ctypes.sizeof(Opts), int(chunk_bytes), int(flags), 0,
+                 ctypes.c_void_p(int(kernel_begin) if kernel_begin else 0),
+                 ctypes.c_void_p(int(kernel_end) if kernel_end else 0))
+        rc = lib.kvcopy_batch_ex(sp, dp, zp, n, int(dir), int(max_wgs), st, ctypes.byref(o))
+    else:
+        rc = lib.kvcopy_batch(sp, dp, zp, n, int(dir), int(max_wgs), st)
+    if check and rc != OK:
+        raise KvcopyError(rc, "kvcopy_batch")
+    return rc
+
+
+def kvcopy_host_alloc_mapped(nbytes: int) -> int:
+    """Mapped pinned host memory; returns its address (same on host and GPU)."""
+    p = ctypes.c_void_p(0)
+    rc = lib.kvcopy_host_alloc_mapped(int(nbytes), ctypes.byref(p))
+    if rc != OK:
+        raise KvcopyError(rc, "kvcopy_host_alloc_mapped")
+    return int(p.value)
+
+
+def kvcopy_host_free(ptr: int) -> None:
+    rc = lib.kvcopy_host_free(ctypes.c_void_p(int(ptr) if ptr else 0))
+    if rc != OK:
+        raise KvcopyError(rc, "kvcopy_host_free")
+
+
+class HostBuffer:
+    """Mapped pinned host memory viewed as a NumPy uint8 array."""
+
+    def __init__(self, nbytes: int):
+        self.nbytes = int(nbytes)
+        self.ptr = kvcopy_host_alloc_mapped(self.nbytes)
+        self.array = np.ctypeslib.as_array((ctypes.c_uint8 * self.nbytes).from_address(self.ptr))
+
+    def free(self):
+        if self.ptr:
+            self.array = None
+            kvcopy_host_free(self.ptr)
+            self.ptr = 0
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:
+            pass

@@ -1,0 +1,214 @@
+/*
+ * kvcopy.h -- C ABI of the batched descriptor copy for AMD Instinct MI355X (gfx950).
+ *
+ * One call moves a batch of n descriptors (src_addr, dst_addr, size): raw
+ * device-visible addresses and byte counts of small, non-contiguous blocks
+ * such as KV-cache pages or MoE expert bank rows.  Blocks move between
+ * mapped pinned host memory and HBM (H2D, D2H) or within HBM (D2D).  The
+ * whole batch costs one descriptor upload and one kernel launch, instead of
+ * one DMA memcpy per fragment.
+ *
+ * Sources (cited by page title and section):
+ *   [PF]  PegaFlow issue #408, "Kernel transfer backend causes decode TPOT
+ *         tail spikes under concurrent KV transfers".
+ *   [VL]  vLLM PR #42212 report, "[Perf] Triton fast path for small CPU->GPU
+ *         swap_blocks_batch in the offloading connector".
+ *   [FT]  FreeToken issue #751, "[Perf] Offloaded decode: gather missed
+ *         experts with a few TMA bulk-copy CTAs (cp.async.bulk, .shared::cta)
+ *         instead of 48 x 1024 LDG threads".
+ *
+ * Conventions shared by every entry point:
+ *   - Every function returns KVCOPY_OK (0) or a negative KVCOPY_E* code.
+ *     Nothing aborts, throws or prints.
+ *   - Invalid arguments are rejected before anything is enqueued.
+ *   - Descriptor arrays are three parallel host arrays of n uint64 values,
+ *     the layout of the three int64 address/size tensors in [VL] "key source
+ *     snippet".  The caller owns them; no entry point keeps a pointer to them
+ *     after it returns.
+ *   - Addresses must be device-visible: device memory, or mapped pinned host
+ *     memory whose device address equals its host address (see
+ *     kvcopy_host_alloc_mapped).  Every address and every size must be a
+ *     multiple of 8 bytes.  A size that is not a multiple of 8 is rejected,
+ *     never truncated.
+ *   - Destinations must not overlap each other or any source (memcpy, not
+ *     memmove, semantics).  This is checked only in validate mode; otherwise
+ *     such input is undefined.  Sources may overlap each other.
+ *   - The result of a batch is exactly that of one memcpy per descriptor;
+ *     under the rule above it does not depend on descriptor order, on the
+ *     chunk size, on max_wgs or on dir.
+ */
+#ifndef KVCOPY_H
+#define KVCOPY_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h> /* hipStream_t, hipEvent_t only */
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Direction hint.  It selects tuning only (which side is host-mapped); the
+ * bytes moved never depend on it.  [PF] "Test setup": H2D and D2H are
+ * submitted concurrently on separate streams. */
+enum {
+    KVCOPY_H2D = 0, /* src in mapped pinned host memory, dst in device memory */
+    KVCOPY_D2H = 1, /* src in device memory, dst in mapped pinned host memory */
+    KVCOPY_D2D = 2  /* both in device memory */
+};
+
+/* Status codes. */
+enum {
+    KVCOPY_OK = 0,
+    KVCOPY_EINVAL = -1,   /* null pointer with n > 0, bad dir, max_wgs < 0, bad option, n too large */
+    KVCOPY_EALIGN = -2,   /* an address or size is not a multiple of 8 bytes */
+    KVCOPY_EOVERLAP = -3, /* validate mode: destinations overlap each other or a source */
+    KVCOPY_ENOMEM = -4,   /* host or device allocation failed */
+    KVCOPY_EHIP = -5      /* a HIP call failed; kvcopy_last_hip_error() has its code */
+};
+
+/* max_wgs == KVCOPY_WGS_ALL: one wavefront per chunk (the full grid).  The
+ * "current full grid" of [PF] "Relevant implementation" launched one block
+ * per descriptor. */
+#define KVCOPY_WGS_ALL 0
+
+/* Default chunk size: [FT] "What we changed" cuts the call's rows into
+ * chunks of up to 16 KiB, each inside one row. */
+#define KVCOPY_CHUNK_DEFAULT 16384u
+#define KVCOPY_CHUNK_MAX (1u << 20)
+
+/* Largest accepted n and largest number of chunks in one call. */
+#define KVCOPY_MAX_DESCS ((uint64_t)1 << 31)
+#define KVCOPY_MAX_CHUNKS ((uint64_t)1 << 31)
+
+/* Option flags for kvcopy_batch_ex. */
+#define KVCOPY_F_VALIDATE 0x1u    /* check the overlap rule (O(n log n)); also on when KVCOPY_VALIDATE=1 */
+#define KVCOPY_F_NO_COALESCE 0x2u /* skip merging of adjacent ranges (for measurement only) */
+#define KVCOPY_F_DESC_MAPPED 0x4u /* the kernel reads the chunk worklist in place from pinned host
+                                     staging instead of an uploaded device copy */
+
+/*
+ * kvcopy_coalesce -- merge list-consecutive adjacent ranges.
+ *
+ * [PF] "Relevant implementation": the memcpy backend merges adjacent ranges
+ * and submits one copy per merged range.  Rule: one pass in list order, no
+ * sort; zero-size descriptors are dropped; a descriptor joins the range
+ * built so far when it starts where that range ends in BOTH source and
+ * destination.  Host-only: no GPU work, no allocation.
+ *
+ * in:  src, dst, sizes -- n entries each (may be NULL when n == 0).
+ * out: out_src, out_dst, out_sizes -- room for n entries; they may be the
+ *      same arrays as the inputs (in-place).  *out_n receives the count m <= n.
+ * errors: KVCOPY_EINVAL for a NULL array with n > 0 or a NULL out_n.
+ *         No alignment check is made here.
+ */
+int kvcopy_coalesce(const uint64_t *src, const uint64_t *dst, const uint64_t *sizes, uint64_t n,
+                    uint64_t *out_src, uint64_t *out_dst, uint64_t *out_sizes, uint64_t *out_n);
+
+/*
+ * kvcopy_plan -- validate, coalesce and chunk a batch (host-only).
+ *
+ * [FT] "What we changed": the call's total bytes are cut into chunks of at
+ * most chunk_bytes that never cross a range.  Merged range i of size s_i
+ * owns c_i = ceil(s_i / chunk_bytes) chunks, numbered from chunk_begin[i] =
+ * sum of c_j over j < i (an exclusive prefix sum); chunk k of range i covers
+ * bytes [(k - chunk_begin[i]) * chunk_bytes, min(... + chunk_bytes, s_i)).
+ *
+ * chunk_bytes: 0 = KVCOPY_CHUNK_DEFAULT; else a multiple of 16, at most
+ *              KVCOPY_CHUNK_MAX (else KVCOPY_EINVAL).
+ * out: filled on success; the plan owns its arrays (release with
+ *      kvcopy_plan_free).  src/dst/size have n_merged entries, chunk_begin
+ *      n_merged + 1.
+ * errors: KVCOPY_EINVAL, KVCOPY_EALIGN, KVCOPY_EOVERLAP (validate mode:
+ *         KVCOPY_VALIDATE=1 in the environment), KVCOPY_ENOMEM.
+ */
+typedef struct {
+    uint64_t n_in;        /* descriptors given */
+    uint64_t n_merged;    /* ranges after dropping zero sizes and merging */
+    uint64_t n_chunks;    /* chunk_begin[n_merged] */
+    uint64_t total_bytes; /* sum of sizes */
+    uint32_t chunk_bytes;
+    uint32_t reserved;
+    const uint64_t *src, *dst, *size; /* n_merged entries each */
+    const uint64_t *chunk_begin;      /* n_merged + 1 entries */
+} kvcopy_plan_t;
+
+int kvcopy_plan(const uint64_t *src, const uint64_t *dst, const uint64_t *sizes, uint64_t n,
+                uint32_t chunk_bytes, kvcopy_plan_t *out);
+void kvcopy_plan_free(kvcopy_plan_t *plan);
+
+/*
+ * kvcopy_batch -- enqueue the whole batch on `stream`; no host sync.
+ *
+ * [PF] "Summary": one descriptor upload and one copy-kernel launch replace
+ * many directional memcpy submissions; "Follow-up", item 2: the transfer
+ * contract is enqueue-only.  [VL] "key source snippet": the descriptor
+ * arrays go to the GPU asynchronously from pinned buffers, then one
+ * persistent copy kernel runs.
+ *
+ * The library plans the batch (coalesce, chunk), writes the chunk worklist
+ * into its own pinned staging slot, uploads it with one async copy on
+ * `stream`, and launches one kernel of min(max_wgs, needed) workgroups of 4
+ * wavefronts on `stream`.  Wavefronts take chunks round-robin and move them
+ * with 16-byte nontemporal loads and stores.
+ *
+ * src_addrs, dst_addrs, sizes: n entries (host arrays; may be NULL if n == 0).
+ * n:       0 is a valid empty call (returns KVCOPY_OK, enqueues nothing).
+ * dir:     KVCOPY_H2D / KVCOPY_D2H / KVCOPY_D2D (tuning only).
+ * max_wgs: workgroup cap ([PF] "Follow-up", item 1: a bounded grid; "Proposed
+ *          direction": max_grid_blocks).  KVCOPY_WGS_ALL (0) = one wavefront
+ *          per chunk.  Negative = KVCOPY_EINVAL.
+ * stream:  HIP stream (NULL = the null stream).
+ * Ownership: the descriptor arrays may be reused as soon as the call
+ *          returns.  The payload memory must stay valid, and unwritten by
+ *          others, until the stream has passed the copy.
+ * Threads: calls from several threads on several streams are safe.
+ * errors:  KVCOPY_EINVAL, KVCOPY_EALIGN, KVCOPY_EOVERLAP (validate mode),
+ *          KVCOPY_ENOMEM, KVCOPY_EHIP.  On KVCOPY_EHIP the stream may hold
+ *          part of the work.
+ */
+int kvcopy_batch(const uint64_t *src_addrs, const uint64_t *dst_addrs, const uint64_t *sizes,
+                 uint64_t n, int dir, int max_wgs, hipStream_t stream);
+
+/* Options for kvcopy_batch_ex.  Zero-initialise, then set struct_size. */
+typedef struct {
+    uint32_t struct_size;   /* sizeof(kvcopy_opts_t) */
+    uint32_t chunk_bytes;   /* 0 = default; else a multiple of 16, <= KVCOPY_CHUNK_MAX */
+    uint32_t flags;         /* KVCOPY_F_* */
+    uint32_t reserved;
+    hipEvent_t kernel_begin; /* if non-NULL: recorded on stream just before the copy kernel */
+    hipEvent_t kernel_end;   /* if non-NULL: recorded on stream just after the copy kernel */
+} kvcopy_opts_t;
+
+/*
+ * kvcopy_batch_ex -- kvcopy_batch with options (chunk size, flags, and
+ * events that bracket the copy kernel alone for timing).  opts may be NULL
+ * (= kvcopy_batch).  Errors as kvcopy_batch, plus KVCOPY_EINVAL for a bad
+ * struct_size, chunk_bytes or unknown flag.
+ */
+int kvcopy_batch_ex(const uint64_t *src_addrs, const uint64_t *dst_addrs, const uint64_t *sizes,
+                    uint64_t n, int dir, int max_wgs, hipStream_t stream,
+                    const kvcopy_opts_t *opts);
+
+/* Static text for a status code ("unknown status" for others). */
+const char *kvcopy_strerror(int code);
+
+/* The hipError_t of this thread's last failed HIP call (0 if none). */
+int kvcopy_last_hip_error(void);
+
+/*
+ * kvcopy_host_alloc_mapped -- pinned host memory that the GPU can address
+ * at the same virtual address ([PF] "Test setup": the host payload is mapped
+ * pinned memory).  bytes > 0; *out receives the pointer.
+ * errors: KVCOPY_EINVAL (bytes == 0 or out NULL), KVCOPY_ENOMEM, KVCOPY_EHIP
+ * (also if the device address differs from the host address).
+ */
+int kvcopy_host_alloc_mapped(uint64_t bytes, void **out);
+
+/* Release memory from kvcopy_host_alloc_mapped.  NULL is a no-op. */
+int kvcopy_host_free(void *p);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVCOPY_H */

@@ -1,0 +1,233 @@
+"""GPU parity: the HIP path through the C ABI against the oracle, bit-exact.
+
+Every case builds the workload's arenas on the GPU (device memory, mapped
+pinned host memory), runs kvcopy_batch, reads every touched arena back
+whole (guard bytes included) and compares it with the oracle's image of the
+same seeded inputs.  Several cases are repeated with a second sentinel so
+that a payload byte equal to the sentinel cannot hide a skipped copy.
+"""
+import numpy as np
+import pytest
+
+import workloads as W
+from expect import assert_same, expected_images
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+WGS = [1, 8, 32, 128, 0]
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+
+
+@pytest.fixture(scope="module")
+def K():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from block_copy_amd import kvcopy
+    return kvcopy
+
+
+def _check(res, batch_ids, what, sentinel=None):
+    wl = res.wl
+    exp = expected_images(wl, batch_ids, res.bases, sentinel)
+    for i, img in enumerate(exp):
+        if img is None:
+            continue
+        bi = next((k for k in batch_ids if i in set(wl.batches[k].dst_arena.tolist())), None)
+        assert_same(res.image(i), img, f"{what} arena {wl.arenas[i].name}", wl, bi, res.bases, i)
+
+
+def _run(res, batch_ids, max_wgs, streams=None, **kw):
+    if streams is None:
+        for k in batch_ids:
+            res.submit(k, max_wgs, None, **kw)
+    else:
+        for k, st in zip(batch_ids, streams):
+            res.submit(k, max_wgs, st, **kw)
+    torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------------------
+# D2D blocks: 1,024 x 4 KiB between two pools of 4,096 blocks
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("max_wgs", WGS)
+def test_d2d_blocks_full(K, max_wgs):
+    from block_copy_amd.harness import Resident
+    wl = W.d2d_blocks(seed=0)
+    res = Resident(wl)
+    for sentinel in (W.SENTINEL_A, W.SENTINEL_B):
+        _say("d2d 1024x4KiB", "max_wgs", max_wgs, "sentinel", hex(sentinel))
+        res.fill(sentinel)
+        _run(res, [0], max_wgs)
+        _check(res, [0], f"d2d max_wgs={max_wgs}", sentinel)
+    res.free()
+
+
+# ---------------------------------------------------------------------------
+# H2D / D2H: 16,384 shuffled x 4 KiB against a 65,536-block pool
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("max_wgs", WGS)
+@pytest.mark.parametrize("direction", ["h2d", "d2h"])
+def test_kv_blocks_one_direction(K, direction, max_wgs):
+    from block_copy_amd.harness import Resident
+    wl = W.kv_blocks(seed=1, directions=direction)
+    res = Resident(wl)
+    _say("kv", direction, "16384x4KiB max_wgs", max_wgs)
+    _run(res, [0], max_wgs)
+    _check(res, [0], f"{direction} max_wgs={max_wgs}")
+    res.free()
+
+
+@pytest.mark.parametrize("max_wgs", [8, 128, 0])
+def test_kv_blocks_concurrent(K, max_wgs):
+    from block_copy_amd.harness import Resident
+    wl = W.kv_blocks(seed=2, directions="both")
+    res = Resident(wl)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    for sentinel in (W.SENTINEL_A, W.SENTINEL_B):
+        _say("kv both concurrent max_wgs", max_wgs, "sentinel", hex(sentinel))
+        res.fill(sentinel)
+        _run(res, [0, 1], max_wgs, streams=[s1, s2])
+        _check(res, [0, 1], f"h2d+d2h max_wgs={max_wgs}", sentinel)
+    res.free()
+
+
+# ---------------------------------------------------------------------------
+# H2D mixed sizes with partial adjacency (coalescing, 8-byte tails)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n", [16, 256, 4096, 65536])
+def test_h2d_mixed(K, n):
+    from block_copy_amd.harness import Resident
+    wl = W.h2d_mixed(seed=3, n=n)
+    res = Resident(wl)
+    for max_wgs in ([1, 32, 0] if n <= 4096 else [64, 0]):
+        _say("h2d mixed n", n, "max_wgs", max_wgs)
+        res.fill()
+        _run(res, [0], max_wgs)
+        _check(res, [0], f"h2d mixed n={n} max_wgs={max_wgs}")
+    res.free()
+
+
+# ---------------------------------------------------------------------------
+# MoE expert gather
+# ---------------------------------------------------------------------------
+
+def test_moe_gather_reduced_many_calls(K):
+    """Successive calls on one stream (more calls than staging slots)."""
+    from block_copy_amd.harness import Resident
+    wl = W.moe_gather(seed=4, calls=12, n_experts=32, n_slots=96, misses=(5, 20))
+    res = Resident(wl)
+    _say("moe reduced 12 calls")
+    _run(res, list(range(12)), 16)
+    _check(res, list(range(12)), "moe reduced 12 calls")
+    res.free()
+
+
+def test_moe_gather_full_size(K):
+    """256 experts x 6 banks on the host, 3,164 slots on the device (5.3 GB)."""
+    from block_copy_amd.harness import Resident
+    wl = W.moe_gather(seed=5, calls=3)
+    res = Resident(wl)
+    for max_wgs in (32, 0):
+        _say("moe full size 3 calls max_wgs", max_wgs)
+        res.fill()
+        _run(res, [0, 1, 2], max_wgs)
+        _check(res, [0, 1, 2], f"moe full max_wgs={max_wgs}")
+    res.free()
+
+
+# ---------------------------------------------------------------------------
+# Irregular batches: misaligned (8 mod 16), zero sizes, shared sources,
+# every direction, chunk sizes, flags
+# ---------------------------------------------------------------------------
+
+DIRS = {"d2d": (W.D2D, "device", "device"), "h2d": (W.H2D, "host", "device"),
+        "d2h": (W.D2H, "device", "host")}
+
+
+@pytest.mark.parametrize("dname", sorted(DIRS))
+@pytest.mark.parametrize("chunk", [16, 1024, 4096, 16384, 65536, 1 << 20])
+def test_irregular_chunk_sizes(K, dname, chunk):
+    from block_copy_amd.harness import Resident
+    d, sw, dw = DIRS[dname]
+    wl = W.irregular(seed=chunk % 97, n=200, max_size=min(80 * 1024, 256 * chunk), dir_=d,
+                     src_where=sw, dst_where=dw, misalign=True, zero_frac=0.05)
+    res = Resident(wl)
+    for max_wgs in (1, 7, 0):
+        _say("irregular", dname, "chunk", chunk, "max_wgs", max_wgs)
+        res.fill()
+        _run(res, [0], max_wgs, chunk_bytes=chunk)
+        _check(res, [0], f"irregular {dname} chunk={chunk} max_wgs={max_wgs}")
+    res.free()
+
+
+@pytest.mark.parametrize("flags", [1, 2, 4, 6])
+def test_irregular_flags(K, flags):
+    from block_copy_amd.harness import Resident
+    wl = W.irregular(seed=40 + flags, n=500, dir_=W.H2D, src_where="host", dst_where="device",
+                     shared_src=(flags == 4))
+    res = Resident(wl)
+    _say("irregular flags", flags)
+    _run(res, [0], 16, flags=flags)
+    _check(res, [0], f"irregular flags={flags}")
+    res.free()
+
+
+def test_tiny_and_empty(K):
+    from block_copy_amd.harness import Resident
+    wl = W.irregular(seed=50, n=3, max_size=24, dir_=W.D2D)
+    res = Resident(wl)
+    _say("tiny and empty")
+    assert K.kvcopy_batch([], [], [], K.D2D) == 0                       # n = 0
+    s, d = res.addrs[0]
+    assert K.kvcopy_batch(s, d, np.zeros(3, np.uint64), K.D2D) == 0     # only zero sizes
+    torch.cuda.synchronize()
+    for i, a in enumerate(wl.arenas):
+        if a.fill == "sentinel":
+            assert np.all(res.image(i) == a.sentinel)
+    _run(res, [0], 0)
+    _check(res, [0], "tiny")
+    res.free()
+
+
+def test_order_independence(K):
+    """A shuffled descriptor list gives the same bytes (distinct destinations)."""
+    from block_copy_amd.harness import Resident
+    wl = W.irregular(seed=60, n=400, dir_=W.D2D)
+    res = Resident(wl)
+    b = wl.batches[0]
+    perm = np.random.default_rng(0).permutation(b.n)
+    s, d = res.addrs[0]
+    _say("order independence")
+    K.kvcopy_batch(s[perm], d[perm], b.size[perm], K.D2D, 8)
+    torch.cuda.synchronize()
+    _check(res, [0], "shuffled order")
+    res.free()
+
+
+def test_error_paths_enqueue_nothing(K):
+    from block_copy_amd.harness import Resident
+    wl = W.irregular(seed=70, n=50, dir_=W.D2D)
+    res = Resident(wl)
+    s, d = res.addrs[0]
+    z = wl.batches[0].size.copy()
+    _say("error paths")
+    bad = z.copy()
+    bad[7] += 4
+    assert K.kvcopy_batch(s, d, bad, K.D2D, check=False) == K.EALIGN
+    assert K.kvcopy_batch(s, d, z, 5, check=False) == K.EINVAL
+    assert K.kvcopy_batch(s, d, z, K.D2D, -1, check=False) == K.EINVAL
+    dd = d.copy()
+    dd[3] = dd[2]                                     # two descriptors write the same bytes
+    assert K.kvcopy_batch(s, dd, z, K.D2D, flags=K.F_VALIDATE, check=False) == K.EOVERLAP
+    torch.cuda.synchronize()
+    for i, a in enumerate(wl.arenas):
+        if a.fill == "sentinel":
+            assert np.all(res.image(i) == a.sentinel), "an error path enqueued work"
+    res.free()

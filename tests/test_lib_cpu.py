@@ -1,0 +1,198 @@
+"""CPU-side checks of libkvcopy.so: exports, host planner parity with the
+oracle's planning steps (bit-exact), argument validation.  No GPU needed:
+every call here either is host-only or fails validation before any HIP call.
+"""
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import plan as oplan
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def K():
+    from block_copy_amd import kvcopy
+    return kvcopy
+
+
+def _declared():
+    names = []
+    for h in os.listdir(os.path.join(ROOT, "include")):
+        if h.endswith(".h"):
+            txt = open(os.path.join(ROOT, "include", h)).read()
+            names += re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(kvcopy_\w+)\s*\(", txt, re.M)
+    return sorted(set(names))
+
+
+def test_header_symbols_are_exported(K):
+    declared = _declared()
+    assert len(declared) >= 9
+    assert sorted(K.EXPORTS) == declared
+    out = subprocess.run(["nm", "-D", "--defined-only", K.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (kvcopy_\w+)", out))
+    for name in declared:
+        assert name in exported, name
+        assert hasattr(K.lib, name)
+
+
+def test_kernel_has_no_scratch(K):
+    """The copy kernel must not spill to private (scratch) memory."""
+    tmp = os.path.join(ROOT, "_build")
+    os.makedirs(tmp, exist_ok=True)
+    out = os.path.join(tmp, "kernel_meta.s")
+    subprocess.run(["hipcc", "--offload-arch=gfx950", "-O3", "-std=c++17", "--cuda-device-only", "-S",
+                    "-I" + os.path.join(ROOT, "include"),
+                    "-I" + os.path.join(ROOT, "block_copy_amd", "csrc"),
+                    os.path.join(ROOT, "block_copy_amd", "csrc", "kvcopy_kernel.hip"), "-o", out],
+                   check=True, capture_output=True)
+    txt = open(out).read()
+    sizes = re.findall(r"\.private_segment_fixed_size:\s+(\d+)", txt)
+    assert sizes and all(int(s) == 0 for s in sizes)
+
+
+# ---------------------------------------------------------------------------
+# Planner parity with the oracle (integer work: bit-exact)
+# ---------------------------------------------------------------------------
+
+def _addr(wl, b):
+    bases = [(i + 1) << 36 for i in range(len(wl.arenas))]
+    return b.addresses(bases)
+
+
+@pytest.mark.parametrize("make", [
+    lambda: W.h2d_mixed(seed=0, n=16),
+    lambda: W.h2d_mixed(seed=1, n=4096),
+    lambda: W.h2d_mixed(seed=2, n=65536),
+    lambda: W.kv_blocks(seed=0, directions="h2d"),
+    lambda: W.moe_gather(seed=0, calls=1),
+    lambda: W.irregular(seed=5, n=1000, zero_frac=0.1),
+])
+@pytest.mark.parametrize("chunk", [0, 16, 4096, 8192, 65536])
+def test_plan_matches_oracle(K, make, chunk):
+    wl = make()
+    b = wl.batches[0]
+    s, d = _addr(wl, b)
+    p = K.kvcopy_plan(s, d, b.size, chunk)
+    C = chunk or K.CHUNK_DEFAULT
+    es, ed, ez = oplan.coalesce(s, d, b.size)
+    assert p.n_in == b.n
+    assert p.n_merged == len(ez)
+    assert p.src.tolist() == es and p.dst.tolist() == ed and p.size.tolist() == ez
+    assert p.chunk_begin.tolist() == oplan.chunk_begin(ez, C)
+    assert p.n_chunks == p.chunk_begin[-1]
+    assert p.total_bytes == int(b.size.sum())
+    assert p.chunk_bytes == C
+
+
+def test_coalesce_matches_oracle_and_golden(K):
+    import json
+    cases = json.load(open(os.path.join(ROOT, "tests", "golden", "coalesce_cases.json")))["cases"]
+    for c in cases:
+        a = np.array(c["in"], dtype=np.uint64).reshape(-1, 3)
+        out = K.kvcopy_coalesce(a[:, 0], a[:, 1], a[:, 2])
+        assert [list(map(int, x)) for x in zip(*out)] == c["out"], c["name"]
+    rng = np.random.default_rng(9)
+    for _ in range(300):
+        n = int(rng.integers(0, 40))
+        s = (8 * rng.integers(0, 50, n)).astype(np.uint64)
+        d = (8 * rng.integers(0, 50, n)).astype(np.uint64)
+        z = (8 * rng.integers(0, 3, n)).astype(np.uint64)
+        # force some chains
+        for i in range(1, n):
+            if rng.random() < 0.4:
+                s[i] = s[i - 1] + z[i - 1]
+                d[i] = d[i - 1] + z[i - 1]
+        got = K.kvcopy_coalesce(s, d, z)
+        exp = oplan.coalesce(s, d, z)
+        assert [g.tolist() for g in got] == [list(e) for e in exp]
+
+
+def test_coalesce_in_place(K):
+    import ctypes
+    s = np.array([0, 8, 16, 100 * 8], np.uint64)
+    d = np.array([64, 72, 80, 8], np.uint64)
+    z = np.array([8, 8, 8, 8], np.uint64)
+    m = ctypes.c_uint64()
+    p = lambda x: x.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64))  # noqa: E731
+    rc = K.lib.kvcopy_coalesce(p(s), p(d), p(z), 4, p(s), p(d), p(z), ctypes.byref(m))
+    assert rc == 0 and m.value == 2
+    assert s[:2].tolist() == [0, 800] and d[:2].tolist() == [64, 8] and z[:2].tolist() == [24, 8]
+
+
+# ---------------------------------------------------------------------------
+# Argument validation: errors come back before anything touches the GPU
+# ---------------------------------------------------------------------------
+
+def test_batch_argument_errors(K):
+    s = np.array([0x10000, 0x20000], np.uint64)
+    d = np.array([0x30000, 0x40000], np.uint64)
+    z = np.array([4096, 4096], np.uint64)
+    call = lambda *a, **k: K.kvcopy_batch(*a, check=False, **k)  # noqa: E731
+    assert call([], [], [], K.H2D) == K.OK                       # empty call
+    assert call(s, d, np.zeros(2, np.uint64), K.H2D) == K.OK     # only zero sizes
+    assert call(s, d, z + 4, K.H2D) == K.EALIGN                   # size not a multiple of 8
+    assert call(s + 4, d, z, K.D2H) == K.EALIGN                   # misaligned source
+    assert call(s, d + 12, z, K.D2D) == K.EALIGN                  # misaligned destination
+    assert call(s, d, z, 3) == K.EINVAL                            # bad direction
+    assert call(s, d, z, -1) == K.EINVAL
+    assert call(s, d, z, K.H2D, -5) == K.EINVAL                    # negative max_wgs
+    assert call(s, d, z, K.H2D, chunk_bytes=24) == K.EINVAL        # chunk not a multiple of 16
+    assert call(s, d, z, K.H2D, chunk_bytes=(1 << 20) + 16) == K.EINVAL
+    assert call(s, d, z, K.H2D, flags=0x100) == K.EINVAL          # unknown flag
+    wrap = np.array([2**64 - 4096], np.uint64)
+    assert call(wrap, d[:1], z[:1], K.H2D) == K.EINVAL             # address range wraps
+    dup = np.array([0x30000, 0x30800], np.uint64)
+    assert call(s, dup, z, K.H2D, flags=K.F_VALIDATE) == K.EOVERLAP  # destinations overlap
+    over = np.array([0x30000, 0x10800], np.uint64)
+    assert call(s, over, z, K.H2D, flags=K.F_VALIDATE) == K.EOVERLAP  # a destination overlaps a source
+
+
+def test_null_pointers_and_struct_size(K):
+    import ctypes
+    u = ctypes.POINTER(ctypes.c_uint64)()
+    assert K.lib.kvcopy_batch(u, u, u, 3, 0, 0, None) == K.EINVAL
+    assert K.lib.kvcopy_batch(u, u, u, 0, 0, 0, None) == K.OK
+    o = K.Opts(ctypes.sizeof(K.Opts) - 8, 0, 0, 0, None, None)
+    s = np.array([0], np.uint64)
+    p = s.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64))
+    assert K.lib.kvcopy_batch_ex(p, p, p, 1, 0, 0, None, ctypes.byref(o)) == K.EINVAL
+    m = ctypes.c_uint64()
+    assert K.lib.kvcopy_coalesce(u, u, u, 2, u, u, u, ctypes.byref(m)) == K.EINVAL
+    assert K.lib.kvcopy_coalesce(u, u, u, 0, u, u, u, None) == K.EINVAL
+    assert K.lib.kvcopy_plan(u, u, u, 0, 0, None) == K.EINVAL
+    assert K.lib.kvcopy_host_alloc_mapped(0, ctypes.byref(ctypes.c_void_p())) == K.EINVAL
+    assert K.lib.kvcopy_host_free(None) == K.OK
+    assert K.kvcopy_strerror(12345) == "unknown status"
+
+
+def test_validate_env_is_strict(K, monkeypatch):
+    s = np.array([0x10000, 0x20000], np.uint64)
+    dup = np.array([0x30000, 0x30800], np.uint64)
+    z = np.array([4096, 4096], np.uint64)
+    monkeypatch.setenv("KVCOPY_VALIDATE", "1")
+    assert K.kvcopy_batch(s, dup, z, K.H2D, check=False) == K.EOVERLAP
+    with pytest.raises(K.KvcopyError):
+        K.kvcopy_plan(s, dup, z)
+    monkeypatch.setenv("KVCOPY_VALIDATE", "yes")                  # unknown value: rejected
+    assert K.kvcopy_batch(s, dup, z, K.H2D, check=False) == K.EINVAL
+    monkeypatch.setenv("KVCOPY_VALIDATE", "0")
+    p = K.kvcopy_plan(s, dup, z)                                  # not validated: planned as given
+    assert p.n_merged == 2
+
+
+def test_plan_edge_cases(K):
+    p = K.kvcopy_plan([], [], [])
+    assert p.n_in == 0 and p.n_merged == 0 and p.n_chunks == 0 and p.chunk_begin.tolist() == [0]
+    p = K.kvcopy_plan([8], [1 << 20], [K.CHUNK_MAX], K.CHUNK_MAX)
+    assert p.n_chunks == 1
+    p = K.kvcopy_plan([8], [1 << 20], [8], 16)
+    assert p.n_chunks == 1 and p.size.tolist() == [8]
+    with pytest.raises(K.KvcopyError):
+        K.kvcopy_plan([8], [16], [8], 8)           # chunk must be a multiple of 16

@@ -1,0 +1,85 @@
+"""The seeded generators keep every descriptor inside its arenas and follow the
+contract (distinct destinations, no destination overlapping a source), and
+produce the shapes the workloads call for.  Checked on the CPU before any of
+their descriptors reach the GPU."""
+import numpy as np
+import pytest
+
+import workloads as W
+
+
+def _check_contract(wl):
+    for b in wl.batches:
+        for arena_ids, offs, role in ((b.src_arena, b.src_off, "src"), (b.dst_arena, b.dst_off, "dst")):
+            lens = np.array([wl.arenas[i].nbytes for i in arena_ids], np.uint64)
+            assert np.all(offs + b.size <= lens), f"{wl.name}: {role} outside its arena"
+            assert np.all(offs % 8 == 0) and np.all(b.size % 8 == 0)
+        # destinations disjoint within a batch
+        key = b.dst_arena.astype(np.uint64) << np.uint64(48) | b.dst_off
+        order = np.argsort(key, kind="stable")
+        k, z = key[order], b.size[order]
+        nz = z > 0
+        k, z = k[nz], z[nz]
+        assert np.all(k[1:] >= k[:-1] + z[:-1]), f"{wl.name}: overlapping destinations"
+        # no destination arena is also a source arena of the same batch
+        assert not set(b.src_arena.tolist()) & set(b.dst_arena.tolist())
+    if len(wl.batches) > 1 and not wl.info.get("sequential"):
+        # concurrent batches: one's destinations never touch another's bytes
+        spans = []
+        for b in wl.batches:
+            spans.append({(int(a), int(o), int(z)) for a, o, z in zip(b.dst_arena, b.dst_off, b.size)})
+        for i, b in enumerate(wl.batches):
+            for j, other in enumerate(wl.batches):
+                if i == j:
+                    continue
+                mine = {(int(a), int(o)) for a, o in zip(b.src_arena, b.src_off)}
+                theirs = {(a, o) for a, o, _ in spans[j]}
+                assert not mine & theirs
+
+
+@pytest.mark.parametrize("make", [
+    lambda: W.d2d_blocks(seed=0),
+    lambda: W.d2d_blocks(seed=1, n=65536, pool_blocks=262144),
+    lambda: W.kv_blocks(seed=0, directions="both"),
+    lambda: W.kv_blocks(seed=1, directions="h2d"),
+    lambda: W.kv_blocks(seed=1, directions="d2h"),
+    lambda: W.h2d_mixed(seed=0, n=16),
+    lambda: W.h2d_mixed(seed=0, n=65536),
+    lambda: W.moe_gather(seed=0, calls=4),
+    lambda: W.moe_gather(seed=4, calls=12, n_experts=32, n_slots=96, misses=(5, 20)),
+    lambda: W.irregular(seed=1, n=300),
+    lambda: W.irregular(seed=2, n=300, shared_src=True),
+    lambda: W.irregular(seed=3, n=300, zero_frac=0.2, misalign=False),
+])
+def test_generators_respect_contract(make):
+    _check_contract(make())
+
+
+def test_shapes():
+    wl = W.kv_blocks(seed=0, directions="both")
+    assert [b.n for b in wl.batches] == [16384, 16384]
+    assert all(b.nbytes == 64 * W.MIB for b in wl.batches)
+    assert wl.arenas[0].nbytes == 65536 * 4096
+    h2d = wl.batches[0]
+    assert sorted((h2d.src_off // 4096).tolist()) == list(range(16384))   # a shuffle of the host buffer
+    d = W.d2d_blocks(seed=0)
+    assert d.batches[0].n == 1024 and d.batches[0].nbytes == 4 * W.MIB
+    assert d.arenas[1].fill == "sentinel" and d.arenas[1].sentinel == 0xA5
+    m = W.moe_gather(seed=0, calls=50)
+    for b in m.batches:
+        assert b.n % 6 == 0 and 26 <= b.n // 6 <= 39
+    assert sum(W.MOE_ROWS) == 1679360
+
+
+def test_mixed_size_distribution():
+    rng = np.random.default_rng(0)
+    s = W.mixed_sizes(rng, 200000)
+    assert s.min() >= 4096 and s.max() <= 28672 and np.all(s % 8 == 0)
+    frac_core = np.mean((s >= 8192) & (s <= 16384))
+    assert 0.69 < frac_core < 0.72                 # 70 % in 8-16 KiB (the side set never hits it)
+    assert 0.45 < np.mean(s % 16 == 8) < 0.55      # about half are not 16 B multiples
+    assert 13.5 * 1024 < s.mean() < 14.1 * 1024
+    wl = W.h2d_mixed(seed=0, n=4096)
+    b = wl.batches[0]
+    cont = (b.src_off[1:] == b.src_off[:-1] + b.size[:-1]) & (b.dst_off[1:] == b.dst_off[:-1] + b.size[:-1])
+    assert int(cont.sum()) == 1024                 # exactly a quarter continue their predecessor
