@@ -35,8 +35,37 @@ sys.path.insert(0, ROOT)
 METRIC = "GB/s for batched 4–16 KiB descriptor copies (H2D/D2H/D2D), % of link/HBM peak"
 PCIE_PEAK_GBS = 64.0      # PCIe 5.0 x16, per direction (MI355X host interface)
 HBM_PEAK_GBS = 8000.0     # MI355X HBM3E
-DEFAULT_MAX_WGS = 0
-KERNEL_NAME = "kvcopy_chunks_kernel"
+# Workgroup cap of the headline: with H2D and D2H running together, a few
+# dozen workgroups per direction keep enough bytes in flight to fill the
+# link; the full grid oversubscribes it (see the max_wgs sweep, --sweep).
+DEFAULT_MAX_WGS = 32
+KERNEL_NAMES = {0: "kvcopy_h2d_kernel", 1: "kvcopy_d2h_kernel"}
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters_kv_bidirectional.json")
+KERNEL_SOURCE = os.path.join(ROOT, "block_copy_amd", "csrc", "kvcopy_kernel.hip")
+
+
+def kernel_source_hash():
+    import hashlib
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(kernel):
+    """HBM/host bytes per launch of `kernel` from the committed PMC summary,
+    or None if there is none or the kernel source changed since it was taken."""
+    try:
+        with open(COUNTERS_FILE) as f:
+            c = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if c.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    k = c.get("kernels", {}).get(kernel)
+    if not k:
+        return None
+    return {"fetch_bytes": k["fetch_bytes_per_dispatch_scaled"],
+            "write_bytes": k["write_bytes_per_dispatch_scaled"],
+            "source": os.path.relpath(COUNTERS_FILE, ROOT)}
 
 
 def log(*a):
@@ -58,6 +87,12 @@ def main():
                     help="time budget of the cpu_baseline sample")
     ap.add_argument("--skip-extras", action="store_true",
                     help="only the headline workload (for profiling runs)")
+    ap.add_argument("--no-events", action="store_true",
+                    help="do not bracket kernels with HIP events (profiler runs); the kernel "
+                         "time is then taken as the step time")
+    ap.add_argument("--counter-calibration", action="store_true",
+                    help="also run a plain 64 MiB elementwise copy kernel 5 times, whose "
+                         "known traffic scales the PMC byte counters")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -115,7 +150,10 @@ def main():
 
     max_wgs = args.max_wgs
     log(f"headline: {n_desc} descriptors, {step_bytes} B per step, max_wgs={max_wgs}")
-    step_s, kern_ms = timed(res, [0, 1], [sA, sB], args.steps, args.warmup, max_wgs)
+    step_s, kern_ms = timed(res, [0, 1], [sA, sB], args.steps, args.warmup, max_wgs,
+                            with_events=not args.no_events)
+    if kern_ms is None:
+        kern_ms = [step_s * 1e3, step_s * 1e3]
     value = gbs(step_bytes, step_s)
     log(f"  bidirectional: {step_s * 1e3:.3f} ms/step, {value:.2f} GB/s; kernel ms {kern_ms}")
 
@@ -140,7 +178,7 @@ def main():
         # each direction alone
         alone = {}
         for j, name in ((0, "h2d"), (1, "d2h")):
-            s, km = timed(res, [j], [sA], args.steps, args.warmup, max_wgs)
+            s, km = timed(res, [j], [sA], args.steps, args.warmup, max_wgs)   # extras only
             alone[name] = {"GBps": round(gbs(wl.batches[j].nbytes, s), 3),
                            "ms_per_call": round(s * 1e3, 4), "kernel_ms": round(km[0], 4)}
             log(f"  {name} alone: {alone[name]}")
@@ -192,6 +230,14 @@ def main():
         del dbuf
         hsrc.free()
         hdst.free()
+
+    if args.counter_calibration:
+        a = torch.arange(16 * W.MIB, dtype=torch.int32, device=dev)   # 64 MiB
+        b = torch.empty_like(a)
+        for _ in range(5):
+            torch.neg(a, out=b)
+        torch.cuda.synchronize()
+        del a, b
 
     # ---------------- verification of the headline workload ----------------
     torch.cuda.synchronize()
@@ -280,12 +326,12 @@ def main():
         },
         "roofline": {
             "bound": "pcie",
-            "kernel": f"{KERNEL_NAME} ({('H2D', 'D2H')[dom]})",
+            "kernel": KERNEL_NAMES[dom],
             "achieved": round(ach[dom], 3),
             "peak": PCIE_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(ach[dom] / PCIE_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(KERNEL_NAMES[dom]),
             "kernel_ms": round(kern_ms[dom], 4),
             "algorithmic_bytes_per_launch": algo[dom],
             "measured_ceiling": meas_ceil,

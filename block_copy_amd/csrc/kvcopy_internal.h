@@ -31,7 +31,8 @@ int merge_ranges(const uint64_t *src, const uint64_t *dst, const uint64_t *size,
                  uint64_t *total_out);
 
 // KVCOPY_EOVERLAP if any two destination ranges overlap or a destination
-// overlaps a source range, else KVCOPY_OK.  O(m log m).
+// overlaps a source range, else KVCOPY_OK.  Zero-size entries are ignored.
+// O(m log m).
 int check_overlap(const uint64_t *src, const uint64_t *dst, const uint64_t *size, uint64_t m);
 
 // begin[i] = sum over j < i of ceil(size[j] / chunk); begin has m + 1 entries.
@@ -42,6 +43,27 @@ uint64_t chunk_prefix(const uint64_t *size, uint64_t m, uint32_t chunk, uint64_t
 void emit_chunks(const uint64_t *src, const uint64_t *dst, const uint64_t *size,
                  const uint64_t *begin, uint64_t m, uint32_t chunk, ChunkRec *out);
 
+// Facts about a descriptor list gathered in one read-only pass.
+struct Prescan {
+    uint64_t nnz;    // descriptors with a non-zero size
+    uint64_t total;  // sum of sizes
+    uint64_t bound;  // upper bound on the chunk count after merging: nnz + total / chunk
+};
+
+// One pass over the three input arrays: 8-byte alignment of every address and
+// size (KVCOPY_EALIGN), no range wrapping past 2^64 and no overflowing total
+// (KVCOPY_EINVAL).  Fills *out on success.
+int prescan(const uint64_t *src, const uint64_t *dst, const uint64_t *size, uint64_t n,
+            uint32_t chunk, Prescan *out);
+
+// The batch path's fused planner: one sequential pass that drops zero sizes,
+// merges list-consecutive adjacent ranges (if `merge`) and writes each closed
+// range's chunks straight into `out` (room for Prescan::bound records).
+// Produces exactly the records emit_chunks() gives for merge_ranges()'s
+// output; returns how many it wrote.
+uint64_t build_worklist(const uint64_t *src, const uint64_t *dst, const uint64_t *size, uint64_t n,
+                        bool merge, uint32_t chunk, ChunkRec *out);
+
 // True when KVCOPY_VALIDATE=1 in the environment; any value other than
 // unset, "0" or "1" makes *bad true (strict parsing).
 bool env_validate(bool *bad);
@@ -51,9 +73,10 @@ bool env_validate(bool *bad);
 constexpr uint32_t kWavesPerWG = 4;
 constexpr uint32_t kThreadsPerWG = 64 * kWavesPerWG;
 
-// Launches the copy kernel: `grid` workgroups, wavefronts take chunks
-// round-robin.  recs must be device-readable (device memory or mapped host
-// memory).  Returns the launch status.
+// Launches the copy kernel for `dir` (one kernel symbol per direction, same
+// algorithm): `grid` workgroups, wavefronts take chunks round-robin.  recs
+// must be device-readable (device memory or mapped host memory).  Returns
+// the launch status.
 hipError_t launch_copy(const ChunkRec *recs, uint32_t n_chunks, uint32_t grid, int dir,
                        hipStream_t stream);
 

@@ -104,8 +104,8 @@ __device__ __forceinline__ void copy_chunk(uint64_t src, uint64_t dst, uint32_t 
     }
 }
 
-__global__ __launch_bounds__(kThreadsPerWG) void kvcopy_chunks_kernel(
-    const ChunkRec *__restrict__ recs, uint32_t n_chunks)
+// The persistent loop: wavefront w takes chunks w, w + W, w + 2W, ...
+__device__ __forceinline__ void copy_worklist(const ChunkRec *__restrict__ recs, uint32_t n_chunks)
 {
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t stride = gridDim.x * kWavesPerWG;
@@ -127,15 +127,35 @@ __global__ __launch_bounds__(kThreadsPerWG) void kvcopy_chunks_kernel(
     }
 }
 
+// One symbol per direction, so that profiles and counters separate them.
+__global__ __launch_bounds__(kThreadsPerWG) void kvcopy_h2d_kernel(const ChunkRec *__restrict__ recs,
+                                                                   uint32_t n_chunks)
+{
+    copy_worklist(recs, n_chunks);
+}
+
+__global__ __launch_bounds__(kThreadsPerWG) void kvcopy_d2h_kernel(const ChunkRec *__restrict__ recs,
+                                                                   uint32_t n_chunks)
+{
+    copy_worklist(recs, n_chunks);
+}
+
+__global__ __launch_bounds__(kThreadsPerWG) void kvcopy_d2d_kernel(const ChunkRec *__restrict__ recs,
+                                                                   uint32_t n_chunks)
+{
+    copy_worklist(recs, n_chunks);
+}
+
 }  // namespace
 
 hipError_t launch_copy(const ChunkRec *recs, uint32_t n_chunks, uint32_t grid, int dir,
                        hipStream_t stream)
 {
-    (void)dir;
+    const void *fn = dir == KVCOPY_H2D   ? reinterpret_cast<const void *>(&kvcopy_h2d_kernel)
+                     : dir == KVCOPY_D2H ? reinterpret_cast<const void *>(&kvcopy_d2h_kernel)
+                                         : reinterpret_cast<const void *>(&kvcopy_d2d_kernel);
     void *args[] = {(void *)&recs, (void *)&n_chunks};
-    return hipLaunchKernel(reinterpret_cast<const void *>(&kvcopy_chunks_kernel), dim3(grid),
-                           dim3(kThreadsPerWG), args, 0, stream);
+    return hipLaunchKernel(fn, dim3(grid), dim3(kThreadsPerWG), args, 0, stream);
 }
 
 }  // namespace kvc

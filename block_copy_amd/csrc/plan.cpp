@@ -70,22 +70,83 @@ int merge_ranges(const uint64_t *src, const uint64_t *dst, const uint64_t *size,
 
 int check_overlap(const uint64_t *src, const uint64_t *dst, const uint64_t *size, uint64_t m)
 {
-    std::vector<std::pair<uint64_t, uint64_t>> d(m);
+    std::vector<std::pair<uint64_t, uint64_t>> d;
+    d.reserve(m);
     for (uint64_t i = 0; i < m; ++i)
-        d[i] = {dst[i], dst[i] + size[i]};
+        if (size[i])
+            d.push_back({dst[i], dst[i] + size[i]});
     std::sort(d.begin(), d.end());
-    for (uint64_t i = 1; i < m; ++i)
+    for (size_t i = 1; i < d.size(); ++i)
         if (d[i].first < d[i - 1].second)
             return KVCOPY_EOVERLAP;
     // Destinations are now disjoint and sorted: a source overlaps one iff the
     // last destination starting before the source's end reaches past its start.
     for (uint64_t i = 0; i < m; ++i) {
+        if (size[i] == 0)
+            continue;
         const uint64_t lo = src[i], hi = src[i] + size[i];
         auto it = std::lower_bound(d.begin(), d.end(), std::make_pair(hi, (uint64_t)0));
         if (it != d.begin() && std::prev(it)->second > lo)
             return KVCOPY_EOVERLAP;
     }
     return KVCOPY_OK;
+}
+
+int prescan(const uint64_t *src, const uint64_t *dst, const uint64_t *size, uint64_t n,
+            uint32_t chunk, Prescan *out)
+{
+    uint64_t bits = 0, total = 0, nnz = 0, bad = 0;
+    for (uint64_t i = 0; i < n; ++i) {
+        const uint64_t s = src[i], d = dst[i], z = size[i];
+        const uint64_t t = total + z;
+        bits |= s | d | z;
+        bad |= (uint64_t)(s + z < s) | (uint64_t)(d + z < d) | (uint64_t)(t < total);
+        total = t;
+        nnz += z != 0;
+    }
+    if (bits & 7u)
+        return KVCOPY_EALIGN;
+    if (bad)
+        return KVCOPY_EINVAL;
+    out->nnz = nnz;
+    out->total = total;
+    out->bound = nnz + total / chunk;
+    return KVCOPY_OK;
+}
+
+uint64_t build_worklist(const uint64_t *src, const uint64_t *dst, const uint64_t *size, uint64_t n,
+                        bool merge, uint32_t chunk, ChunkRec *out)
+{
+    ChunkRec *w = out;
+    uint64_t cs = 0, cd = 0, cn = 0;   // the open range
+    auto close = [&]() {
+        if (cn <= chunk) {
+            *w++ = ChunkRec{cs, cd, (uint32_t)cn, 0};
+            return;
+        }
+        for (uint64_t off = 0; off < cn; off += chunk) {
+            const uint64_t left = cn - off;
+            *w++ = ChunkRec{cs + off, cd + off, (uint32_t)(left < chunk ? left : chunk), 0};
+        }
+    };
+    for (uint64_t i = 0; i < n; ++i) {
+        const uint64_t z = size[i];
+        if (z == 0)
+            continue;
+        const uint64_t s = src[i], d = dst[i];
+        if (merge && cn != 0 && cs + cn == s && cd + cn == d) {
+            cn += z;
+            continue;
+        }
+        if (cn != 0)
+            close();
+        cs = s;
+        cd = d;
+        cn = z;
+    }
+    if (cn != 0)
+        close();
+    return (uint64_t)(w - out);
 }
 
 uint64_t chunk_prefix(const uint64_t *size, uint64_t m, uint32_t chunk, uint64_t *begin)

@@ -43,40 +43,6 @@ struct Slot {
     bool busy = false;         // owned by a call in progress
 };
 
-// Per-thread planning scratch: merged ranges and their chunk prefix.  The
-// plan is made before any HIP call, so argument errors never depend on the
-// GPU, and planning runs outside the ring's lock.
-struct Scratch {
-    std::vector<uint64_t> ms, md, mz, mb;
-    uint64_t m = 0, n_chunks = 0;
-};
-thread_local Scratch t_scratch;
-
-int plan_batch(Scratch &sc, const uint64_t *src, const uint64_t *dst, const uint64_t *sizes,
-               uint64_t n, uint32_t chunk, uint32_t flags, bool validate)
-{
-    if (sc.ms.size() < n) {
-        try {
-            sc.ms.resize(n);
-            sc.md.resize(n);
-            sc.mz.resize(n);
-            sc.mb.resize(n + 1);
-        } catch (...) {
-            return KVCOPY_ENOMEM;
-        }
-    }
-    uint64_t total = 0;
-    sc.m = sc.n_chunks = 0;
-    int rc = merge_ranges(src, dst, sizes, n, !(flags & KVCOPY_F_NO_COALESCE), sc.ms.data(),
-                          sc.md.data(), sc.mz.data(), &sc.m, &total);
-    if (rc != KVCOPY_OK)
-        return rc;
-    if (validate && (rc = check_overlap(sc.ms.data(), sc.md.data(), sc.mz.data(), sc.m)) != KVCOPY_OK)
-        return rc;
-    sc.n_chunks = chunk_prefix(sc.mz.data(), sc.m, chunk, sc.mb.data());
-    return sc.n_chunks > KVCOPY_MAX_CHUNKS ? KVCOPY_EINVAL : KVCOPY_OK;
-}
-
 struct DeviceRing {
     std::mutex mu;
     Slot slots[kSlotsPerDevice];
@@ -160,20 +126,22 @@ uint32_t grid_for(uint64_t n_chunks, int max_wgs)
     return (uint32_t)max_wgs;
 }
 
-// Enqueues upload + kernel for the planned batch.  The slot is held.
-int run_in_slot(Slot *s, const Scratch &sc, int dir, int max_wgs, hipStream_t stream,
+// Plans the batch straight into the slot's pinned staging, then enqueues the
+// worklist upload and the kernel.  The slot is held by this call.
+int run_in_slot(Slot *s, const uint64_t *src, const uint64_t *dst, const uint64_t *sizes,
+                uint64_t n, const Prescan &pre, int dir, int max_wgs, hipStream_t stream,
                 uint32_t chunk, uint32_t flags, hipEvent_t ev_begin, hipEvent_t ev_end)
 {
     if (s->recorded) {
-        hipError_t e = hipEventSynchronize(s->done);
+        hipError_t e = hipEventSynchronize(s->done);   // the slot's previous kernel is done
         if (e != hipSuccess)
             return hip_fail(e);
     }
-    const uint64_t n_chunks = sc.n_chunks;
     int rc;
-    if ((rc = reserve(s, n_chunks)) != KVCOPY_OK)
+    if ((rc = reserve(s, pre.bound)) != KVCOPY_OK)
         return rc;
-    emit_chunks(sc.ms.data(), sc.md.data(), sc.mz.data(), sc.mb.data(), sc.m, chunk, s->host);
+    const uint64_t n_chunks =
+        build_worklist(src, dst, sizes, n, !(flags & KVCOPY_F_NO_COALESCE), chunk, s->host);
 
     const ChunkRec *recs = s->host;   // mapped: device-readable at the host address
     if (!(flags & KVCOPY_F_DESC_MAPPED)) {
@@ -238,10 +206,16 @@ extern "C" int kvcopy_batch_ex(const uint64_t *src_addrs, const uint64_t *dst_ad
     if (bad_env)
         return KVCOPY_EINVAL;
 
-    Scratch &sc = t_scratch;
-    int rc = plan_batch(sc, src_addrs, dst_addrs, sizes, n, chunk, flags, validate);
-    if (rc != KVCOPY_OK || sc.m == 0)
-        return rc;   // an argument error, or only zero-size descriptors: nothing enqueued
+    Prescan pre;
+    int rc = prescan(src_addrs, dst_addrs, sizes, n, chunk, &pre);
+    if (rc != KVCOPY_OK)
+        return rc;
+    if (pre.bound > KVCOPY_MAX_CHUNKS)
+        return KVCOPY_EINVAL;
+    if (validate && (rc = check_overlap(src_addrs, dst_addrs, sizes, n)) != KVCOPY_OK)
+        return rc;
+    if (pre.nnz == 0)
+        return KVCOPY_OK;   // only zero-size descriptors: nothing to enqueue
 
     int device = 0;
     hipError_t e = hipGetDevice(&device);
@@ -251,7 +225,8 @@ extern "C" int kvcopy_batch_ex(const uint64_t *src_addrs, const uint64_t *dst_ad
     Slot *slot;
     while ((slot = acquire(ring)) == nullptr)
         std::this_thread::yield();
-    rc = run_in_slot(slot, sc, dir, max_wgs, stream, chunk, flags, ev_begin, ev_end);
+    rc = run_in_slot(slot, src_addrs, dst_addrs, sizes, n, pre, dir, max_wgs, stream, chunk, flags,
+                     ev_begin, ev_end);
     release(ring, slot);
     return rc;
 }
