@@ -1,32 +1,41 @@
 #!/usr/bin/env python3
 """Benchmark of the batched descriptor copy on one MI355X.
 
-Workload (the headline): bidirectional bursts of 16,384 shuffled 4 KiB
-descriptors host->device plus 16,384 shuffled 4 KiB descriptors
+Default workload (the headline): bidirectional bursts of 16,384 shuffled
+4 KiB descriptors host->device plus 16,384 shuffled 4 KiB descriptors
 device->host, submitted concurrently on two streams against a 65,536-block
 (256 MiB) device KV pool and mapped pinned host buffers (64 MiB per
 direction).  One step = one such burst through the whole path: validate,
-coalesce and chunk on the host, one worklist upload and one kernel launch
+coalesce and chunk on the host, one worklist placement and one kernel launch
 per direction.  ``value`` is payload bytes moved per second (GB/s = 1e9 B/s)
 over the timed steps, inputs resident before the timed region.
 
-Also reported, each in the same run: each direction alone; the contiguous
+Also reported in the same run: each direction alone; the contiguous
 hipMemcpyAsync ceilings of the host link (the practical peak); one
 hipMemcpyAsync per fragment (the baseline the method replaces); the D2D
-gather of 1,024 x 4 KiB blocks and a scaled D2D variant against HBM; and
-the CPU oracle timed on the host cores on a bounded sample.  Every GPU result
-is checked bit-exact against the oracle before the line is printed.
+gather of 1,024 x 4 KiB blocks and a scaled D2D variant against HBM; and the
+CPU oracle timed on the host cores on a bounded sample.  Every GPU result is
+checked bit-exact against the oracle images of that leg before the line is
+printed.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--max-wgs G]
+Other workloads (``--workload``), one JSON line each:
+  d2d           1,024 x 4 KiB D2D gather (and 65,536 x 4 KiB) against HBM
+  mixed         H2D with mixed 4-28 KiB sizes, N = 16, 256, 4,096, 65,536
+  moe           MoE expert gather, 100 seeded calls of 26-39 experts x 6 banks
+  interference  decode-loop step times while bidirectional bursts run every 50 ms
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--max-wgs G] [--workload X]
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import statistics
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -39,33 +48,10 @@ HBM_PEAK_GBS = 8000.0     # MI355X HBM3E
 # dozen workgroups per direction keep enough bytes in flight to fill the
 # link; the full grid oversubscribes it (see the max_wgs sweep, --sweep).
 DEFAULT_MAX_WGS = 32
-KERNEL_NAMES = {0: "kvcopy_h2d_kernel", 1: "kvcopy_d2h_kernel"}
+REC_BYTES = 24            # one worklist record per chunk
+KERNEL_NAMES = {0: "kvcopy_h2d_kernel", 1: "kvcopy_d2h_kernel", 2: "kvcopy_d2d_kernel"}
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters_kv_bidirectional.json")
 KERNEL_SOURCE = os.path.join(ROOT, "block_copy_amd", "csrc", "kvcopy_kernel.hip")
-
-
-def kernel_source_hash():
-    import hashlib
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
-
-
-def measured_traffic(kernel):
-    """HBM/host bytes per launch of `kernel` from the committed PMC summary,
-    or None if there is none or the kernel source changed since it was taken."""
-    try:
-        with open(COUNTERS_FILE) as f:
-            c = json.load(f)
-    except (OSError, ValueError):
-        return None
-    if c.get("kernel_source_sha256") != kernel_source_hash():
-        return None
-    k = c.get("kernels", {}).get(kernel)
-    if not k:
-        return None
-    return {"fetch_bytes": k["fetch_bytes_per_dispatch_scaled"],
-            "write_bytes": k["write_bytes_per_dispatch_scaled"],
-            "source": os.path.relpath(COUNTERS_FILE, ROOT)}
 
 
 def log(*a):
@@ -76,70 +62,79 @@ def gbs(nbytes, seconds):
     return nbytes / seconds / 1e9
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--max-wgs", type=int, default=DEFAULT_MAX_WGS)
-    ap.add_argument("--sweep", action="store_true", help="also sweep max_wgs per direction (stderr)")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0,
-                    help="time budget of the cpu_baseline sample")
-    ap.add_argument("--skip-extras", action="store_true",
-                    help="only the headline workload (for profiling runs)")
-    ap.add_argument("--no-events", action="store_true",
-                    help="do not bracket kernels with HIP events (profiler runs); the kernel "
-                         "time is then taken as the step time")
-    ap.add_argument("--counter-calibration", action="store_true",
-                    help="also run a plain 64 MiB elementwise copy kernel 5 times, whose "
-                         "known traffic scales the PMC byte counters")
-    args = ap.parse_args()
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: the copy path has no multi-GPU step "
-              "(see the sharding note in DESIGN.md); run with --gpus 1", file=sys.stderr)
-        sys.exit(2)
+def pct(xs, q):
+    xs = sorted(xs)
+    if not xs:
+        return None
+    k = min(len(xs) - 1, max(0, int(round(q / 100.0 * (len(xs) - 1)))))
+    return xs[k]
 
-    import numpy as np
-    import torch
 
-    import workloads as W
-    from block_copy_amd import hiprt
-    from block_copy_amd import kvcopy as K
-    from block_copy_amd.harness import Resident
+def kernel_source_hash():
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
 
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(1)
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    props = torch.cuda.get_device_properties(dev)
-    log(f"device: {props.name} ({props.gcnArchName}), {props.multi_processor_count} CUs")
 
-    # ---------------- headline: bidirectional 16,384 x 4 KiB per direction ---------------
-    wl = W.kv_blocks(seed=0, directions="both")
-    res = Resident(wl)
-    sA, sB = torch.cuda.Stream(), torch.cuda.Stream()
-    step_bytes = wl.nbytes
-    n_desc = sum(b.n for b in wl.batches)
+def measured_traffic(kernel):
+    """Bytes per launch of `kernel` from the committed PMC summary, or None if
+    there is none or the kernel source changed since it was taken."""
+    try:
+        with open(COUNTERS_FILE) as f:
+            c = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if c.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    k = c.get("kernels", {}).get(kernel)
+    if not k:
+        return None
+    f, w = k["fetch_bytes_per_dispatch_scaled"], k["write_bytes_per_dispatch_scaled"]
+    return {"bytes": f + w, "fetch_bytes": f, "write_bytes": w,
+            "source": os.path.relpath(COUNTERS_FILE, ROOT)}
 
-    def run_steps(r, batch_ids, streams, k, max_wgs, events=None):
+
+class Ctx:
+    """GPU handles shared by the workloads."""
+
+    def __init__(self, args):
+        import numpy as np
+        import torch
+
+        import workloads as W
+        from block_copy_amd import hiprt
+        from block_copy_amd import kvcopy as K
+        from block_copy_amd.harness import Resident
+        self.np, self.torch, self.W, self.hiprt, self.K, self.Resident = np, torch, W, hiprt, K, Resident
+        self.args = args
+        if not torch.cuda.is_available():
+            print("bench.py needs a GPU", file=sys.stderr)
+            sys.exit(1)
+        self.dev = torch.device("cuda:0")
+        torch.cuda.set_device(self.dev)
+        p = torch.cuda.get_device_properties(self.dev)
+        log(f"device: {p.name} ({p.gcnArchName}), {p.multi_processor_count} CUs")
+        self.sA, self.sB = torch.cuda.Stream(), torch.cuda.Stream()
+
+    def run_steps(self, r, batch_ids, streams, k, max_wgs, events=None, **kw):
         for i in range(k):
             for j, (bi, st) in enumerate(zip(batch_ids, streams)):
-                kw = {}
+                extra = dict(kw)
                 if events is not None:
-                    kw = dict(kernel_begin=events[i][j][0].h, kernel_end=events[i][j][1].h)
-                r.submit(bi, max_wgs, st, **kw)
+                    extra.update(kernel_begin=events[i][j][0].h, kernel_end=events[i][j][1].h)
+                g = max_wgs[j] if isinstance(max_wgs, (list, tuple)) else max_wgs
+                r.submit(bi, g, st, **extra)
 
-    def timed(r, batch_ids, streams, k, w, max_wgs, with_events=True):
+    def timed(self, r, batch_ids, streams, k, w, max_wgs, with_events=True, **kw):
         """Seconds per step over k timed steps (after w warm-up steps), and the
-        mean kernel-only duration (ms) of each batch from HIP events."""
-        run_steps(r, batch_ids, streams, w, max_wgs)
+        mean kernel-only duration (ms) of each batch from HIP events recorded on
+        the stream each kernel runs on."""
+        torch = self.torch
+        self.run_steps(r, batch_ids, streams, w, max_wgs, **kw)
         torch.cuda.synchronize()
-        evs = [[(hiprt.Event(), hiprt.Event()) for _ in batch_ids] for _ in range(k)] \
+        evs = [[(self.hiprt.Event(), self.hiprt.Event()) for _ in batch_ids] for _ in range(k)] \
             if with_events else None
         t0 = time.perf_counter()
-        run_steps(r, batch_ids, streams, k, max_wgs, evs)
+        self.run_steps(r, batch_ids, streams, k, max_wgs, evs, **kw)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
         kern = None
@@ -148,19 +143,97 @@ def main():
                     for j in range(len(batch_ids))]
         return (t1 - t0) / k, kern
 
+    def latency(self, r, bi, max_wgs, k=100, w=10, **kw):
+        """Per-call latency of isolated calls: host time inside kvcopy_batch,
+        GPU time from an event recorded before the call to one after it, and
+        the synchronous wall time of call + stream sync."""
+        hiprt, st = self.hiprt, self.sA
+        for _ in range(w):
+            r.submit(bi, max_wgs, st, **kw)
+        hiprt.stream_sync(st)
+        host, gpu, wall = [], [], []
+        for _ in range(k):
+            e0, e1 = hiprt.Event(), hiprt.Event()
+            t0 = time.perf_counter()
+            e0.record(st)
+            t1 = time.perf_counter()
+            r.submit(bi, max_wgs, st, **kw)
+            t2 = time.perf_counter()
+            e1.record(st)
+            hiprt.stream_sync(st)
+            t3 = time.perf_counter()
+            host.append((t2 - t1) * 1e6)
+            gpu.append(e0.elapsed_ms(e1) * 1e3)
+            wall.append((t3 - t0) * 1e6)
+        rd = lambda x: round(x, 2)  # noqa: E731
+        return {"host_us_p50": rd(pct(host, 50)), "gpu_us_p50": rd(pct(gpu, 50)),
+                "gpu_us_p99": rd(pct(gpu, 99)), "wall_us_p50": rd(pct(wall, 50)),
+                "wall_us_p99": rd(pct(wall, 99))}
+
+    def oracle_images(self, wl, r, batch_ids):
+        """Host images after applying the batches with the oracle (arena index -> image)."""
+        import oracle
+        np = self.np
+        touched = set()
+        for k in batch_ids:
+            b = wl.batches[k]
+            touched |= set(b.src_arena.tolist()) | set(b.dst_arena.tolist())
+        imgs = {i: (wl.arenas[i].host_image().copy() if wl.arenas[i].fill == "random"
+                    else np.full(wl.arenas[i].nbytes, wl.arenas[i].sentinel, np.uint8))
+                for i in touched}
+        for k in batch_ids:
+            b = wl.batches[k]
+            s, d = r.addrs[k]
+            src_ids = sorted(set(b.src_arena.tolist()))
+            dst_ids = sorted(set(b.dst_arena.tolist()))
+            snap = {i: imgs[i].copy() for i in src_ids}
+            oracle.copy(s, d, b.size, [(r.bases[i], snap[i]) for i in src_ids],
+                        [(r.bases[i], imgs[i]) for i in dst_ids])
+        return imgs
+
+    def verify(self, wl, r, batch_ids, what):
+        """Bit-exact check of every destination arena against the oracle; exits on mismatch."""
+        np = self.np
+        exp = self.oracle_images(wl, r, batch_ids)
+        dsts = set()
+        for k in batch_ids:
+            dsts |= set(wl.batches[k].dst_arena.tolist())
+        for i in sorted(dsts):
+            got = r.image(i)
+            if not np.array_equal(got, exp[i]):
+                bad = int(np.flatnonzero(got != exp[i])[0])
+                log(f"PARITY FAILURE ({what}) in arena {wl.arenas[i].name} at byte {bad}")
+                sys.exit(3)
+
+
+def base_line(args, value, unit, step_s, config, dtype="u8", higher=True):
+    return {"metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(step_s * 1e3, 4), "higher_is_better": higher,
+            "scaling": "weak", "vs_baseline": None, "dtype": dtype, "data": "synthetic",
+            "config": config}
+
+
+# ---------------------------------------------------------------------------
+# Headline: bidirectional KV block bursts
+# ---------------------------------------------------------------------------
+
+def bench_kv(c: Ctx, args):
+    np, torch, W, K, hiprt = c.np, c.torch, c.W, c.K, c.hiprt
+    wl = W.kv_blocks(seed=0, directions="both")
+    res = c.Resident(wl)
+    sA, sB = c.sA, c.sB
+    step_bytes = wl.nbytes
+    n_desc = sum(b.n for b in wl.batches)
     max_wgs = args.max_wgs
     log(f"headline: {n_desc} descriptors, {step_bytes} B per step, max_wgs={max_wgs}")
-    step_s, kern_ms = timed(res, [0, 1], [sA, sB], args.steps, args.warmup, max_wgs,
-                            with_events=not args.no_events)
+    step_s, kern_ms = c.timed(res, [0, 1], [sA, sB], args.steps, args.warmup, max_wgs,
+                              with_events=not args.no_events)
     if kern_ms is None:
         kern_ms = [step_s * 1e3, step_s * 1e3]
     value = gbs(step_bytes, step_s)
     log(f"  bidirectional: {step_s * 1e3:.3f} ms/step, {value:.2f} GB/s; kernel ms {kern_ms}")
-
-    # worklist bytes the kernel reads per launch: one 24-byte record per chunk
-    plan = [K.kvcopy_plan(*res.addrs[j], wl.batches[j].size) for j in range(2)]
-    meta = [p.n_chunks * 24 for p in plan]
-    algo = [wl.batches[j].nbytes + meta[j] for j in range(2)]
+    plans = [K.kvcopy_plan(*res.addrs[j], wl.batches[j].size) for j in range(2)]
+    algo = [wl.batches[j].nbytes + plans[j].n_chunks * REC_BYTES for j in range(2)]
     ach = [gbs(algo[j], kern_ms[j] / 1e3) for j in range(2)]
 
     extras = {}
@@ -168,87 +241,45 @@ def main():
         sweep = {}
         for name, ids, sts in (("h2d", [0], [sA]), ("d2h", [1], [sA]), ("both", [0, 1], [sA, sB])):
             for g in (1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 0):
-                s_, km = timed(res, ids, sts, max(3, args.steps // 2), 2, g)
+                s_, km = c.timed(res, ids, sts, max(3, args.steps // 2), 2, g)
                 nbytes = sum(wl.batches[i].nbytes for i in ids)
                 sweep[f"{name}/{g}"] = round(gbs(nbytes, s_), 2)
                 log(f"  sweep {name} max_wgs={g}: {gbs(nbytes, s_):.2f} GB/s, kernel ms "
                     f"{[round(x, 3) for x in km]}")
         extras["max_wgs_sweep_GBps"] = sweep
     if not args.skip_extras:
-        # each direction alone
         alone = {}
         for j, name in ((0, "h2d"), (1, "d2h")):
-            s, km = timed(res, [j], [sA], args.steps, args.warmup, max_wgs)   # extras only
+            s, km = c.timed(res, [j], [sA], args.steps, args.warmup, max_wgs)
             alone[name] = {"GBps": round(gbs(wl.batches[j].nbytes, s), 3),
                            "ms_per_call": round(s * 1e3, 4), "kernel_ms": round(km[0], 4)}
             log(f"  {name} alone: {alone[name]}")
         extras["per_direction_alone"] = alone
-
-        # contiguous ceilings: 64 MiB from/to mapped pinned memory, separate buffers
-        nb = 64 * W.MIB
-        hsrc = K.HostBuffer(nb)
-        hdst = K.HostBuffer(nb)
-        hsrc.array[:] = 7
-        dbuf = torch.empty(2 * nb, dtype=torch.uint8, device=dev)
-
-        def ceiling(kinds, reps=10):
-            streams = [sA, sB]
-            times = []
-            for r in range(reps + 2):
-                torch.cuda.synchronize()
-                t0 = time.perf_counter()
-                for i, kind in enumerate(kinds):
-                    if kind == "h2d":
-                        hiprt.memcpy_async(dbuf.data_ptr(), hsrc.ptr, nb, hiprt.H2D_KIND, streams[i])
-                    else:
-                        hiprt.memcpy_async(hdst.ptr, dbuf.data_ptr() + nb, nb, hiprt.D2H_KIND, streams[i])
-                torch.cuda.synchronize()
-                if r >= 2:
-                    times.append(time.perf_counter() - t0)
-            return gbs(nb * len(kinds), statistics.median(times))
-
-        ceil = {"h2d": ceiling(["h2d"]), "d2h": ceiling(["d2h"]), "both": ceiling(["h2d", "d2h"])}
-        extras["contiguous_memcpy_ceiling_GBps"] = {k: round(v, 3) for k, v in ceil.items()}
+        extras["contiguous_memcpy_ceiling_GBps"] = ceilings(c)
         log(f"  contiguous ceilings: {extras['contiguous_memcpy_ceiling_GBps']}")
-
-        # one hipMemcpyAsync per fragment (after coalescing), one stream
         frag = {}
         for j, name, kind in ((0, "h2d", hiprt.H2D_KIND), (1, "d2h", hiprt.D2H_KIND)):
-            p = plan[j]
-            reps = 2
-            torch.cuda.synchronize()
-            t0 = time.perf_counter()
-            for _ in range(reps):
-                for s_, d_, z_ in zip(p.src.tolist(), p.dst.tolist(), p.size.tolist()):
-                    hiprt.memcpy_async(d_, s_, z_, kind, sA)
-            torch.cuda.synchronize()
-            dt = (time.perf_counter() - t0) / reps
+            dt = per_fragment(c, plans[j], kind, reps=2)
             frag[name] = {"GBps": round(gbs(wl.batches[j].nbytes, dt), 3),
-                          "ms_per_call": round(dt * 1e3, 3), "copies": int(p.n_merged)}
+                          "ms_per_call": round(dt * 1e3, 3), "copies": int(plans[j].n_merged)}
             log(f"  per-fragment hipMemcpyAsync {name}: {frag[name]}")
         extras["per_fragment_memcpy"] = frag
-        del dbuf
-        hsrc.free()
-        hdst.free()
 
     if args.counter_calibration:
-        a = torch.arange(16 * W.MIB, dtype=torch.int32, device=dev)   # 64 MiB
+        a = torch.arange(16 * W.MIB, dtype=torch.int32, device=c.dev)   # 64 MiB
         b = torch.empty_like(a)
         for _ in range(5):
             torch.neg(a, out=b)
         torch.cuda.synchronize()
         del a, b
 
-    # ---------------- verification of the headline workload ----------------
+    # verification + cpu_baseline (the oracle on host images of the same step)
     torch.cuda.synchronize()
-    final = {i: res.image(i) for i in (0, 2)}      # device pool, host D2H destination
-
-    # ---------------- cpu_baseline: the oracle on host images of the same step --------------
+    final = {i: res.image(i) for i in (0, 2)}        # device pool, host D2H destination
     import oracle
-    imgs = [a.host_image().copy() if a.fill == "random" else
-            np.full(a.nbytes, a.sentinel, np.uint8) for a in wl.arenas]
+    imgs = [a.host_image().copy() if a.fill == "random" else np.full(a.nbytes, a.sentinel, np.uint8)
+            for a in wl.arenas]
     src_snap = {0: imgs[0].copy(), 1: imgs[1]}
-    bases = res.bases
 
     def oracle_step():
         moved = 0
@@ -256,7 +287,8 @@ def main():
             b = wl.batches[j]
             s, d = res.addrs[j]
             si, di = int(b.src_arena[0]), int(b.dst_arena[0])
-            moved += oracle.copy(s, d, b.size, [(bases[si], src_snap[si])], [(bases[di], imgs[di])])
+            moved += oracle.copy(s, d, b.size, [(res.bases[si], src_snap[si])],
+                                 [(res.bases[di], imgs[di])])
         return moved
 
     reps, moved, t0 = 0, 0, time.perf_counter()
@@ -276,77 +308,361 @@ def main():
     log("  parity: bit-exact against the oracle")
     res.free()
 
-    # ---------------- D2D: 1,024 x 4 KiB, and a scaled variant -------------------------------
     if not args.skip_extras:
-        d2d = {}
-        for name, wld in (("1024x4KiB", W.d2d_blocks(seed=0)),
-                          ("65536x4KiB", W.d2d_blocks(seed=1, n=65536, pool_blocks=262144))):
-            r2 = Resident(wld)
-            s, km = timed(r2, [0], [sA], args.steps, args.warmup, 0)
-            pl = K.kvcopy_plan(*r2.addrs[0], wld.batches[0].size)
-            hbm_bytes = 2 * wld.batches[0].nbytes + pl.n_chunks * 24
-            d2d[name] = {"GBps_payload": round(gbs(wld.batches[0].nbytes, s), 2),
-                         "us_per_call": round(s * 1e6, 2), "kernel_us": round(km[0] * 1e3, 2),
-                         "hbm_GBps_kernel": round(gbs(hbm_bytes, km[0] / 1e3), 1),
-                         "frac_hbm_peak": round(gbs(hbm_bytes, km[0] / 1e3) / HBM_PEAK_GBS, 4)}
-            img = r2.image(1)
-            exp = np.full(wld.arenas[1].nbytes, wld.arenas[1].sentinel, np.uint8)
-            b = wld.batches[0]
-            sa, da = r2.addrs[0]
-            oracle.copy(sa, da, b.size, [(r2.bases[0], wld.arenas[0].host_image())],
-                        [(r2.bases[1], exp)])
-            if not np.array_equal(img, exp):
-                log(f"PARITY FAILURE in d2d {name}")
-                sys.exit(3)
-            log(f"  d2d {name}: {d2d[name]} (bit-exact)")
-            r2.free()
-        extras["d2d"] = d2d
+        extras["d2d"] = d2d_results(c, args)
 
     dom = 0 if kern_ms[0] >= kern_ms[1] else 1
     meas_ceil = extras.get("contiguous_memcpy_ceiling_GBps", {}).get(("h2d", "d2h")[dom])
-    line = {
-        "metric": METRIC,
-        "value": round(value, 3),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(step_s * 1e3, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "u8",
-        "data": "synthetic",
-        "config": {
-            "workload": "bidirectional KV block burst: 16,384 shuffled 4 KiB H2D + 16,384 shuffled "
-                        "4 KiB D2H per step, concurrent on two streams, 65,536-block device pool, "
-                        "mapped pinned host buffers",
-            "descriptors_per_step": n_desc, "bytes_per_step": step_bytes,
-            "max_wgs": max_wgs, "chunk_bytes": K.CHUNK_DEFAULT, "seed": 0,
-        },
-        "roofline": {
-            "bound": "pcie",
-            "kernel": KERNEL_NAMES[dom],
-            "achieved": round(ach[dom], 3),
-            "peak": PCIE_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(ach[dom] / PCIE_PEAK_GBS, 4),
-            "traffic": measured_traffic(KERNEL_NAMES[dom]),
-            "kernel_ms": round(kern_ms[dom], 4),
-            "algorithmic_bytes_per_launch": algo[dom],
-            "measured_ceiling": meas_ceil,
-            "frac_of_measured_ceiling": round(ach[dom] / meas_ceil, 4) if meas_ceil else None,
-            "other_kernel": {"dir": ("H2D", "D2H")[1 - dom], "achieved": round(ach[1 - dom], 3),
-                             "kernel_ms": round(kern_ms[1 - dom], 4)},
-        },
-        "cpu_baseline": {
-            "value": round(cpu_gbs, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{reps} full steps (16,384 H2D + 16,384 D2H descriptors of 4 KiB each, "
-                      f"per-descriptor memcpy between host images), {cpu_s:.1f} s",
-        },
-        "parity": "bit-exact vs oracle",
-    }
+    line = base_line(args, round(value, 3), "GB/s", step_s, {
+        "workload": "bidirectional KV block burst: 16,384 shuffled 4 KiB H2D + 16,384 shuffled "
+                    "4 KiB D2H per step, concurrent on two streams, 65,536-block device pool, "
+                    "mapped pinned host buffers",
+        "descriptors_per_step": n_desc, "bytes_per_step": step_bytes,
+        "max_wgs": max_wgs, "chunk_bytes": K.CHUNK_DEFAULT, "seed": 0})
+    line["roofline"] = {
+        "bound": "pcie", "kernel": KERNEL_NAMES[dom], "achieved": round(ach[dom], 3),
+        "peak": PCIE_PEAK_GBS, "unit": "GB/s", "frac": round(ach[dom] / PCIE_PEAK_GBS, 4),
+        "traffic": measured_traffic(KERNEL_NAMES[dom]),
+        "kernel_ms": round(kern_ms[dom], 4), "algorithmic_bytes_per_launch": algo[dom],
+        "measured_ceiling": meas_ceil,
+        "frac_of_measured_ceiling": round(ach[dom] / meas_ceil, 4) if meas_ceil else None,
+        "other_kernel": {"kernel": KERNEL_NAMES[1 - dom], "achieved": round(ach[1 - dom], 3),
+                         "kernel_ms": round(kern_ms[1 - dom], 4)}}
+    line["cpu_baseline"] = {
+        "value": round(cpu_gbs, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+        "sample": f"{reps} full steps (16,384 H2D + 16,384 D2H descriptors of 4 KiB each, "
+                  f"per-descriptor memcpy between host images), {cpu_s:.1f} s"}
+    line["parity"] = "bit-exact vs oracle"
     line.update(extras)
+    return line
+
+
+def ceilings(c: Ctx, nb=None, reps=10):
+    """Contiguous hipMemcpyAsync of 64 MiB from/to mapped pinned memory, per
+    direction and both together on two streams (GB/s, median of reps)."""
+    torch, hiprt, K, W = c.torch, c.hiprt, c.K, c.W
+    nb = nb or 64 * W.MIB
+    hsrc, hdst = K.HostBuffer(nb), K.HostBuffer(nb)
+    hsrc.array[:] = 7
+    dbuf = torch.empty(2 * nb, dtype=torch.uint8, device=c.dev)
+
+    def one(kinds):
+        times = []
+        for r in range(reps + 2):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for i, kind in enumerate(kinds):
+                st = (c.sA, c.sB)[i]
+                if kind == "h2d":
+                    hiprt.memcpy_async(dbuf.data_ptr(), hsrc.ptr, nb, hiprt.H2D_KIND, st)
+                else:
+                    hiprt.memcpy_async(hdst.ptr, dbuf.data_ptr() + nb, nb, hiprt.D2H_KIND, st)
+            torch.cuda.synchronize()
+            if r >= 2:
+                times.append(time.perf_counter() - t0)
+        return round(gbs(nb * len(kinds), statistics.median(times)), 3)
+
+    out = {"h2d": one(["h2d"]), "d2h": one(["d2h"]), "both": one(["h2d", "d2h"])}
+    del dbuf
+    hsrc.free()
+    hdst.free()
+    return out
+
+
+def per_fragment(c: Ctx, plan, kind, reps=2):
+    """Seconds per batch for one hipMemcpyAsync per (coalesced) range on one stream."""
+    torch, hiprt = c.torch, c.hiprt
+    srcs, dsts, sizes = plan.src.tolist(), plan.dst.tolist(), plan.size.tolist()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        for s_, d_, z_ in zip(srcs, dsts, sizes):
+            hiprt.memcpy_async(d_, s_, z_, kind, c.sA)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / reps
+
+
+# ---------------------------------------------------------------------------
+# D2D
+# ---------------------------------------------------------------------------
+
+def d2d_results(c: Ctx, args):
+    torch, W, K, hiprt = c.torch, c.W, c.K, c.hiprt
+    out = {}
+    for name, wld in (("1024x4KiB", W.d2d_blocks(seed=0)),
+                      ("65536x4KiB", W.d2d_blocks(seed=1, n=65536, pool_blocks=262144))):
+        r = c.Resident(wld)
+        s, km = c.timed(r, [0], [c.sA], args.steps, args.warmup, 0)
+        pl = K.kvcopy_plan(*r.addrs[0], wld.batches[0].size)
+        hbm = 2 * wld.batches[0].nbytes + pl.n_chunks * REC_BYTES
+        out[name] = {"GBps_payload": round(gbs(wld.batches[0].nbytes, s), 2),
+                     "us_per_call_pipelined": round(s * 1e6, 2), "kernel_us": round(km[0] * 1e3, 2),
+                     "hbm_GBps_kernel": round(gbs(hbm, km[0] / 1e3), 1),
+                     "frac_hbm_peak_kernel": round(gbs(hbm, km[0] / 1e3) / HBM_PEAK_GBS, 4),
+                     "latency": c.latency(r, 0, 0, k=50, w=5)}
+        c.verify(wld, r, [0], f"d2d {name}")
+        log(f"  d2d {name}: {out[name]} (bit-exact)")
+        r.free()
+    big = torch.empty(2 << 30, dtype=torch.uint8, device=c.dev)
+    cont = {}
+    for nbytes in (256 << 20, 1 << 30):
+        ms = []
+        for _ in range(5):
+            e1, e2 = hiprt.Event(), hiprt.Event()
+            e1.record(c.sA)
+            hiprt.memcpy_async(big.data_ptr() + (1 << 30), big.data_ptr(), nbytes, hiprt.D2D_KIND, c.sA)
+            e2.record(c.sA)
+            ms.append(e1.elapsed_ms(e2))
+        cont[f"{nbytes >> 20}MiB"] = round(gbs(2 * nbytes, statistics.median(ms) / 1e3), 1)
+    del big
+    out["contiguous_memcpy_hbm_GBps"] = cont
+    log(f"  contiguous D2D hipMemcpyAsync (HBM GB/s): {cont}")
+    return out
+
+
+def bench_d2d(c: Ctx, args):
+    res = d2d_results(c, args)
+    r1 = res["1024x4KiB"]
+    line = base_line(args, r1["GBps_payload"], "GB/s", r1["us_per_call_pipelined"] / 1e6, {
+        "workload": "D2D gather/scatter of 1,024 x 4 KiB blocks between two 4,096-block pools; "
+                    "also 65,536 x 4 KiB between two 1 GiB pools",
+        "max_wgs": 0, "chunk_bytes": c.K.CHUNK_DEFAULT, "seed": 0})
+    big = res["65536x4KiB"]
+    line["roofline"] = {"bound": "hbm", "kernel": KERNEL_NAMES[2],
+                        "achieved": big["hbm_GBps_kernel"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": big["frac_hbm_peak_kernel"], "traffic": measured_traffic(KERNEL_NAMES[2]),
+                        "workload_of_roofline": "65536x4KiB",
+                        "measured_ceiling": res["contiguous_memcpy_hbm_GBps"]["256MiB"]}
+    line["d2d"] = res
+    line["parity"] = "bit-exact vs oracle"
+    return line
+
+
+# ---------------------------------------------------------------------------
+# Mixed sizes
+# ---------------------------------------------------------------------------
+
+def bench_mixed(c: Ctx, args):
+    W, K, hiprt = c.W, c.K, c.hiprt
+    rows = {}
+    for n in (16, 256, 4096, 65536):
+        wl = W.h2d_mixed(seed=0, n=n)
+        r = c.Resident(wl)
+        b = wl.batches[0]
+        pl = K.kvcopy_plan(*r.addrs[0], b.size)
+        k = max(5, min(args.steps * 5, 200 if n <= 256 else args.steps))
+        s, km = c.timed(r, [0], [c.sA], k, args.warmup, args.max_wgs)
+        lat = c.latency(r, 0, args.max_wgs, k=50 if n <= 4096 else 10, w=5)
+        frag_s = per_fragment(c, pl, hiprt.H2D_KIND, reps=2 if n <= 4096 else 1)
+        rows[str(n)] = {"bytes": b.nbytes, "merged": int(pl.n_merged), "chunks": int(pl.n_chunks),
+                        "GBps": round(gbs(b.nbytes, s), 2), "kernel_us": round(km[0] * 1e3, 2),
+                        "kernel_GBps": round(gbs(b.nbytes, km[0] / 1e3), 2), "latency": lat,
+                        "per_fragment_GBps": round(gbs(b.nbytes, frag_s), 3)}
+        c.verify(wl, r, [0], f"mixed {n}")
+        log(f"  mixed N={n}: {rows[str(n)]} (bit-exact)")
+        r.free()
+    top = rows["65536"]
+    line = base_line(args, top["GBps"], "GB/s", top["bytes"] / top["GBps"] / 1e9, {
+        "workload": "H2D with mixed sizes (70% in 8-16 KiB, rest 4-8 and 16-28 KiB, 8-byte "
+                    "multiples), 25% of descriptors adjacent in both arenas, N = 16 .. 65,536; "
+                    "value at N = 65,536",
+        "max_wgs": args.max_wgs, "chunk_bytes": K.CHUNK_DEFAULT, "seed": 0})
+    line["per_n"] = rows
+    line["parity"] = "bit-exact vs oracle"
+    return line
+
+
+# ---------------------------------------------------------------------------
+# MoE expert gather
+# ---------------------------------------------------------------------------
+
+def bench_moe(c: Ctx, args):
+    W, K, hiprt = c.W, c.K, c.hiprt
+    calls = 100
+    wl = W.moe_gather(seed=0, calls=calls)
+    r = c.Resident(wl)
+    out = {}
+    # byte-balanced: 16 KiB chunks dealt to all wavefronts; unbalanced: one
+    # wavefront per row (chunk = 1 MiB), the descriptor-granular work split
+    for name, chunk in (("byte_balanced_16KiB", 0), ("one_wave_per_row", K.CHUNK_MAX)):
+        for g in (8, 32, 128, 0):
+            t_us, sizes = [], []
+            for i in range(calls):
+                e0, e1 = hiprt.Event(), hiprt.Event()
+                e0.record(c.sA)
+                r.submit(i, g, c.sA, chunk_bytes=chunk)
+                e1.record(c.sA)
+                t_us.append(e0.elapsed_ms(e1) * 1e3)
+                sizes.append(wl.batches[i].nbytes)
+            rates = [gbs(z, t / 1e6) for z, t in zip(sizes, t_us)]
+            out[f"{name}/max_wgs={g}"] = {
+                "call_us_p50": round(pct(t_us, 50), 1), "call_us_p99": round(pct(t_us, 99), 1),
+                "GBps_p50": round(pct(rates, 50), 2), "GBps_total": round(gbs(sum(sizes), sum(t_us) / 1e6), 2)}
+            log(f"  moe {name} max_wgs={g}: {out[f'{name}/max_wgs={g}']}")
+    c.verify(wl, r, list(range(calls)), "moe")     # every call wrote its slots; the last writes win
+    r.free()
+    best = max((v["GBps_total"], k) for k, v in out.items() if k.startswith("byte_balanced"))
+    line = base_line(args, best[0], "GB/s", 0.0, {
+        "workload": "MoE expert gather: 100 seeded calls, each 26-39 experts x 6 bank rows "
+                    "(1 MiB, 64 KiB, 4 KiB, 512 KiB, 32 KiB, 4 KiB) from pinned host banks into "
+                    "random slots of a 3,164-slot device cache; one call per step",
+        "best": best[1], "seed": 0})
+    line["ms_per_step"] = round(out[best[1]]["call_us_p50"] / 1e3, 4)
+    line["steps"] = calls
+    line["per_setting"] = out
+    line["parity"] = "bit-exact vs oracle"
+    return line
+
+
+# ---------------------------------------------------------------------------
+# Interference: decode loop vs bidirectional bursts
+# ---------------------------------------------------------------------------
+
+def bench_interference(c: Ctx, args):
+    torch, W, K, hiprt = c.torch, c.W, c.K, c.hiprt
+    from block_copy_amd.decode_load import Chain
+    d_model, d_ff, n_gemv = 2560, 9728, 36
+    g = torch.Generator(device=c.dev)
+    g.manual_seed(0)
+    weights, acts = [], [torch.randn(d_model, generator=g, device=c.dev).to(torch.bfloat16)]
+    for i in range(n_gemv):
+        shape = (d_ff, d_model) if i % 2 == 0 else (d_model, d_ff)
+        weights.append((torch.randn(shape, generator=g, device=c.dev) * 0.02).to(torch.bfloat16))
+        acts.append(torch.empty(shape[0], dtype=torch.bfloat16, device=c.dev))
+    chain = Chain(weights, acts)
+    wbytes = sum(w.numel() * 2 for w in weights)
+    sD = torch.cuda.Stream()
+    wl = W.kv_blocks(seed=0, directions="both")
+    r = c.Resident(wl)
+    period = 0.050
+    steps, warm = args.decode_steps, 32
+
+    def run(mode):
+        stop = threading.Event()
+        moved = [0]
+        bursts = [0]
+
+        def transfer():
+            nxt = time.perf_counter()
+            while not stop.is_set():
+                if mode == "direct":
+                    for j, kind, st in ((0, hiprt.H2D_KIND, c.sA), (1, hiprt.D2H_KIND, c.sB)):
+                        b = wl.batches[j]
+                        s_, d_ = r.addrs[j]
+                        for x, y, z in zip(s_.tolist(), d_.tolist(), b.size.tolist()):
+                            hiprt.memcpy_async(y, x, z, kind, st)
+                else:
+                    r.submit(0, mode, c.sA)
+                    r.submit(1, mode, c.sB)
+                hiprt.stream_sync(c.sA)
+                hiprt.stream_sync(c.sB)
+                moved[0] += wl.nbytes
+                bursts[0] += 1
+                nxt += period
+                delay = nxt - time.perf_counter()
+                if delay > 0:
+                    stop.wait(delay)
+                else:
+                    nxt = time.perf_counter()
+
+        th = None
+        for _ in range(warm):
+            chain.run(sD)
+        hiprt.stream_sync(sD)
+        t_start = time.perf_counter()
+        if mode != "none":
+            th = threading.Thread(target=transfer, daemon=True)
+            th.start()
+        gpu_ms, wall_ms = [], []
+        for _ in range(steps):
+            e0, e1 = hiprt.Event(), hiprt.Event()
+            t0 = time.perf_counter()
+            e0.record(sD)
+            chain.run(sD)
+            e1.record(sD)
+            hiprt.stream_sync(sD)
+            wall_ms.append((time.perf_counter() - t0) * 1e3)
+            gpu_ms.append(e0.elapsed_ms(e1))
+        dur = time.perf_counter() - t_start
+        if th is not None:
+            stop.set()
+            th.join()
+        return gpu_ms, wall_ms, moved[0] / dur, bursts[0]
+
+    modes = ["none", "direct", 8, 32, 128, 0]
+    results = {str(m): {"gpu": [], "wall": [], "rate": [], "bursts": 0} for m in modes}
+    for rep in range(args.decode_runs):
+        order = modes[rep % len(modes):] + modes[:rep % len(modes)]
+        for m in order:
+            gms, wms, rate, nb = run(m)
+            rr = results[str(m)]
+            rr["gpu"].append(gms)
+            rr["wall"].append(wms)
+            rr["rate"].append(rate)
+            rr["bursts"] += nb
+            log(f"  interference run {rep} mode {m}: p50 {pct(gms, 50):.3f} p99 {pct(gms, 99):.3f} "
+                f"max {max(gms):.3f} ms (GPU), wall p99 {pct(wms, 99):.3f} ms, "
+                f"{rate / 2**30:.3f} GiB/s, {nb} bursts")
+    hiprt.stream_sync(c.sA)
+    hiprt.stream_sync(c.sB)
+    c.verify(wl, r, [0, 1], "interference bursts")
+    r.free()
+    table = {}
+    for m, rr in results.items():
+        def agg(key, q):
+            return round(statistics.mean(pct(x, q) for x in rr[key]), 4)
+        table[m] = {"gpu_ms_mean": round(statistics.mean(statistics.mean(x) for x in rr["gpu"]), 4),
+                    "gpu_ms_p50": agg("gpu", 50), "gpu_ms_p99": agg("gpu", 99),
+                    "gpu_ms_max": round(max(max(x) for x in rr["gpu"]), 4),
+                    "wall_ms_p50": agg("wall", 50), "wall_ms_p99": agg("wall", 99),
+                    "wall_ms_max": round(max(max(x) for x in rr["wall"]), 4),
+                    "transfer_GiBps": round(statistics.mean(rr["rate"]) / 2**30, 3),
+                    "bursts": rr["bursts"]}
+    base = table["none"]["gpu_ms_p99"]
+    for m in table:
+        table[m]["p99_vs_none"] = round(table[m]["gpu_ms_p99"] / base - 1, 4)
+    line = base_line(args, table["32"]["gpu_ms_p99"], "ms", table["none"]["gpu_ms_mean"] / 1e3, {
+        "workload": f"decode loop of {n_gemv} bf16 GEMVs ({d_ff}x{d_model} and {d_model}x{d_ff}, "
+                    f"{wbytes / 1e9:.2f} GB of distinct weights per step) while a bidirectional "
+                    "burst (16,384 x 4 KiB H2D + 16,384 x 4 KiB D2H) starts every 50 ms; value = "
+                    "decode step p99 (GPU time) with max_wgs = 32",
+        "decode_steps_per_run": steps, "runs_per_mode": args.decode_runs, "seed": 0},
+        dtype="bf16", higher=False)
+    line["modes"] = table
+    line["parity"] = "bit-exact vs oracle (last burst)"
+    return line
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--max-wgs", type=int, default=DEFAULT_MAX_WGS)
+    ap.add_argument("--workload", default="kv", choices=["kv", "d2d", "mixed", "moe", "interference"])
+    ap.add_argument("--sweep", action="store_true", help="also sweep max_wgs per direction (stderr)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="time budget of the cpu_baseline sample")
+    ap.add_argument("--skip-extras", action="store_true",
+                    help="only the headline workload (for profiling runs)")
+    ap.add_argument("--no-events", action="store_true",
+                    help="do not bracket kernels with HIP events (profiler runs); the kernel "
+                         "time is then taken as the step time")
+    ap.add_argument("--counter-calibration", action="store_true",
+                    help="also run a plain 64 MiB elementwise copy kernel 5 times, whose "
+                         "known traffic scales the PMC byte counters")
+    ap.add_argument("--decode-steps", type=int, default=1536)
+    ap.add_argument("--decode-runs", type=int, default=3)
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the copy path has no multi-GPU step "
+              "(the sharding plan is in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    c = Ctx(args)
+    fn = {"kv": bench_kv, "d2d": bench_d2d, "mixed": bench_mixed, "moe": bench_moe,
+          "interference": bench_interference}[args.workload]
+    line = fn(c, args)
     print(json.dumps(line), flush=True)
 
 

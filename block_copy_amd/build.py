@@ -16,6 +16,10 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(PKG, "libkvcopy.so")
+# Measurement-only library: the synthetic decode loop (bf16 GEMV chain) that
+# co-runs with copy bursts in the interference benchmark.
+LOAD_OUT = os.path.join(PKG, "libkvload.so")
+LOAD_SOURCES = ["gemv_load.hip"]
 BUILD_DIR = os.path.join(ROOT, "_build")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 ARCH = "gfx950"
@@ -55,8 +59,16 @@ def build(verbose: bool = False) -> str:
     tmp = OUT + ".tmp"
     _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
     os.replace(tmp, OUT)
+    load_objs = []
+    for src in LOAD_SOURCES:
+        obj = os.path.join(BUILD_DIR, src + ".o")
+        _run([hipcc, *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        load_objs.append(obj)
+    tmp = LOAD_OUT + ".tmp"
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *load_objs, "-o", tmp])
+    os.replace(tmp, LOAD_OUT)
     if verbose:
-        print(f"built {OUT}")
+        print(f"built {OUT} and {LOAD_OUT}")
     return OUT
 
 

@@ -39,6 +39,7 @@ struct Slot {
     ChunkRec *dev = nullptr;   // device twin the worklist is uploaded to
     uint64_t cap = 0;          // capacity in records
     hipEvent_t done = nullptr; // recorded after the last kernel that read this slot
+    hipEvent_t uploaded = nullptr;  // recorded on the upload stream after the worklist copy
     bool recorded = false;
     bool busy = false;         // owned by a call in progress
 };
@@ -47,6 +48,7 @@ struct DeviceRing {
     std::mutex mu;
     Slot slots[kSlotsPerDevice];
     unsigned next = 0;
+    hipStream_t upload = nullptr;   // library-owned, non-blocking, default priority
 };
 
 std::mutex g_rings_mu;
@@ -60,6 +62,21 @@ DeviceRing *ring_for(int device)
     if (g_rings[device] == nullptr)
         g_rings[device] = new DeviceRing();
     return g_rings[device];
+}
+
+// The device's upload stream, created on first use (with that device current).
+int upload_stream(DeviceRing *r, hipStream_t *out)
+{
+    std::lock_guard<std::mutex> g(r->mu);
+    if (r->upload == nullptr) {
+        hipError_t e = hipStreamCreateWithFlags(&r->upload, hipStreamNonBlocking);
+        if (e != hipSuccess) {
+            r->upload = nullptr;
+            return hip_fail(e);
+        }
+    }
+    *out = r->upload;
+    return KVCOPY_OK;
 }
 
 // Takes the next slot that no other call holds.  Returns nullptr only if
@@ -130,7 +147,8 @@ uint32_t grid_for(uint64_t n_chunks, int max_wgs)
 // worklist upload and the kernel.  The slot is held by this call.
 int run_in_slot(Slot *s, const uint64_t *src, const uint64_t *dst, const uint64_t *sizes,
                 uint64_t n, const Prescan &pre, int dir, int max_wgs, hipStream_t stream,
-                uint32_t chunk, uint32_t flags, hipEvent_t ev_begin, hipEvent_t ev_end)
+                hipStream_t up, uint32_t chunk, uint32_t flags, hipEvent_t ev_begin,
+                hipEvent_t ev_end)
 {
     if (s->recorded) {
         hipError_t e = hipEventSynchronize(s->done);   // the slot's previous kernel is done
@@ -144,10 +162,23 @@ int run_in_slot(Slot *s, const uint64_t *src, const uint64_t *dst, const uint64_
         build_worklist(src, dst, sizes, n, !(flags & KVCOPY_F_NO_COALESCE), chunk, s->host);
 
     const ChunkRec *recs = s->host;   // mapped: device-readable at the host address
-    if (!(flags & KVCOPY_F_DESC_MAPPED)) {
-        hipError_t e = hipMemcpyAsync(s->dev, s->host, (size_t)n_chunks * sizeof(ChunkRec),
-                                      hipMemcpyHostToDevice, stream);
-        if (e != hipSuccess)
+    const bool upload = (flags & KVCOPY_F_DESC_UPLOAD) ||
+                        (!(flags & KVCOPY_F_DESC_MAPPED) && n_chunks > KVCOPY_MAPPED_MAX_CHUNKS);
+    if (upload) {
+        // The copy runs on the library's stream, so it can overlap work that
+        // is still queued on the caller's stream; the caller's stream then
+        // waits for it before the kernel.  The device twin is free: the
+        // slot's previous kernel has completed (waited on above).
+        hipError_t e;
+        if (s->uploaded == nullptr &&
+            (e = hipEventCreateWithFlags(&s->uploaded, hipEventDisableTiming)) != hipSuccess)
+            return hip_fail(e);
+        if ((e = hipMemcpyAsync(s->dev, s->host, (size_t)n_chunks * sizeof(ChunkRec),
+                                hipMemcpyHostToDevice, up)) != hipSuccess)
+            return hip_fail(e);
+        if ((e = hipEventRecord(s->uploaded, up)) != hipSuccess)
+            return hip_fail(e);
+        if ((e = hipStreamWaitEvent(stream, s->uploaded, 0)) != hipSuccess)
             return hip_fail(e);
         recs = s->dev;
     }
@@ -187,7 +218,10 @@ extern "C" int kvcopy_batch_ex(const uint64_t *src_addrs, const uint64_t *dst_ad
                 return KVCOPY_EINVAL;
             chunk = opts->chunk_bytes;
         }
-        if (opts->flags & ~(KVCOPY_F_VALIDATE | KVCOPY_F_NO_COALESCE | KVCOPY_F_DESC_MAPPED))
+        if (opts->flags & ~(KVCOPY_F_VALIDATE | KVCOPY_F_NO_COALESCE | KVCOPY_F_DESC_MAPPED |
+                            KVCOPY_F_DESC_UPLOAD))
+            return KVCOPY_EINVAL;
+        if ((opts->flags & KVCOPY_F_DESC_MAPPED) && (opts->flags & KVCOPY_F_DESC_UPLOAD))
             return KVCOPY_EINVAL;
         flags = opts->flags;
         ev_begin = opts->kernel_begin;
@@ -222,11 +256,14 @@ extern "C" int kvcopy_batch_ex(const uint64_t *src_addrs, const uint64_t *dst_ad
     if (e != hipSuccess)
         return hip_fail(e);
     DeviceRing *ring = ring_for(device);
+    hipStream_t up = nullptr;
+    if ((rc = upload_stream(ring, &up)) != KVCOPY_OK)
+        return rc;
     Slot *slot;
     while ((slot = acquire(ring)) == nullptr)
         std::this_thread::yield();
-    rc = run_in_slot(slot, src_addrs, dst_addrs, sizes, n, pre, dir, max_wgs, stream, chunk, flags,
-                     ev_begin, ev_end);
+    rc = run_in_slot(slot, src_addrs, dst_addrs, sizes, n, pre, dir, max_wgs, stream, up, chunk,
+                     flags, ev_begin, ev_end);
     release(ring, slot);
     return rc;
 }

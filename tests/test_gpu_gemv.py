@@ -1,0 +1,52 @@
+"""The measurement-only bf16 GEMV (the synthetic decode loop of the
+interference benchmark) against a float32 CPU reference of the same product."""
+import pytest
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def DL():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from block_copy_amd import decode_load
+    return decode_load
+
+
+def _ref(W, x):
+    return W.float().cpu() @ x.float().cpu()
+
+
+@pytest.mark.parametrize("rows,cols", [(9728, 2560), (2560, 9728), (7, 8), (65, 1032), (1, 4096)])
+def test_gemv_matches_fp32_reference(DL, rows, cols):
+    print("[case] gemv", rows, cols, flush=True)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(rows * 7 + cols)
+    W = (torch.randn(rows, cols, generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+    x = torch.randn(cols, generator=g, device="cuda").to(torch.bfloat16)
+    y = torch.empty(rows, dtype=torch.bfloat16, device="cuda")
+    DL.gemv(W, x, y)
+    torch.cuda.synchronize()
+    ref = _ref(W, x)
+    got = y.float().cpu()
+    # bf16 output rounding (half an ulp = 2^-8 relative) plus fp32 summation-order noise
+    tol = ref.abs() * 2.0 ** -8 + 1e-5 * ref.abs().max() + 1e-6
+    assert torch.all((got - ref).abs() <= tol), float(((got - ref).abs() - tol).max())
+
+
+def test_chain_runs_products_in_order(DL):
+    print("[case] gemv chain", flush=True)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1)
+    shapes = [(96, 64), (64, 96), (96, 64)]
+    Ws = [(torch.randn(s, generator=g, device="cuda") * 0.1).to(torch.bfloat16) for s in shapes]
+    acts = [torch.randn(64, generator=g, device="cuda").to(torch.bfloat16)]
+    acts += [torch.empty(s[0], dtype=torch.bfloat16, device="cuda") for s in shapes]
+    DL.Chain(Ws, acts).run()
+    torch.cuda.synchronize()
+    for i, W in enumerate(Ws):
+        ref = _ref(W, acts[i])
+        got = acts[i + 1].float().cpu()
+        tol = ref.abs() * 2.0 ** -8 + 1e-5 * ref.abs().max() + 1e-6
+        assert torch.all((got - ref).abs() <= tol), i

@@ -167,7 +167,7 @@ def test_irregular_chunk_sizes(K, dname, chunk):
     res.free()
 
 
-@pytest.mark.parametrize("flags", [1, 2, 4, 6])
+@pytest.mark.parametrize("flags", [1, 2, 4, 6, 8, 10])
 def test_irregular_flags(K, flags):
     from block_copy_amd.harness import Resident
     wl = W.irregular(seed=40 + flags, n=500, dir_=W.H2D, src_where="host", dst_where="device",
