@@ -30,6 +30,8 @@ Prints ONE JSON line on stdout; progress goes to stderr.
 from __future__ import annotations
 
 import argparse
+import contextlib
+import gc
 import hashlib
 import json
 import os
@@ -47,10 +49,11 @@ HBM_PEAK_GBS = 8000.0     # MI355X HBM3E
 # Workgroup cap of the headline: with H2D and D2H running together, a few
 # dozen workgroups per direction keep enough bytes in flight to fill the
 # link; the full grid oversubscribes it (see the max_wgs sweep, --sweep).
-DEFAULT_MAX_WGS = 32
+DEFAULT_MAX_WGS = 128
 REC_BYTES = 24            # one worklist record per chunk
 KERNEL_NAMES = {0: "kvcopy_h2d_kernel", 1: "kvcopy_d2h_kernel", 2: "kvcopy_d2d_kernel"}
-COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters_kv_bidirectional.json")
+COUNTERS_KV = os.path.join(ROOT, "profiles", "counters_kv_bidirectional.json")
+COUNTERS_D2D = os.path.join(ROOT, "profiles", "counters_d2d_blocks.json")
 KERNEL_SOURCE = os.path.join(ROOT, "block_copy_amd", "csrc", "kvcopy_kernel.hip")
 
 
@@ -70,16 +73,29 @@ def pct(xs, q):
     return xs[k]
 
 
+@contextlib.contextmanager
+def no_gc():
+    """Timed regions run with Python's cyclic garbage collector paused: a
+    full collection in a process that holds torch takes tens of milliseconds
+    and would land inside whichever call happens to trigger it."""
+    gc.collect()
+    gc.disable()
+    try:
+        yield
+    finally:
+        gc.enable()
+
+
 def kernel_source_hash():
     with open(KERNEL_SOURCE, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def measured_traffic(kernel):
+def measured_traffic(kernel, path=COUNTERS_KV):
     """Bytes per launch of `kernel` from the committed PMC summary, or None if
     there is none or the kernel source changed since it was taken."""
     try:
-        with open(COUNTERS_FILE) as f:
+        with open(path) as f:
             c = json.load(f)
     except (OSError, ValueError):
         return None
@@ -90,7 +106,7 @@ def measured_traffic(kernel):
         return None
     f, w = k["fetch_bytes_per_dispatch_scaled"], k["write_bytes_per_dispatch_scaled"]
     return {"bytes": f + w, "fetch_bytes": f, "write_bytes": w,
-            "source": os.path.relpath(COUNTERS_FILE, ROOT)}
+            "source": os.path.relpath(path, ROOT)}
 
 
 class Ctx:
@@ -116,6 +132,8 @@ class Ctx:
         self.sA, self.sB = torch.cuda.Stream(), torch.cuda.Stream()
 
     def run_steps(self, r, batch_ids, streams, k, max_wgs, events=None, **kw):
+        if self.args.desc_upload:
+            kw["flags"] = kw.get("flags", 0) | self.K.F_DESC_UPLOAD
         for i in range(k):
             for j, (bi, st) in enumerate(zip(batch_ids, streams)):
                 extra = dict(kw)
@@ -129,18 +147,21 @@ class Ctx:
         mean kernel-only duration (ms) of each batch from HIP events recorded on
         the stream each kernel runs on."""
         torch = self.torch
+        with_events = with_events and not self.args.no_events
         self.run_steps(r, batch_ids, streams, w, max_wgs, **kw)
         torch.cuda.synchronize()
         evs = [[(self.hiprt.Event(), self.hiprt.Event()) for _ in batch_ids] for _ in range(k)] \
             if with_events else None
-        t0 = time.perf_counter()
-        self.run_steps(r, batch_ids, streams, k, max_wgs, evs, **kw)
-        torch.cuda.synchronize()
-        t1 = time.perf_counter()
-        kern = None
+        with no_gc():
+            t0 = time.perf_counter()
+            self.run_steps(r, batch_ids, streams, k, max_wgs, evs, **kw)
+            torch.cuda.synchronize()
+            t1 = time.perf_counter()
         if evs:
             kern = [statistics.mean(evs[i][j][0].elapsed_ms(evs[i][j][1]) for i in range(k))
                     for j in range(len(batch_ids))]
+        else:   # profiler runs: no events; the step time stands in for the kernel time
+            kern = [(t1 - t0) / k * 1e3] * len(batch_ids)
         return (t1 - t0) / k, kern
 
     def latency(self, r, bi, max_wgs, k=100, w=10, **kw):
@@ -148,23 +169,28 @@ class Ctx:
         GPU time from an event recorded before the call to one after it, and
         the synchronous wall time of call + stream sync."""
         hiprt, st = self.hiprt, self.sA
+        if self.args.no_events:
+            return None
+        if self.args.desc_upload:
+            kw["flags"] = kw.get("flags", 0) | self.K.F_DESC_UPLOAD
         for _ in range(w):
             r.submit(bi, max_wgs, st, **kw)
         hiprt.stream_sync(st)
         host, gpu, wall = [], [], []
-        for _ in range(k):
-            e0, e1 = hiprt.Event(), hiprt.Event()
-            t0 = time.perf_counter()
-            e0.record(st)
-            t1 = time.perf_counter()
-            r.submit(bi, max_wgs, st, **kw)
-            t2 = time.perf_counter()
-            e1.record(st)
-            hiprt.stream_sync(st)
-            t3 = time.perf_counter()
-            host.append((t2 - t1) * 1e6)
-            gpu.append(e0.elapsed_ms(e1) * 1e3)
-            wall.append((t3 - t0) * 1e6)
+        evs = [(hiprt.Event(), hiprt.Event()) for _ in range(k)]
+        with no_gc():
+            for e0, e1 in evs:
+                t0 = time.perf_counter()
+                e0.record(st)
+                t1 = time.perf_counter()
+                r.submit(bi, max_wgs, st, **kw)
+                t2 = time.perf_counter()
+                e1.record(st)
+                hiprt.stream_sync(st)
+                t3 = time.perf_counter()
+                host.append((t2 - t1) * 1e6)
+                wall.append((t3 - t0) * 1e6)
+        gpu = [e0.elapsed_ms(e1) * 1e3 for e0, e1 in evs]
         rd = lambda x: round(x, 2)  # noqa: E731
         return {"host_us_p50": rd(pct(host, 50)), "gpu_us_p50": rd(pct(gpu, 50)),
                 "gpu_us_p99": rd(pct(gpu, 99)), "wall_us_p50": rd(pct(wall, 50)),
@@ -226,10 +252,7 @@ def bench_kv(c: Ctx, args):
     n_desc = sum(b.n for b in wl.batches)
     max_wgs = args.max_wgs
     log(f"headline: {n_desc} descriptors, {step_bytes} B per step, max_wgs={max_wgs}")
-    step_s, kern_ms = c.timed(res, [0, 1], [sA, sB], args.steps, args.warmup, max_wgs,
-                              with_events=not args.no_events)
-    if kern_ms is None:
-        kern_ms = [step_s * 1e3, step_s * 1e3]
+    step_s, kern_ms = c.timed(res, [0, 1], [sA, sB], args.steps, args.warmup, max_wgs)
     value = gbs(step_bytes, step_s)
     log(f"  bidirectional: {step_s * 1e3:.3f} ms/step, {value:.2f} GB/s; kernel ms {kern_ms}")
     plans = [K.kvcopy_plan(*res.addrs[j], wl.batches[j].size) for j in range(2)]
@@ -266,12 +289,7 @@ def bench_kv(c: Ctx, args):
         extras["per_fragment_memcpy"] = frag
 
     if args.counter_calibration:
-        a = torch.arange(16 * W.MIB, dtype=torch.int32, device=c.dev)   # 64 MiB
-        b = torch.empty_like(a)
-        for _ in range(5):
-            torch.neg(a, out=b)
-        torch.cuda.synchronize()
-        del a, b
+        counter_calibration(c)
 
     # verification + cpu_baseline (the oracle on host images of the same step)
     torch.cuda.synchronize()
@@ -335,6 +353,18 @@ def bench_kv(c: Ctx, args):
     line["parity"] = "bit-exact vs oracle"
     line.update(extras)
     return line
+
+
+def counter_calibration(c: Ctx):
+    """A plain elementwise kernel of known traffic (reads 64 MiB, writes 64 MiB),
+    run 5 times, whose PMC byte counts scale those of the copy kernels."""
+    torch = c.torch
+    a = torch.arange(16 * c.W.MIB, dtype=torch.int32, device=c.dev)
+    b = torch.empty_like(a)
+    for _ in range(5):
+        torch.neg(a, out=b)
+    torch.cuda.synchronize()
+    del a, b
 
 
 def ceilings(c: Ctx, nb=None, reps=10):
@@ -422,6 +452,8 @@ def d2d_results(c: Ctx, args):
 
 def bench_d2d(c: Ctx, args):
     res = d2d_results(c, args)
+    if args.counter_calibration:
+        counter_calibration(c)
     r1 = res["1024x4KiB"]
     line = base_line(args, r1["GBps_payload"], "GB/s", r1["us_per_call_pipelined"] / 1e6, {
         "workload": "D2D gather/scatter of 1,024 x 4 KiB blocks between two 4,096-block pools; "
@@ -430,7 +462,7 @@ def bench_d2d(c: Ctx, args):
     big = res["65536x4KiB"]
     line["roofline"] = {"bound": "hbm", "kernel": KERNEL_NAMES[2],
                         "achieved": big["hbm_GBps_kernel"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                        "frac": big["frac_hbm_peak_kernel"], "traffic": measured_traffic(KERNEL_NAMES[2]),
+                        "frac": big["frac_hbm_peak_kernel"], "traffic": measured_traffic(KERNEL_NAMES[2], COUNTERS_D2D),
                         "workload_of_roofline": "65536x4KiB",
                         "measured_ceiling": res["contiguous_memcpy_hbm_GBps"]["256MiB"]}
     line["d2d"] = res
@@ -487,13 +519,14 @@ def bench_moe(c: Ctx, args):
     for name, chunk in (("byte_balanced_16KiB", 0), ("one_wave_per_row", K.CHUNK_MAX)):
         for g in (8, 32, 128, 0):
             t_us, sizes = [], []
-            for i in range(calls):
-                e0, e1 = hiprt.Event(), hiprt.Event()
-                e0.record(c.sA)
-                r.submit(i, g, c.sA, chunk_bytes=chunk)
-                e1.record(c.sA)
-                t_us.append(e0.elapsed_ms(e1) * 1e3)
-                sizes.append(wl.batches[i].nbytes)
+            with no_gc():
+                for i in range(calls):
+                    e0, e1 = hiprt.Event(), hiprt.Event()
+                    e0.record(c.sA)
+                    r.submit(i, g, c.sA, chunk_bytes=chunk)
+                    e1.record(c.sA)
+                    t_us.append(e0.elapsed_ms(e1) * 1e3)
+                    sizes.append(wl.batches[i].nbytes)
             rates = [gbs(z, t / 1e6) for z, t in zip(sizes, t_us)]
             out[f"{name}/max_wgs={g}"] = {
                 "call_us_p50": round(pct(t_us, 50), 1), "call_us_p99": round(pct(t_us, 99), 1),
@@ -574,15 +607,16 @@ def bench_interference(c: Ctx, args):
             th = threading.Thread(target=transfer, daemon=True)
             th.start()
         gpu_ms, wall_ms = [], []
-        for _ in range(steps):
-            e0, e1 = hiprt.Event(), hiprt.Event()
-            t0 = time.perf_counter()
-            e0.record(sD)
-            chain.run(sD)
-            e1.record(sD)
-            hiprt.stream_sync(sD)
-            wall_ms.append((time.perf_counter() - t0) * 1e3)
-            gpu_ms.append(e0.elapsed_ms(e1))
+        evs = [(hiprt.Event(), hiprt.Event()) for _ in range(steps)]
+        with no_gc():
+            for e0, e1 in evs:
+                t0 = time.perf_counter()
+                e0.record(sD)
+                chain.run(sD)
+                e1.record(sD)
+                hiprt.stream_sync(sD)
+                wall_ms.append((time.perf_counter() - t0) * 1e3)
+        gpu_ms = [e0.elapsed_ms(e1) for e0, e1 in evs]
         dur = time.perf_counter() - t_start
         if th is not None:
             stop.set()
@@ -651,6 +685,9 @@ def main():
     ap.add_argument("--counter-calibration", action="store_true",
                     help="also run a plain 64 MiB elementwise copy kernel 5 times, whose "
                          "known traffic scales the PMC byte counters")
+    ap.add_argument("--desc-upload", action="store_true",
+                    help="upload worklists to device memory before each kernel (KVCOPY_F_DESC_UPLOAD) "
+                         "instead of reading them in place from pinned staging")
     ap.add_argument("--decode-steps", type=int, default=1536)
     ap.add_argument("--decode-runs", type=int, default=3)
     args = ap.parse_args()

@@ -1,21 +1,28 @@
-// runtime.cpp -- kvcopy_batch: staging, upload, launch, errors; host allocation helpers.
+// runtime.cpp -- kvcopy_batch: staging, launch, errors; host allocation helpers.
 //
-// A call plans the batch into a library-owned pinned staging slot, uploads
-// the chunk worklist with one async copy on the caller's stream and launches
-// one copy kernel on the same stream (PegaFlow issue #408, "Summary": one
-// descriptor upload and one copy-kernel launch).  The vLLM PR #42212 report,
-// section "review highlights", notes that descriptor buffers that are not
-// pinned make the "async" upload synchronous, and that the buffers are
-// allocated once and reused: here each device keeps a ring of pinned slots,
-// each with a device-side twin and an event recorded after the kernel that
-// last read it.  A slot is reused only after that event has completed, so a
-// caller never waits on its own stream inside the call except when all
-// slots are still in flight.
+// A call plans the batch straight into a library-owned pinned staging ring
+// and launches one copy kernel on the caller's stream (PegaFlow issue #408,
+// "Summary": one descriptor upload and one copy-kernel launch per batch).
+// The kernel reads its worklist in place from the pinned ring, over the host
+// link, with vector loads of 64 records at a time: the worklist crosses the
+// link once, as part of the kernel's own traffic, with no separate copy and
+// no copy-engine latency in front of the kernel.  (KVCOPY_F_DESC_UPLOAD
+// instead copies it into a device twin of the ring with hipMemcpyAsync on
+// the caller's stream.)
+//
+// The vLLM PR #42212 report, section "review highlights", points out that
+// descriptor buffers must be pinned for the transfer to be asynchronous, and
+// that they are allocated once and reused.  Here each device has one pinned
+// ring, sized once (it grows only if a single call needs more than a quarter
+// of it).  Each call takes the next free region of the ring; the region is
+// released when an event recorded after the call's kernel has completed.  A
+// call waits on the host only when the ring is full of regions whose kernels
+// are still running.
 #include <stdlib.h>
 #include <string.h>
 
+#include <deque>
 #include <mutex>
-#include <thread>
 #include <vector>
 
 #include "kvcopy.h"
@@ -32,107 +39,150 @@ int hip_fail(hipError_t e)
     return KVCOPY_EHIP;
 }
 
-constexpr int kSlotsPerDevice = 8;
+constexpr uint64_t kRingMinBytes = 16ull << 20;   // 16 MiB: ~700 K worklist records
+constexpr uint64_t kAlign = 256;
 
-struct Slot {
-    ChunkRec *host = nullptr;  // pinned, mapped staging (device-readable at the same address)
-    ChunkRec *dev = nullptr;   // device twin the worklist is uploaded to
-    uint64_t cap = 0;          // capacity in records
-    hipEvent_t done = nullptr; // recorded after the last kernel that read this slot
-    hipEvent_t uploaded = nullptr;  // recorded on the upload stream after the worklist copy
-    bool recorded = false;
-    bool busy = false;         // owned by a call in progress
+struct InFlight {
+    uint64_t begin, end;   // byte range of the ring
+    hipEvent_t done;       // recorded after the kernel that reads the range
 };
 
-struct DeviceRing {
-    std::mutex mu;
-    Slot slots[kSlotsPerDevice];
-    unsigned next = 0;
-    hipStream_t upload = nullptr;   // library-owned, non-blocking, default priority
+struct Staging {
+    std::mutex mu;             // held for a whole call: planning is host-side and short
+    uint8_t *host = nullptr;   // pinned, mapped (device address == host address)
+    uint8_t *dev = nullptr;    // device twin, allocated on first KVCOPY_F_DESC_UPLOAD
+    uint64_t cap = 0;
+    uint64_t head = 0;         // next free byte
+    std::deque<InFlight> inflight;   // allocation order == ring order
+    std::vector<hipEvent_t> spare;   // completed events, reused
 };
 
-std::mutex g_rings_mu;
-std::vector<DeviceRing *> g_rings;   // indexed by device ordinal; never freed
+std::mutex g_staging_mu;
+std::vector<Staging *> g_staging;   // indexed by device ordinal; lives until process exit
 
-DeviceRing *ring_for(int device)
+Staging *staging_for(int device)
 {
-    std::lock_guard<std::mutex> g(g_rings_mu);
-    if ((size_t)device >= g_rings.size())
-        g_rings.resize((size_t)device + 1, nullptr);
-    if (g_rings[device] == nullptr)
-        g_rings[device] = new DeviceRing();
-    return g_rings[device];
+    std::lock_guard<std::mutex> g(g_staging_mu);
+    if ((size_t)device >= g_staging.size())
+        g_staging.resize((size_t)device + 1, nullptr);
+    if (g_staging[device] == nullptr)
+        g_staging[device] = new Staging();
+    return g_staging[device];
 }
 
-// The device's upload stream, created on first use (with that device current).
-int upload_stream(DeviceRing *r, hipStream_t *out)
+// Retires the oldest in-flight region: waits for its kernel if `wait`, else
+// only polls.  Returns 1 if retired, 0 if still running (poll), or an error.
+int retire_front(Staging *st, bool wait)
 {
-    std::lock_guard<std::mutex> g(r->mu);
-    if (r->upload == nullptr) {
-        hipError_t e = hipStreamCreateWithFlags(&r->upload, hipStreamNonBlocking);
-        if (e != hipSuccess) {
-            r->upload = nullptr;
-            return hip_fail(e);
-        }
-    }
-    *out = r->upload;
-    return KVCOPY_OK;
-}
-
-// Takes the next slot that no other call holds.  Returns nullptr only if
-// every slot is busy (more concurrent callers than slots); the caller retries.
-Slot *acquire(DeviceRing *r)
-{
-    std::lock_guard<std::mutex> g(r->mu);
-    for (int t = 0; t < kSlotsPerDevice; ++t) {
-        Slot *s = &r->slots[(r->next + t) % kSlotsPerDevice];
-        if (!s->busy) {
-            s->busy = true;
-            r->next = (r->next + t + 1) % kSlotsPerDevice;
-            return s;
-        }
-    }
-    return nullptr;
-}
-
-void release(DeviceRing *r, Slot *s)
-{
-    std::lock_guard<std::mutex> g(r->mu);
-    s->busy = false;
-}
-
-// Grows the slot to hold `need` records.  The slot's previous GPU work has
-// completed (its event was waited on), so the old buffers can go.
-int reserve(Slot *s, uint64_t need)
-{
-    if (need <= s->cap)
-        return KVCOPY_OK;
-    uint64_t cap = s->cap ? s->cap : 4096;
-    while (cap < need)
-        cap *= 2;
-    if (s->host) {
-        hipHostFree(s->host);
-        s->host = nullptr;
-    }
-    if (s->dev) {
-        hipFree(s->dev);
-        s->dev = nullptr;
-    }
-    s->cap = 0;
-    const size_t bytes = (size_t)cap * sizeof(ChunkRec);
-    hipError_t e = hipHostMalloc((void **)&s->host, bytes, hipHostMallocMapped | hipHostMallocPortable);
-    if (e == hipErrorOutOfMemory)
-        return KVCOPY_ENOMEM;
+    const InFlight f = st->inflight.front();
+    const hipError_t e = wait ? hipEventSynchronize(f.done) : hipEventQuery(f.done);
+    if (e == hipErrorNotReady)
+        return 0;
     if (e != hipSuccess)
         return hip_fail(e);
-    e = hipMalloc((void **)&s->dev, bytes);
-    if (e != hipSuccess) {
-        hipHostFree(s->host);
-        s->host = nullptr;
-        return e == hipErrorOutOfMemory ? KVCOPY_ENOMEM : hip_fail(e);
+    st->spare.push_back(f.done);
+    st->inflight.pop_front();
+    if (st->inflight.empty())
+        st->head = 0;
+    return 1;
+}
+
+int drain(Staging *st)
+{
+    while (!st->inflight.empty()) {
+        const int rc = retire_front(st, true);
+        if (rc < 0)
+            return rc;
     }
-    s->cap = cap;
     return KVCOPY_OK;
+}
+
+// Makes the ring at least 4 x `need` bytes (and allocates the device twin if
+// `want_dev`).  Old buffers are released only after every kernel using them
+// has completed.
+int grow(Staging *st, uint64_t need, bool want_dev)
+{
+    uint64_t cap = st->cap ? st->cap : kRingMinBytes;
+    while (cap < 4 * need)
+        cap *= 2;
+    const bool resize = cap != st->cap;
+    if (!resize && (!want_dev || st->dev))
+        return KVCOPY_OK;
+    int rc = drain(st);
+    if (rc != KVCOPY_OK)
+        return rc;
+    if (resize) {
+        if (st->host)
+            hipHostFree(st->host);
+        if (st->dev)
+            hipFree(st->dev);
+        st->host = nullptr;
+        st->dev = nullptr;
+        st->cap = 0;
+    }
+    hipError_t e;
+    if (st->host == nullptr) {
+        e = hipHostMalloc((void **)&st->host, cap, hipHostMallocMapped | hipHostMallocPortable);
+        if (e != hipSuccess) {
+            st->host = nullptr;
+            return e == hipErrorOutOfMemory ? KVCOPY_ENOMEM : hip_fail(e);
+        }
+    }
+    if (want_dev && st->dev == nullptr) {
+        e = hipMalloc((void **)&st->dev, cap);
+        if (e != hipSuccess) {
+            st->dev = nullptr;
+            st->cap = cap;   // the host ring is valid
+            return e == hipErrorOutOfMemory ? KVCOPY_ENOMEM : hip_fail(e);
+        }
+    }
+    st->cap = cap;
+    st->head = 0;
+    return KVCOPY_OK;
+}
+
+// Reserves `need` bytes at the ring's head (wrapping to 0 when the end of the
+// ring is too short), retiring completed regions and waiting for running
+// ones only when they are in the way.  *off receives the region's start.
+int reserve(Staging *st, uint64_t need, bool want_dev, uint64_t *off)
+{
+    if (4 * need > st->cap || (want_dev && st->dev == nullptr)) {
+        const int rc = grow(st, need, want_dev);
+        if (rc != KVCOPY_OK)
+            return rc;
+    }
+    while (!st->inflight.empty()) {   // retire whatever has finished, without waiting
+        const int rc = retire_front(st, false);
+        if (rc < 0)
+            return rc;
+        if (rc == 0)
+            break;
+    }
+    for (;;) {
+        if (st->inflight.empty()) {
+            *off = 0;
+            return KVCOPY_OK;
+        }
+        const uint64_t head = st->head, tail = st->inflight.front().begin;
+        if (head > tail) {          // used [tail, head): free [head, cap) and [0, tail)
+            if (head + need <= st->cap) {
+                *off = head;
+                return KVCOPY_OK;
+            }
+            if (need <= tail) {
+                *off = 0;
+                return KVCOPY_OK;
+            }
+        } else if (head < tail) {   // used wraps: free [head, tail)
+            if (head + need <= tail) {
+                *off = head;
+                return KVCOPY_OK;
+            }
+        }                           // head == tail: the ring is full
+        const int rc = retire_front(st, true);
+        if (rc < 0)
+            return rc;
+    }
 }
 
 uint32_t grid_for(uint64_t n_chunks, int max_wgs)
@@ -143,46 +193,32 @@ uint32_t grid_for(uint64_t n_chunks, int max_wgs)
     return (uint32_t)max_wgs;
 }
 
-// Plans the batch straight into the slot's pinned staging, then enqueues the
-// worklist upload and the kernel.  The slot is held by this call.
-int run_in_slot(Slot *s, const uint64_t *src, const uint64_t *dst, const uint64_t *sizes,
-                uint64_t n, const Prescan &pre, int dir, int max_wgs, hipStream_t stream,
-                hipStream_t up, uint32_t chunk, uint32_t flags, hipEvent_t ev_begin,
-                hipEvent_t ev_end)
+// Plans the batch into the staging ring and enqueues the kernel (and, with
+// KVCOPY_F_DESC_UPLOAD, the worklist copy before it).  Called with st->mu held.
+int run_locked(Staging *st, const uint64_t *src, const uint64_t *dst, const uint64_t *sizes,
+               uint64_t n, const Prescan &pre, int dir, int max_wgs, hipStream_t stream,
+               uint32_t chunk, uint32_t flags, hipEvent_t ev_begin, hipEvent_t ev_end)
 {
-    if (s->recorded) {
-        hipError_t e = hipEventSynchronize(s->done);   // the slot's previous kernel is done
-        if (e != hipSuccess)
-            return hip_fail(e);
-    }
-    int rc;
-    if ((rc = reserve(s, pre.bound)) != KVCOPY_OK)
+    const bool upload = (flags & KVCOPY_F_DESC_UPLOAD) != 0;
+    const uint64_t need = (pre.bound * sizeof(ChunkRec) + kAlign - 1) / kAlign * kAlign;
+    uint64_t off = 0;
+    int rc = reserve(st, need, upload, &off);
+    if (rc != KVCOPY_OK)
         return rc;
+    ChunkRec *host = reinterpret_cast<ChunkRec *>(st->host + off);
     const uint64_t n_chunks =
-        build_worklist(src, dst, sizes, n, !(flags & KVCOPY_F_NO_COALESCE), chunk, s->host);
+        build_worklist(src, dst, sizes, n, !(flags & KVCOPY_F_NO_COALESCE), chunk, host);
+    const uint64_t used = (n_chunks * sizeof(ChunkRec) + kAlign - 1) / kAlign * kAlign;
 
-    const ChunkRec *recs = s->host;   // mapped: device-readable at the host address
-    const bool upload = (flags & KVCOPY_F_DESC_UPLOAD) ||
-                        (!(flags & KVCOPY_F_DESC_MAPPED) && n_chunks > KVCOPY_MAPPED_MAX_CHUNKS);
-    if (upload) {
-        // The copy runs on the library's stream, so it can overlap work that
-        // is still queued on the caller's stream; the caller's stream then
-        // waits for it before the kernel.  The device twin is free: the
-        // slot's previous kernel has completed (waited on above).
-        hipError_t e;
-        if (s->uploaded == nullptr &&
-            (e = hipEventCreateWithFlags(&s->uploaded, hipEventDisableTiming)) != hipSuccess)
-            return hip_fail(e);
-        if ((e = hipMemcpyAsync(s->dev, s->host, (size_t)n_chunks * sizeof(ChunkRec),
-                                hipMemcpyHostToDevice, up)) != hipSuccess)
-            return hip_fail(e);
-        if ((e = hipEventRecord(s->uploaded, up)) != hipSuccess)
-            return hip_fail(e);
-        if ((e = hipStreamWaitEvent(stream, s->uploaded, 0)) != hipSuccess)
-            return hip_fail(e);
-        recs = s->dev;
-    }
+    const ChunkRec *recs = host;   // read in place: mapped at the same address on the device
     hipError_t e;
+    if (upload) {
+        ChunkRec *dev = reinterpret_cast<ChunkRec *>(st->dev + off);
+        if ((e = hipMemcpyAsync(dev, host, n_chunks * sizeof(ChunkRec), hipMemcpyHostToDevice,
+                                stream)) != hipSuccess)
+            return hip_fail(e);
+        recs = dev;
+    }
     if (ev_begin && (e = hipEventRecord(ev_begin, stream)) != hipSuccess)
         return hip_fail(e);
     if ((e = launch_copy(recs, (uint32_t)n_chunks, grid_for(n_chunks, max_wgs), dir, stream)) !=
@@ -190,12 +226,19 @@ int run_in_slot(Slot *s, const uint64_t *src, const uint64_t *dst, const uint64_
         return hip_fail(e);
     if (ev_end && (e = hipEventRecord(ev_end, stream)) != hipSuccess)
         return hip_fail(e);
-    if (s->done == nullptr &&
-        (e = hipEventCreateWithFlags(&s->done, hipEventDisableTiming)) != hipSuccess)
+    hipEvent_t done;
+    if (!st->spare.empty()) {
+        done = st->spare.back();
+        st->spare.pop_back();
+    } else if ((e = hipEventCreateWithFlags(&done, hipEventDisableTiming)) != hipSuccess) {
         return hip_fail(e);
-    if ((e = hipEventRecord(s->done, stream)) != hipSuccess)
+    }
+    if ((e = hipEventRecord(done, stream)) != hipSuccess) {
+        st->spare.push_back(done);
         return hip_fail(e);
-    s->recorded = true;
+    }
+    st->inflight.push_back(InFlight{off, off + used, done});
+    st->head = off + used;
     return KVCOPY_OK;
 }
 
@@ -218,10 +261,7 @@ extern "C" int kvcopy_batch_ex(const uint64_t *src_addrs, const uint64_t *dst_ad
                 return KVCOPY_EINVAL;
             chunk = opts->chunk_bytes;
         }
-        if (opts->flags & ~(KVCOPY_F_VALIDATE | KVCOPY_F_NO_COALESCE | KVCOPY_F_DESC_MAPPED |
-                            KVCOPY_F_DESC_UPLOAD))
-            return KVCOPY_EINVAL;
-        if ((opts->flags & KVCOPY_F_DESC_MAPPED) && (opts->flags & KVCOPY_F_DESC_UPLOAD))
+        if (opts->flags & ~(KVCOPY_F_VALIDATE | KVCOPY_F_NO_COALESCE | KVCOPY_F_DESC_UPLOAD))
             return KVCOPY_EINVAL;
         flags = opts->flags;
         ev_begin = opts->kernel_begin;
@@ -252,20 +292,13 @@ extern "C" int kvcopy_batch_ex(const uint64_t *src_addrs, const uint64_t *dst_ad
         return KVCOPY_OK;   // only zero-size descriptors: nothing to enqueue
 
     int device = 0;
-    hipError_t e = hipGetDevice(&device);
+    const hipError_t e = hipGetDevice(&device);
     if (e != hipSuccess)
         return hip_fail(e);
-    DeviceRing *ring = ring_for(device);
-    hipStream_t up = nullptr;
-    if ((rc = upload_stream(ring, &up)) != KVCOPY_OK)
-        return rc;
-    Slot *slot;
-    while ((slot = acquire(ring)) == nullptr)
-        std::this_thread::yield();
-    rc = run_in_slot(slot, src_addrs, dst_addrs, sizes, n, pre, dir, max_wgs, stream, up, chunk,
-                     flags, ev_begin, ev_end);
-    release(ring, slot);
-    return rc;
+    Staging *st = staging_for(device);
+    std::lock_guard<std::mutex> g(st->mu);
+    return run_locked(st, src_addrs, dst_addrs, sizes, n, pre, dir, max_wgs, stream, chunk, flags,
+                      ev_begin, ev_end);
 }
 
 extern "C" int kvcopy_batch(const uint64_t *src_addrs, const uint64_t *dst_addrs,

@@ -22,8 +22,7 @@ OK, EINVAL, EALIGN, EOVERLAP, ENOMEM, EHIP = 0, -1, -2, -3, -4, -5
 WGS_ALL = 0
 CHUNK_DEFAULT = 16384
 CHUNK_MAX = 1 << 20
-F_VALIDATE, F_NO_COALESCE, F_DESC_MAPPED, F_DESC_UPLOAD = 0x1, 0x2, 0x4, 0x8
-MAPPED_MAX_CHUNKS = 1024
+F_VALIDATE, F_NO_COALESCE, F_DESC_UPLOAD = 0x1, 0x2, 0x8
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvcopy.so")
 

@@ -80,18 +80,13 @@ enum {
 #define KVCOPY_MAX_DESCS ((uint64_t)1 << 31)
 #define KVCOPY_MAX_CHUNKS ((uint64_t)1 << 31)
 
-/* Option flags for kvcopy_batch_ex.  Where the kernel finds the worklist:
- * by default small worklists (at most KVCOPY_MAPPED_MAX_CHUNKS chunks) are
- * read in place from the pinned staging slot over the host link (no upload,
- * lowest latency), larger ones are uploaded to HBM by an async copy on a
- * library-owned stream and the caller's stream waits for it (the upload
- * overlaps earlier work on the caller's stream).  The two DESC flags force
- * one placement; setting both is KVCOPY_EINVAL. */
+/* Option flags for kvcopy_batch_ex.  By default the kernel reads the
+ * worklist in place from the library's pinned staging ring (it crosses the
+ * host link once, as part of the kernel's own loads); KVCOPY_F_DESC_UPLOAD
+ * first copies it into device memory with hipMemcpyAsync on `stream`. */
 #define KVCOPY_F_VALIDATE 0x1u    /* check the overlap rule (O(n log n)); also on when KVCOPY_VALIDATE=1 */
 #define KVCOPY_F_NO_COALESCE 0x2u /* skip merging of adjacent ranges (for measurement only) */
-#define KVCOPY_F_DESC_MAPPED 0x4u /* always read the worklist in place from pinned host staging */
-#define KVCOPY_F_DESC_UPLOAD 0x8u /* always upload the worklist to device memory first */
-#define KVCOPY_MAPPED_MAX_CHUNKS 1024u
+#define KVCOPY_F_DESC_UPLOAD 0x8u /* upload the worklist to device memory before the kernel */
 
 /*
  * kvcopy_coalesce -- merge list-consecutive adjacent ranges.
@@ -153,12 +148,15 @@ void kvcopy_plan_free(kvcopy_plan_t *plan);
  * persistent copy kernel runs.
  *
  * The library plans the batch (coalesce, chunk), writes the chunk worklist
- * into its own pinned staging slot (uploading large worklists with one async
- * copy, see the KVCOPY_F_DESC_* flags), and launches one kernel of
- * min(max_wgs, needed) workgroups of 4 wavefronts on `stream`.  Wavefronts
- * take chunks round-robin and move them with 16-byte nontemporal loads and
- * stores.  The call is not capturable into a HIP graph: the worklist is
- * planned on the host at call time.
+ * into its own pinned staging ring, and launches one kernel of
+ * min(max_wgs, needed) workgroups of 4 wavefronts on `stream`.  Each
+ * wavefront takes an equal contiguous share of the chunks and moves them
+ * with 16-byte nontemporal loads and stores.  The staging region is
+ * recycled once an event recorded after the kernel has completed; the call
+ * waits on the host only if the whole ring is still in use.  Calls on one
+ * device are serialised on the host while they plan (microseconds).  The
+ * call is not capturable into a HIP graph: the worklist is planned on the
+ * host at call time.
  *
  * src_addrs, dst_addrs, sizes: n entries (host arrays; may be NULL if n == 0).
  * n:       0 is a valid empty call (returns KVCOPY_OK, enqueues nothing).

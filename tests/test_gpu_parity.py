@@ -167,11 +167,11 @@ def test_irregular_chunk_sizes(K, dname, chunk):
     res.free()
 
 
-@pytest.mark.parametrize("flags", [1, 2, 4, 6, 8, 10])
+@pytest.mark.parametrize("flags", [0, 1, 2, 8, 10, 11])
 def test_irregular_flags(K, flags):
     from block_copy_amd.harness import Resident
     wl = W.irregular(seed=40 + flags, n=500, dir_=W.H2D, src_where="host", dst_where="device",
-                     shared_src=(flags == 4))
+                     shared_src=(flags in (0, 8)))
     res = Resident(wl)
     _say("irregular flags", flags)
     _run(res, [0], 16, flags=flags)
