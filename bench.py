@@ -438,6 +438,13 @@ def d2d_results(c: Ctx, args):
     for nbytes in (256 << 20, 1 << 30):
         ms = []
         for _ in range(5):
+            if args.no_events:          # profiler runs: wall clock around a synchronised copy
+                hiprt.stream_sync(c.sA)
+                t0 = time.perf_counter()
+                hiprt.memcpy_async(big.data_ptr() + (1 << 30), big.data_ptr(), nbytes, hiprt.D2D_KIND, c.sA)
+                hiprt.stream_sync(c.sA)
+                ms.append((time.perf_counter() - t0) * 1e3)
+                continue
             e1, e2 = hiprt.Event(), hiprt.Event()
             e1.record(c.sA)
             hiprt.memcpy_async(big.data_ptr() + (1 << 30), big.data_ptr(), nbytes, hiprt.D2D_KIND, c.sA)
