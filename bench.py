@@ -591,6 +591,19 @@ def bench_interference(c: Ctx, args):
                         s_, d_ = r.addrs[j]
                         for x, y, z in zip(s_.tolist(), d_.tolist(), b.size.tolist()):
                             hiprt.memcpy_async(y, x, z, kind, st)
+                elif isinstance(mode, str) and mode.startswith("job"):
+                    # paced pieces: the next piece goes only after the previous completed
+                    piece = int(mode.split(":")[1])
+                    jobs = [K.kvcopy_job_create(*r.addrs[j], wl.batches[j].size, wl.batches[j].dir,
+                                                0, piece, st.cuda_stream)
+                            for j, st in ((0, c.sA), (1, c.sB))]
+                    pending = list(jobs)
+                    while pending:
+                        pending = [jb for jb in pending if not K.kvcopy_job_poll(jb)]
+                        if pending:
+                            time.sleep(20e-6)      # yield the worker while a piece runs
+                    for jb in jobs:
+                        K.kvcopy_job_destroy(jb)
                 else:
                     r.submit(0, mode, c.sA)
                     r.submit(1, mode, c.sB)
@@ -630,7 +643,7 @@ def bench_interference(c: Ctx, args):
             th.join()
         return gpu_ms, wall_ms, moved[0] / dur, bursts[0]
 
-    modes = ["none", "direct", 8, 32, 128, 0]
+    modes = ["none", "direct", 8, 32, 128, 0, "job:1024", "job:2048", "job:4096"]
     results = {str(m): {"gpu": [], "wall": [], "rate": [], "bursts": 0} for m in modes}
     for rep in range(args.decode_runs):
         order = modes[rep % len(modes):] + modes[:rep % len(modes)]

@@ -21,17 +21,19 @@
 #include <stdlib.h>
 #include <string.h>
 
-#include <deque>
 #include <mutex>
 #include <vector>
 
 #include "kvcopy.h"
 #include "kvcopy_internal.h"
+#include "staging_ring.h"
 
 namespace kvc {
 namespace {
 
 thread_local int t_last_hip_error = 0;
+
+}  // namespace
 
 int hip_fail(hipError_t e)
 {
@@ -39,22 +41,35 @@ int hip_fail(hipError_t e)
     return KVCOPY_EHIP;
 }
 
+namespace {
+
 constexpr uint64_t kRingMinBytes = 16ull << 20;   // 16 MiB: ~700 K worklist records
 constexpr uint64_t kAlign = 256;
 
-struct InFlight {
-    uint64_t begin, end;   // byte range of the ring
-    hipEvent_t done;       // recorded after the kernel that reads the range
+// Event operations of the staging ring on HIP events.
+struct HipEventOps {
+    std::vector<hipEvent_t> *spare;   // completed events, reused by later calls
+    int poll(hipEvent_t e)
+    {
+        const hipError_t r = hipEventQuery(e);
+        if (r == hipErrorNotReady)
+            return 0;
+        return r == hipSuccess ? 1 : hip_fail(r);
+    }
+    int wait(hipEvent_t e)
+    {
+        const hipError_t r = hipEventSynchronize(e);
+        return r == hipSuccess ? 0 : hip_fail(r);
+    }
+    void recycle(hipEvent_t e) { spare->push_back(e); }
 };
 
 struct Staging {
     std::mutex mu;             // held for a whole call: planning is host-side and short
     uint8_t *host = nullptr;   // pinned, mapped (device address == host address)
     uint8_t *dev = nullptr;    // device twin, allocated on first KVCOPY_F_DESC_UPLOAD
-    uint64_t cap = 0;
-    uint64_t head = 0;         // next free byte
-    std::deque<InFlight> inflight;   // allocation order == ring order
-    std::vector<hipEvent_t> spare;   // completed events, reused
+    std::vector<hipEvent_t> spare;
+    StagingRing<hipEvent_t, HipEventOps> ring{HipEventOps{&spare}};
 };
 
 std::mutex g_staging_mu;
@@ -70,45 +85,18 @@ Staging *staging_for(int device)
     return g_staging[device];
 }
 
-// Retires the oldest in-flight region: waits for its kernel if `wait`, else
-// only polls.  Returns 1 if retired, 0 if still running (poll), or an error.
-int retire_front(Staging *st, bool wait)
-{
-    const InFlight f = st->inflight.front();
-    const hipError_t e = wait ? hipEventSynchronize(f.done) : hipEventQuery(f.done);
-    if (e == hipErrorNotReady)
-        return 0;
-    if (e != hipSuccess)
-        return hip_fail(e);
-    st->spare.push_back(f.done);
-    st->inflight.pop_front();
-    if (st->inflight.empty())
-        st->head = 0;
-    return 1;
-}
-
-int drain(Staging *st)
-{
-    while (!st->inflight.empty()) {
-        const int rc = retire_front(st, true);
-        if (rc < 0)
-            return rc;
-    }
-    return KVCOPY_OK;
-}
-
 // Makes the ring at least 4 x `need` bytes (and allocates the device twin if
 // `want_dev`).  Old buffers are released only after every kernel using them
 // has completed.
 int grow(Staging *st, uint64_t need, bool want_dev)
 {
-    uint64_t cap = st->cap ? st->cap : kRingMinBytes;
+    uint64_t cap = st->ring.capacity() ? st->ring.capacity() : kRingMinBytes;
     while (cap < 4 * need)
         cap *= 2;
-    const bool resize = cap != st->cap;
+    const bool resize = cap != st->ring.capacity();
     if (!resize && (!want_dev || st->dev))
         return KVCOPY_OK;
-    int rc = drain(st);
+    int rc = st->ring.drain();
     if (rc != KVCOPY_OK)
         return rc;
     if (resize) {
@@ -118,7 +106,7 @@ int grow(Staging *st, uint64_t need, bool want_dev)
             hipFree(st->dev);
         st->host = nullptr;
         st->dev = nullptr;
-        st->cap = 0;
+        st->ring.reset(0);
     }
     hipError_t e;
     if (st->host == nullptr) {
@@ -128,61 +116,15 @@ int grow(Staging *st, uint64_t need, bool want_dev)
             return e == hipErrorOutOfMemory ? KVCOPY_ENOMEM : hip_fail(e);
         }
     }
+    st->ring.reset(cap);
     if (want_dev && st->dev == nullptr) {
         e = hipMalloc((void **)&st->dev, cap);
         if (e != hipSuccess) {
             st->dev = nullptr;
-            st->cap = cap;   // the host ring is valid
             return e == hipErrorOutOfMemory ? KVCOPY_ENOMEM : hip_fail(e);
         }
     }
-    st->cap = cap;
-    st->head = 0;
     return KVCOPY_OK;
-}
-
-// Reserves `need` bytes at the ring's head (wrapping to 0 when the end of the
-// ring is too short), retiring completed regions and waiting for running
-// ones only when they are in the way.  *off receives the region's start.
-int reserve(Staging *st, uint64_t need, bool want_dev, uint64_t *off)
-{
-    if (4 * need > st->cap || (want_dev && st->dev == nullptr)) {
-        const int rc = grow(st, need, want_dev);
-        if (rc != KVCOPY_OK)
-            return rc;
-    }
-    while (!st->inflight.empty()) {   // retire whatever has finished, without waiting
-        const int rc = retire_front(st, false);
-        if (rc < 0)
-            return rc;
-        if (rc == 0)
-            break;
-    }
-    for (;;) {
-        if (st->inflight.empty()) {
-            *off = 0;
-            return KVCOPY_OK;
-        }
-        const uint64_t head = st->head, tail = st->inflight.front().begin;
-        if (head > tail) {          // used [tail, head): free [head, cap) and [0, tail)
-            if (head + need <= st->cap) {
-                *off = head;
-                return KVCOPY_OK;
-            }
-            if (need <= tail) {
-                *off = 0;
-                return KVCOPY_OK;
-            }
-        } else if (head < tail) {   // used wraps: free [head, tail)
-            if (head + need <= tail) {
-                *off = head;
-                return KVCOPY_OK;
-            }
-        }                           // head == tail: the ring is full
-        const int rc = retire_front(st, true);
-        if (rc < 0)
-            return rc;
-    }
 }
 
 uint32_t grid_for(uint64_t n_chunks, int max_wgs)
@@ -202,8 +144,12 @@ int run_locked(Staging *st, const uint64_t *src, const uint64_t *dst, const uint
     const bool upload = (flags & KVCOPY_F_DESC_UPLOAD) != 0;
     const uint64_t need = (pre.bound * sizeof(ChunkRec) + kAlign - 1) / kAlign * kAlign;
     uint64_t off = 0;
-    int rc = reserve(st, need, upload, &off);
-    if (rc != KVCOPY_OK)
+    int rc;
+    if (4 * need > st->ring.capacity() || (upload && st->dev == nullptr)) {
+        if ((rc = grow(st, need, upload)) != KVCOPY_OK)
+            return rc;
+    }
+    if ((rc = st->ring.reserve(need, &off)) != KVCOPY_OK)
         return rc;
     ChunkRec *host = reinterpret_cast<ChunkRec *>(st->host + off);
     const uint64_t n_chunks =
@@ -237,8 +183,7 @@ int run_locked(Staging *st, const uint64_t *src, const uint64_t *dst, const uint
         st->spare.push_back(done);
         return hip_fail(e);
     }
-    st->inflight.push_back(InFlight{off, off + used, done});
-    st->head = off + used;
+    st->ring.commit(off, used, done);
     return KVCOPY_OK;
 }
 

@@ -29,7 +29,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvcopy.s
 # Every symbol include/kvcopy.h declares.
 EXPORTS = ("kvcopy_coalesce", "kvcopy_plan", "kvcopy_plan_free", "kvcopy_batch",
            "kvcopy_batch_ex", "kvcopy_strerror", "kvcopy_last_hip_error",
-           "kvcopy_host_alloc_mapped", "kvcopy_host_free")
+           "kvcopy_host_alloc_mapped", "kvcopy_host_free", "kvcopy_job_create",
+           "kvcopy_job_poll", "kvcopy_job_wait", "kvcopy_job_destroy")
 
 
 class KvcopyError(RuntimeError):
@@ -84,6 +85,16 @@ def _load():
     lib.kvcopy_host_alloc_mapped.argtypes = [ctypes.c_uint64, ctypes.POINTER(ctypes.c_void_p)]
     lib.kvcopy_host_free.restype = ctypes.c_int
     lib.kvcopy_host_free.argtypes = [ctypes.c_void_p]
+    lib.kvcopy_job_create.restype = ctypes.c_int
+    lib.kvcopy_job_create.argtypes = [u64p, u64p, u64p, ctypes.c_uint64, ctypes.c_int, ctypes.c_int,
+                                      ctypes.c_uint64, ctypes.c_void_p,
+                                      ctypes.POINTER(ctypes.c_void_p)]
+    lib.kvcopy_job_poll.restype = ctypes.c_int
+    lib.kvcopy_job_poll.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int)]
+    lib.kvcopy_job_wait.restype = ctypes.c_int
+    lib.kvcopy_job_wait.argtypes = [ctypes.c_void_p]
+    lib.kvcopy_job_destroy.restype = None
+    lib.kvcopy_job_destroy.argtypes = [ctypes.c_void_p]
     return lib
 
 
@@ -235,3 +246,38 @@ class HostBuffer:
             self.free()
         except Exception:
             pass
+
+
+def kvcopy_job_create(src_addrs, dst_addrs, sizes, dir: int, max_wgs: int = WGS_ALL,
+                      piece_descs: int = 0, stream=None) -> int:
+    """A paced job (see include/kvcopy.h); returns its handle."""
+    s, sp = _u64(src_addrs)
+    d, dp = _u64(dst_addrs)
+    z, zp = _u64(sizes)
+    n = _n(s, d, z)
+    h = ctypes.c_void_p(0)
+    st = ctypes.c_void_p(int(stream) if stream else 0)
+    rc = lib.kvcopy_job_create(sp, dp, zp, n, int(dir), int(max_wgs), int(piece_descs), st,
+                               ctypes.byref(h))
+    if rc != OK:
+        raise KvcopyError(rc, "kvcopy_job_create")
+    return int(h.value)
+
+
+def kvcopy_job_poll(job: int) -> bool:
+    """Submits the next piece if the previous one completed; True once all completed."""
+    done = ctypes.c_int(0)
+    rc = lib.kvcopy_job_poll(ctypes.c_void_p(job), ctypes.byref(done))
+    if rc != OK:
+        raise KvcopyError(rc, "kvcopy_job_poll")
+    return bool(done.value)
+
+
+def kvcopy_job_wait(job: int) -> None:
+    rc = lib.kvcopy_job_wait(ctypes.c_void_p(job))
+    if rc != OK:
+        raise KvcopyError(rc, "kvcopy_job_wait")
+
+
+def kvcopy_job_destroy(job: int) -> None:
+    lib.kvcopy_job_destroy(ctypes.c_void_p(job))

@@ -214,6 +214,43 @@ int kvcopy_host_alloc_mapped(uint64_t bytes, void **out);
 /* Release memory from kvcopy_host_alloc_mapped.  NULL is a no-op. */
 int kvcopy_host_free(void *p);
 
+/*
+ * Paced submission with completion backpressure.
+ *
+ * [PF] "Follow-up", item 2, and "Proposed direction": splitting a transfer
+ * into pieces helps co-running decode only if each piece is submitted after
+ * the previous one has completed; enqueueing all pieces at once does not,
+ * and a fixed sleep adds nothing.  The progress belongs in the caller's
+ * transfer worker as an event-driven state machine, which a job is: it
+ * holds a batch split into pieces of at most `piece_descs` descriptors and
+ * submits piece k+1 (as one kvcopy_batch on `stream`) only from a
+ * kvcopy_job_poll call that finds piece k's kernel completed.  Nothing here
+ * blocks except kvcopy_job_wait.
+ *
+ * kvcopy_job_create: copies the three arrays (the caller may reuse them at
+ *   once); submits nothing.  piece_descs == 0 means one piece (the whole
+ *   batch).  Validation as kvcopy_batch (the whole list is checked here, so
+ *   a piece never fails on its arguments later).
+ *   errors: KVCOPY_EINVAL (also out == NULL), KVCOPY_EALIGN, KVCOPY_EOVERLAP
+ *   (validate mode), KVCOPY_ENOMEM.
+ * kvcopy_job_poll: if no piece is in flight or the one in flight has
+ *   completed, submits the next piece; *done = 1 once every piece has
+ *   completed (then further polls do nothing).  Never waits.
+ *   errors: KVCOPY_EINVAL (NULL job or done), as kvcopy_batch for a submit.
+ * kvcopy_job_wait: polls until done, blocking on each piece's event.
+ * kvcopy_job_destroy: frees the job (call it only once no piece is in
+ *   flight, i.e. after done, or after a failed poll).  NULL is a no-op.
+ * A job is used by one thread at a time.
+ */
+typedef struct kvcopy_job kvcopy_job_t;
+
+int kvcopy_job_create(const uint64_t *src_addrs, const uint64_t *dst_addrs, const uint64_t *sizes,
+                      uint64_t n, int dir, int max_wgs, uint64_t piece_descs, hipStream_t stream,
+                      kvcopy_job_t **out);
+int kvcopy_job_poll(kvcopy_job_t *job, int *done);
+int kvcopy_job_wait(kvcopy_job_t *job);
+void kvcopy_job_destroy(kvcopy_job_t *job);
+
 #ifdef __cplusplus
 }
 #endif

@@ -231,3 +231,119 @@ def test_error_paths_enqueue_nothing(K):
         if a.fill == "sentinel":
             assert np.all(res.image(i) == a.sentinel), "an error path enqueued work"
     res.free()
+
+
+# ---------------------------------------------------------------------------
+# The staging ring under load: wrap-around, growth, several host threads
+# ---------------------------------------------------------------------------
+
+def test_many_calls_wrap_the_staging_ring(K):
+    """More worklist bytes queued than the ring holds: calls wait for ring
+    space (kernels on two streams finish out of order) and every call still
+    copies the right bytes."""
+    from block_copy_amd.harness import Resident
+    wl = W.irregular(seed=80, n=3000, max_size=4096, dir_=W.D2D)   # ~3,000 chunks = 72 KB of records
+    res = Resident(wl)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    _say("ring wrap: 600 calls on two streams")
+    for i in range(600):                                              # ~43 MB of records > 16 MiB
+        res.submit(0, 2 if i % 2 else 0, s1 if i % 2 else s2, flags=K.F_DESC_UPLOAD if i % 3 == 0 else 0)
+    torch.cuda.synchronize()
+    _check(res, [0], "after ring wrap")
+    res.free()
+
+
+def test_ring_growth_with_calls_in_flight(K):
+    """A call whose worklist needs more than a quarter of the ring grows it
+    while earlier calls are still queued."""
+    from block_copy_amd.harness import Resident
+    small = W.irregular(seed=81, n=500, max_size=8192, dir_=W.D2D)
+    big = W.irregular(seed=82, n=240, max_size=32768, dir_=W.D2D)    # ~3.9 MB payload
+    rs, rb = Resident(small), Resident(big)
+    s1 = torch.cuda.Stream()
+    _say("ring growth")
+    for _ in range(20):
+        rs.submit(0, 1, s1)
+    rb.submit(0, 64, s1, chunk_bytes=16)          # 16-byte chunks: > 240 K records (> 4 MiB)
+    for _ in range(5):
+        rs.submit(0, 1, s1)
+    torch.cuda.synchronize()
+    _check(rs, [0], "small batch around ring growth")
+    _check(rb, [0], "batch that grew the ring")
+    rs.free()
+    rb.free()
+
+
+def test_threads_share_the_library(K):
+    """Four host threads, each with its own stream and arenas, submit at once."""
+    import threading
+    from block_copy_amd.harness import Resident
+    wls = [W.irregular(seed=90 + t, n=400, max_size=16384, dir_=d, src_where=sw, dst_where=dw)
+           for t, (d, sw, dw) in enumerate([DIRS["d2d"], DIRS["h2d"], DIRS["d2h"], DIRS["d2d"]])]
+    rs = [Resident(wl) for wl in wls]
+    streams = [torch.cuda.Stream() for _ in rs]
+    errors = []
+
+    def worker(t):
+        try:
+            for i in range(30):
+                rs[t].submit(0, [0, 8, 32][i % 3], streams[t])
+        except Exception as e:   # noqa: BLE001 - reported below
+            errors.append(e)
+
+    _say("four threads")
+    th = [threading.Thread(target=worker, args=(t,)) for t in range(4)]
+    for x in th:
+        x.start()
+    for x in th:
+        x.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for t, r in enumerate(rs):
+        _check(r, [0], f"thread {t}")
+        r.free()
+
+
+
+# ---------------------------------------------------------------------------
+# Paced jobs: a batch in pieces, each submitted after the previous completed
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("piece", [0, 1, 7, 100, 2048])
+def test_job_pieces_give_the_same_bytes(K, piece):
+    import time
+    from block_copy_amd.harness import Resident
+    wl = W.kv_blocks(seed=3, directions="both", n=2048, pool_blocks=8192)
+    res = Resident(wl)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    _say("job pieces", piece)
+    jobs = []
+    for j, st in ((0, s1), (1, s2)):
+        s, d = res.addrs[j]
+        jobs.append(K.kvcopy_job_create(s, d, wl.batches[j].size, wl.batches[j].dir, 16, piece,
+                                        st.cuda_stream))
+    pending = list(jobs)
+    t0 = time.time()
+    while pending:
+        pending = [jb for jb in pending if not K.kvcopy_job_poll(jb)]
+        assert time.time() - t0 < 60, "job did not finish"
+    for jb in jobs:
+        K.kvcopy_job_destroy(jb)
+    torch.cuda.synchronize()
+    _check(res, [0, 1], f"jobs piece={piece}")
+    res.free()
+
+
+def test_job_wait(K):
+    from block_copy_amd.harness import Resident
+    wl = W.irregular(seed=95, n=300, dir_=W.D2D)
+    res = Resident(wl)
+    s, d = res.addrs[0]
+    _say("job wait")
+    jb = K.kvcopy_job_create(s, d, wl.batches[0].size, K.D2D, 0, 32)
+    K.kvcopy_job_wait(jb)
+    assert K.kvcopy_job_poll(jb) is True
+    K.kvcopy_job_destroy(jb)
+    torch.cuda.synchronize()
+    _check(res, [0], "job wait")
+    res.free()

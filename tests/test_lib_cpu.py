@@ -197,3 +197,28 @@ def test_plan_edge_cases(K):
     assert p.n_chunks == 1 and p.size.tolist() == [8]
     with pytest.raises(K.KvcopyError):
         K.kvcopy_plan([8], [16], [8], 8)           # chunk must be a multiple of 16
+
+
+def test_job_argument_errors(K):
+    import ctypes
+    s = np.array([0x10000, 0x20000], np.uint64)
+    d = np.array([0x30000, 0x40000], np.uint64)
+    z = np.array([4096, 4096], np.uint64)
+    with pytest.raises(K.KvcopyError) as e:
+        K.kvcopy_job_create(s, d, z + 4, K.H2D)
+    assert e.value.code == K.EALIGN
+    with pytest.raises(K.KvcopyError) as e:
+        K.kvcopy_job_create(s, d, z, 7)
+    assert e.value.code == K.EINVAL
+    with pytest.raises(K.KvcopyError) as e:
+        K.kvcopy_job_create(s, d, z, K.D2D, -2)
+    assert e.value.code == K.EINVAL
+    u = ctypes.POINTER(ctypes.c_uint64)()
+    assert K.lib.kvcopy_job_create(u, u, u, 0, 0, 0, 0, None, None) == K.EINVAL
+    assert K.lib.kvcopy_job_poll(None, ctypes.byref(ctypes.c_int())) == K.EINVAL
+    assert K.lib.kvcopy_job_wait(None) == K.EINVAL
+    K.lib.kvcopy_job_destroy(None)
+    # an empty job is done at the first poll, without touching the GPU
+    j = K.kvcopy_job_create([], [], [], K.D2D)
+    assert K.kvcopy_job_poll(j) is True
+    K.kvcopy_job_destroy(j)

@@ -1,4 +1,5 @@
-"""Native checks of the host planner's internals (compiled with g++, CPU only)."""
+"""Native checks of host-side internals: the planner and the staging ring
+(compiled with g++, CPU only)."""
 import os
 import subprocess
 
@@ -28,3 +29,14 @@ def test_planner_under_sanitizers(tmp_path):
                     os.path.join(csrc, "plan.cpp"), "-o", str(exe)], check=True)
     out = subprocess.run([str(exe)], capture_output=True, text=True)
     assert out.returncode == 0, out.stdout + out.stderr
+
+
+def test_staging_ring_never_hands_out_bytes_in_use(tmp_path):
+    exe = tmp_path / "ring_check"
+    csrc = os.path.join(ROOT, "block_copy_amd", "csrc")
+    subprocess.run(["g++", "-O1", "-g", "-std=c++17", "-fsanitize=address,undefined",
+                    "-fno-sanitize-recover=all", "-I" + csrc,
+                    os.path.join(ROOT, "tests", "native", "ring_check.cpp"), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert out.returncode == 0, out.stdout + out.stderr
+    assert out.stdout.startswith("ok")
