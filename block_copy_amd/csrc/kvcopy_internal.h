@@ -84,4 +84,14 @@ constexpr uint32_t kThreadsPerWG = 64 * kWavesPerWG;
 hipError_t launch_copy(const ChunkRec *recs, uint32_t n_chunks, uint32_t grid, int dir,
                        hipStream_t stream);
 
+// ---- device-resident batches (device_batch.hip) ---------------------------
+
+uint64_t device_workspace_bytes(uint64_t max_n);
+
+// Enqueues the plan kernel (one workgroup) and the copy kernel (`grid`
+// workgroups) on `stream`.
+hipError_t launch_device_batch(const uint64_t *src, const uint64_t *dst, const uint64_t *size,
+                               const uint64_t *d_n, uint64_t max_n, uint32_t chunk, uint32_t grid,
+                               void *workspace, hipStream_t stream);
+
 }  // namespace kvc

@@ -29,85 +29,7 @@
 namespace kvc {
 namespace {
 
-typedef uint32_t v4u __attribute__((ext_vector_type(4)));
-#define KVC_GLOBAL __attribute__((address_space(1)))
-
-// Raw buffer resources.  The fourth descriptor word is the gfx9-family raw
-// buffer format (32-bit data format, no swizzle, no stride).  A buffer access
-// at an offset at or beyond num_records is dropped (stores) or reads zero
-// (loads); every vector access here is either wholly inside or wholly
-// outside its range, so the lanes past the end of a short row need no exec
-// masking.  Without per-row branches the compiler keeps all loads of a pass
-// in flight and waits with vmcnt(N) before each store, never vmcnt(0).
-constexpr int kRsrcWord3 = 0x00020000;
-// Cache policy: loads plain, stores nontemporal ("nt", bit 1 of the
-// cache-policy operand on gfx940+).  Measured on MI355X for 65,536 random
-// 4 KiB blocks between two 1 GiB device pools: plain loads with nt stores
-// move 6.4-6.5 TB/s of HBM traffic, against 4.8-4.9 TB/s with nt on both
-// sides or on neither (and 5.3 TB/s for one contiguous hipMemcpy).  For
-// mapped host memory the four combinations are within noise of each other.
-constexpr int kLoadPolicy = 0;
-constexpr int kStorePolicy = 2;
-constexpr uint32_t kRowBytes = 64u * 16u;          // one wavefront instruction: 1 KiB
-constexpr int kMaxRows = 16;                       // 16 KiB per pass, 64 VGPRs of data
-constexpr uint32_t kPassBytes = kRowBytes * kMaxRows;
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(uint64_t base, uint32_t bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(base), 0, (int)bytes,
-                                             kRsrcWord3);
-}
-
-// R rows of 1 KiB: all loads first, then all stores.
-template <int R>
-__device__ __forceinline__ void copy_rows(__amdgpu_buffer_rsrc_t rs, __amdgpu_buffer_rsrc_t rd,
-                                          uint32_t voff)
-{
-    v4u v[R];
-#pragma unroll
-    for (int j = 0; j < R; ++j)
-        v[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(voff + j * kRowBytes), 0,
-                                                     kLoadPolicy);
-#pragma unroll
-    for (int j = 0; j < R; ++j)
-        __builtin_amdgcn_raw_buffer_store_b128(v[j], rd, (int)(voff + j * kRowBytes), 0,
-                                               kStorePolicy);
-}
-
-// One wavefront copies one chunk.  src, dst and bytes are wave-uniform.
-__device__ __forceinline__ void copy_chunk(uint64_t src, uint64_t dst, uint32_t bytes,
-                                           uint32_t lane)
-{
-    const uint32_t body = bytes & ~15u;
-    const uint32_t voff = lane * 16u;
-    for (uint32_t off = 0; off < body; off += kPassBytes) {
-        const uint32_t pb = body - off < kPassBytes ? body - off : kPassBytes;
-        const __amdgpu_buffer_rsrc_t rs = rsrc(src + off, pb);
-        const __amdgpu_buffer_rsrc_t rd = rsrc(dst + off, pb);
-        switch ((pb + kRowBytes - 1) / kRowBytes) {
-        case 1: copy_rows<1>(rs, rd, voff); break;
-        case 2: copy_rows<2>(rs, rd, voff); break;
-        case 3: copy_rows<3>(rs, rd, voff); break;
-        case 4: copy_rows<4>(rs, rd, voff); break;
-        case 5: copy_rows<5>(rs, rd, voff); break;
-        case 6: copy_rows<6>(rs, rd, voff); break;
-        case 7: copy_rows<7>(rs, rd, voff); break;
-        case 8: copy_rows<8>(rs, rd, voff); break;
-        case 9: copy_rows<9>(rs, rd, voff); break;
-        case 10: copy_rows<10>(rs, rd, voff); break;
-        case 11: copy_rows<11>(rs, rd, voff); break;
-        case 12: copy_rows<12>(rs, rd, voff); break;
-        case 13: copy_rows<13>(rs, rd, voff); break;
-        case 14: copy_rows<14>(rs, rd, voff); break;
-        case 15: copy_rows<15>(rs, rd, voff); break;
-        default: copy_rows<16>(rs, rd, voff); break;
-        }
-    }
-    if ((bytes & 8u) && lane == 0) {   // a range that ends in an odd 8-byte word
-        const uint64_t w = *reinterpret_cast<KVC_GLOBAL const uint64_t *>(src + body);
-        __builtin_nontemporal_store(w, reinterpret_cast<KVC_GLOBAL uint64_t *>(dst + body));
-    }
-}
+#include "copy_chunk.h"
 
 // The persistent loop.  Wavefront w of W owns the contiguous chunk range
 // [w*C/W, (w+1)*C/W): every wavefront gets the same number of chunks to

@@ -246,6 +246,35 @@ extern "C" int kvcopy_batch_ex(const uint64_t *src_addrs, const uint64_t *dst_ad
                       ev_begin, ev_end);
 }
 
+extern "C" uint64_t kvcopy_device_workspace_bytes(uint64_t max_n)
+{
+    return device_workspace_bytes(max_n);
+}
+
+extern "C" int kvcopy_batch_device(const uint64_t *d_src, const uint64_t *d_dst,
+                                   const uint64_t *d_sizes, const uint64_t *d_n, uint64_t max_n,
+                                   int dir, int max_wgs, uint32_t chunk_bytes, void *workspace,
+                                   hipStream_t stream)
+{
+    if (dir != KVCOPY_H2D && dir != KVCOPY_D2H && dir != KVCOPY_D2D)
+        return KVCOPY_EINVAL;
+    if (max_wgs < 0 || max_n > KVCOPY_MAX_DESCS)
+        return KVCOPY_EINVAL;
+    if (chunk_bytes == 0)
+        chunk_bytes = KVCOPY_CHUNK_DEFAULT;
+    if ((chunk_bytes & 15u) || chunk_bytes > KVCOPY_CHUNK_MAX)
+        return KVCOPY_EINVAL;
+    if (max_n == 0)
+        return KVCOPY_OK;
+    if (!d_src || !d_dst || !d_sizes || !d_n || !workspace ||
+        (reinterpret_cast<uintptr_t>(workspace) & 255u))
+        return KVCOPY_EINVAL;
+    const uint32_t grid = max_wgs ? (uint32_t)max_wgs : 1024u;
+    const hipError_t e =
+        launch_device_batch(d_src, d_dst, d_sizes, d_n, max_n, chunk_bytes, grid, workspace, stream);
+    return e == hipSuccess ? KVCOPY_OK : hip_fail(e);
+}
+
 extern "C" int kvcopy_batch(const uint64_t *src_addrs, const uint64_t *dst_addrs,
                             const uint64_t *sizes, uint64_t n, int dir, int max_wgs,
                             hipStream_t stream)

@@ -30,7 +30,9 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvcopy.s
 EXPORTS = ("kvcopy_coalesce", "kvcopy_plan", "kvcopy_plan_free", "kvcopy_batch",
            "kvcopy_batch_ex", "kvcopy_strerror", "kvcopy_last_hip_error",
            "kvcopy_host_alloc_mapped", "kvcopy_host_free", "kvcopy_job_create",
-           "kvcopy_job_poll", "kvcopy_job_wait", "kvcopy_job_destroy")
+           "kvcopy_job_poll", "kvcopy_job_wait", "kvcopy_job_destroy",
+           "kvcopy_device_workspace_bytes", "kvcopy_batch_device")
+DEVICE_BAD_ALIGN, DEVICE_TOO_MANY_CHUNKS = 1, 2
 
 
 class KvcopyError(RuntimeError):
@@ -95,6 +97,13 @@ def _load():
     lib.kvcopy_job_wait.argtypes = [ctypes.c_void_p]
     lib.kvcopy_job_destroy.restype = None
     lib.kvcopy_job_destroy.argtypes = [ctypes.c_void_p]
+    lib.kvcopy_device_workspace_bytes.restype = ctypes.c_uint64
+    lib.kvcopy_device_workspace_bytes.argtypes = [ctypes.c_uint64]
+    lib.kvcopy_batch_device.restype = ctypes.c_int
+    lib.kvcopy_batch_device.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int,
+                                        ctypes.c_int, ctypes.c_uint32, ctypes.c_void_p,
+                                        ctypes.c_void_p]
     return lib
 
 
@@ -281,3 +290,21 @@ def kvcopy_job_wait(job: int) -> None:
 
 def kvcopy_job_destroy(job: int) -> None:
     lib.kvcopy_job_destroy(ctypes.c_void_p(job))
+
+
+def kvcopy_device_workspace_bytes(max_n: int) -> int:
+    return int(lib.kvcopy_device_workspace_bytes(int(max_n)))
+
+
+def kvcopy_batch_device(d_src: int, d_dst: int, d_sizes: int, d_n: int, max_n: int, dir: int,
+                        max_wgs: int, workspace: int, stream=None, chunk_bytes: int = 0,
+                        check: bool = True) -> int:
+    """Device-resident batch (see include/kvcopy.h).  All pointers are device
+    addresses (ints), e.g. torch tensors' data_ptr()."""
+    st = ctypes.c_void_p(int(stream) if stream else 0)
+    p = lambda x: ctypes.c_void_p(int(x) if x else 0)  # noqa: E731
+    rc = lib.kvcopy_batch_device(p(d_src), p(d_dst), p(d_sizes), p(d_n), int(max_n), int(dir),
+                                 int(max_wgs), int(chunk_bytes), p(workspace), st)
+    if check and rc != OK:
+        raise KvcopyError(rc, "kvcopy_batch_device")
+    return rc

@@ -251,6 +251,48 @@ int kvcopy_job_poll(kvcopy_job_t *job, int *done);
 int kvcopy_job_wait(kvcopy_job_t *job);
 void kvcopy_job_destroy(kvcopy_job_t *job);
 
+/*
+ * Device-resident batches (graph-capturable).
+ *
+ * [FT] "What we changed": the gather reads its miss count on the device, so
+ * the launch has a fixed shape and a CUDA graph can capture it.  Here the
+ * three descriptor arrays and the count live in device memory, written by
+ * earlier GPU work; kvcopy_batch_device enqueues two kernels of fixed shape
+ * on `stream` and does no host planning, allocation or synchronisation, so
+ * the call can be captured in a HIP graph and replayed with new contents.
+ *   1. one workgroup reads the count n (clamped to max_n), checks 8-byte
+ *      alignment of every address and size, and writes into the workspace
+ *      the exclusive prefix sum of the per-descriptor chunk counts
+ *      ceil(size / chunk_bytes) (the chunk numbering of kvcopy_plan, but
+ *      without coalescing);
+ *   2. max_wgs workgroups copy the chunks, wavefront w of W taking chunks
+ *      [w*C/W, (w+1)*C/W).
+ * If any descriptor is misaligned, nothing is copied and the workspace's
+ * first 64-bit word (its status) is KVCOPY_DEVICE_BAD_ALIGN; it is
+ * KVCOPY_DEVICE_TOO_MANY_CHUNKS if the batch has 2^31 chunks or more, else
+ * 0 once the plan kernel has run.  Destinations must not overlap each other or
+ * a source (not checked on the device).
+ *
+ * d_src, d_dst, d_sizes: device arrays of max_n uint64 each (entries past
+ *   the device count are not read).  d_n: device uint64, the count.
+ * max_wgs: the copy kernel's workgroups; 0 selects 1024.
+ * chunk_bytes: 0 = KVCOPY_CHUNK_DEFAULT; else a multiple of 16, at most
+ *   KVCOPY_CHUNK_MAX.
+ * workspace: caller-owned device memory of kvcopy_device_workspace_bytes(max_n)
+ *   bytes, 256-byte aligned; it must not be used by another call that may
+ *   run at the same time.
+ * errors (host side, nothing enqueued): KVCOPY_EINVAL (NULL pointer with
+ *   max_n > 0, max_n > KVCOPY_MAX_DESCS, bad dir / max_wgs / chunk_bytes,
+ *   misaligned workspace); KVCOPY_EHIP.  max_n == 0 is a no-op.
+ */
+#define KVCOPY_DEVICE_BAD_ALIGN 1
+#define KVCOPY_DEVICE_TOO_MANY_CHUNKS 2
+
+uint64_t kvcopy_device_workspace_bytes(uint64_t max_n);
+int kvcopy_batch_device(const uint64_t *d_src, const uint64_t *d_dst, const uint64_t *d_sizes,
+                        const uint64_t *d_n, uint64_t max_n, int dir, int max_wgs,
+                        uint32_t chunk_bytes, void *workspace, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -222,3 +222,20 @@ def test_job_argument_errors(K):
     j = K.kvcopy_job_create([], [], [], K.D2D)
     assert K.kvcopy_job_poll(j) is True
     K.kvcopy_job_destroy(j)
+
+
+def test_device_batch_argument_errors(K):
+    call = lambda *a, **k: K.kvcopy_batch_device(*a, check=False, **k)  # noqa: E731
+    assert call(0, 0, 0, 0, 0, K.D2D, 8, 0) == K.OK                 # max_n == 0: no-op
+    assert call(0, 0, 0, 0, 10, K.D2D, 8, 0) == K.EINVAL            # NULL arrays
+    good = dict(d_src=1 << 20, d_dst=2 << 20, d_sizes=3 << 20, d_n=4 << 20)
+    assert call(*good.values(), 10, 9, 8, 5 << 20) == K.EINVAL      # bad dir
+    assert call(*good.values(), 10, K.D2D, -1, 5 << 20) == K.EINVAL  # bad max_wgs
+    assert call(*good.values(), 10, K.D2D, 8, (5 << 20) + 8) == K.EINVAL   # misaligned workspace
+    assert call(*good.values(), 10, K.D2D, 8, 5 << 20, chunk_bytes=24) == K.EINVAL
+    assert call(*good.values(), 2**31 + 1, K.D2D, 8, 5 << 20) == K.EINVAL
+    # workspace: 32-byte header + 8 bytes per prefix entry, rounded up to 256
+    assert K.kvcopy_device_workspace_bytes(0) == 256
+    assert K.kvcopy_device_workspace_bytes(27) == 256
+    assert K.kvcopy_device_workspace_bytes(28) == 512
+    assert K.kvcopy_device_workspace_bytes(1000) == (32 + 8 * 1001 + 255) // 256 * 256
