@@ -643,7 +643,7 @@ def bench_interference(c: Ctx, args):
             th.join()
         return gpu_ms, wall_ms, moved[0] / dur, bursts[0]
 
-    modes = ["none", "direct", 8, 32, 128, 0, "job:1024", "job:2048", "job:4096"]
+    modes = ["none", "direct", 1, 2, 8, 32, 128, 0, "job:1024", "job:2048", "job:4096"]
     results = {str(m): {"gpu": [], "wall": [], "rate": [], "bursts": 0} for m in modes}
     for rep in range(args.decode_runs):
         order = modes[rep % len(modes):] + modes[:rep % len(modes)]

@@ -92,9 +92,12 @@ def test_device_count_is_clamped_to_max_n(K):
     max_n = 150
     dn = _dev_u64([10**9])
     ws, base = _workspace(K, max_n)
+    # keep the device arrays referenced until the kernels have run: a
+    # temporary's memory goes back to torch's allocator at once
+    ds, dt, dz = _dev_u64(s), _dev_u64(d), _dev_u64(b.size)
     _say("device count clamp")
-    K.kvcopy_batch_device(_dev_u64(s).data_ptr(), _dev_u64(d).data_ptr(), _dev_u64(b.size).data_ptr(),
-                          dn.data_ptr(), max_n, W.D2D, 8, base)
+    K.kvcopy_batch_device(ds.data_ptr(), dt.data_ptr(), dz.data_ptr(), dn.data_ptr(), max_n,
+                          W.D2D, 8, base)
     torch.cuda.synchronize()
     exp = np.full(wl.arenas[1].nbytes, wl.arenas[1].sentinel, np.uint8)
     oracle.copy(s[:max_n], d[:max_n], b.size[:max_n], [(res.bases[0], wl.arenas[0].host_image())],
@@ -112,9 +115,10 @@ def test_device_misaligned_descriptor_copies_nothing(K):
     z = b.size.copy()
     z[57] += 4
     ws, base = _workspace(K, 100)
+    ds, dt, dz, dn = _dev_u64(s), _dev_u64(d), _dev_u64(z), _dev_u64([100])
     _say("device misaligned")
-    K.kvcopy_batch_device(_dev_u64(s).data_ptr(), _dev_u64(d).data_ptr(), _dev_u64(z).data_ptr(),
-                          _dev_u64([100]).data_ptr(), 100, W.D2D, 8, base)
+    K.kvcopy_batch_device(ds.data_ptr(), dt.data_ptr(), dz.data_ptr(), dn.data_ptr(), 100, W.D2D,
+                          8, base)
     torch.cuda.synchronize()
     assert _status(base) == K.DEVICE_BAD_ALIGN
     assert np.all(res.image(1) == wl.arenas[1].sentinel)
@@ -128,9 +132,10 @@ def test_device_empty_count(K):
     b = wl.batches[0]
     s, d = res.addrs[0]
     ws, base = _workspace(K, 50)
+    ds, dt, dz, dn = _dev_u64(s), _dev_u64(d), _dev_u64(b.size), _dev_u64([0])
     _say("device count 0")
-    K.kvcopy_batch_device(_dev_u64(s).data_ptr(), _dev_u64(d).data_ptr(), _dev_u64(b.size).data_ptr(),
-                          _dev_u64([0]).data_ptr(), 50, W.D2D, 8, base)
+    K.kvcopy_batch_device(ds.data_ptr(), dt.data_ptr(), dz.data_ptr(), dn.data_ptr(), 50, W.D2D,
+                          8, base)
     torch.cuda.synchronize()
     assert _status(base) == 0
     assert np.all(res.image(1) == wl.arenas[1].sentinel)
