@@ -154,7 +154,7 @@ def test_device_batch_in_a_hip_graph(K):
     """Captured once; replayed with new descriptor lists and counts written by
     eager copies between replays; every replay checked against the oracle."""
     from block_copy_amd.harness import Resident
-    slot, n_slots, max_n = 8192, 512, 600
+    slot, n_slots, max_n = 8192, 1024, 600
     wl = W.Workload("graph", [W.Arena("src", 4 << 20, "device", "random", seed=77),
                               W.Arena("dst", slot * n_slots, "host", "sentinel")], [])
     res = Resident(wl)
