@@ -54,7 +54,8 @@ REC_BYTES = 24            # one worklist record per chunk
 KERNEL_NAMES = {0: "kvcopy_h2d_kernel", 1: "kvcopy_d2h_kernel", 2: "kvcopy_d2d_kernel"}
 COUNTERS_KV = os.path.join(ROOT, "profiles", "counters_kv_bidirectional.json")
 COUNTERS_D2D = os.path.join(ROOT, "profiles", "counters_d2d_blocks.json")
-KERNEL_SOURCE = os.path.join(ROOT, "block_copy_amd", "csrc", "kvcopy_kernel.hip")
+KERNEL_SOURCES = [os.path.join(ROOT, "block_copy_amd", "csrc", f)
+                  for f in ("kvcopy_kernel.hip", "copy_chunk.h")]
 
 
 def log(*a):
@@ -87,8 +88,11 @@ def no_gc():
 
 
 def kernel_source_hash():
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def measured_traffic(kernel, path=COUNTERS_KV):
@@ -278,6 +282,12 @@ def bench_kv(c: Ctx, args):
                            "ms_per_call": round(s * 1e3, 4), "kernel_ms": round(km[0], 4)}
             log(f"  {name} alone: {alone[name]}")
         extras["per_direction_alone"] = alone
+        # the startup probe's choice, and the headline step at that cap
+        auto = {"h2d_d2h": K.kvcopy_autotune(K.H2D)}
+        s_, km = c.timed(res, [0, 1], [sA, sB], args.steps, args.warmup, K.WGS_AUTO)
+        auto["bidirectional_GBps_at_auto"] = round(gbs(step_bytes, s_), 3)
+        extras["autotune"] = auto
+        log(f"  autotune: {auto}")
         extras["contiguous_memcpy_ceiling_GBps"] = ceilings(c)
         log(f"  contiguous ceilings: {extras['contiguous_memcpy_ceiling_GBps']}")
         frag = {}

@@ -24,7 +24,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 ARCH = "gfx950"
 
-HOST_SOURCES = ["plan.cpp", "runtime.cpp", "jobs.cpp"]
+HOST_SOURCES = ["plan.cpp", "runtime.cpp", "jobs.cpp", "autotune.cpp"]
 HIP_SOURCES = ["kvcopy_kernel.hip", "device_batch.hip"]
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",

@@ -1,0 +1,156 @@
+// autotune.cpp -- kvcopy_autotune: a startup probe for the workgroup cap.
+//
+// FreeToken issue #751, section "Proposal", question 1: pick the worker
+// count from a small startup probe, aiming at bytes in flight rather than
+// threads.  The vLLM PR #42212 report, section "key source snippet" (the
+// tuned constants), keeps the smallest worker count within 5% of peak.  The
+// probe times shuffled 4 KiB blocks at a ladder of caps and keeps the
+// smallest cap within 5% of the best rate.  For H2D and D2H both directions
+// run together, which is how KV offload bursts arrive (PegaFlow issue #408,
+// "Test setup": H2D and D2H concurrently on separate streams).
+#include <stdint.h>
+
+#include <algorithm>
+#include <vector>
+
+#include "kvcopy.h"
+#include "kvcopy_internal.h"
+
+namespace {
+
+constexpr uint64_t kBlocks = 8192;
+constexpr uint64_t kBlock = 4096;
+constexpr uint64_t kBytes = kBlocks * kBlock;   // 32 MiB per direction
+constexpr int kReps = 3;
+const int kCaps[] = {1, 2, 4, 8, 16, 32, 64, 128, 256, KVCOPY_WGS_ALL};
+
+uint64_t splitmix(uint64_t &s)
+{
+    uint64_t z = (s += 0x9E3779B97F4A7C15ull);
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+
+// Block offsets of `a` in shuffled order (Fisher-Yates).
+std::vector<uint64_t> shuffled(uint64_t base, uint64_t seed)
+{
+    std::vector<uint64_t> v(kBlocks);
+    for (uint64_t i = 0; i < kBlocks; ++i)
+        v[i] = base + i * kBlock;
+    for (uint64_t i = kBlocks - 1; i > 0; --i)
+        std::swap(v[i], v[splitmix(seed) % (i + 1)]);
+    return v;
+}
+
+struct Probe {
+    void *host[2] = {nullptr, nullptr};
+    void *dev[2] = {nullptr, nullptr};
+    hipStream_t s[2] = {nullptr, nullptr};
+    hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
+    ~Probe()
+    {
+        for (hipStream_t x : s)
+            if (x)
+                hipStreamSynchronize(x);
+        for (void *p : host)
+            if (p)
+                hipHostFree(p);
+        for (void *p : dev)
+            if (p)
+                hipFree(p);
+        for (hipEvent_t e : ev)
+            if (e)
+                hipEventDestroy(e);
+        for (hipStream_t x : s)
+            if (x)
+                hipStreamDestroy(x);
+    }
+};
+
+}  // namespace
+
+extern "C" int kvcopy_autotune(int dir, int *out_wgs)
+{
+    if (dir != KVCOPY_H2D && dir != KVCOPY_D2H && dir != KVCOPY_D2D)
+        return KVCOPY_EINVAL;
+    int device = 0;
+    hipError_t e = hipGetDevice(&device);
+    if (e != hipSuccess)
+        return kvc::hip_fail(e);
+    Probe p;
+    const bool d2d = dir == KVCOPY_D2D;
+    for (int i = 0; i < 2; ++i) {
+        if (!d2d && (e = hipHostMalloc(&p.host[i], kBytes, hipHostMallocMapped | hipHostMallocPortable)) !=
+                        hipSuccess)
+            return e == hipErrorOutOfMemory ? KVCOPY_ENOMEM : kvc::hip_fail(e);
+        if ((e = hipMalloc(&p.dev[i], kBytes)) != hipSuccess)
+            return e == hipErrorOutOfMemory ? KVCOPY_ENOMEM : kvc::hip_fail(e);
+        if ((e = hipStreamCreateWithFlags(&p.s[i], hipStreamNonBlocking)) != hipSuccess)
+            return kvc::hip_fail(e);
+    }
+    for (hipEvent_t &x : p.ev)
+        if ((e = hipEventCreate(&x)) != hipSuccess)
+            return kvc::hip_fail(e);
+
+    // Batches: D2D dev0 -> dev1; otherwise H2D host0 -> dev0 and D2H dev1 -> host1.
+    struct B {
+        std::vector<uint64_t> src, dst, size;
+        int dir;
+    } b[2];
+    const int nb = d2d ? 1 : 2;
+    if (d2d) {
+        b[0] = {shuffled((uint64_t)p.dev[0], 1), shuffled((uint64_t)p.dev[1], 2),
+                std::vector<uint64_t>(kBlocks, kBlock), KVCOPY_D2D};
+    } else {
+        b[0] = {shuffled((uint64_t)p.host[0], 3), shuffled((uint64_t)p.dev[0], 4),
+                std::vector<uint64_t>(kBlocks, kBlock), KVCOPY_H2D};
+        b[1] = {shuffled((uint64_t)p.dev[1], 5), shuffled((uint64_t)p.host[1], 6),
+                std::vector<uint64_t>(kBlocks, kBlock), KVCOPY_D2H};
+    }
+
+    double rate[sizeof(kCaps) / sizeof(kCaps[0])] = {};
+    double best = 0;
+    for (size_t c = 0; c < sizeof(kCaps) / sizeof(kCaps[0]); ++c) {
+        for (int rep = -1; rep < kReps; ++rep) {   // rep -1: warm-up, untimed
+            if (rep == 0) {
+                if ((e = hipEventRecord(p.ev[0], p.s[0])) != hipSuccess ||
+                    (e = hipStreamWaitEvent(p.s[1], p.ev[0], 0)) != hipSuccess)
+                    return kvc::hip_fail(e);
+            }
+            for (int j = 0; j < nb; ++j) {
+                const int rc = kvcopy_batch(b[j].src.data(), b[j].dst.data(), b[j].size.data(),
+                                            kBlocks, b[j].dir, kCaps[c], p.s[j]);
+                if (rc != KVCOPY_OK)
+                    return rc;
+            }
+        }
+        if ((e = hipEventRecord(p.ev[1], p.s[0])) != hipSuccess ||
+            (e = hipEventRecord(p.ev[2], p.s[1])) != hipSuccess ||
+            (e = hipEventSynchronize(p.ev[1])) != hipSuccess ||
+            (e = hipEventSynchronize(p.ev[2])) != hipSuccess)
+            return kvc::hip_fail(e);
+        float ms0 = 0, ms1 = 0;
+        if ((e = hipEventElapsedTime(&ms0, p.ev[0], p.ev[1])) != hipSuccess ||
+            (e = hipEventElapsedTime(&ms1, p.ev[0], p.ev[2])) != hipSuccess)
+            return kvc::hip_fail(e);
+        const double ms = std::max(ms0, nb == 2 ? ms1 : 0.0f);
+        rate[c] = ms > 0 ? (double)(kBytes * nb * kReps) / (ms * 1e-3) : 0;
+        best = std::max(best, rate[c]);
+    }
+    int chosen = KVCOPY_WGS_ALL;
+    for (size_t c = 0; c < sizeof(kCaps) / sizeof(kCaps[0]); ++c)
+        if (rate[c] >= 0.95 * best) {
+            chosen = kCaps[c];
+            break;
+        }
+    if (d2d) {
+        kvc::set_tuned_wgs(device, KVCOPY_D2D, chosen);
+    } else {
+        kvc::set_tuned_wgs(device, KVCOPY_H2D, chosen);
+        kvc::set_tuned_wgs(device, KVCOPY_D2H, chosen);
+    }
+    if (out_wgs)
+        *out_wgs = chosen;
+    return KVCOPY_OK;
+}

@@ -36,7 +36,7 @@ extern "C" int kvcopy_job_create(const uint64_t *src_addrs, const uint64_t *dst_
     *out = nullptr;
     if (dir != KVCOPY_H2D && dir != KVCOPY_D2H && dir != KVCOPY_D2D)
         return KVCOPY_EINVAL;
-    if (max_wgs < 0 || n > KVCOPY_MAX_DESCS || (n > 0 && (!src_addrs || !dst_addrs || !sizes)))
+    if (max_wgs < KVCOPY_WGS_AUTO || n > KVCOPY_MAX_DESCS || (n > 0 && (!src_addrs || !dst_addrs || !sizes)))
         return KVCOPY_EINVAL;
     bool bad_env = false;
     const bool validate = kvc::env_validate(&bad_env);

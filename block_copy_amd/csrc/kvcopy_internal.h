@@ -68,6 +68,9 @@ uint64_t build_worklist(const uint64_t *src, const uint64_t *dst, const uint64_t
 // unset, "0" or "1" makes *bad true (strict parsing).
 bool env_validate(bool *bad);
 
+// Records `wgs` as the KVCOPY_WGS_AUTO cap of `dir` on `device`.
+void set_tuned_wgs(int device, int dir, int wgs);
+
 // Records e as this thread's last HIP error (kvcopy_last_hip_error) and
 // returns KVCOPY_EHIP.
 int hip_fail(hipError_t e);

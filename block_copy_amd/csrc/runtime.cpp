@@ -66,6 +66,7 @@ struct HipEventOps {
 
 struct Staging {
     std::mutex mu;             // held for a whole call: planning is host-side and short
+    int tuned[3] = {-2, -2, -2};   // kvcopy_autotune's cap per direction (-2: not tuned)
     uint8_t *host = nullptr;   // pinned, mapped (device address == host address)
     uint8_t *dev = nullptr;    // device twin, allocated on first KVCOPY_F_DESC_UPLOAD
     std::vector<hipEvent_t> spare;
@@ -127,6 +128,16 @@ int grow(Staging *st, uint64_t need, bool want_dev)
     return KVCOPY_OK;
 }
 
+// KVCOPY_WGS_AUTO: the tuned cap if the device was probed, else the fixed
+// defaults measured on MI355X (128 for the host-link directions, the full
+// grid for D2D).
+int resolve_auto(const Staging *st, int dir)
+{
+    if (st->tuned[dir] >= 0)
+        return st->tuned[dir];
+    return dir == KVCOPY_D2D ? KVCOPY_WGS_ALL : 128;
+}
+
 uint32_t grid_for(uint64_t n_chunks, int max_wgs)
 {
     const uint64_t full = (n_chunks + kWavesPerWG - 1) / kWavesPerWG;   // one wavefront per chunk
@@ -167,6 +178,8 @@ int run_locked(Staging *st, const uint64_t *src, const uint64_t *dst, const uint
     }
     if (ev_begin && (e = hipEventRecord(ev_begin, stream)) != hipSuccess)
         return hip_fail(e);
+    if (max_wgs == KVCOPY_WGS_AUTO)
+        max_wgs = resolve_auto(st, dir);
     if ((e = launch_copy(recs, (uint32_t)n_chunks, grid_for(n_chunks, max_wgs), dir, stream)) !=
         hipSuccess)
         return hip_fail(e);
@@ -188,6 +201,14 @@ int run_locked(Staging *st, const uint64_t *src, const uint64_t *dst, const uint
 }
 
 }  // namespace
+
+void set_tuned_wgs(int device, int dir, int wgs)
+{
+    Staging *st = staging_for(device);
+    std::lock_guard<std::mutex> g(st->mu);
+    st->tuned[dir] = wgs;
+}
+
 }  // namespace kvc
 
 using namespace kvc;
@@ -214,7 +235,7 @@ extern "C" int kvcopy_batch_ex(const uint64_t *src_addrs, const uint64_t *dst_ad
     }
     if (dir != KVCOPY_H2D && dir != KVCOPY_D2H && dir != KVCOPY_D2D)
         return KVCOPY_EINVAL;
-    if (max_wgs < 0 || n > KVCOPY_MAX_DESCS)
+    if (max_wgs < KVCOPY_WGS_AUTO || n > KVCOPY_MAX_DESCS)
         return KVCOPY_EINVAL;
     if (n == 0)
         return KVCOPY_OK;
@@ -258,7 +279,7 @@ extern "C" int kvcopy_batch_device(const uint64_t *d_src, const uint64_t *d_dst,
 {
     if (dir != KVCOPY_H2D && dir != KVCOPY_D2H && dir != KVCOPY_D2D)
         return KVCOPY_EINVAL;
-    if (max_wgs < 0 || max_n > KVCOPY_MAX_DESCS)
+    if (max_wgs < KVCOPY_WGS_AUTO || max_n > KVCOPY_MAX_DESCS)
         return KVCOPY_EINVAL;
     if (chunk_bytes == 0)
         chunk_bytes = KVCOPY_CHUNK_DEFAULT;
@@ -269,6 +290,15 @@ extern "C" int kvcopy_batch_device(const uint64_t *d_src, const uint64_t *d_dst,
     if (!d_src || !d_dst || !d_sizes || !d_n || !workspace ||
         (reinterpret_cast<uintptr_t>(workspace) & 255u))
         return KVCOPY_EINVAL;
+    if (max_wgs == KVCOPY_WGS_AUTO) {
+        int device = 0;
+        const hipError_t e = hipGetDevice(&device);
+        if (e != hipSuccess)
+            return hip_fail(e);
+        Staging *st = staging_for(device);
+        std::lock_guard<std::mutex> g(st->mu);
+        max_wgs = resolve_auto(st, dir);
+    }
     const uint32_t grid = max_wgs ? (uint32_t)max_wgs : 1024u;
     const hipError_t e =
         launch_device_batch(d_src, d_dst, d_sizes, d_n, max_n, chunk_bytes, grid, workspace, stream);

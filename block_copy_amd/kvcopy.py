@@ -19,7 +19,7 @@ import numpy as np
 
 H2D, D2H, D2D = 0, 1, 2
 OK, EINVAL, EALIGN, EOVERLAP, ENOMEM, EHIP = 0, -1, -2, -3, -4, -5
-WGS_ALL = 0
+WGS_ALL, WGS_AUTO = 0, -1
 CHUNK_DEFAULT = 16384
 CHUNK_MAX = 1 << 20
 F_VALIDATE, F_NO_COALESCE, F_DESC_UPLOAD = 0x1, 0x2, 0x8
@@ -31,7 +31,7 @@ EXPORTS = ("kvcopy_coalesce", "kvcopy_plan", "kvcopy_plan_free", "kvcopy_batch",
            "kvcopy_batch_ex", "kvcopy_strerror", "kvcopy_last_hip_error",
            "kvcopy_host_alloc_mapped", "kvcopy_host_free", "kvcopy_job_create",
            "kvcopy_job_poll", "kvcopy_job_wait", "kvcopy_job_destroy",
-           "kvcopy_device_workspace_bytes", "kvcopy_batch_device")
+           "kvcopy_device_workspace_bytes", "kvcopy_batch_device", "kvcopy_autotune")
 DEVICE_BAD_ALIGN, DEVICE_TOO_MANY_CHUNKS = 1, 2
 
 
@@ -97,6 +97,8 @@ def _load():
     lib.kvcopy_job_wait.argtypes = [ctypes.c_void_p]
     lib.kvcopy_job_destroy.restype = None
     lib.kvcopy_job_destroy.argtypes = [ctypes.c_void_p]
+    lib.kvcopy_autotune.restype = ctypes.c_int
+    lib.kvcopy_autotune.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
     lib.kvcopy_device_workspace_bytes.restype = ctypes.c_uint64
     lib.kvcopy_device_workspace_bytes.argtypes = [ctypes.c_uint64]
     lib.kvcopy_batch_device.restype = ctypes.c_int
@@ -308,3 +310,12 @@ def kvcopy_batch_device(d_src: int, d_dst: int, d_sizes: int, d_n: int, max_n: i
     if check and rc != OK:
         raise KvcopyError(rc, "kvcopy_batch_device")
     return rc
+
+
+def kvcopy_autotune(dir: int) -> int:
+    """Run the startup probe for `dir` on the current device; returns the chosen cap."""
+    w = ctypes.c_int(0)
+    rc = lib.kvcopy_autotune(int(dir), ctypes.byref(w))
+    if rc != OK:
+        raise KvcopyError(rc, "kvcopy_autotune")
+    return int(w.value)

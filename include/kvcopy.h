@@ -59,7 +59,7 @@ enum {
 /* Status codes. */
 enum {
     KVCOPY_OK = 0,
-    KVCOPY_EINVAL = -1,   /* null pointer with n > 0, bad dir, max_wgs < 0, bad option, n too large */
+    KVCOPY_EINVAL = -1,   /* null pointer with n > 0, bad dir, max_wgs < -1, bad option, n too large */
     KVCOPY_EALIGN = -2,   /* an address or size is not a multiple of 8 bytes */
     KVCOPY_EOVERLAP = -3, /* validate mode: destinations overlap each other or a source */
     KVCOPY_ENOMEM = -4,   /* host or device allocation failed */
@@ -68,8 +68,15 @@ enum {
 
 /* max_wgs == KVCOPY_WGS_ALL: one wavefront per chunk (the full grid).  The
  * "current full grid" of [PF] "Relevant implementation" launched one block
- * per descriptor. */
+ * per descriptor.
+ * max_wgs == KVCOPY_WGS_AUTO: the device's tuned cap for `dir` when
+ * kvcopy_autotune has run on this device, else a fixed default measured on
+ * MI355X: 128 for H2D and D2H (the best cap with both directions running
+ * together; either direction alone already fills the host link with 8),
+ * the full grid for D2D.  [PF] "Proposed direction": the cap should come
+ * from a device-aware profile, not a universal constant. */
 #define KVCOPY_WGS_ALL 0
+#define KVCOPY_WGS_AUTO (-1)
 
 /* Default chunk size: [FT] "What we changed" cuts the call's rows into
  * chunks of up to 16 KiB, each inside one row. */
@@ -163,7 +170,8 @@ void kvcopy_plan_free(kvcopy_plan_t *plan);
  * dir:     KVCOPY_H2D / KVCOPY_D2H / KVCOPY_D2D (tuning only).
  * max_wgs: workgroup cap ([PF] "Follow-up", item 1: a bounded grid; "Proposed
  *          direction": max_grid_blocks).  KVCOPY_WGS_ALL (0) = one wavefront
- *          per chunk.  Negative = KVCOPY_EINVAL.
+ *          per chunk; KVCOPY_WGS_AUTO (-1) = the device's tuned or default
+ *          cap.  Below -1 = KVCOPY_EINVAL.
  * stream:  HIP stream (NULL = the null stream).
  * Ownership: the descriptor arrays may be reused as soon as the call
  *          returns.  The payload memory must stay valid, and unwritten by
@@ -252,6 +260,25 @@ int kvcopy_job_wait(kvcopy_job_t *job);
 void kvcopy_job_destroy(kvcopy_job_t *job);
 
 /*
+ * kvcopy_autotune -- a startup probe that picks the workgroup cap.
+ *
+ * [FT] "Proposal", question 1, suggests choosing the worker count from a
+ * small startup probe and targeting bytes in flight rather than threads;
+ * the vLLM PR #42212 report ("key source snippet", the tuned constants)
+ * picks the smallest number of workers within 5% of peak bandwidth.  This
+ * call does both on the current device: it allocates its own probe buffers
+ * (32 MiB of mapped pinned host memory and 32 MiB of device memory per
+ * direction, freed before it returns), times 8,192 shuffled 4 KiB blocks
+ * per direction at caps 1, 2, 4 ... 256 and the full grid (for H2D or D2H
+ * both directions run together, as in a KV offload burst), and records the
+ * smallest cap within 5% of the best rate as the device's KVCOPY_WGS_AUTO
+ * cap for `dir` (for H2D or D2H: for both).  Blocks until done (tens of ms).
+ * out_wgs (may be NULL) receives the chosen cap (0 = full grid).
+ * errors: KVCOPY_EINVAL (bad dir), KVCOPY_ENOMEM, KVCOPY_EHIP.
+ */
+int kvcopy_autotune(int dir, int *out_wgs);
+
+/*
  * Device-resident batches (graph-capturable).
  *
  * [FT] "What we changed": the gather reads its miss count on the device, so
@@ -275,7 +302,8 @@ void kvcopy_job_destroy(kvcopy_job_t *job);
  *
  * d_src, d_dst, d_sizes: device arrays of max_n uint64 each (entries past
  *   the device count are not read).  d_n: device uint64, the count.
- * max_wgs: the copy kernel's workgroups; 0 selects 1024.
+ * max_wgs: the copy kernel's workgroups; 0 selects 1024; KVCOPY_WGS_AUTO the
+ *   device's tuned or default cap (1024 where that is the full grid).
  * chunk_bytes: 0 = KVCOPY_CHUNK_DEFAULT; else a multiple of 16, at most
  *   KVCOPY_CHUNK_MAX.
  * workspace: caller-owned device memory of kvcopy_device_workspace_bytes(max_n)

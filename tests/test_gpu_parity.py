@@ -347,3 +347,25 @@ def test_job_wait(K):
     torch.cuda.synchronize()
     _check(res, [0], "job wait")
     res.free()
+
+
+
+# ---------------------------------------------------------------------------
+# KVCOPY_WGS_AUTO before and after the startup probe
+# ---------------------------------------------------------------------------
+
+def test_auto_cap_and_autotune(K):
+    from block_copy_amd.harness import Resident
+    wl = W.kv_blocks(seed=4, directions="both", n=4096, pool_blocks=16384)
+    res = Resident(wl)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    _say("auto cap, default")
+    _run(res, [0, 1], K.WGS_AUTO, streams=[s1, s2])
+    _check(res, [0, 1], "WGS_AUTO default")
+    _say("autotune")
+    caps = {K.kvcopy_autotune(K.H2D), K.kvcopy_autotune(K.D2D)}
+    assert caps <= {1, 2, 4, 8, 16, 32, 64, 128, 256, 0}, caps
+    res.fill()
+    _run(res, [0, 1], K.WGS_AUTO, streams=[s1, s2])
+    _check(res, [0, 1], "WGS_AUTO tuned")
+    res.free()

@@ -142,7 +142,8 @@ def test_batch_argument_errors(K):
     assert call(s, d + 12, z, K.D2D) == K.EALIGN                  # misaligned destination
     assert call(s, d, z, 3) == K.EINVAL                            # bad direction
     assert call(s, d, z, -1) == K.EINVAL
-    assert call(s, d, z, K.H2D, -5) == K.EINVAL                    # negative max_wgs
+    assert call(s, d, z, K.H2D, -5) == K.EINVAL                    # max_wgs below WGS_AUTO
+    assert call(s, d, z, K.H2D, -2) == K.EINVAL
     assert call(s, d, z, K.H2D, chunk_bytes=24) == K.EINVAL        # chunk not a multiple of 16
     assert call(s, d, z, K.H2D, chunk_bytes=(1 << 20) + 16) == K.EINVAL
     assert call(s, d, z, K.H2D, flags=0x100) == K.EINVAL          # unknown flag
@@ -230,7 +231,7 @@ def test_device_batch_argument_errors(K):
     assert call(0, 0, 0, 0, 10, K.D2D, 8, 0) == K.EINVAL            # NULL arrays
     good = dict(d_src=1 << 20, d_dst=2 << 20, d_sizes=3 << 20, d_n=4 << 20)
     assert call(*good.values(), 10, 9, 8, 5 << 20) == K.EINVAL      # bad dir
-    assert call(*good.values(), 10, K.D2D, -1, 5 << 20) == K.EINVAL  # bad max_wgs
+    assert call(*good.values(), 10, K.D2D, -2, 5 << 20) == K.EINVAL  # bad max_wgs
     assert call(*good.values(), 10, K.D2D, 8, (5 << 20) + 8) == K.EINVAL   # misaligned workspace
     assert call(*good.values(), 10, K.D2D, 8, 5 << 20, chunk_bytes=24) == K.EINVAL
     assert call(*good.values(), 2**31 + 1, K.D2D, 8, 5 << 20) == K.EINVAL
@@ -239,3 +240,9 @@ def test_device_batch_argument_errors(K):
     assert K.kvcopy_device_workspace_bytes(27) == 256
     assert K.kvcopy_device_workspace_bytes(28) == 512
     assert K.kvcopy_device_workspace_bytes(1000) == (32 + 8 * 1001 + 255) // 256 * 256
+
+
+def test_autotune_rejects_bad_direction(K):
+    import ctypes
+    assert K.lib.kvcopy_autotune(3, None) == K.EINVAL
+    assert K.lib.kvcopy_autotune(-1, ctypes.byref(ctypes.c_int())) == K.EINVAL
