@@ -222,7 +222,7 @@ def test_error_paths_enqueue_nothing(K):
     bad[7] += 4
     assert K.kvcopy_batch(s, d, bad, K.D2D, check=False) == K.EALIGN
     assert K.kvcopy_batch(s, d, z, 5, check=False) == K.EINVAL
-    assert K.kvcopy_batch(s, d, z, K.D2D, -1, check=False) == K.EINVAL
+    assert K.kvcopy_batch(s, d, z, K.D2D, -2, check=False) == K.EINVAL
     dd = d.copy()
     dd[3] = dd[2]                                     # two descriptors write the same bytes
     assert K.kvcopy_batch(s, dd, z, K.D2D, flags=K.F_VALIDATE, check=False) == K.EOVERLAP
