@@ -283,7 +283,8 @@ def bench_kv(c: Ctx, args):
             log(f"  {name} alone: {alone[name]}")
         extras["per_direction_alone"] = alone
         # the startup probe's choice, and the headline step at that cap
-        auto = {"h2d_d2h": K.kvcopy_autotune(K.H2D)}
+        cap, rates = K.kvcopy_autotune(K.H2D, sA.cuda_stream, sB.cuda_stream)
+        auto = {"h2d_d2h": cap, "probe_GBps": {str(k): round(v, 2) for k, v in rates.items()}}
         s_, km = c.timed(res, [0, 1], [sA, sB], args.steps, args.warmup, K.WGS_AUTO)
         auto["bidirectional_GBps_at_auto"] = round(gbs(step_bytes, s_), 3)
         extras["autotune"] = auto

@@ -22,7 +22,7 @@ constexpr uint64_t kBlocks = 8192;
 constexpr uint64_t kBlock = 4096;
 constexpr uint64_t kBytes = kBlocks * kBlock;   // 32 MiB per direction
 constexpr int kReps = 3;
-const int kCaps[] = {1, 2, 4, 8, 16, 32, 64, 128, 256, KVCOPY_WGS_ALL};
+const int kCaps[KVCOPY_AUTOTUNE_NCAPS] = KVCOPY_AUTOTUNE_CAPS;
 
 uint64_t splitmix(uint64_t &s)
 {
@@ -47,6 +47,7 @@ struct Probe {
     void *host[2] = {nullptr, nullptr};
     void *dev[2] = {nullptr, nullptr};
     hipStream_t s[2] = {nullptr, nullptr};
+    bool own[2] = {false, false};   // streams created here (destroyed at the end)
     hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
     ~Probe()
     {
@@ -62,15 +63,16 @@ struct Probe {
         for (hipEvent_t e : ev)
             if (e)
                 hipEventDestroy(e);
-        for (hipStream_t x : s)
-            if (x)
-                hipStreamDestroy(x);
+        for (int i = 0; i < 2; ++i)
+            if (own[i])
+                hipStreamDestroy(s[i]);
     }
 };
 
 }  // namespace
 
-extern "C" int kvcopy_autotune(int dir, int *out_wgs)
+extern "C" int kvcopy_autotune(int dir, hipStream_t s0, hipStream_t s1, int *out_wgs,
+                               double *out_rates)
 {
     if (dir != KVCOPY_H2D && dir != KVCOPY_D2H && dir != KVCOPY_D2D)
         return KVCOPY_EINVAL;
@@ -86,8 +88,14 @@ extern "C" int kvcopy_autotune(int dir, int *out_wgs)
             return e == hipErrorOutOfMemory ? KVCOPY_ENOMEM : kvc::hip_fail(e);
         if ((e = hipMalloc(&p.dev[i], kBytes)) != hipSuccess)
             return e == hipErrorOutOfMemory ? KVCOPY_ENOMEM : kvc::hip_fail(e);
-        if ((e = hipStreamCreateWithFlags(&p.s[i], hipStreamNonBlocking)) != hipSuccess)
-            return kvc::hip_fail(e);
+        const hipStream_t given = i == 0 ? s0 : s1;
+        if (given) {
+            p.s[i] = given;
+        } else {
+            if ((e = hipStreamCreateWithFlags(&p.s[i], hipStreamNonBlocking)) != hipSuccess)
+                return kvc::hip_fail(e);
+            p.own[i] = true;
+        }
     }
     for (hipEvent_t &x : p.ev)
         if ((e = hipEventCreate(&x)) != hipSuccess)
@@ -109,7 +117,7 @@ extern "C" int kvcopy_autotune(int dir, int *out_wgs)
                 std::vector<uint64_t>(kBlocks, kBlock), KVCOPY_D2H};
     }
 
-    double rate[sizeof(kCaps) / sizeof(kCaps[0])] = {};
+    double rate[KVCOPY_AUTOTUNE_NCAPS] = {};
     double best = 0;
     for (size_t c = 0; c < sizeof(kCaps) / sizeof(kCaps[0]); ++c) {
         for (int rep = -1; rep < kReps; ++rep) {   // rep -1: warm-up, untimed
@@ -152,5 +160,8 @@ extern "C" int kvcopy_autotune(int dir, int *out_wgs)
     }
     if (out_wgs)
         *out_wgs = chosen;
+    if (out_rates)
+        for (int c = 0; c < KVCOPY_AUTOTUNE_NCAPS; ++c)
+            out_rates[c] = rate[c];
     return KVCOPY_OK;
 }

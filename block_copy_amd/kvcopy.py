@@ -98,7 +98,8 @@ def _load():
     lib.kvcopy_job_destroy.restype = None
     lib.kvcopy_job_destroy.argtypes = [ctypes.c_void_p]
     lib.kvcopy_autotune.restype = ctypes.c_int
-    lib.kvcopy_autotune.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
+    lib.kvcopy_autotune.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                    ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_double)]
     lib.kvcopy_device_workspace_bytes.restype = ctypes.c_uint64
     lib.kvcopy_device_workspace_bytes.argtypes = [ctypes.c_uint64]
     lib.kvcopy_batch_device.restype = ctypes.c_int
@@ -312,10 +313,16 @@ def kvcopy_batch_device(d_src: int, d_dst: int, d_sizes: int, d_n: int, max_n: i
     return rc
 
 
-def kvcopy_autotune(dir: int) -> int:
-    """Run the startup probe for `dir` on the current device; returns the chosen cap."""
+AUTOTUNE_CAPS = (1, 2, 4, 8, 16, 32, 64, 128, 256, 0)
+
+
+def kvcopy_autotune(dir: int, s0=None, s1=None):
+    """Run the startup probe for `dir` on the current device (see include/kvcopy.h).
+    Returns (chosen cap, {cap: GB/s})."""
     w = ctypes.c_int(0)
-    rc = lib.kvcopy_autotune(int(dir), ctypes.byref(w))
+    rates = (ctypes.c_double * len(AUTOTUNE_CAPS))()
+    p = lambda x: ctypes.c_void_p(int(x) if x else 0)  # noqa: E731
+    rc = lib.kvcopy_autotune(int(dir), p(s0), p(s1), ctypes.byref(w), rates)
     if rc != OK:
         raise KvcopyError(rc, "kvcopy_autotune")
-    return int(w.value)
+    return int(w.value), {c: rates[i] / 1e9 for i, c in enumerate(AUTOTUNE_CAPS)}

@@ -269,14 +269,21 @@ void kvcopy_job_destroy(kvcopy_job_t *job);
  * call does both on the current device: it allocates its own probe buffers
  * (32 MiB of mapped pinned host memory and 32 MiB of device memory per
  * direction, freed before it returns), times 8,192 shuffled 4 KiB blocks
- * per direction at caps 1, 2, 4 ... 256 and the full grid (for H2D or D2H
- * both directions run together, as in a KV offload burst), and records the
- * smallest cap within 5% of the best rate as the device's KVCOPY_WGS_AUTO
- * cap for `dir` (for H2D or D2H: for both).  Blocks until done (tens of ms).
- * out_wgs (may be NULL) receives the chosen cap (0 = full grid).
+ * per direction at each cap of KVCOPY_AUTOTUNE_CAPS (for H2D or D2H both
+ * directions run together, H2D on s0 and D2H on s1, as in a KV offload
+ * burst; D2D runs on s0), and records the smallest cap within 5% of the
+ * best rate as the device's KVCOPY_WGS_AUTO cap for `dir` (for H2D or D2H:
+ * for both).  Blocks until done (tens of ms).
+ * s0, s1: the streams the caller will copy on (the hardware queues they map
+ *   to matter); NULL = streams created for the probe.
+ * out_wgs (may be NULL): the chosen cap (0 = full grid).
+ * out_rates (may be NULL): KVCOPY_AUTOTUNE_NCAPS doubles, bytes per second
+ *   at each cap, in the order of KVCOPY_AUTOTUNE_CAPS.
  * errors: KVCOPY_EINVAL (bad dir), KVCOPY_ENOMEM, KVCOPY_EHIP.
  */
-int kvcopy_autotune(int dir, int *out_wgs);
+#define KVCOPY_AUTOTUNE_NCAPS 10
+#define KVCOPY_AUTOTUNE_CAPS {1, 2, 4, 8, 16, 32, 64, 128, 256, 0}
+int kvcopy_autotune(int dir, hipStream_t s0, hipStream_t s1, int *out_wgs, double *out_rates);
 
 /*
  * Device-resident batches (graph-capturable).

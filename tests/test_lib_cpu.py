@@ -244,5 +244,5 @@ def test_device_batch_argument_errors(K):
 
 def test_autotune_rejects_bad_direction(K):
     import ctypes
-    assert K.lib.kvcopy_autotune(3, None) == K.EINVAL
-    assert K.lib.kvcopy_autotune(-1, ctypes.byref(ctypes.c_int())) == K.EINVAL
+    assert K.lib.kvcopy_autotune(3, None, None, None, None) == K.EINVAL
+    assert K.lib.kvcopy_autotune(-1, None, None, ctypes.byref(ctypes.c_int()), None) == K.EINVAL
