@@ -593,10 +593,19 @@ def bench_interference(c: Ctx, args):
     period = 0.050
     steps, warm = args.decode_steps, 32
 
+    masked = {}
+
     def run(mode):
         stop = threading.Event()
         moved = [0]
         bursts = [0]
+        sa, sb = c.sA, c.sB
+        if isinstance(mode, str) and mode.startswith("cumask"):
+            # copy streams restricted to the first N compute units
+            ncu = int(mode.split(":")[1])
+            if ncu not in masked:
+                masked[ncu] = (hiprt.CUMaskStream(range(ncu)), hiprt.CUMaskStream(range(ncu)))
+            sa, sb = masked[ncu]
 
         def transfer():
             nxt = time.perf_counter()
@@ -621,10 +630,11 @@ def bench_interference(c: Ctx, args):
                     for jb in jobs:
                         K.kvcopy_job_destroy(jb)
                 else:
-                    r.submit(0, mode, c.sA)
-                    r.submit(1, mode, c.sB)
-                hiprt.stream_sync(c.sA)
-                hiprt.stream_sync(c.sB)
+                    g = K.WGS_ALL if isinstance(mode, str) else mode
+                    r.submit(0, g, sa)
+                    r.submit(1, g, sb)
+                hiprt.stream_sync(sa)
+                hiprt.stream_sync(sb)
                 moved[0] += wl.nbytes
                 bursts[0] += 1
                 nxt += period
@@ -659,7 +669,8 @@ def bench_interference(c: Ctx, args):
             th.join()
         return gpu_ms, wall_ms, moved[0] / dur, bursts[0]
 
-    modes = ["none", "direct", 1, 2, 8, 32, 128, 0, "job:1024", "job:2048", "job:4096"]
+    modes = ["none", "direct", 1, 2, 8, 32, 128, 0, "job:1024", "job:2048", "job:4096",
+             "cumask:8", "cumask:32"]
     results = {str(m): {"gpu": [], "wall": [], "rate": [], "bursts": 0} for m in modes}
     for rep in range(args.decode_runs):
         order = modes[rep % len(modes):] + modes[:rep % len(modes)]

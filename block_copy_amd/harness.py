@@ -62,7 +62,7 @@ class Resident:
     def submit(self, batch_idx: int, max_wgs: int = K.WGS_ALL, stream=None, **kw) -> int:
         b = self.wl.batches[batch_idx]
         s, d = self.addrs[batch_idx]
-        st = stream.cuda_stream if isinstance(stream, torch.cuda.Stream) else stream
+        st = getattr(stream, "cuda_stream", stream)
         return K.kvcopy_batch(s, d, b.size, b.dir, max_wgs, st, **kw)
 
     def free(self):

@@ -33,8 +33,12 @@ hip.hipMemcpyAsync.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t
                                ctypes.c_void_p]
 hip.hipStreamSynchronize.argtypes = [ctypes.c_void_p]
 hip.hipDeviceSynchronize.argtypes = []
+hip.hipExtStreamCreateWithCUMask.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint32,
+                                             ctypes.POINTER(ctypes.c_uint32)]
+hip.hipStreamDestroy.argtypes = [ctypes.c_void_p]
 for _f in ("hipEventCreate", "hipEventRecord", "hipEventSynchronize", "hipEventElapsedTime",
-           "hipEventDestroy", "hipMemcpyAsync", "hipStreamSynchronize", "hipDeviceSynchronize"):
+           "hipEventDestroy", "hipMemcpyAsync", "hipStreamSynchronize", "hipDeviceSynchronize",
+           "hipExtStreamCreateWithCUMask", "hipStreamDestroy"):
     getattr(hip, _f).restype = ctypes.c_int
 
 
@@ -78,3 +82,22 @@ def memcpy_async(dst: int, src: int, nbytes: int, kind: int, stream) -> None:
 
 def stream_sync(stream) -> None:
     check(hip.hipStreamSynchronize(_s(stream)), "hipStreamSynchronize")
+
+
+class CUMaskStream:
+    """A stream whose kernels may run only on the given compute units
+    (default priority).  `cus`: iterable of CU indices in [0, 256)."""
+
+    def __init__(self, cus, total=256):
+        words = (ctypes.c_uint32 * ((total + 31) // 32))()
+        for c in cus:
+            words[c // 32] |= 1 << (c % 32)
+        h = ctypes.c_void_p()
+        check(hip.hipExtStreamCreateWithCUMask(ctypes.byref(h), len(words), words),
+              "hipExtStreamCreateWithCUMask")
+        self.cuda_stream = h.value
+
+    def destroy(self):
+        if self.cuda_stream:
+            check(hip.hipStreamDestroy(self.cuda_stream), "hipStreamDestroy")
+            self.cuda_stream = None
