@@ -80,12 +80,24 @@ int hip_fail(hipError_t e);
 constexpr uint32_t kWavesPerWG = 4;
 constexpr uint32_t kThreadsPerWG = 64 * kWavesPerWG;
 
-// Launches the copy kernel for `dir` (one kernel symbol per direction, same
-// algorithm): `grid` workgroups, wavefronts take chunks round-robin.  recs
-// must be device-readable (device memory or mapped host memory).  Returns
-// the launch status.
+// Launches the copy kernel for `dir` (one kernel symbol per direction and
+// loop, same result): `grid` workgroups; wavefront w of W copies the chunks
+// [w*C/W, (w+1)*C/W), one chunk at a time or, if `pipelined`, as a stream of
+// 4 KiB pieces with two 16 KiB passes in flight.  recs must be
+// device-readable (device memory or mapped host memory).  Returns the launch
+// status.
 hipError_t launch_copy(const ChunkRec *recs, uint32_t n_chunks, uint32_t grid, int dir,
-                       hipStream_t stream);
+                       bool pipelined, hipStream_t stream);
+
+// The library's choice of copy loop when no KVCOPY_F_PIPELINE /
+// KVCOPY_F_PER_CHUNK flag forces one: pipelined for small grids (at most 4
+// workgroups on the host link, 256 for D2D) in which every wavefront has at
+// least two chunks.
+inline bool pipeline_pays(int dir, uint32_t grid, uint64_t n_chunks)
+{
+    const uint32_t max_grid = dir == 2 /* KVCOPY_D2D */ ? 256u : 4u;
+    return grid <= max_grid && n_chunks >= 2ull * grid * kWavesPerWG;
+}
 
 // ---- device-resident batches (device_batch.hip) ---------------------------
 

@@ -1,4 +1,4 @@
-// kvcopy_kernel.hip -- the persistent, workgroup-capped copy kernel (gfx950).
+// kvcopy_kernel.hip -- the persistent, workgroup-capped copy kernels (gfx950).
 //
 // Work unit: one chunk of the worklist (at most chunk_bytes, never crossing a
 // range; FreeToken issue #751 "gather missed experts with a few TMA
@@ -13,14 +13,21 @@
 //
 // Data path (CDNA4): each lane moves 16-byte vectors with
 // buffer_load_dwordx4 / nontemporal buffer_store_dwordx4, lanes interleaved
-// so that one wavefront instruction covers 1 KiB of contiguous bytes.  A wavefront
-// issues the loads for up to 16 KiB (16 vectors per lane, 64 VGPRs) before
-// the first store, so a single wavefront keeps up to 16 KiB of reads in
-// flight; the worklist records are fetched 64 at a time and one batch
-// ahead.  Addresses only need 8-byte alignment: gfx950 serves
-// 8-byte-aligned dwordx4 accesses directly, so no head peeling or register
-// shifting is needed when src and dst differ mod 16.  A range whose size is
-// an odd multiple of 8 ends in one 8-byte word, moved by lane 0.
+// so that one wavefront instruction covers 1 KiB of contiguous bytes.
+// Addresses only need 8-byte alignment: gfx950 serves 8-byte-aligned dwordx4
+// accesses directly, so no head peeling or register shifting is needed when
+// src and dst differ mod 16.  A range whose size is an odd multiple of 8
+// ends in one 8-byte word.
+//
+// Two loops, same result:
+//   - per-chunk: a wavefront issues the loads of one chunk (up to 16 KiB, 16
+//     vectors per lane) before its first store, then moves to the next chunk;
+//   - pipelined: a wavefront streams its chunks as 4 KiB pieces in passes of
+//     16 KiB, the loads of the next pass in flight while the current one is
+//     stored.  It keeps 16-32 KiB of reads outstanding per wavefront even
+//     for 4 KiB descriptors, which pays when only a few workgroups run.
+// The worklist records are fetched 64 at a time (one per lane) and one batch
+// ahead in both loops.
 #include <hip/hip_runtime.h>
 
 #include "kvcopy.h"
@@ -85,35 +92,210 @@ __device__ __forceinline__ void copy_worklist(const ChunkRec *__restrict__ recs,
     }
 }
 
-// One symbol per direction, so that profiles and counters separate them.
-__global__ __launch_bounds__(kThreadsPerWG) void kvcopy_h2d_kernel(const ChunkRec *__restrict__ recs,
-                                                                   uint32_t n_chunks)
+// ---- pipelined variant ------------------------------------------------------
+//
+// The loop above keeps one chunk's loads in flight per wavefront: with 4 KiB
+// descriptors that is 4 KiB, and the wavefront waits a full memory round trip
+// per chunk.  The pipelined loop instead cuts the wavefront's chunk list into
+// a stream of pieces of at most 4 KiB (four 1 KiB rows) and moves them in
+// passes of four pieces (16 KiB), two passes in flight: the loads of pass
+// p+1 are issued before the stores of pass p, so a wavefront always has 16 to
+// 32 KiB of reads outstanding whatever the descriptor size.  Pieces of one
+// pass may come from different chunks.  A piece's 8-byte tail (a chunk that
+// ends in an odd 8-byte word) rides in the same pass as one 8-byte access
+// whose buffer range is empty when there is no tail, so the code has no
+// per-piece branches and every wait is a counted vmcnt.
+constexpr uint32_t kPieceBytes = 4096;
+constexpr int kPiecesPerPass = 4;
+constexpr int kRowsPerPiece = (int)(kPieceBytes / kRowBytes);
+typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+
+struct Piece {
+    uint64_t src, dst;
+    uint32_t len;   // 0: the stream is exhausted
+};
+
+__device__ __forceinline__ uint64_t uniform64(uint64_t v)
 {
-    copy_worklist(recs, n_chunks);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return ((uint64_t)hi << 32) | lo;
 }
 
-__global__ __launch_bounds__(kThreadsPerWG) void kvcopy_d2h_kernel(const ChunkRec *__restrict__ recs,
-                                                                   uint32_t n_chunks)
+// A buffer resource from wave-uniform values.  The values are uniform by
+// construction, but the compiler may carry some of them through the loop in
+// VGPRs; readfirstlane keeps the resource in SGPRs (without it the compiler
+// wraps each access in a waterfall loop over the lanes).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_u(uint64_t base, uint32_t bytes)
 {
-    copy_worklist(recs, n_chunks);
+    return rsrc(uniform64(base), __builtin_amdgcn_readfirstlane(bytes));
 }
 
-__global__ __launch_bounds__(kThreadsPerWG) void kvcopy_d2d_kernel(const ChunkRec *__restrict__ recs,
-                                                                   uint32_t n_chunks)
+// Worklist records through a buffer resource: lanes past the end of the
+// wavefront's share read zeros, so the batch fetch needs no lane branches.
+__device__ __forceinline__ Rec fetch_recs(const ChunkRec *recs, uint32_t first, uint32_t end,
+                                          uint32_t lane)
 {
-    copy_worklist(recs, n_chunks);
+    const uint32_t avail = first < end ? end - first : 0u;
+    const uint32_t nrec = avail < 64u ? avail : 64u;
+    const __amdgpu_buffer_rsrc_t r =
+        rsrc_u(reinterpret_cast<uintptr_t>(recs + first), nrec * (uint32_t)sizeof(ChunkRec));
+    const uint32_t o = lane * (uint32_t)sizeof(ChunkRec);
+    const v2u s = __builtin_amdgcn_raw_buffer_load_b64(r, (int)o, 0, 0);
+    const v2u d = __builtin_amdgcn_raw_buffer_load_b64(r, (int)(o + 8), 0, 0);
+    const uint32_t b = __builtin_amdgcn_raw_buffer_load_b32(r, (int)(o + 16), 0, 0);
+    return Rec{((uint64_t)s.y << 32) | s.x, ((uint64_t)d.y << 32) | d.x, b};
 }
+
+__device__ __forceinline__ uint32_t wave_incl_scan32(uint32_t v, uint32_t lane)
+{
+#pragma unroll
+    for (uint32_t d = 1; d < 64; d <<= 1) {
+        const uint32_t o = __shfl_up(v, d, 64);
+        v += lane >= d ? o : 0u;
+    }
+    return v;
+}
+
+// One batch of up to 64 chunks, one record per lane, seen as a list of
+// pieces: lane j's chunk owns pieces [pstart_j, pend_j) of the batch.
+struct PieceBatch {
+    Rec rec;
+    uint32_t pstart, pend;
+    uint32_t total;   // pieces in the batch (wave-uniform)
+
+    __device__ __forceinline__ void open(const Rec &r, uint32_t lane)
+    {
+        rec = r;
+        const uint32_t pc = (r.bytes + kPieceBytes - 1u) / kPieceBytes;   // 0 past the share
+        pend = wave_incl_scan32(pc, lane);
+        pstart = pend - pc;
+        total = __builtin_amdgcn_readlane(pend, 63);
+    }
+    // Piece q (wave-uniform); len 0 once q >= total.  No branches: the lane
+    // that owns q is found with a ballot.
+    __device__ __forceinline__ Piece at(uint32_t q) const
+    {
+        const uint64_t m = __ballot(q >= pstart && q < pend);
+        const uint32_t j = m ? (uint32_t)__builtin_ctzll(m) : 0u;
+        const uint32_t off = (q - __builtin_amdgcn_readlane(pstart, j)) * kPieceBytes;
+        const uint32_t left = __builtin_amdgcn_readlane(rec.bytes, j) - off;
+        const uint32_t len = left < kPieceBytes ? left : kPieceBytes;
+        return Piece{lane_u64(rec.src, j) + off, lane_u64(rec.dst, j) + off, m ? len : 0u};
+    }
+};
+
+template <int P>
+__device__ __forceinline__ void load_pass(const Piece (&p)[P], v4u (&v)[P * kRowsPerPiece],
+                                          v2u (&t)[P], uint32_t lane)
+{
+#pragma unroll
+    for (int k = 0; k < P; ++k) {
+        const uint32_t body = p[k].len & ~15u;
+        const __amdgpu_buffer_rsrc_t rs = rsrc_u(p[k].src, body);
+#pragma unroll
+        for (int r = 0; r < kRowsPerPiece; ++r)
+            v[k * kRowsPerPiece + r] = __builtin_amdgcn_raw_buffer_load_b128(
+                rs, (int)(lane * 16u + r * kRowBytes), 0, kLoadPolicy);
+        const __amdgpu_buffer_rsrc_t rt = rsrc_u(p[k].src + body, p[k].len & 8u);
+        t[k] = __builtin_amdgcn_raw_buffer_load_b64(rt, (int)(lane * 8u), 0, kLoadPolicy);
+    }
+}
+
+template <int P>
+__device__ __forceinline__ void store_pass(const Piece (&p)[P], const v4u (&v)[P * kRowsPerPiece],
+                                           const v2u (&t)[P], uint32_t lane)
+{
+#pragma unroll
+    for (int k = 0; k < P; ++k) {
+        const uint32_t body = p[k].len & ~15u;
+        const __amdgpu_buffer_rsrc_t rd = rsrc_u(p[k].dst, body);
+#pragma unroll
+        for (int r = 0; r < kRowsPerPiece; ++r)
+            __builtin_amdgcn_raw_buffer_store_b128(v[k * kRowsPerPiece + r], rd,
+                                                   (int)(lane * 16u + r * kRowBytes), 0,
+                                                   kStorePolicy);
+        const __amdgpu_buffer_rsrc_t rt = rsrc_u(p[k].dst + body, p[k].len & 8u);
+        __builtin_amdgcn_raw_buffer_store_b64(t[k], rt, (int)(lane * 8u), 0, kStorePolicy);
+    }
+}
+
+__device__ __forceinline__ void copy_worklist_pipelined(const ChunkRec *__restrict__ recs,
+                                                        uint32_t n_chunks)
+{
+    constexpr int P = kPiecesPerPass;
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t nw = gridDim.x * kWavesPerWG;
+    const uint32_t w = __builtin_amdgcn_readfirstlane(blockIdx.x * kWavesPerWG + (threadIdx.x >> 6));
+    const uint32_t lo = (uint32_t)((uint64_t)w * n_chunks / nw);
+    const uint32_t hi = (uint32_t)((uint64_t)(w + 1) * n_chunks / nw);
+    if (lo >= hi)
+        return;
+    Rec nxt = fetch_recs(recs, lo, hi, lane);
+    for (uint32_t base = lo; base < hi; base += 64u) {
+        PieceBatch bt;
+        bt.open(nxt, lane);
+        nxt = fetch_recs(recs, base + 64u, hi, lane);   // prefetch the next batch
+        Piece a[P], b[P];
+        v4u va[P * kRowsPerPiece], vb[P * kRowsPerPiece];
+        v2u ta[P], tb[P];
+        uint32_t q = 0;
+#pragma unroll
+        for (int k = 0; k < P; ++k)
+            a[k] = bt.at(q + k);
+        q += P;
+        load_pass(a, va, ta, lane);
+        for (;;) {
+#pragma unroll
+            for (int k = 0; k < P; ++k)
+                b[k] = bt.at(q + k);
+            q += P;
+            load_pass(b, vb, tb, lane);
+            store_pass(a, va, ta, lane);
+            if (q - P >= bt.total)
+                break;
+#pragma unroll
+            for (int k = 0; k < P; ++k)
+                a[k] = bt.at(q + k);
+            q += P;
+            load_pass(a, va, ta, lane);
+            store_pass(b, vb, tb, lane);
+            if (q - P >= bt.total)
+                break;
+        }
+    }
+}
+
+// One symbol per direction and loop, so that profiles and counters separate them.
+#define KVC_KERNEL(name, body)                                                                     \
+    __global__ __launch_bounds__(kThreadsPerWG) void name(const ChunkRec *__restrict__ recs,     \
+                                                          uint32_t n_chunks)                     \
+    {                                                                                              \
+        body(recs, n_chunks);                                                                      \
+    }
+KVC_KERNEL(kvcopy_h2d_kernel, copy_worklist)
+KVC_KERNEL(kvcopy_d2h_kernel, copy_worklist)
+KVC_KERNEL(kvcopy_d2d_kernel, copy_worklist)
+KVC_KERNEL(kvcopy_h2d_pipe_kernel, copy_worklist_pipelined)
+KVC_KERNEL(kvcopy_d2h_pipe_kernel, copy_worklist_pipelined)
+KVC_KERNEL(kvcopy_d2d_pipe_kernel, copy_worklist_pipelined)
+#undef KVC_KERNEL
 
 }  // namespace
 
 hipError_t launch_copy(const ChunkRec *recs, uint32_t n_chunks, uint32_t grid, int dir,
-                       hipStream_t stream)
+                       bool pipelined, hipStream_t stream)
 {
-    const void *fn = dir == KVCOPY_H2D   ? reinterpret_cast<const void *>(&kvcopy_h2d_kernel)
-                     : dir == KVCOPY_D2H ? reinterpret_cast<const void *>(&kvcopy_d2h_kernel)
-                                         : reinterpret_cast<const void *>(&kvcopy_d2d_kernel);
+    static const void *const fns[2][3] = {
+        {reinterpret_cast<const void *>(&kvcopy_h2d_kernel),
+         reinterpret_cast<const void *>(&kvcopy_d2h_kernel),
+         reinterpret_cast<const void *>(&kvcopy_d2d_kernel)},
+        {reinterpret_cast<const void *>(&kvcopy_h2d_pipe_kernel),
+         reinterpret_cast<const void *>(&kvcopy_d2h_pipe_kernel),
+         reinterpret_cast<const void *>(&kvcopy_d2d_pipe_kernel)}};
     void *args[] = {(void *)&recs, (void *)&n_chunks};
-    return hipLaunchKernel(fn, dim3(grid), dim3(kThreadsPerWG), args, 0, stream);
+    return hipLaunchKernel(fns[pipelined ? 1 : 0][dir], dim3(grid), dim3(kThreadsPerWG), args, 0,
+                           stream);
 }
 
 }  // namespace kvc

@@ -180,8 +180,10 @@ int run_locked(Staging *st, const uint64_t *src, const uint64_t *dst, const uint
         return hip_fail(e);
     if (max_wgs == KVCOPY_WGS_AUTO)
         max_wgs = resolve_auto(st, dir);
-    if ((e = launch_copy(recs, (uint32_t)n_chunks, grid_for(n_chunks, max_wgs), dir, stream)) !=
-        hipSuccess)
+    const uint32_t grid = grid_for(n_chunks, max_wgs);
+    const bool pipelined = (flags & KVCOPY_F_PIPELINE) != 0 ||
+                           (!(flags & KVCOPY_F_PER_CHUNK) && pipeline_pays(dir, grid, n_chunks));
+    if ((e = launch_copy(recs, (uint32_t)n_chunks, grid, dir, pipelined, stream)) != hipSuccess)
         return hip_fail(e);
     if (ev_end && (e = hipEventRecord(ev_end, stream)) != hipSuccess)
         return hip_fail(e);
@@ -227,7 +229,10 @@ extern "C" int kvcopy_batch_ex(const uint64_t *src_addrs, const uint64_t *dst_ad
                 return KVCOPY_EINVAL;
             chunk = opts->chunk_bytes;
         }
-        if (opts->flags & ~(KVCOPY_F_VALIDATE | KVCOPY_F_NO_COALESCE | KVCOPY_F_DESC_UPLOAD))
+        if (opts->flags & ~(KVCOPY_F_VALIDATE | KVCOPY_F_NO_COALESCE | KVCOPY_F_DESC_UPLOAD |
+                            KVCOPY_F_PIPELINE | KVCOPY_F_PER_CHUNK))
+            return KVCOPY_EINVAL;
+        if ((opts->flags & KVCOPY_F_PIPELINE) && (opts->flags & KVCOPY_F_PER_CHUNK))
             return KVCOPY_EINVAL;
         flags = opts->flags;
         ev_begin = opts->kernel_begin;

@@ -94,6 +94,17 @@ enum {
 #define KVCOPY_F_VALIDATE 0x1u    /* check the overlap rule (O(n log n)); also on when KVCOPY_VALIDATE=1 */
 #define KVCOPY_F_NO_COALESCE 0x2u /* skip merging of adjacent ranges (for measurement only) */
 #define KVCOPY_F_DESC_UPLOAD 0x8u /* upload the worklist to device memory before the kernel */
+/* Copy loop.  By default the library picks one per call: the pipelined loop
+ * (each wavefront streams its chunks as 4 KiB pieces with two 16 KiB passes
+ * in flight) when the grid is small -- at most 4 workgroups for H2D/D2H, 256
+ * for D2D -- and every wavefront has at least two chunks; otherwise the
+ * per-chunk loop (one chunk's loads in flight per wavefront).  Measured on
+ * MI355X, the pipelined loop moves 35-40% more bytes per workgroup at 1-4
+ * workgroups, but with both directions on the host link at 16+ workgroups
+ * per direction its deeper queues of host reads cut the pair's rate by a
+ * third.  These flags force one loop (setting both is KVCOPY_EINVAL). */
+#define KVCOPY_F_PIPELINE 0x10u
+#define KVCOPY_F_PER_CHUNK 0x20u
 
 /*
  * kvcopy_coalesce -- merge list-consecutive adjacent ranges.

@@ -59,6 +59,22 @@ int main()
             ++cases;
         }
     }
+    // The copy-loop choice: pipelined only for small grids in which every
+    // wavefront has at least two chunks (4 workgroups on the host link, 256
+    // for D2D).
+    struct { int dir; uint32_t grid; uint64_t chunks; bool want; } pol[] = {
+        {KVCOPY_H2D, 1, 8, true},      {KVCOPY_H2D, 1, 7, false},   {KVCOPY_H2D, 4, 32, true},
+        {KVCOPY_H2D, 5, 1000, false},  {KVCOPY_D2H, 4, 16384, true}, {KVCOPY_D2H, 128, 16384, false},
+        {KVCOPY_D2D, 256, 2048, true}, {KVCOPY_D2D, 256, 2047, false}, {KVCOPY_D2D, 257, 65536, false},
+        {KVCOPY_D2D, 64, 65536, true},
+    };
+    for (const auto &c : pol) {
+        if (pipeline_pays(c.dir, c.grid, c.chunks) != c.want) {
+            printf("pipeline_pays(%d, %u, %llu) != %d\n", c.dir, c.grid,
+                   (unsigned long long)c.chunks, (int)c.want);
+            return 1;
+        }
+    }
     printf("ok %d cases\n", cases);
     return 0;
 }
