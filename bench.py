@@ -168,6 +168,32 @@ class Ctx:
             kern = [(t1 - t0) / k * 1e3] * len(batch_ids)
         return (t1 - t0) / k, kern
 
+    def timed_bracketed(self, r, batch_ids, streams, k, w, max_wgs, **kw):
+        """Seconds per step over k timed steps, and each stream's mean kernel
+        duration (ms): one HIP event pair per stream brackets its k kernels,
+        which run back to back, so no event sits between two kernels."""
+        torch, hiprt = self.torch, self.hiprt
+        self.run_steps(r, batch_ids, streams, w, max_wgs, **kw)
+        torch.cuda.synchronize()
+        use_ev = not self.args.no_events
+        evs = [(hiprt.Event(), hiprt.Event()) for _ in batch_ids] if use_ev else None
+        with no_gc():
+            t0 = time.perf_counter()
+            if use_ev:
+                for (e0, _), st in zip(evs, streams):
+                    e0.record(st)
+            self.run_steps(r, batch_ids, streams, k, max_wgs, **kw)
+            if use_ev:
+                for (_, e1), st in zip(evs, streams):
+                    e1.record(st)
+            torch.cuda.synchronize()
+            t1 = time.perf_counter()
+        if use_ev:
+            kern = [e0.elapsed_ms(e1) / k for e0, e1 in evs]
+        else:
+            kern = [(t1 - t0) / k * 1e3] * len(batch_ids)
+        return (t1 - t0) / k, kern
+
     def latency(self, r, bi, max_wgs, k=100, w=10, **kw):
         """Per-call latency of isolated calls: host time inside kvcopy_batch,
         GPU time from an event recorded before the call to one after it, and
@@ -256,14 +282,13 @@ def bench_kv(c: Ctx, args):
     n_desc = sum(b.n for b in wl.batches)
     max_wgs = args.max_wgs
     log(f"headline: {n_desc} descriptors, {step_bytes} B per step, max_wgs={max_wgs}")
-    # The timed steps carry no HIP events (recording events between the
-    # kernels perturbs how the two streams overlap); a second, evented run of
-    # the same steps gives the kernel-only durations for the roofline.
-    step_s, _ = c.timed(res, [0, 1], [sA, sB], args.steps, args.warmup, max_wgs, with_events=False)
+    # No HIP event sits between two kernels (events recorded between the
+    # kernels perturb how the two streams overlap): one event pair per stream
+    # brackets that stream's back-to-back kernels over the timed steps.
+    step_s, kern_ms = c.timed_bracketed(res, [0, 1], [sA, sB], args.steps, args.warmup, max_wgs)
     value = gbs(step_bytes, step_s)
-    ev_step_s, kern_ms = c.timed(res, [0, 1], [sA, sB], args.steps, 2, max_wgs)
-    log(f"  bidirectional: {step_s * 1e3:.3f} ms/step, {value:.2f} GB/s; evented run "
-        f"{ev_step_s * 1e3:.3f} ms/step, kernel ms {kern_ms}")
+    log(f"  bidirectional: {step_s * 1e3:.3f} ms/step, {value:.2f} GB/s; mean kernel ms per "
+        f"stream {kern_ms}")
     plans = [K.kvcopy_plan(*res.addrs[j], wl.batches[j].size) for j in range(2)]
     algo = [wl.batches[j].nbytes + plans[j].n_chunks * REC_BYTES for j in range(2)]
     ach = [gbs(algo[j], kern_ms[j] / 1e3) for j in range(2)]
@@ -298,16 +323,19 @@ def bench_kv(c: Ctx, args):
         log(f"  contiguous ceilings: {extras['contiguous_memcpy_ceiling_GBps']}")
         frag = {}
         for j, name, kind in ((0, "h2d", hiprt.H2D_KIND), (1, "d2h", hiprt.D2H_KIND)):
-            dt = per_fragment(c, plans[j], kind, reps=2)
-            frag[name] = {"GBps": round(gbs(wl.batches[j].nbytes, dt), 3),
-                          "ms_per_call": round(dt * 1e3, 3), "copies": int(plans[j].n_merged)}
-            log(f"  per-fragment hipMemcpyAsync {name}: {frag[name]}")
-        extras["per_fragment_memcpy"] = frag
+            frag[name] = dma_baselines(c, plans[j], wl.batches[j].nbytes, kind)
+            log(f"  DMA baselines {name}: {frag[name]}")
+        extras["dma_baselines"] = frag
+        extras["dma_baselines_rocm_runtime"] = dma_runtime_baselines()
 
     if args.counter_calibration:
         counter_calibration(c)
 
-    # verification + cpu_baseline (the oracle on host images of the same step)
+    # verification + cpu_baseline (the oracle on host images of the same step).
+    # The DMA baselines above wrote the same destination arenas, so refill
+    # them and run one more kernel step before reading the images back.
+    res.fill()
+    c.run_steps(res, [0, 1], [sA, sB], 1, max_wgs)
     torch.cuda.synchronize()
     final = {i: res.image(i) for i in (0, 2)}        # device pool, host D2H destination
     import oracle
@@ -428,6 +456,34 @@ def per_fragment(c: Ctx, plan, kind, reps=2):
     return (time.perf_counter() - t0) / reps
 
 
+def dma_runtime_baselines():
+    """The DMA baselines of block_copy_amd/dma_baselines.py, run in a child
+    process without torch (on ROCm's own HIP runtime, which exports
+    hipMemcpyBatchAsync); None if the child fails."""
+    import subprocess
+    try:
+        r = subprocess.run([sys.executable, "-m", "block_copy_amd.dma_baselines"], cwd=ROOT,
+                           capture_output=True, text=True, timeout=300)
+    except subprocess.TimeoutExpired:
+        log("  DMA baselines child timed out")
+        return None
+    for ln in r.stderr.splitlines():
+        if "amdgpu.ids" not in ln:
+            log(f"  [dma child] {ln}")
+    if r.returncode != 0:
+        log(f"  DMA baselines child exited with {r.returncode}")
+        return None
+    return json.loads(r.stdout.strip().splitlines()[-1])
+
+
+def dma_baselines(c: Ctx, plan, nbytes, kind, reps=2):
+    """One hipMemcpyAsync per (coalesced) range on one stream, in this process
+    (on the HIP runtime the kernel runs on)."""
+    dt = per_fragment(c, plan, kind, reps=reps)
+    return {"per_fragment": {"GBps": round(gbs(nbytes, dt), 3), "ms_per_call": round(dt * 1e3, 3),
+                             "copies": int(plan.n_merged)}}
+
+
 # ---------------------------------------------------------------------------
 # D2D
 # ---------------------------------------------------------------------------
@@ -447,6 +503,9 @@ def d2d_results(c: Ctx, args):
                      "frac_hbm_peak_kernel": round(gbs(hbm, km[0] / 1e3) / HBM_PEAK_GBS, 4),
                      "latency": c.latency(r, 0, 0, k=50, w=5)}
         c.verify(wld, r, [0], f"d2d {name}")
+        if name == "1024x4KiB":     # after the check: the DMA baselines write the same bytes
+            out[name]["dma_baselines"] = dma_baselines(c, pl, wld.batches[0].nbytes,
+                                                       hiprt.D2D_KIND, reps=5)
         log(f"  d2d {name}: {out[name]} (bit-exact)")
         r.free()
     big = torch.empty(2 << 30, dtype=torch.uint8, device=c.dev)
@@ -508,12 +567,12 @@ def bench_mixed(c: Ctx, args):
         k = max(5, min(args.steps * 5, 200 if n <= 256 else args.steps))
         s, km = c.timed(r, [0], [c.sA], k, args.warmup, args.max_wgs)
         lat = c.latency(r, 0, args.max_wgs, k=50 if n <= 4096 else 10, w=5)
-        frag_s = per_fragment(c, pl, hiprt.H2D_KIND, reps=2 if n <= 4096 else 1)
+        c.verify(wl, r, [0], f"mixed {n}")       # before the DMA baselines write the same bytes
+        dma = dma_baselines(c, pl, b.nbytes, hiprt.H2D_KIND, reps=2 if n <= 4096 else 1)
         rows[str(n)] = {"bytes": b.nbytes, "merged": int(pl.n_merged), "chunks": int(pl.n_chunks),
                         "GBps": round(gbs(b.nbytes, s), 2), "kernel_us": round(km[0] * 1e3, 2),
                         "kernel_GBps": round(gbs(b.nbytes, km[0] / 1e3), 2), "latency": lat,
-                        "per_fragment_GBps": round(gbs(b.nbytes, frag_s), 3)}
-        c.verify(wl, r, [0], f"mixed {n}")
+                        "dma_baselines": dma}
         log(f"  mixed N={n}: {rows[str(n)]} (bit-exact)")
         r.free()
     top = rows["65536"]

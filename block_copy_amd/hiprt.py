@@ -1,7 +1,10 @@
 """Minimal ctypes access to the HIP runtime for timing and baselines.
 
 Used by bench.py and the tests for events on a given stream and for the
-plain hipMemcpyAsync baselines (contiguous ceilings, one copy per fragment).
+plain DMA baselines (contiguous ceilings, one hipMemcpyAsync per fragment,
+one hipMemcpyBatchAsync per list).  In a process that has imported torch,
+the HIP runtime already loaded is torch's own copy, and this module (like
+libkvcopy.so) binds to it.
 """
 from __future__ import annotations
 
@@ -36,9 +39,39 @@ hip.hipDeviceSynchronize.argtypes = []
 hip.hipExtStreamCreateWithCUMask.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint32,
                                              ctypes.POINTER(ctypes.c_uint32)]
 hip.hipStreamDestroy.argtypes = [ctypes.c_void_p]
+hip.hipMalloc.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_size_t]
+hip.hipFree.argtypes = [ctypes.c_void_p]
+hip.hipHostMalloc.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_size_t, ctypes.c_uint]
+hip.hipHostFree.argtypes = [ctypes.c_void_p]
+hip.hipMemset.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t]
+hip.hipStreamCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+hip.hipRuntimeGetVersion.argtypes = [ctypes.POINTER(ctypes.c_int)]
+
+
+class _MemLocation(ctypes.Structure):
+    """hipMemLocation."""
+    _fields_ = [("type", ctypes.c_int), ("id", ctypes.c_int)]
+
+
+class _MemcpyAttributes(ctypes.Structure):
+    """hipMemcpyAttributes."""
+    _fields_ = [("srcAccessOrder", ctypes.c_int), ("srcLocHint", _MemLocation),
+                ("dstLocHint", _MemLocation), ("flags", ctypes.c_uint)]
+
+
+_SRC_ACCESS_ORDER_STREAM = 1                    # hipMemcpySrcAccessOrderStream
+_LOC_DEVICE, _LOC_HOST = 1, 2                    # hipMemLocationTypeDevice / Host
+_u64p = ctypes.POINTER(ctypes.c_uint64)
+_has_batch = hasattr(hip, "hipMemcpyBatchAsync")
+if _has_batch:
+    hip.hipMemcpyBatchAsync.argtypes = [_u64p, _u64p, _u64p, ctypes.c_size_t,
+                                        ctypes.POINTER(_MemcpyAttributes), _u64p, ctypes.c_size_t,
+                                        _u64p, ctypes.c_void_p]
+    hip.hipMemcpyBatchAsync.restype = ctypes.c_int
 for _f in ("hipEventCreate", "hipEventRecord", "hipEventSynchronize", "hipEventElapsedTime",
            "hipEventDestroy", "hipMemcpyAsync", "hipStreamSynchronize", "hipDeviceSynchronize",
-           "hipExtStreamCreateWithCUMask", "hipStreamDestroy"):
+           "hipExtStreamCreateWithCUMask", "hipStreamDestroy", "hipMalloc", "hipFree",
+           "hipHostMalloc", "hipHostFree", "hipMemset", "hipStreamCreate", "hipRuntimeGetVersion"):
     getattr(hip, _f).restype = ctypes.c_int
 
 
@@ -80,6 +113,34 @@ def memcpy_async(dst: int, src: int, nbytes: int, kind: int, stream) -> None:
     check(hip.hipMemcpyAsync(dst, src, nbytes, kind, _s(stream)), "hipMemcpyAsync")
 
 
+def memcpy_batch_async(dsts, srcs, sizes, stream, src_host: bool, dst_host: bool,
+                       with_attrs: bool = True) -> int:
+    """One hipMemcpyBatchAsync call for the whole list (the runtime's batched
+    DMA path), in stream order; dsts/srcs/sizes are uint64 NumPy arrays of
+    equal length.  with_attrs=False passes no copy attributes (the runtime's
+    header marks them unsupported).  Returns the hipError_t (0 on success);
+    raises if the runtime does not export the call."""
+    import numpy as np
+    if not _has_batch:
+        raise RuntimeError("hipMemcpyBatchAsync is not exported by this HIP runtime")
+    d = np.ascontiguousarray(dsts, dtype=np.uint64)
+    s = np.ascontiguousarray(srcs, dtype=np.uint64)
+    z = np.ascontiguousarray(sizes, dtype=np.uint64)
+    if not (len(d) == len(s) == len(z)):
+        raise ValueError("dsts, srcs and sizes must have the same length")
+    attrs = _MemcpyAttributes(_SRC_ACCESS_ORDER_STREAM,
+                              _MemLocation(_LOC_HOST if src_host else _LOC_DEVICE, 0),
+                              _MemLocation(_LOC_HOST if dst_host else _LOC_DEVICE, 0), 0)
+    idx = np.zeros(1, np.uint64)
+    fail = np.zeros(1, np.uint64)
+    p = lambda a: a.ctypes.data_as(_u64p)  # noqa: E731
+    if not with_attrs:
+        return int(hip.hipMemcpyBatchAsync(p(d), p(s), p(z), len(d), None, None, 0, p(fail),
+                                           _s(stream)))
+    return int(hip.hipMemcpyBatchAsync(p(d), p(s), p(z), len(d), ctypes.byref(attrs), p(idx), 1,
+                                       p(fail), _s(stream)))
+
+
 def stream_sync(stream) -> None:
     check(hip.hipStreamSynchronize(_s(stream)), "hipStreamSynchronize")
 
@@ -101,3 +162,44 @@ class CUMaskStream:
         if self.cuda_stream:
             check(hip.hipStreamDestroy(self.cuda_stream), "hipStreamDestroy")
             self.cuda_stream = None
+
+
+def runtime_version() -> int:
+    v = ctypes.c_int(0)
+    check(hip.hipRuntimeGetVersion(ctypes.byref(v)), "hipRuntimeGetVersion")
+    return int(v.value)
+
+
+def has_memcpy_batch() -> bool:
+    return _has_batch
+
+
+def device_alloc(nbytes: int) -> int:
+    p = ctypes.c_void_p()
+    check(hip.hipMalloc(ctypes.byref(p), nbytes), "hipMalloc")
+    return int(p.value)
+
+
+def device_free(ptr: int) -> None:
+    check(hip.hipFree(ctypes.c_void_p(ptr)), "hipFree")
+
+
+def host_alloc_mapped(nbytes: int) -> int:
+    """Pinned host memory, mapped and portable (device address == host address)."""
+    p = ctypes.c_void_p()
+    check(hip.hipHostMalloc(ctypes.byref(p), nbytes, 0x2 | 0x1), "hipHostMalloc")
+    return int(p.value)
+
+
+def host_free(ptr: int) -> None:
+    check(hip.hipHostFree(ctypes.c_void_p(ptr)), "hipHostFree")
+
+
+def memset(ptr: int, value: int, nbytes: int) -> None:
+    check(hip.hipMemset(ctypes.c_void_p(ptr), value, nbytes), "hipMemset")
+
+
+def stream_create() -> int:
+    h = ctypes.c_void_p()
+    check(hip.hipStreamCreate(ctypes.byref(h)), "hipStreamCreate")
+    return int(h.value)
