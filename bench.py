@@ -688,6 +688,11 @@ def bench_interference(c: Ctx, args):
                             time.sleep(20e-6)      # yield the worker while a piece runs
                     for jb in jobs:
                         K.kvcopy_job_destroy(jb)
+                elif isinstance(mode, str) and mode.startswith("pipe"):
+                    # the pipelined loop forced at a small cap
+                    g = int(mode.split(":")[1])
+                    r.submit(0, g, sa, flags=K.F_PIPELINE)
+                    r.submit(1, g, sb, flags=K.F_PIPELINE)
                 else:
                     g = K.WGS_ALL if isinstance(mode, str) else mode
                     r.submit(0, g, sa)
@@ -728,8 +733,8 @@ def bench_interference(c: Ctx, args):
             th.join()
         return gpu_ms, wall_ms, moved[0] / dur, bursts[0]
 
-    modes = ["none", "direct", 1, 2, 8, 32, 128, 0, "job:1024", "job:2048", "job:4096",
-             "cumask:8", "cumask:32"]
+    modes = ["none", "direct", 1, 2, 8, 32, 128, 0, "pipe:1", "pipe:4", "job:1024", "job:2048",
+             "job:4096", "cumask:8", "cumask:32"]
     results = {str(m): {"gpu": [], "wall": [], "rate": [], "bursts": 0} for m in modes}
     for rep in range(args.decode_runs):
         order = modes[rep % len(modes):] + modes[:rep % len(modes)]

@@ -89,14 +89,30 @@ constexpr uint32_t kThreadsPerWG = 64 * kWavesPerWG;
 hipError_t launch_copy(const ChunkRec *recs, uint32_t n_chunks, uint32_t grid, int dir,
                        bool pipelined, hipStream_t stream);
 
-// The library's choice of copy loop when no KVCOPY_F_PIPELINE /
-// KVCOPY_F_PER_CHUNK flag forces one: pipelined for small grids (at most 4
-// workgroups on the host link, 256 for D2D) in which every wavefront has at
-// least two chunks.
+// KVCOPY_F_DYNAMIC: the per-chunk loop with chunks claimed at run time.
+// claim points at two zeroed device counters (next chunk, wavefronts done);
+// every wavefront claims `grain` chunks at a time with an atomic add, one
+// batch ahead, and the last wavefront to finish resets both counters to zero.
+hipError_t launch_copy_dynamic(const ChunkRec *recs, uint32_t n_chunks, uint32_t grid, int dir,
+                               uint32_t *claim, uint32_t grain, hipStream_t stream);
+
+// Chunks per claim: about four claims per wavefront, at most 64 (one record
+// per lane), at least 1.
+inline uint32_t claim_grain(uint64_t n_chunks, uint32_t grid)
+{
+    const uint64_t per = n_chunks / (4ull * grid * kWavesPerWG);
+    return per < 1 ? 1u : per > 64 ? 64u : (uint32_t)per;
+}
+
+// The library's choice of copy loop when no loop flag forces one: the
+// pipelined loop for D2D grids of at most 256 workgroups in which every
+// wavefront has at least two chunks, else the per-chunk loop.  (On the host
+// link the pipelined loop moves more bytes per workgroup at small grids but
+// lengthens co-running kernels' worst steps several times over, and small
+// grids are the setting chosen to protect them; there it is opt-in.)
 inline bool pipeline_pays(int dir, uint32_t grid, uint64_t n_chunks)
 {
-    const uint32_t max_grid = dir == 2 /* KVCOPY_D2D */ ? 256u : 4u;
-    return grid <= max_grid && n_chunks >= 2ull * grid * kWavesPerWG;
+    return dir == 2 /* KVCOPY_D2D */ && grid <= 256u && n_chunks >= 2ull * grid * kWavesPerWG;
 }
 
 // ---- device-resident batches (device_batch.hip) ---------------------------

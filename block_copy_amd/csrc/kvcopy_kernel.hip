@@ -266,6 +266,52 @@ __device__ __forceinline__ void copy_worklist_pipelined(const ChunkRec *__restri
     }
 }
 
+// ---- dynamic claiming ---------------------------------------------------------
+//
+// The per-chunk loop over chunks claimed at run time: lane 0 adds `grain` to
+// the call's claim counter (a device-memory atomic) and the wavefront copies
+// the chunks [b, b + grain) it got, having already claimed and started
+// fetching the records of its next batch.  The last wavefront to finish (the
+// one whose increment of the done counter completes the grid) resets both
+// counters to zero for the next call that uses them; every other wavefront
+// has made its final claim before its own done increment, so no claim can
+// follow the reset.
+__device__ __forceinline__ uint32_t claim_batch(uint32_t *claim, uint32_t grain, uint32_t lane)
+{
+    uint32_t b = 0;
+    if (lane == 0)
+        b = atomicAdd(claim, grain);
+    return __builtin_amdgcn_readfirstlane(b);
+}
+
+__device__ __forceinline__ void copy_worklist_dynamic(const ChunkRec *__restrict__ recs,
+                                                      uint32_t n_chunks, uint32_t *claim,
+                                                      uint32_t grain)
+{
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t nw = gridDim.x * kWavesPerWG;
+    uint32_t b = claim_batch(claim, grain, lane);
+    Rec cur = fetch_recs(recs, b, b < n_chunks ? (n_chunks - b < grain ? n_chunks : b + grain) : b,
+                         lane);
+    while (b < n_chunks) {
+        const uint32_t cnt = n_chunks - b < grain ? n_chunks - b : grain;
+        const uint32_t nb = claim_batch(claim, grain, lane);   // claim ahead
+        const uint32_t ncnt = nb < n_chunks ? (n_chunks - nb < grain ? n_chunks - nb : grain) : 0u;
+        const Rec nxt = fetch_recs(recs, nb, nb + ncnt, lane);
+        for (uint32_t j = 0; j < cnt; ++j)
+            copy_chunk(lane_u64(cur.src, j), lane_u64(cur.dst, j),
+                       __builtin_amdgcn_readlane(cur.bytes, j), lane);
+        cur = nxt;
+        b = nb;
+    }
+    if (lane == 0) {
+        if (atomicAdd(claim + 1, 1u) == nw - 1) {
+            atomicExch(claim, 0u);
+            atomicExch(claim + 1, 0u);
+        }
+    }
+}
+
 // One symbol per direction and loop, so that profiles and counters separate them.
 #define KVC_KERNEL(name, body)                                                                     \
     __global__ __launch_bounds__(kThreadsPerWG) void name(const ChunkRec *__restrict__ recs,     \
@@ -280,6 +326,18 @@ KVC_KERNEL(kvcopy_h2d_pipe_kernel, copy_worklist_pipelined)
 KVC_KERNEL(kvcopy_d2h_pipe_kernel, copy_worklist_pipelined)
 KVC_KERNEL(kvcopy_d2d_pipe_kernel, copy_worklist_pipelined)
 #undef KVC_KERNEL
+
+#define KVC_DYN_KERNEL(name)                                                                       \
+    __global__ __launch_bounds__(kThreadsPerWG) void name(const ChunkRec *__restrict__ recs,     \
+                                                          uint32_t n_chunks, uint32_t *claim,    \
+                                                          uint32_t grain)                        \
+    {                                                                                              \
+        copy_worklist_dynamic(recs, n_chunks, claim, grain);                                       \
+    }
+KVC_DYN_KERNEL(kvcopy_h2d_dyn_kernel)
+KVC_DYN_KERNEL(kvcopy_d2h_dyn_kernel)
+KVC_DYN_KERNEL(kvcopy_d2d_dyn_kernel)
+#undef KVC_DYN_KERNEL
 
 }  // namespace
 
@@ -296,6 +354,16 @@ hipError_t launch_copy(const ChunkRec *recs, uint32_t n_chunks, uint32_t grid, i
     void *args[] = {(void *)&recs, (void *)&n_chunks};
     return hipLaunchKernel(fns[pipelined ? 1 : 0][dir], dim3(grid), dim3(kThreadsPerWG), args, 0,
                            stream);
+}
+
+hipError_t launch_copy_dynamic(const ChunkRec *recs, uint32_t n_chunks, uint32_t grid, int dir,
+                               uint32_t *claim, uint32_t grain, hipStream_t stream)
+{
+    static const void *const fns[3] = {reinterpret_cast<const void *>(&kvcopy_h2d_dyn_kernel),
+                                       reinterpret_cast<const void *>(&kvcopy_d2h_dyn_kernel),
+                                       reinterpret_cast<const void *>(&kvcopy_d2d_dyn_kernel)};
+    void *args[] = {(void *)&recs, (void *)&n_chunks, (void *)&claim, (void *)&grain};
+    return hipLaunchKernel(fns[dir], dim3(grid), dim3(kThreadsPerWG), args, 0, stream);
 }
 
 }  // namespace kvc

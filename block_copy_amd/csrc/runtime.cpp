@@ -69,6 +69,12 @@ struct Staging {
     int tuned[3] = {-2, -2, -2};   // kvcopy_autotune's cap per direction (-2: not tuned)
     uint8_t *host = nullptr;   // pinned, mapped (device address == host address)
     uint8_t *dev = nullptr;    // device twin, allocated on first KVCOPY_F_DESC_UPLOAD
+    // KVCOPY_F_DYNAMIC: one pair of claim counters (next chunk, wavefronts
+    // done) per 256-byte granule of the ring, in device memory, allocated on
+    // first use and zeroed once.  A call uses the pair of its region's first
+    // granule, which no other region in flight shares; the call's last
+    // wavefront resets the pair to zero.
+    uint32_t *claims = nullptr;
     std::vector<hipEvent_t> spare;
     StagingRing<hipEvent_t, HipEventOps> ring{HipEventOps{&spare}};
 };
@@ -87,15 +93,15 @@ Staging *staging_for(int device)
 }
 
 // Makes the ring at least 4 x `need` bytes (and allocates the device twin if
-// `want_dev`).  Old buffers are released only after every kernel using them
-// has completed.
-int grow(Staging *st, uint64_t need, bool want_dev)
+// `want_dev`, the claim counters if `want_claims`).  Old buffers are
+// released only after every kernel using them has completed.
+int grow(Staging *st, uint64_t need, bool want_dev, bool want_claims)
 {
     uint64_t cap = st->ring.capacity() ? st->ring.capacity() : kRingMinBytes;
     while (cap < 4 * need)
         cap *= 2;
     const bool resize = cap != st->ring.capacity();
-    if (!resize && (!want_dev || st->dev))
+    if (!resize && (!want_dev || st->dev) && (!want_claims || st->claims))
         return KVCOPY_OK;
     int rc = st->ring.drain();
     if (rc != KVCOPY_OK)
@@ -105,8 +111,13 @@ int grow(Staging *st, uint64_t need, bool want_dev)
             hipHostFree(st->host);
         if (st->dev)
             hipFree(st->dev);
+        if (st->claims) {
+            want_claims = true;
+            hipFree(st->claims);
+        }
         st->host = nullptr;
         st->dev = nullptr;
+        st->claims = nullptr;
         st->ring.reset(0);
     }
     hipError_t e;
@@ -123,6 +134,21 @@ int grow(Staging *st, uint64_t need, bool want_dev)
         if (e != hipSuccess) {
             st->dev = nullptr;
             return e == hipErrorOutOfMemory ? KVCOPY_ENOMEM : hip_fail(e);
+        }
+    }
+    if (want_claims && st->claims == nullptr) {
+        const uint64_t bytes = cap / kAlign * 2 * sizeof(uint32_t);
+        e = hipMalloc((void **)&st->claims, bytes);
+        if (e != hipSuccess) {
+            st->claims = nullptr;
+            return e == hipErrorOutOfMemory ? KVCOPY_ENOMEM : hip_fail(e);
+        }
+        // Once, at allocation (the ring is drained): from here on every
+        // kernel leaves its pair at zero.
+        if ((e = hipMemset(st->claims, 0, bytes)) != hipSuccess) {
+            hipFree(st->claims);
+            st->claims = nullptr;
+            return hip_fail(e);
         }
     }
     return KVCOPY_OK;
@@ -153,11 +179,13 @@ int run_locked(Staging *st, const uint64_t *src, const uint64_t *dst, const uint
                uint32_t chunk, uint32_t flags, hipEvent_t ev_begin, hipEvent_t ev_end)
 {
     const bool upload = (flags & KVCOPY_F_DESC_UPLOAD) != 0;
+    const bool dynamic = (flags & KVCOPY_F_DYNAMIC) != 0;
     const uint64_t need = (pre.bound * sizeof(ChunkRec) + kAlign - 1) / kAlign * kAlign;
     uint64_t off = 0;
     int rc;
-    if (4 * need > st->ring.capacity() || (upload && st->dev == nullptr)) {
-        if ((rc = grow(st, need, upload)) != KVCOPY_OK)
+    if (4 * need > st->ring.capacity() || (upload && st->dev == nullptr) ||
+        (dynamic && st->claims == nullptr)) {
+        if ((rc = grow(st, need, upload, dynamic)) != KVCOPY_OK)
             return rc;
     }
     if ((rc = st->ring.reserve(need, &off)) != KVCOPY_OK)
@@ -181,9 +209,16 @@ int run_locked(Staging *st, const uint64_t *src, const uint64_t *dst, const uint
     if (max_wgs == KVCOPY_WGS_AUTO)
         max_wgs = resolve_auto(st, dir);
     const uint32_t grid = grid_for(n_chunks, max_wgs);
-    const bool pipelined = (flags & KVCOPY_F_PIPELINE) != 0 ||
-                           (!(flags & KVCOPY_F_PER_CHUNK) && pipeline_pays(dir, grid, n_chunks));
-    if ((e = launch_copy(recs, (uint32_t)n_chunks, grid, dir, pipelined, stream)) != hipSuccess)
+    if (dynamic) {
+        uint32_t *claim = st->claims + off / kAlign * 2;
+        e = launch_copy_dynamic(recs, (uint32_t)n_chunks, grid, dir, claim,
+                                claim_grain(n_chunks, grid), stream);
+    } else {
+        const bool pipelined = (flags & KVCOPY_F_PIPELINE) != 0 ||
+                               (!(flags & KVCOPY_F_PER_CHUNK) && pipeline_pays(dir, grid, n_chunks));
+        e = launch_copy(recs, (uint32_t)n_chunks, grid, dir, pipelined, stream);
+    }
+    if (e != hipSuccess)
         return hip_fail(e);
     if (ev_end && (e = hipEventRecord(ev_end, stream)) != hipSuccess)
         return hip_fail(e);
@@ -230,9 +265,10 @@ extern "C" int kvcopy_batch_ex(const uint64_t *src_addrs, const uint64_t *dst_ad
             chunk = opts->chunk_bytes;
         }
         if (opts->flags & ~(KVCOPY_F_VALIDATE | KVCOPY_F_NO_COALESCE | KVCOPY_F_DESC_UPLOAD |
-                            KVCOPY_F_PIPELINE | KVCOPY_F_PER_CHUNK))
+                            KVCOPY_F_PIPELINE | KVCOPY_F_PER_CHUNK | KVCOPY_F_DYNAMIC))
             return KVCOPY_EINVAL;
-        if ((opts->flags & KVCOPY_F_PIPELINE) && (opts->flags & KVCOPY_F_PER_CHUNK))
+        const uint32_t loops = opts->flags & (KVCOPY_F_PIPELINE | KVCOPY_F_PER_CHUNK | KVCOPY_F_DYNAMIC);
+        if (loops & (loops - 1))   // more than one loop forced
             return KVCOPY_EINVAL;
         flags = opts->flags;
         ev_begin = opts->kernel_begin;

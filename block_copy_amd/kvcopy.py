@@ -22,7 +22,8 @@ OK, EINVAL, EALIGN, EOVERLAP, ENOMEM, EHIP = 0, -1, -2, -3, -4, -5
 WGS_ALL, WGS_AUTO = 0, -1
 CHUNK_DEFAULT = 16384
 CHUNK_MAX = 1 << 20
-F_VALIDATE, F_NO_COALESCE, F_DESC_UPLOAD, F_PIPELINE, F_PER_CHUNK = 0x1, 0x2, 0x8, 0x10, 0x20
+F_VALIDATE, F_NO_COALESCE, F_DESC_UPLOAD = 0x1, 0x2, 0x8
+F_PIPELINE, F_PER_CHUNK, F_DYNAMIC = 0x10, 0x20, 0x40
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvcopy.so")
 

@@ -94,17 +94,28 @@ enum {
 #define KVCOPY_F_VALIDATE 0x1u    /* check the overlap rule (O(n log n)); also on when KVCOPY_VALIDATE=1 */
 #define KVCOPY_F_NO_COALESCE 0x2u /* skip merging of adjacent ranges (for measurement only) */
 #define KVCOPY_F_DESC_UPLOAD 0x8u /* upload the worklist to device memory before the kernel */
-/* Copy loop.  By default the library picks one per call: the pipelined loop
- * (each wavefront streams its chunks as 4 KiB pieces with two 16 KiB passes
- * in flight) when the grid is small -- at most 4 workgroups for H2D/D2H, 256
- * for D2D -- and every wavefront has at least two chunks; otherwise the
- * per-chunk loop (one chunk's loads in flight per wavefront).  Measured on
- * MI355X, the pipelined loop moves 35-40% more bytes per workgroup at 1-4
- * workgroups, but with both directions on the host link at 16+ workgroups
- * per direction its deeper queues of host reads cut the pair's rate by a
- * third.  These flags force one loop (setting both is KVCOPY_EINVAL). */
+/* Copy loop.  Two loops give the same bytes: the per-chunk loop (a
+ * wavefront has one chunk's loads in flight) and the pipelined loop (a
+ * wavefront streams its chunks as 4 KiB pieces with two 16 KiB passes in
+ * flight).  By default D2D calls use the pipelined loop when the grid has at
+ * most 256 workgroups and every wavefront at least two chunks, and all other
+ * calls the per-chunk loop.  Measured on MI355X: with 1-4 workgroups the
+ * pipelined loop moves 35-40% more bytes per workgroup over the host link,
+ * but it lengthens a co-running decode loop's worst steps several times over
+ * (small grids being the setting chosen to protect such work), and with both
+ * host-link directions at 16+ workgroups each it cuts the pair's rate by a
+ * third; so on the host link it is opt-in.  These flags force one loop
+ * (setting more than one loop flag is KVCOPY_EINVAL). */
 #define KVCOPY_F_PIPELINE 0x10u
 #define KVCOPY_F_PER_CHUNK 0x20u
+/* The per-chunk loop with chunks claimed at run time instead of an equal
+ * contiguous share per wavefront: a wavefront claims a batch of chunks
+ * (about a quarter of its fair share, at most 64) with an atomic add on a
+ * counter in device memory, one batch ahead, so faster wavefronts take more
+ * chunks.  The library owns the counters (allocated and zeroed on first use,
+ * reset by each kernel's last wavefront).  Exclusive with the two flags
+ * above. */
+#define KVCOPY_F_DYNAMIC 0x40u
 
 /*
  * kvcopy_coalesce -- merge list-consecutive adjacent ranges.

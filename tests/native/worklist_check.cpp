@@ -59,12 +59,11 @@ int main()
             ++cases;
         }
     }
-    // The copy-loop choice: pipelined only for small grids in which every
-    // wavefront has at least two chunks (4 workgroups on the host link, 256
-    // for D2D).
+    // The default copy-loop choice: pipelined only for D2D grids of at most
+    // 256 workgroups in which every wavefront has at least two chunks.
     struct { int dir; uint32_t grid; uint64_t chunks; bool want; } pol[] = {
-        {KVCOPY_H2D, 1, 8, true},      {KVCOPY_H2D, 1, 7, false},   {KVCOPY_H2D, 4, 32, true},
-        {KVCOPY_H2D, 5, 1000, false},  {KVCOPY_D2H, 4, 16384, true}, {KVCOPY_D2H, 128, 16384, false},
+        {KVCOPY_H2D, 1, 8, false},     {KVCOPY_H2D, 4, 32, false},     {KVCOPY_D2H, 4, 16384, false},
+        {KVCOPY_D2H, 128, 16384, false}, {KVCOPY_D2D, 1, 8, true},     {KVCOPY_D2D, 1, 7, false},
         {KVCOPY_D2D, 256, 2048, true}, {KVCOPY_D2D, 256, 2047, false}, {KVCOPY_D2D, 257, 65536, false},
         {KVCOPY_D2D, 64, 65536, true},
     };
@@ -72,6 +71,18 @@ int main()
         if (pipeline_pays(c.dir, c.grid, c.chunks) != c.want) {
             printf("pipeline_pays(%d, %u, %llu) != %d\n", c.dir, c.grid,
                    (unsigned long long)c.chunks, (int)c.want);
+            return 1;
+        }
+    }
+    // Dynamic claims: about four claims per wavefront, between 1 and 64 chunks.
+    struct { uint64_t chunks; uint32_t grid; uint32_t want; } gr[] = {
+        {1024, 256, 1}, {16384, 128, 8}, {16384, 1, 64}, {65536, 16384, 1}, {3, 1, 1},
+        {4096, 4, 64}, {2048, 4, 32},
+    };
+    for (const auto &c : gr) {
+        if (claim_grain(c.chunks, c.grid) != c.want) {
+            printf("claim_grain(%llu, %u) = %u, want %u\n", (unsigned long long)c.chunks, c.grid,
+                   claim_grain(c.chunks, c.grid), c.want);
             return 1;
         }
     }

@@ -102,15 +102,87 @@ def test_pipelined_d2d_large_chunks_and_upload(K):
     res.free()
 
 
-@pytest.mark.parametrize("max_wgs", [1, 4])
-@pytest.mark.parametrize("direction", ["h2d", "d2h"])
-def test_per_chunk_loop_forced_on_small_grids(K, direction, max_wgs):
-    """Small grids pick the pipelined loop by default; the per-chunk loop must
-    still give the same bytes when forced."""
+@pytest.mark.parametrize("max_wgs", [1, 64])
+def test_per_chunk_loop_forced_on_small_d2d_grids(K, max_wgs):
+    """Small D2D grids pick the pipelined loop by default; the per-chunk loop
+    must still give the same bytes when forced."""
     from block_copy_amd.harness import Resident
-    wl = W.kv_blocks(seed=5, directions=direction)
+    wl = W.d2d_blocks(seed=5)
     res = Resident(wl)
-    _say("per-chunk forced", direction, "max_wgs", max_wgs)
+    _say("per-chunk forced d2d max_wgs", max_wgs)
     _run(res, [0], max_wgs, flags=K.F_PER_CHUNK)
-    _check(res, [0], f"per-chunk {direction} max_wgs={max_wgs}")
+    _check(res, [0], f"per-chunk d2d max_wgs={max_wgs}")
+    res.free()
+
+
+# ---------------------------------------------------------------------------
+# Dynamic claiming (KVCOPY_F_DYNAMIC): chunks claimed with device atomics
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dname", sorted(DIRS))
+@pytest.mark.parametrize("chunk", [16, 4096, 16384])
+def test_dynamic_irregular(K, dname, chunk):
+    from block_copy_amd.harness import Resident
+    d, sw, dw = DIRS[dname]
+    wl = W.irregular(seed=chunk % 83 + 11, n=300, max_size=min(80 * 1024, 256 * chunk), dir_=d,
+                     src_where=sw, dst_where=dw, misalign=True, zero_frac=0.05)
+    res = Resident(wl)
+    for max_wgs in (1, 5, 0):
+        _say("dynamic irregular", dname, "chunk", chunk, "max_wgs", max_wgs)
+        res.fill()
+        _run(res, [0], max_wgs, chunk_bytes=chunk, flags=K.F_DYNAMIC)
+        _check(res, [0], f"dynamic irregular {dname} chunk={chunk} max_wgs={max_wgs}")
+    res.free()
+
+
+@pytest.mark.parametrize("max_wgs", [1, 8, 128, 0])
+def test_dynamic_kv_concurrent(K, max_wgs):
+    """Two calls in flight at once on two streams, each with its own counters."""
+    from block_copy_amd.harness import Resident
+    wl = W.kv_blocks(seed=6, directions="both")
+    res = Resident(wl)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    _say("dynamic kv both max_wgs", max_wgs)
+    _run(res, [0, 1], max_wgs, streams=[s1, s2], flags=K.F_DYNAMIC)
+    _check(res, [0, 1], f"dynamic h2d+d2h max_wgs={max_wgs}")
+    res.free()
+
+
+def test_dynamic_counters_reset_across_many_calls(K):
+    """Every call must find its claim counters at zero.  (a) 100 KV bursts
+    (393 KiB of worklist each, so the 16 MiB staging ring wraps twice), H2D
+    on one stream and D2H on another, dynamic and static calls mixed; every
+    burst writes the same bytes, so the final images are those of one burst.
+    (b) 40 MoE gathers with different slots on one stream, in order."""
+    from block_copy_amd.harness import Resident
+    wl = W.kv_blocks(seed=8, directions="both")
+    res = Resident(wl)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    _say("dynamic: 100 kv bursts on two streams, mixed with static calls")
+    for i in range(100):
+        flags = K.F_DYNAMIC if i % 3 else 0
+        res.submit(i % 2, (1, 4, 16, 0)[(i // 2) % 4], s1 if i % 2 else s2, flags=flags)
+    torch.cuda.synchronize()
+    _check(res, [0, 1], "dynamic kv bursts")
+    res.free()
+    wl = W.moe_gather(seed=7, calls=40, n_experts=24, n_slots=80, misses=(3, 12))
+    res = Resident(wl)
+    st = torch.cuda.Stream()
+    _say("dynamic: 40 moe calls on one stream")
+    for i in range(40):
+        res.submit(i, (1, 4, 16, 0)[i % 4], st, flags=K.F_DYNAMIC if i % 3 else 0)
+    torch.cuda.synchronize()
+    _check(res, list(range(40)), "dynamic moe calls")
+    res.free()
+
+
+def test_dynamic_d2d_large(K):
+    from block_copy_amd.harness import Resident
+    wl = W.d2d_blocks(seed=1, n=65536, pool_blocks=262144)
+    res = Resident(wl)
+    for max_wgs in (512, 0):
+        _say("dynamic d2d 65536x4KiB max_wgs", max_wgs)
+        res.fill()
+        _run(res, [0], max_wgs, flags=K.F_DYNAMIC)
+        _check(res, [0], f"dynamic d2d 65536 max_wgs={max_wgs}")
     res.free()

@@ -149,6 +149,8 @@ def test_batch_argument_errors(K):
     assert call(s, d, z, K.H2D, flags=0x100) == K.EINVAL          # unknown flag
     assert call(s, d, z, K.H2D, flags=0x4) == K.EINVAL            # a retired flag value
     assert call(s, d, z, K.H2D, flags=K.F_PIPELINE | K.F_PER_CHUNK) == K.EINVAL  # two loops forced
+    assert call(s, d, z, K.H2D, flags=K.F_DYNAMIC | K.F_PIPELINE) == K.EINVAL
+    assert call(s, d, z, K.H2D, flags=K.F_DYNAMIC | K.F_PER_CHUNK) == K.EINVAL
     wrap = np.array([2**64 - 4096], np.uint64)
     assert call(wrap, d[:1], z[:1], K.H2D) == K.EINVAL             # address range wraps
     dup = np.array([0x30000, 0x30800], np.uint64)
