@@ -42,19 +42,30 @@ def test_header_symbols_are_exported(K):
         assert hasattr(K.lib, name)
 
 
-def test_kernel_has_no_scratch(K):
-    """The copy kernel must not spill to private (scratch) memory."""
+@pytest.mark.parametrize("src", ["kvcopy_kernel.hip", "device_batch.hip"])
+def test_kernels_have_no_scratch_or_spills(K, src):
+    """No copy kernel may use private (scratch) memory or spill registers;
+    every direction of every loop has its own symbol."""
+    from block_copy_amd import build as B
     tmp = os.path.join(ROOT, "_build")
     os.makedirs(tmp, exist_ok=True)
-    out = os.path.join(tmp, "kernel_meta.s")
-    subprocess.run(["hipcc", "--offload-arch=gfx950", "-O3", "-std=c++17", "--cuda-device-only", "-S",
+    out = os.path.join(tmp, src + ".meta.s")
+    subprocess.run(["hipcc", *B.HIPCC_FLAGS, "--cuda-device-only", "-S",
                     "-I" + os.path.join(ROOT, "include"),
                     "-I" + os.path.join(ROOT, "block_copy_amd", "csrc"),
-                    os.path.join(ROOT, "block_copy_amd", "csrc", "kvcopy_kernel.hip"), "-o", out],
+                    os.path.join(ROOT, "block_copy_amd", "csrc", src), "-o", out],
                    check=True, capture_output=True)
     txt = open(out).read()
     sizes = re.findall(r"\.private_segment_fixed_size:\s+(\d+)", txt)
+    spills = re.findall(r"\.[sv]gpr_spill_count:\s+(\d+)", txt)
     assert sizes and all(int(s) == 0 for s in sizes)
+    assert spills and all(int(s) == 0 for s in spills)
+    names = set(re.findall(r"\.name:\s+_ZN3kvc12_GLOBAL__N_1\d+(kvcopy_\w+?_kernel)E", txt))
+    if src == "kvcopy_kernel.hip":
+        want = {f"kvcopy_{d}{v}_kernel" for d in ("h2d", "d2h", "d2d") for v in ("", "_pipe", "_dyn")}
+    else:
+        want = {"kvcopy_device_plan_kernel", "kvcopy_device_copy_kernel"}
+    assert names == want, names
 
 
 # ---------------------------------------------------------------------------
