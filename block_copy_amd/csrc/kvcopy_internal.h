@@ -80,6 +80,19 @@ int hip_fail(hipError_t e);
 constexpr uint32_t kWavesPerWG = 4;
 constexpr uint32_t kThreadsPerWG = 64 * kWavesPerWG;
 
+// A worklist small enough to travel in the kernel arguments (3,080 bytes of
+// kernel arguments; HIP allows 4 KiB): no staging region, no completion
+// event, and no round trip over the host link before the first copy.
+constexpr uint32_t kInlineRecs = 128;
+struct InlineWork {
+    uint32_t n_chunks;
+    uint32_t reserved;
+    ChunkRec rec[kInlineRecs];
+};
+
+// Launches the per-chunk loop over an inline worklist (w.n_chunks <= kInlineRecs).
+hipError_t launch_copy_inline(const InlineWork &w, uint32_t grid, int dir, hipStream_t stream);
+
 // Launches the copy kernel for `dir` (one kernel symbol per direction and
 // loop, same result): `grid` workgroups; wavefront w of W copies the chunks
 // [w*C/W, (w+1)*C/W), one chunk at a time or, if `pipelined`, as a stream of

@@ -312,6 +312,24 @@ __device__ __forceinline__ void copy_worklist_dynamic(const ChunkRec *__restrict
     }
 }
 
+// ---- inline worklist ----------------------------------------------------------
+//
+// The per-chunk loop over a worklist passed by value in the kernel
+// arguments: the records are read with scalar loads from the kernel-argument
+// segment, so nothing crosses the host link before the first data load.
+__device__ __forceinline__ void copy_inline(const InlineWork &w)
+{
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t nw = gridDim.x * kWavesPerWG;
+    const uint32_t wv = __builtin_amdgcn_readfirstlane(blockIdx.x * kWavesPerWG + (threadIdx.x >> 6));
+    const uint32_t n = w.n_chunks;
+    const uint32_t lo = wv * n / nw, hi = (wv + 1) * n / nw;   // n <= 128: no overflow
+    for (uint32_t j = lo; j < hi; ++j) {
+        const uint32_t k = __builtin_amdgcn_readfirstlane(j);
+        copy_chunk(w.rec[k].src, w.rec[k].dst, w.rec[k].bytes, lane);
+    }
+}
+
 // One symbol per direction and loop, so that profiles and counters separate them.
 #define KVC_KERNEL(name, body)                                                                     \
     __global__ __launch_bounds__(kThreadsPerWG) void name(const ChunkRec *__restrict__ recs,     \
@@ -326,6 +344,16 @@ KVC_KERNEL(kvcopy_h2d_pipe_kernel, copy_worklist_pipelined)
 KVC_KERNEL(kvcopy_d2h_pipe_kernel, copy_worklist_pipelined)
 KVC_KERNEL(kvcopy_d2d_pipe_kernel, copy_worklist_pipelined)
 #undef KVC_KERNEL
+
+#define KVC_INLINE_KERNEL(name)                                                                    \
+    __global__ __launch_bounds__(kThreadsPerWG) void name(const InlineWork w)                     \
+    {                                                                                              \
+        copy_inline(w);                                                                            \
+    }
+KVC_INLINE_KERNEL(kvcopy_h2d_inline_kernel)
+KVC_INLINE_KERNEL(kvcopy_d2h_inline_kernel)
+KVC_INLINE_KERNEL(kvcopy_d2d_inline_kernel)
+#undef KVC_INLINE_KERNEL
 
 #define KVC_DYN_KERNEL(name)                                                                       \
     __global__ __launch_bounds__(kThreadsPerWG) void name(const ChunkRec *__restrict__ recs,     \
@@ -354,6 +382,15 @@ hipError_t launch_copy(const ChunkRec *recs, uint32_t n_chunks, uint32_t grid, i
     void *args[] = {(void *)&recs, (void *)&n_chunks};
     return hipLaunchKernel(fns[pipelined ? 1 : 0][dir], dim3(grid), dim3(kThreadsPerWG), args, 0,
                            stream);
+}
+
+hipError_t launch_copy_inline(const InlineWork &w, uint32_t grid, int dir, hipStream_t stream)
+{
+    static const void *const fns[3] = {reinterpret_cast<const void *>(&kvcopy_h2d_inline_kernel),
+                                       reinterpret_cast<const void *>(&kvcopy_d2h_inline_kernel),
+                                       reinterpret_cast<const void *>(&kvcopy_d2d_inline_kernel)};
+    void *args[] = {(void *)&w};
+    return hipLaunchKernel(fns[dir], dim3(grid), dim3(kThreadsPerWG), args, 0, stream);
 }
 
 hipError_t launch_copy_dynamic(const ChunkRec *recs, uint32_t n_chunks, uint32_t grid, int dir,

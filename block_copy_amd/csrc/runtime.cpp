@@ -237,6 +237,38 @@ int run_locked(Staging *st, const uint64_t *src, const uint64_t *dst, const uint
     return KVCOPY_OK;
 }
 
+constexpr int kNotInline = 1;   // run_inline's "use the staging ring instead"
+
+// Small batches (at most kInlineRecs chunks): the worklist goes to the GPU in
+// the kernel arguments, so the call needs no staging region and no
+// completion event, and the kernel makes no round trip over the host link
+// for its records.  Returns kNotInline when the default policy would pick
+// the pipelined loop for this grid (small D2D grids).
+int run_inline(Staging *st, const uint64_t *src, const uint64_t *dst, const uint64_t *sizes,
+               uint64_t n, int dir, int max_wgs, hipStream_t stream, uint32_t chunk,
+               uint32_t flags, hipEvent_t ev_begin, hipEvent_t ev_end)
+{
+    if (max_wgs == KVCOPY_WGS_AUTO) {
+        std::lock_guard<std::mutex> g(st->mu);
+        max_wgs = resolve_auto(st, dir);
+    }
+    InlineWork w;
+    w.reserved = 0;
+    w.n_chunks = (uint32_t)build_worklist(src, dst, sizes, n, !(flags & KVCOPY_F_NO_COALESCE),
+                                          chunk, w.rec);
+    const uint32_t grid = grid_for(w.n_chunks, max_wgs);
+    if (!(flags & KVCOPY_F_PER_CHUNK) && pipeline_pays(dir, grid, w.n_chunks))
+        return kNotInline;
+    hipError_t e;
+    if (ev_begin && (e = hipEventRecord(ev_begin, stream)) != hipSuccess)
+        return hip_fail(e);
+    if ((e = launch_copy_inline(w, grid, dir, stream)) != hipSuccess)
+        return hip_fail(e);
+    if (ev_end && (e = hipEventRecord(ev_end, stream)) != hipSuccess)
+        return hip_fail(e);
+    return KVCOPY_OK;
+}
+
 }  // namespace
 
 void set_tuned_wgs(int device, int dir, int wgs)
@@ -303,6 +335,13 @@ extern "C" int kvcopy_batch_ex(const uint64_t *src_addrs, const uint64_t *dst_ad
     if (e != hipSuccess)
         return hip_fail(e);
     Staging *st = staging_for(device);
+    if (pre.bound <= kInlineRecs &&
+        !(flags & (KVCOPY_F_DESC_UPLOAD | KVCOPY_F_PIPELINE | KVCOPY_F_DYNAMIC))) {
+        const int rc = run_inline(st, src_addrs, dst_addrs, sizes, n, dir, max_wgs, stream, chunk,
+                                  flags, ev_begin, ev_end);
+        if (rc != kNotInline)
+            return rc;
+    }
     std::lock_guard<std::mutex> g(st->mu);
     return run_locked(st, src_addrs, dst_addrs, sizes, n, pre, dir, max_wgs, stream, chunk, flags,
                       ev_begin, ev_end);

@@ -180,9 +180,11 @@ void kvcopy_plan_free(kvcopy_plan_t *plan);
  * into its own pinned staging ring, and launches one kernel of
  * min(max_wgs, needed) workgroups of 4 wavefronts on `stream`.  Each
  * wavefront takes an equal contiguous share of the chunks and moves them
- * with 16-byte nontemporal loads and stores.  The staging region is
+ * with 16-byte loads and nontemporal 16-byte stores.  The staging region is
  * recycled once an event recorded after the kernel has completed; the call
- * waits on the host only if the whole ring is still in use.  Calls on one
+ * waits on the host only if the whole ring is still in use.  A batch of at
+ * most 128 chunks instead passes its worklist in the kernel arguments (no
+ * staging region, no event).  Calls on one
  * device are serialised on the host while they plan (microseconds).  The
  * call is not capturable into a HIP graph: the worklist is planned on the
  * host at call time.

@@ -1,10 +1,16 @@
-"""GPU parity of the pipelined copy loop (KVCOPY_F_PIPELINE) against the oracle.
+"""GPU parity of every copy loop against the oracle, bit-exact.
 
-The pipelined loop streams each wavefront's chunks as 4 KiB pieces, two
-16 KiB passes in flight, with pieces of one pass drawn from different chunks
-and 8-byte tails riding in the same pass.  Every case reads the touched
-arenas back whole (guard bytes included) and compares them bit-exact with
-the oracle's images of the same seeded inputs.
+- pipelined (KVCOPY_F_PIPELINE, and the default for small D2D grids): each
+  wavefront streams its chunks as 4 KiB pieces, two 16 KiB passes in flight,
+  pieces of one pass drawn from different chunks, 8-byte tails in the same
+  pass;
+- per-chunk forced where the default would pick the pipelined loop;
+- dynamic claims (KVCOPY_F_DYNAMIC): chunks claimed with device atomics,
+  counters reset by each kernel's last wavefront;
+- inline worklists (the default for batches of at most 128 chunks): the
+  records travel in the kernel arguments.
+Every case reads the touched arenas back whole (guard bytes included) and
+compares them with the oracle's images of the same seeded inputs.
 """
 import pytest
 
@@ -185,4 +191,49 @@ def test_dynamic_d2d_large(K):
         res.fill()
         _run(res, [0], max_wgs, flags=K.F_DYNAMIC)
         _check(res, [0], f"dynamic d2d 65536 max_wgs={max_wgs}")
+    res.free()
+
+
+# ---------------------------------------------------------------------------
+# Inline worklists: batches of at most 128 chunks
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dname", sorted(DIRS))
+@pytest.mark.parametrize("case", ["one", "few", "full", "tiny_chunks"])
+def test_inline_worklist(K, dname, case):
+    """Small batches whose chunk bound fits the kernel arguments: 1 descriptor,
+    a few, a batch close to the 128-record limit, and 16-byte chunks."""
+    from block_copy_amd.harness import Resident
+    d, sw, dw = DIRS[dname]
+    n, max_size, chunk = {"one": (1, 16 * 1024, 0), "few": (7, 40 * 1024, 0),
+                          "full": (60, 16 * 1024, 0), "tiny_chunks": (20, 64, 16)}[case]
+    wl = W.irregular(seed=len(case) * 7 + n, n=n, max_size=max_size, dir_=d, src_where=sw,
+                     dst_where=dw, misalign=True, zero_frac=0.1 if n > 1 else 0.0)
+    res = Resident(wl)
+    s, dd = res.addrs[0]
+    pl = K.kvcopy_plan(s, dd, wl.batches[0].size, chunk)
+    assert pl.n_chunks <= 128
+    for max_wgs in (1, 2, 0):
+        _say("inline", dname, case, "chunks", pl.n_chunks, "max_wgs", max_wgs)
+        res.fill()
+        _run(res, [0], max_wgs, chunk_bytes=chunk)
+        _check(res, [0], f"inline {dname} {case} max_wgs={max_wgs}")
+    res.free()
+
+
+def test_inline_and_ring_calls_interleaved(K):
+    """Small (inline) and large (staging ring) batches alternating on two streams."""
+    from block_copy_amd.harness import Resident
+    wl = W.kv_blocks(seed=9, directions="both")
+    res = Resident(wl)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    (hs, hd), (ds, dd) = res.addrs
+    z = wl.batches[0].size
+    _say("inline and ring calls interleaved")
+    for i in range(0, 16384, 1024):
+        K.kvcopy_batch(hs[i:i + 1024], hd[i:i + 1024], z[i:i + 1024], K.H2D, 8, s1.cuda_stream)
+        for j in range(i, i + 1024, 64):       # 64 blocks = 64 chunks: inline
+            K.kvcopy_batch(ds[j:j + 64], dd[j:j + 64], z[j:j + 64], K.D2H, 0, s2.cuda_stream)
+    torch.cuda.synchronize()
+    _check(res, [0, 1], "inline and ring interleaved")
     res.free()
