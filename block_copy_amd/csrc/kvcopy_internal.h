@@ -97,17 +97,20 @@ hipError_t launch_copy_inline(const InlineWork &w, uint32_t grid, int dir, hipSt
 // loop, same result): `grid` workgroups; wavefront w of W copies the chunks
 // [w*C/W, (w+1)*C/W), one chunk at a time or, if `pipelined`, as a stream of
 // 4 KiB pieces with two 16 KiB passes in flight.  recs must be
-// device-readable (device memory or mapped host memory).  Returns the launch
+// device-readable (device memory or mapped host memory).  `done` (may be
+// null) is bound to the kernel's own completion (hipExtLaunchKernel's stop
+// event), which costs no separate marker on the stream.  Returns the launch
 // status.
 hipError_t launch_copy(const ChunkRec *recs, uint32_t n_chunks, uint32_t grid, int dir,
-                       bool pipelined, hipStream_t stream);
+                       bool pipelined, hipStream_t stream, hipEvent_t done);
 
 // KVCOPY_F_DYNAMIC: the per-chunk loop with chunks claimed at run time.
 // claim points at two zeroed device counters (next chunk, wavefronts done);
 // every wavefront claims `grain` chunks at a time with an atomic add, one
 // batch ahead, and the last wavefront to finish resets both counters to zero.
 hipError_t launch_copy_dynamic(const ChunkRec *recs, uint32_t n_chunks, uint32_t grid, int dir,
-                               uint32_t *claim, uint32_t grain, hipStream_t stream);
+                               uint32_t *claim, uint32_t grain, hipStream_t stream,
+                               hipEvent_t done);
 
 // Chunks per claim: about four claims per wavefront, at most 64 (one record
 // per lane), at least 1.

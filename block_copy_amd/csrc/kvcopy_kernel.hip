@@ -28,6 +28,7 @@
 //     for 4 KiB descriptors, which pays when only a few workgroups run.
 // The worklist records are fetched 64 at a time (one per lane) and one batch
 // ahead in both loops.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include "kvcopy.h"
@@ -370,7 +371,7 @@ KVC_DYN_KERNEL(kvcopy_d2d_dyn_kernel)
 }  // namespace
 
 hipError_t launch_copy(const ChunkRec *recs, uint32_t n_chunks, uint32_t grid, int dir,
-                       bool pipelined, hipStream_t stream)
+                       bool pipelined, hipStream_t stream, hipEvent_t done)
 {
     static const void *const fns[2][3] = {
         {reinterpret_cast<const void *>(&kvcopy_h2d_kernel),
@@ -380,8 +381,8 @@ hipError_t launch_copy(const ChunkRec *recs, uint32_t n_chunks, uint32_t grid, i
          reinterpret_cast<const void *>(&kvcopy_d2h_pipe_kernel),
          reinterpret_cast<const void *>(&kvcopy_d2d_pipe_kernel)}};
     void *args[] = {(void *)&recs, (void *)&n_chunks};
-    return hipLaunchKernel(fns[pipelined ? 1 : 0][dir], dim3(grid), dim3(kThreadsPerWG), args, 0,
-                           stream);
+    return hipExtLaunchKernel(fns[pipelined ? 1 : 0][dir], dim3(grid), dim3(kThreadsPerWG), args, 0,
+                              stream, nullptr, done, 0);
 }
 
 hipError_t launch_copy_inline(const InlineWork &w, uint32_t grid, int dir, hipStream_t stream)
@@ -394,13 +395,15 @@ hipError_t launch_copy_inline(const InlineWork &w, uint32_t grid, int dir, hipSt
 }
 
 hipError_t launch_copy_dynamic(const ChunkRec *recs, uint32_t n_chunks, uint32_t grid, int dir,
-                               uint32_t *claim, uint32_t grain, hipStream_t stream)
+                               uint32_t *claim, uint32_t grain, hipStream_t stream,
+                               hipEvent_t done)
 {
     static const void *const fns[3] = {reinterpret_cast<const void *>(&kvcopy_h2d_dyn_kernel),
                                        reinterpret_cast<const void *>(&kvcopy_d2h_dyn_kernel),
                                        reinterpret_cast<const void *>(&kvcopy_d2d_dyn_kernel)};
     void *args[] = {(void *)&recs, (void *)&n_chunks, (void *)&claim, (void *)&grain};
-    return hipLaunchKernel(fns[dir], dim3(grid), dim3(kThreadsPerWG), args, 0, stream);
+    return hipExtLaunchKernel(fns[dir], dim3(grid), dim3(kThreadsPerWG), args, 0, stream, nullptr,
+                              done, 0);
 }
 
 }  // namespace kvc

@@ -208,20 +208,9 @@ int run_locked(Staging *st, const uint64_t *src, const uint64_t *dst, const uint
         return hip_fail(e);
     if (max_wgs == KVCOPY_WGS_AUTO)
         max_wgs = resolve_auto(st, dir);
-    const uint32_t grid = grid_for(n_chunks, max_wgs);
-    if (dynamic) {
-        uint32_t *claim = st->claims + off / kAlign * 2;
-        e = launch_copy_dynamic(recs, (uint32_t)n_chunks, grid, dir, claim,
-                                claim_grain(n_chunks, grid), stream);
-    } else {
-        const bool pipelined = (flags & KVCOPY_F_PIPELINE) != 0 ||
-                               (!(flags & KVCOPY_F_PER_CHUNK) && pipeline_pays(dir, grid, n_chunks));
-        e = launch_copy(recs, (uint32_t)n_chunks, grid, dir, pipelined, stream);
-    }
-    if (e != hipSuccess)
-        return hip_fail(e);
-    if (ev_end && (e = hipEventRecord(ev_end, stream)) != hipSuccess)
-        return hip_fail(e);
+    // The region's completion event is bound to the kernel itself (the stop
+    // event of hipExtLaunchKernel): recording a separate event after the
+    // kernel measured 4.3 us of extra GPU time per call on MI355X.
     hipEvent_t done;
     if (!st->spare.empty()) {
         done = st->spare.back();
@@ -229,11 +218,23 @@ int run_locked(Staging *st, const uint64_t *src, const uint64_t *dst, const uint
     } else if ((e = hipEventCreateWithFlags(&done, hipEventDisableTiming)) != hipSuccess) {
         return hip_fail(e);
     }
-    if ((e = hipEventRecord(done, stream)) != hipSuccess) {
+    const uint32_t grid = grid_for(n_chunks, max_wgs);
+    if (dynamic) {
+        uint32_t *claim = st->claims + off / kAlign * 2;
+        e = launch_copy_dynamic(recs, (uint32_t)n_chunks, grid, dir, claim,
+                                claim_grain(n_chunks, grid), stream, done);
+    } else {
+        const bool pipelined = (flags & KVCOPY_F_PIPELINE) != 0 ||
+                               (!(flags & KVCOPY_F_PER_CHUNK) && pipeline_pays(dir, grid, n_chunks));
+        e = launch_copy(recs, (uint32_t)n_chunks, grid, dir, pipelined, stream, done);
+    }
+    if (e != hipSuccess) {
         st->spare.push_back(done);
         return hip_fail(e);
     }
     st->ring.commit(off, used, done);
+    if (ev_end && (e = hipEventRecord(ev_end, stream)) != hipSuccess)
+        return hip_fail(e);
     return KVCOPY_OK;
 }
 

@@ -253,6 +253,34 @@ def test_many_calls_wrap_the_staging_ring(K):
     res.free()
 
 
+def test_ring_regions_outlive_their_kernels(K):
+    """300 calls with different worklists on one stream, each on a single
+    workgroup (2,048 chunks of 64 bytes per wavefront; every other call with
+    the per-chunk loop forced), so the GPU falls far behind the host and the
+    16 MiB staging ring (192 KiB of worklist per call) fills several times:
+    every region must stay intact until its kernel has completed, or some
+    call copies another call's descriptors and its own destinations keep the
+    sentinel."""
+    from block_copy_amd.harness import Resident
+    wl = W.distinct_calls(seed=12)
+    res = Resident(wl)
+    st = torch.cuda.Stream()
+    _say("300 distinct calls, one workgroup each, one stream")
+    import time
+    t0 = time.perf_counter()
+    for i in range(len(wl.batches)):
+        res.submit(i, 1, st, flags=K.F_PER_CHUNK if i % 2 else 0)
+    t1 = time.perf_counter()
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    _say(f"submitted in {t1 - t0:.3f} s, all done after {t2 - t0:.3f} s")
+    # The host had to wait for ring space: most of the GPU time passed
+    # inside the submission loop.
+    assert t1 - t0 > 0.5 * (t2 - t0)
+    _check(res, list(range(len(wl.batches))), "distinct calls")
+    res.free()
+
+
 def test_ring_growth_with_calls_in_flight(K):
     """A call whose worklist needs more than a quarter of the ring grows it
     while earlier calls are still queued."""

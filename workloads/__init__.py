@@ -118,6 +118,25 @@ def d2d_blocks(seed=0, n=1024, pool_blocks=4096, block=4 * KIB, sentinel=SENTINE
                     {"n": n, "block": block, "pool_blocks": pool_blocks})
 
 
+def distinct_calls(seed=0, calls=300, n=8192, block=64, src_blocks=65536, sentinel=SENTINEL_A):
+    """`calls` D2D batches of n blocks each, every batch writing its own
+    destination blocks: batch i scatters n seeded random source blocks (drawn
+    with replacement from a random pool) to a seeded permutation of
+    destination blocks [i*n, (i+1)*n).  No two batches touch the same
+    destination byte, so every call's result stays visible in the final
+    image and a call that ran with another call's worklist shows up."""
+    rng = np.random.default_rng(seed)
+    arenas = [Arena("src", src_blocks * block, "device", "random", seed=seed * 1000 + 1),
+              Arena("dst", calls * n * block, "device", "sentinel", sentinel=sentinel)]
+    batches = []
+    for i in range(calls):
+        src = rng.integers(0, src_blocks, n).astype(np.uint64)
+        dst = (np.uint64(i * n) + rng.permutation(n).astype(np.uint64))
+        batches.append(_batch(D2D, 0, src * block, 1, dst * block, np.full(n, block, np.uint64)))
+    return Workload(f"distinct_{calls}x{n}x{block}B", arenas, batches,
+                    {"calls": calls, "n": n, "block": block, "sequential": True})
+
+
 def kv_blocks(seed=0, directions="both", n=16384, pool_blocks=65536, block=4 * KIB,
               sentinel=SENTINEL_A):
     """H2D and/or D2H batches of n shuffled blocks against a device KV pool.
