@@ -21,7 +21,9 @@ namespace {
 constexpr uint64_t kBlocks = 8192;
 constexpr uint64_t kBlock = 4096;
 constexpr uint64_t kBytes = kBlocks * kBlock;   // 32 MiB per direction
-constexpr int kReps = 3;
+constexpr int kWarm = 2;                         // untimed batches per cap
+constexpr int kReps = 6;                         // timed batches per cap
+constexpr int kSweeps = 2;                       // ascending, then descending
 const int kCaps[KVCOPY_AUTOTUNE_NCAPS] = KVCOPY_AUTOTUNE_CAPS;
 
 uint64_t splitmix(uint64_t &s)
@@ -117,10 +119,15 @@ extern "C" int kvcopy_autotune(int dir, hipStream_t s0, hipStream_t s1, int *out
                 std::vector<uint64_t>(kBlocks, kBlock), KVCOPY_D2H};
     }
 
+    // Each cap is timed in two sweeps (ascending, then descending) and keeps
+    // its better rate, so one slow window (a fresh stream's first batches,
+    // say) cannot decide the choice.
     double rate[KVCOPY_AUTOTUNE_NCAPS] = {};
     double best = 0;
-    for (size_t c = 0; c < sizeof(kCaps) / sizeof(kCaps[0]); ++c) {
-        for (int rep = -1; rep < kReps; ++rep) {   // rep -1: warm-up, untimed
+    const int ncaps = (int)(sizeof(kCaps) / sizeof(kCaps[0]));
+    for (int k = 0; k < kSweeps * ncaps; ++k) {
+        const int c = k < ncaps ? k : 2 * ncaps - 1 - k;
+        for (int rep = -kWarm; rep < kReps; ++rep) {   // negative reps: warm-up, untimed
             if (rep == 0) {
                 if ((e = hipEventRecord(p.ev[0], p.s[0])) != hipSuccess ||
                     (e = hipStreamWaitEvent(p.s[1], p.ev[0], 0)) != hipSuccess)
@@ -143,11 +150,12 @@ extern "C" int kvcopy_autotune(int dir, hipStream_t s0, hipStream_t s1, int *out
             (e = hipEventElapsedTime(&ms1, p.ev[0], p.ev[2])) != hipSuccess)
             return kvc::hip_fail(e);
         const double ms = std::max(ms0, nb == 2 ? ms1 : 0.0f);
-        rate[c] = ms > 0 ? (double)(kBytes * nb * kReps) / (ms * 1e-3) : 0;
+        const double r = ms > 0 ? (double)(kBytes * nb * kReps) / (ms * 1e-3) : 0;
+        rate[c] = std::max(rate[c], r);
         best = std::max(best, rate[c]);
     }
     int chosen = KVCOPY_WGS_ALL;
-    for (size_t c = 0; c < sizeof(kCaps) / sizeof(kCaps[0]); ++c)
+    for (int c = 0; c < ncaps; ++c)
         if (rate[c] >= 0.95 * best) {
             chosen = kCaps[c];
             break;

@@ -90,19 +90,21 @@ struct InlineWork {
     ChunkRec rec[kInlineRecs];
 };
 
-// Launches the per-chunk loop over an inline worklist (w.n_chunks <= kInlineRecs).
-hipError_t launch_copy_inline(const InlineWork &w, uint32_t grid, int dir, hipStream_t stream);
+// Launches the per-chunk loop over an inline worklist (w.n_chunks <= kInlineRecs);
+// start / stop as for launch_copy.
+hipError_t launch_copy_inline(const InlineWork &w, uint32_t grid, int dir, hipStream_t stream,
+                              hipEvent_t start, hipEvent_t stop);
 
 // Launches the copy kernel for `dir` (one kernel symbol per direction and
 // loop, same result): `grid` workgroups; wavefront w of W copies the chunks
 // [w*C/W, (w+1)*C/W), one chunk at a time or, if `pipelined`, as a stream of
 // 4 KiB pieces with two 16 KiB passes in flight.  recs must be
-// device-readable (device memory or mapped host memory).  `done` (may be
-// null) is bound to the kernel's own completion (hipExtLaunchKernel's stop
-// event), which costs no separate marker on the stream.  Returns the launch
-// status.
+// device-readable (device memory or mapped host memory).  `start` and `stop`
+// (either may be null) are bound to the kernel's own start and completion
+// (hipExtLaunchKernel's events), which costs no separate marker on the
+// stream.  Returns the launch status.
 hipError_t launch_copy(const ChunkRec *recs, uint32_t n_chunks, uint32_t grid, int dir,
-                       bool pipelined, hipStream_t stream, hipEvent_t done);
+                       bool pipelined, hipStream_t stream, hipEvent_t start, hipEvent_t stop);
 
 // KVCOPY_F_DYNAMIC: the per-chunk loop with chunks claimed at run time.
 // claim points at two zeroed device counters (next chunk, wavefronts done);
@@ -110,7 +112,7 @@ hipError_t launch_copy(const ChunkRec *recs, uint32_t n_chunks, uint32_t grid, i
 // batch ahead, and the last wavefront to finish resets both counters to zero.
 hipError_t launch_copy_dynamic(const ChunkRec *recs, uint32_t n_chunks, uint32_t grid, int dir,
                                uint32_t *claim, uint32_t grain, hipStream_t stream,
-                               hipEvent_t done);
+                               hipEvent_t start, hipEvent_t stop);
 
 // Chunks per claim: about four claims per wavefront, at most 64 (one record
 // per lane), at least 1.

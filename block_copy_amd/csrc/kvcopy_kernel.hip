@@ -371,7 +371,7 @@ KVC_DYN_KERNEL(kvcopy_d2d_dyn_kernel)
 }  // namespace
 
 hipError_t launch_copy(const ChunkRec *recs, uint32_t n_chunks, uint32_t grid, int dir,
-                       bool pipelined, hipStream_t stream, hipEvent_t done)
+                       bool pipelined, hipStream_t stream, hipEvent_t start, hipEvent_t stop)
 {
     static const void *const fns[2][3] = {
         {reinterpret_cast<const void *>(&kvcopy_h2d_kernel),
@@ -382,28 +382,30 @@ hipError_t launch_copy(const ChunkRec *recs, uint32_t n_chunks, uint32_t grid, i
          reinterpret_cast<const void *>(&kvcopy_d2d_pipe_kernel)}};
     void *args[] = {(void *)&recs, (void *)&n_chunks};
     return hipExtLaunchKernel(fns[pipelined ? 1 : 0][dir], dim3(grid), dim3(kThreadsPerWG), args, 0,
-                              stream, nullptr, done, 0);
+                              stream, start, stop, 0);
 }
 
-hipError_t launch_copy_inline(const InlineWork &w, uint32_t grid, int dir, hipStream_t stream)
+hipError_t launch_copy_inline(const InlineWork &w, uint32_t grid, int dir, hipStream_t stream,
+                              hipEvent_t start, hipEvent_t stop)
 {
     static const void *const fns[3] = {reinterpret_cast<const void *>(&kvcopy_h2d_inline_kernel),
                                        reinterpret_cast<const void *>(&kvcopy_d2h_inline_kernel),
                                        reinterpret_cast<const void *>(&kvcopy_d2d_inline_kernel)};
     void *args[] = {(void *)&w};
-    return hipLaunchKernel(fns[dir], dim3(grid), dim3(kThreadsPerWG), args, 0, stream);
+    return hipExtLaunchKernel(fns[dir], dim3(grid), dim3(kThreadsPerWG), args, 0, stream, start,
+                              stop, 0);
 }
 
 hipError_t launch_copy_dynamic(const ChunkRec *recs, uint32_t n_chunks, uint32_t grid, int dir,
                                uint32_t *claim, uint32_t grain, hipStream_t stream,
-                               hipEvent_t done)
+                               hipEvent_t start, hipEvent_t stop)
 {
     static const void *const fns[3] = {reinterpret_cast<const void *>(&kvcopy_h2d_dyn_kernel),
                                        reinterpret_cast<const void *>(&kvcopy_d2h_dyn_kernel),
                                        reinterpret_cast<const void *>(&kvcopy_d2d_dyn_kernel)};
     void *args[] = {(void *)&recs, (void *)&n_chunks, (void *)&claim, (void *)&grain};
-    return hipExtLaunchKernel(fns[dir], dim3(grid), dim3(kThreadsPerWG), args, 0, stream, nullptr,
-                              done, 0);
+    return hipExtLaunchKernel(fns[dir], dim3(grid), dim3(kThreadsPerWG), args, 0, stream, start,
+                              stop, 0);
 }
 
 }  // namespace kvc

@@ -204,13 +204,15 @@ int run_locked(Staging *st, const uint64_t *src, const uint64_t *dst, const uint
             return hip_fail(e);
         recs = dev;
     }
-    if (ev_begin && (e = hipEventRecord(ev_begin, stream)) != hipSuccess)
-        return hip_fail(e);
     if (max_wgs == KVCOPY_WGS_AUTO)
         max_wgs = resolve_auto(st, dir);
     // The region's completion event is bound to the kernel itself (the stop
     // event of hipExtLaunchKernel): recording a separate event after the
-    // kernel measured 4.3 us of extra GPU time per call on MI355X.
+    // kernel measured 4.3 us of extra GPU time per call on MI355X.  When the
+    // caller asks for the kernel's own start and end (timing), those take
+    // the launch's event slots and the completion event is recorded after
+    // the kernel instead.
+    const bool timed = ev_begin != nullptr || ev_end != nullptr;
     hipEvent_t done;
     if (!st->spare.empty()) {
         done = st->spare.back();
@@ -219,22 +221,23 @@ int run_locked(Staging *st, const uint64_t *src, const uint64_t *dst, const uint
         return hip_fail(e);
     }
     const uint32_t grid = grid_for(n_chunks, max_wgs);
+    hipEvent_t start = timed ? ev_begin : nullptr, stop = timed ? ev_end : done;
     if (dynamic) {
         uint32_t *claim = st->claims + off / kAlign * 2;
         e = launch_copy_dynamic(recs, (uint32_t)n_chunks, grid, dir, claim,
-                                claim_grain(n_chunks, grid), stream, done);
+                                claim_grain(n_chunks, grid), stream, start, stop);
     } else {
         const bool pipelined = (flags & KVCOPY_F_PIPELINE) != 0 ||
                                (!(flags & KVCOPY_F_PER_CHUNK) && pipeline_pays(dir, grid, n_chunks));
-        e = launch_copy(recs, (uint32_t)n_chunks, grid, dir, pipelined, stream, done);
+        e = launch_copy(recs, (uint32_t)n_chunks, grid, dir, pipelined, stream, start, stop);
     }
+    if (e == hipSuccess && timed)
+        e = hipEventRecord(done, stream);
     if (e != hipSuccess) {
         st->spare.push_back(done);
         return hip_fail(e);
     }
     st->ring.commit(off, used, done);
-    if (ev_end && (e = hipEventRecord(ev_end, stream)) != hipSuccess)
-        return hip_fail(e);
     return KVCOPY_OK;
 }
 
@@ -260,14 +263,8 @@ int run_inline(Staging *st, const uint64_t *src, const uint64_t *dst, const uint
     const uint32_t grid = grid_for(w.n_chunks, max_wgs);
     if (!(flags & KVCOPY_F_PER_CHUNK) && pipeline_pays(dir, grid, w.n_chunks))
         return kNotInline;
-    hipError_t e;
-    if (ev_begin && (e = hipEventRecord(ev_begin, stream)) != hipSuccess)
-        return hip_fail(e);
-    if ((e = launch_copy_inline(w, grid, dir, stream)) != hipSuccess)
-        return hip_fail(e);
-    if (ev_end && (e = hipEventRecord(ev_end, stream)) != hipSuccess)
-        return hip_fail(e);
-    return KVCOPY_OK;
+    const hipError_t e = launch_copy_inline(w, grid, dir, stream, ev_begin, ev_end);
+    return e == hipSuccess ? KVCOPY_OK : hip_fail(e);
 }
 
 }  // namespace

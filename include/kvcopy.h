@@ -214,13 +214,15 @@ typedef struct {
     uint32_t chunk_bytes;   /* 0 = default; else a multiple of 16, <= KVCOPY_CHUNK_MAX */
     uint32_t flags;         /* KVCOPY_F_* */
     uint32_t reserved;
-    hipEvent_t kernel_begin; /* if non-NULL: recorded on stream just before the copy kernel */
-    hipEvent_t kernel_end;   /* if non-NULL: recorded on stream just after the copy kernel */
+    hipEvent_t kernel_begin; /* if non-NULL: bound to the copy kernel's start (hipExtLaunchKernel) */
+    hipEvent_t kernel_end;   /* if non-NULL: bound to the copy kernel's completion */
 } kvcopy_opts_t;
 
 /*
  * kvcopy_batch_ex -- kvcopy_batch with options (chunk size, flags, and
- * events that bracket the copy kernel alone for timing).  opts may be NULL
+ * events bound to the copy kernel's own start and end, for timing: their
+ * elapsed time is the kernel's execution alone).  Events must be created
+ * with timing enabled.  opts may be NULL
  * (= kvcopy_batch).  Errors as kvcopy_batch, plus KVCOPY_EINVAL for a bad
  * struct_size, chunk_bytes or unknown flag.
  */
@@ -292,12 +294,14 @@ void kvcopy_job_destroy(kvcopy_job_t *job);
  * picks the smallest number of workers within 5% of peak bandwidth.  This
  * call does both on the current device: it allocates its own probe buffers
  * (32 MiB of mapped pinned host memory and 32 MiB of device memory per
- * direction, freed before it returns), times 8,192 shuffled 4 KiB blocks
- * per direction at each cap of KVCOPY_AUTOTUNE_CAPS (for H2D or D2H both
- * directions run together, H2D on s0 and D2H on s1, as in a KV offload
- * burst; D2D runs on s0), and records the smallest cap within 5% of the
- * best rate as the device's KVCOPY_WGS_AUTO cap for `dir` (for H2D or D2H:
- * for both).  Blocks until done (tens of ms).
+ * direction, freed before it returns), times six batches of 8,192 shuffled
+ * 4 KiB blocks per direction at each cap of KVCOPY_AUTOTUNE_CAPS, after two
+ * untimed ones (for H2D or D2H both directions run together, H2D on s0 and
+ * D2H on s1, as in a KV offload burst; D2D runs on s0), in two sweeps over
+ * the caps (ascending, then descending) keeping each cap's better rate, and
+ * records the smallest cap within 5% of the best rate as the device's
+ * KVCOPY_WGS_AUTO cap for `dir` (for H2D or D2H: for both).  Blocks until
+ * done (about a tenth of a second).
  * s0, s1: the streams the caller will copy on (the hardware queues they map
  *   to matter); NULL = streams created for the probe.
  * out_wgs (may be NULL): the chosen cap (0 = full grid).
