@@ -494,14 +494,21 @@ def d2d_results(c: Ctx, args):
     for name, wld in (("1024x4KiB", W.d2d_blocks(seed=0)),
                       ("65536x4KiB", W.d2d_blocks(seed=1, n=65536, pool_blocks=262144))):
         r = c.Resident(wld)
-        s, km = c.timed(r, [0], [c.sA], args.steps, args.warmup, 0)
+        # back-to-back calls with no per-launch event (call rate), then the
+        # same calls with the kernel's own start/end events (kernel time)
+        s, stream_ms = c.timed_bracketed(r, [0], [c.sA], args.steps, args.warmup, 0)
+        _, km = c.timed(r, [0], [c.sA], args.steps, 2, 0)
         pl = K.kvcopy_plan(*r.addrs[0], wld.batches[0].size)
         hbm = 2 * wld.batches[0].nbytes + pl.n_chunks * REC_BYTES
         out[name] = {"GBps_payload": round(gbs(wld.batches[0].nbytes, s), 2),
-                     "us_per_call_pipelined": round(s * 1e6, 2), "kernel_us": round(km[0] * 1e3, 2),
+                     "us_per_call_pipelined": round(s * 1e6, 2),
+                     "gpu_us_per_call_back_to_back": round(stream_ms[0] * 1e3, 2),
+                     "kernel_us": round(km[0] * 1e3, 2),
                      "hbm_GBps_kernel": round(gbs(hbm, km[0] / 1e3), 1),
                      "frac_hbm_peak_kernel": round(gbs(hbm, km[0] / 1e3) / HBM_PEAK_GBS, 4),
                      "latency": c.latency(r, 0, 0, k=50, w=5)}
+        if name == "1024x4KiB":
+            out[name]["mall_flushed"] = d2d_flushed(c, r, k=max(20, args.steps))
         c.verify(wld, r, [0], f"d2d {name}")
         if name == "1024x4KiB":     # after the check: the DMA baselines write the same bytes
             out[name]["dma_baselines"] = dma_baselines(c, pl, wld.batches[0].nbytes,
@@ -530,6 +537,35 @@ def d2d_results(c: Ctx, args):
     out["contiguous_memcpy_hbm_GBps"] = cont
     log(f"  contiguous D2D hipMemcpyAsync (HBM GB/s): {cont}")
     return out
+
+
+def d2d_flushed(c: Ctx, r, k=20):
+    """The 1,024 x 4 KiB gather with the 256 MB MALL (Infinity Cache) flushed
+    before every call: a 512 MiB scrub kernel runs on the same stream first,
+    outside the kernel's own start/end events.  Returns the median kernel
+    time and the HBM rate it implies, and the per-call GPU time."""
+    torch, hiprt = c.torch, c.hiprt
+    if c.args.no_events:
+        return None
+    scrub = torch.zeros(512 << 20, dtype=torch.uint8, device=c.dev)
+    kern, call = [], []
+    with torch.cuda.stream(c.sA):
+        for i in range(k + 3):
+            scrub.add_(1)
+            e0, e1, k0, k1 = hiprt.Event(), hiprt.Event(), hiprt.Event(), hiprt.Event()
+            e0.record(c.sA)
+            r.submit(0, 0, c.sA, kernel_begin=k0.h, kernel_end=k1.h)
+            e1.record(c.sA)
+            if i >= 3:
+                kern.append(k0.elapsed_ms(k1) * 1e3)
+                call.append(e0.elapsed_ms(e1) * 1e3)
+    c.sA.synchronize()
+    del scrub
+    nbytes = r.wl.batches[0].nbytes
+    kt = statistics.median(kern)
+    return {"kernel_us_p50": round(kt, 2), "hbm_GBps_kernel": round(gbs(2 * nbytes, kt / 1e6), 1),
+            "gpu_us_p50": round(statistics.median(call), 2), "calls": k,
+            "scrub": "512 MiB written on the same stream before each call"}
 
 
 def bench_d2d(c: Ctx, args):
@@ -565,7 +601,8 @@ def bench_mixed(c: Ctx, args):
         b = wl.batches[0]
         pl = K.kvcopy_plan(*r.addrs[0], b.size)
         k = max(5, min(args.steps * 5, 200 if n <= 256 else args.steps))
-        s, km = c.timed(r, [0], [c.sA], k, args.warmup, args.max_wgs)
+        s, _ = c.timed_bracketed(r, [0], [c.sA], k, args.warmup, args.max_wgs)
+        _, km = c.timed(r, [0], [c.sA], k, 2, args.max_wgs)
         lat = c.latency(r, 0, args.max_wgs, k=50 if n <= 4096 else 10, w=5)
         c.verify(wl, r, [0], f"mixed {n}")       # before the DMA baselines write the same bytes
         dma = dma_baselines(c, pl, b.nbytes, hiprt.H2D_KIND, reps=2 if n <= 4096 else 1)

@@ -56,11 +56,18 @@ struct Prescan {
 int prescan(const uint64_t *src, const uint64_t *dst, const uint64_t *size, uint64_t n,
             uint32_t chunk, Prescan *out);
 
-// The batch path's fused planner: one sequential pass that drops zero sizes,
+// The batch path's fused planner: one sequential pass that checks what
+// prescan() checks (same error codes, same priority), drops zero sizes,
 // merges list-consecutive adjacent ranges (if `merge`) and writes each closed
-// range's chunks straight into `out` (room for Prescan::bound records).
-// Produces exactly the records emit_chunks() gives for merge_ranges()'s
-// output; returns how many it wrote.
+// range's chunks straight into out[0 .. cap).  *n_chunks receives the number
+// of records the batch needs, which may exceed cap: then only the first cap
+// were written, and the caller plans again with room for *n_chunks.  The
+// records are exactly those emit_chunks() gives for merge_ranges()'s output.
+int build_checked(const uint64_t *src, const uint64_t *dst, const uint64_t *size, uint64_t n,
+                  bool merge, uint32_t chunk, ChunkRec *out, uint64_t cap, uint64_t *n_chunks);
+
+// build_checked without the checks' result and without a cap (room for
+// Prescan::bound records); returns how many records it wrote.
 uint64_t build_worklist(const uint64_t *src, const uint64_t *dst, const uint64_t *size, uint64_t n,
                         bool merge, uint32_t chunk, ChunkRec *out);
 

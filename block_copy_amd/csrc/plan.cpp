@@ -114,26 +114,38 @@ int prescan(const uint64_t *src, const uint64_t *dst, const uint64_t *size, uint
     return KVCOPY_OK;
 }
 
-uint64_t build_worklist(const uint64_t *src, const uint64_t *dst, const uint64_t *size, uint64_t n,
-                        bool merge, uint32_t chunk, ChunkRec *out)
+int build_checked(const uint64_t *src, const uint64_t *dst, const uint64_t *size, uint64_t n,
+                  bool merge, uint32_t chunk, ChunkRec *out, uint64_t cap, uint64_t *n_chunks)
 {
-    ChunkRec *w = out;
+    uint64_t bits = 0, bad = 0, total = 0, w = 0;
     uint64_t cs = 0, cd = 0, cn = 0;   // the open range
     auto close = [&]() {
-        if (cn <= chunk) {
-            *w++ = ChunkRec{cs, cd, (uint32_t)cn, 0};
+        if (cn <= chunk) {   // the common case: one chunk per range
+            if (w < cap)
+                out[w] = ChunkRec{cs, cd, (uint32_t)cn, 0};
+            ++w;
             return;
         }
-        for (uint64_t off = 0; off < cn; off += chunk) {
-            const uint64_t left = cn - off;
-            *w++ = ChunkRec{cs + off, cd + off, (uint32_t)(left < chunk ? left : chunk), 0};
+        // Count arithmetically and write only what fits: an invalid list (a
+        // size that wraps, say) is rejected after the pass, and must not cost
+        // a loop over its chunks first.
+        const uint64_t k = cn / chunk + (cn % chunk != 0);
+        const uint64_t room = w < cap ? cap - w : 0;
+        const uint64_t put = k < room ? k : room;
+        for (uint64_t j = 0; j < put; ++j) {
+            const uint64_t off = j * chunk, left = cn - off;
+            out[w + j] = ChunkRec{cs + off, cd + off, (uint32_t)(left < chunk ? left : chunk), 0};
         }
+        w += k;
     };
     for (uint64_t i = 0; i < n; ++i) {
-        const uint64_t z = size[i];
+        const uint64_t s = src[i], d = dst[i], z = size[i];
+        const uint64_t t = total + z;
+        bits |= s | d | z;
+        bad |= (uint64_t)(s + z < s) | (uint64_t)(d + z < d) | (uint64_t)(t < total);
+        total = t;
         if (z == 0)
             continue;
-        const uint64_t s = src[i], d = dst[i];
         if (merge && cn != 0 && cs + cn == s && cd + cn == d) {
             cn += z;
             continue;
@@ -146,7 +158,20 @@ uint64_t build_worklist(const uint64_t *src, const uint64_t *dst, const uint64_t
     }
     if (cn != 0)
         close();
-    return (uint64_t)(w - out);
+    if (bits & 7u)
+        return KVCOPY_EALIGN;
+    if (bad)
+        return KVCOPY_EINVAL;
+    *n_chunks = w;
+    return KVCOPY_OK;
+}
+
+uint64_t build_worklist(const uint64_t *src, const uint64_t *dst, const uint64_t *size, uint64_t n,
+                        bool merge, uint32_t chunk, ChunkRec *out)
+{
+    uint64_t w = 0;
+    (void)build_checked(src, dst, size, n, merge, chunk, out, ~0ull, &w);
+    return w;
 }
 
 uint64_t chunk_prefix(const uint64_t *size, uint64_t m, uint32_t chunk, uint64_t *begin)

@@ -173,26 +173,43 @@ uint32_t grid_for(uint64_t n_chunks, int max_wgs)
 }
 
 // Plans the batch into the staging ring and enqueues the kernel (and, with
-// KVCOPY_F_DESC_UPLOAD, the worklist copy before it).  Called with st->mu held.
+// KVCOPY_F_DESC_UPLOAD, the worklist copy before it).  Called with st->mu
+// held.  One checked pass validates the list and writes its worklist into a
+// region sized for `hint` records (the descriptor count, or the exact chunk
+// count when known); only a batch with more chunks than that (ranges longer
+// than a chunk) is planned a second time into a region of the exact size.
 int run_locked(Staging *st, const uint64_t *src, const uint64_t *dst, const uint64_t *sizes,
-               uint64_t n, const Prescan &pre, int dir, int max_wgs, hipStream_t stream,
+               uint64_t n, uint64_t hint, int dir, int max_wgs, hipStream_t stream,
                uint32_t chunk, uint32_t flags, hipEvent_t ev_begin, hipEvent_t ev_end)
 {
     const bool upload = (flags & KVCOPY_F_DESC_UPLOAD) != 0;
     const bool dynamic = (flags & KVCOPY_F_DYNAMIC) != 0;
-    const uint64_t need = (pre.bound * sizeof(ChunkRec) + kAlign - 1) / kAlign * kAlign;
-    uint64_t off = 0;
+    const bool merge = !(flags & KVCOPY_F_NO_COALESCE);
+    uint64_t off = 0, n_chunks = 0;
+    ChunkRec *host = nullptr;
     int rc;
-    if (4 * need > st->ring.capacity() || (upload && st->dev == nullptr) ||
-        (dynamic && st->claims == nullptr)) {
-        if ((rc = grow(st, need, upload, dynamic)) != KVCOPY_OK)
+    for (int pass = 0; pass < 2; ++pass) {
+        const uint64_t room = hint ? hint : 1;
+        const uint64_t need = (room * sizeof(ChunkRec) + kAlign - 1) / kAlign * kAlign;
+        if (4 * need > st->ring.capacity() || (upload && st->dev == nullptr) ||
+            (dynamic && st->claims == nullptr)) {
+            if ((rc = grow(st, need, upload, dynamic)) != KVCOPY_OK)
+                return rc;
+        }
+        if ((rc = st->ring.reserve(need, &off)) != KVCOPY_OK)
             return rc;
+        host = reinterpret_cast<ChunkRec *>(st->host + off);
+        if ((rc = build_checked(src, dst, sizes, n, merge, chunk, host, room, &n_chunks)) !=
+            KVCOPY_OK)
+            return rc;   // nothing committed: the region stays free
+        if (n_chunks == 0)
+            return KVCOPY_OK;   // only zero-size descriptors: nothing to enqueue
+        if (n_chunks > KVCOPY_MAX_CHUNKS)
+            return KVCOPY_EINVAL;
+        if (n_chunks <= room)
+            break;
+        hint = n_chunks;   // plan again into a region of the exact size
     }
-    if ((rc = st->ring.reserve(need, &off)) != KVCOPY_OK)
-        return rc;
-    ChunkRec *host = reinterpret_cast<ChunkRec *>(st->host + off);
-    const uint64_t n_chunks =
-        build_worklist(src, dst, sizes, n, !(flags & KVCOPY_F_NO_COALESCE), chunk, host);
     const uint64_t used = (n_chunks * sizeof(ChunkRec) + kAlign - 1) / kAlign * kAlign;
 
     const ChunkRec *recs = host;   // read in place: mapped at the same address on the device
@@ -246,20 +263,30 @@ constexpr int kNotInline = 1;   // run_inline's "use the staging ring instead"
 // Small batches (at most kInlineRecs chunks): the worklist goes to the GPU in
 // the kernel arguments, so the call needs no staging region and no
 // completion event, and the kernel makes no round trip over the host link
-// for its records.  Returns kNotInline when the default policy would pick
-// the pipelined loop for this grid (small D2D grids).
+// for its records.  Returns kNotInline, with *chunks set to the batch's
+// chunk count, when the worklist does not fit or the default policy would
+// pick the pipelined loop for this grid (small D2D grids).
 int run_inline(Staging *st, const uint64_t *src, const uint64_t *dst, const uint64_t *sizes,
                uint64_t n, int dir, int max_wgs, hipStream_t stream, uint32_t chunk,
-               uint32_t flags, hipEvent_t ev_begin, hipEvent_t ev_end)
+               uint32_t flags, hipEvent_t ev_begin, hipEvent_t ev_end, uint64_t *chunks)
 {
+    InlineWork w;
+    w.reserved = 0;
+    uint64_t need = 0;
+    const int rc = build_checked(src, dst, sizes, n, !(flags & KVCOPY_F_NO_COALESCE), chunk, w.rec,
+                                 kInlineRecs, &need);
+    if (rc != KVCOPY_OK)
+        return rc;
+    if (need == 0)
+        return KVCOPY_OK;   // only zero-size descriptors: nothing to enqueue
+    *chunks = need;
+    if (need > kInlineRecs)
+        return kNotInline;
+    w.n_chunks = (uint32_t)need;
     if (max_wgs == KVCOPY_WGS_AUTO) {
         std::lock_guard<std::mutex> g(st->mu);
         max_wgs = resolve_auto(st, dir);
     }
-    InlineWork w;
-    w.reserved = 0;
-    w.n_chunks = (uint32_t)build_worklist(src, dst, sizes, n, !(flags & KVCOPY_F_NO_COALESCE),
-                                          chunk, w.rec);
     const uint32_t grid = grid_for(w.n_chunks, max_wgs);
     if (!(flags & KVCOPY_F_PER_CHUNK) && pipeline_pays(dir, grid, w.n_chunks))
         return kNotInline;
@@ -317,31 +344,41 @@ extern "C" int kvcopy_batch_ex(const uint64_t *src_addrs, const uint64_t *dst_ad
     if (bad_env)
         return KVCOPY_EINVAL;
 
-    Prescan pre;
-    int rc = prescan(src_addrs, dst_addrs, sizes, n, chunk, &pre);
-    if (rc != KVCOPY_OK)
-        return rc;
-    if (pre.bound > KVCOPY_MAX_CHUNKS)
-        return KVCOPY_EINVAL;
-    if (validate && (rc = check_overlap(src_addrs, dst_addrs, sizes, n)) != KVCOPY_OK)
-        return rc;
-    if (pre.nnz == 0)
-        return KVCOPY_OK;   // only zero-size descriptors: nothing to enqueue
+    // Validation errors come back before anything is enqueued; the alignment
+    // and range checks are part of the planning pass, except in validate
+    // mode, where they run first so that they keep priority over the
+    // overlap check.
+    if (validate) {
+        Prescan pre;
+        int rc = prescan(src_addrs, dst_addrs, sizes, n, chunk, &pre);
+        if (rc != KVCOPY_OK)
+            return rc;
+        if ((rc = check_overlap(src_addrs, dst_addrs, sizes, n)) != KVCOPY_OK)
+            return rc;
+    }
 
     int device = 0;
     const hipError_t e = hipGetDevice(&device);
-    if (e != hipSuccess)
-        return hip_fail(e);
+    if (e != hipSuccess) {
+        // Argument errors keep priority over a failing runtime.
+        Prescan pre;
+        const int rc = prescan(src_addrs, dst_addrs, sizes, n, chunk, &pre);
+        if (rc != KVCOPY_OK)
+            return rc;
+        if (pre.bound > KVCOPY_MAX_CHUNKS)
+            return KVCOPY_EINVAL;
+        return pre.nnz == 0 ? KVCOPY_OK : hip_fail(e);
+    }
     Staging *st = staging_for(device);
-    if (pre.bound <= kInlineRecs &&
-        !(flags & (KVCOPY_F_DESC_UPLOAD | KVCOPY_F_PIPELINE | KVCOPY_F_DYNAMIC))) {
+    uint64_t hint = n;   // records per descriptor: exact unless ranges exceed a chunk
+    if (n <= kInlineRecs && !(flags & (KVCOPY_F_DESC_UPLOAD | KVCOPY_F_PIPELINE | KVCOPY_F_DYNAMIC))) {
         const int rc = run_inline(st, src_addrs, dst_addrs, sizes, n, dir, max_wgs, stream, chunk,
-                                  flags, ev_begin, ev_end);
+                                  flags, ev_begin, ev_end, &hint);
         if (rc != kNotInline)
             return rc;
     }
     std::lock_guard<std::mutex> g(st->mu);
-    return run_locked(st, src_addrs, dst_addrs, sizes, n, pre, dir, max_wgs, stream, chunk, flags,
+    return run_locked(st, src_addrs, dst_addrs, sizes, n, hint, dir, max_wgs, stream, chunk, flags,
                       ev_begin, ev_end);
 }
 

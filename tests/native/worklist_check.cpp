@@ -3,6 +3,7 @@
 // emit_chunks) gives, for random descriptor lists with zero sizes, chains of
 // adjacent ranges, and ranges longer than a chunk; prescan's bound must hold.
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <random>
 #include <vector>
@@ -12,12 +13,13 @@
 
 using namespace kvc;
 
-int main()
+int main(int argc, char **argv)
 {
+    const int trials = argc > 1 ? atoi(argv[1]) : 3000;   // fewer under the sanitizers
     std::mt19937_64 rng(12345);
     const uint32_t chunks[] = {16, 64, 4096, 16384, 65536};
     int cases = 0;
-    for (int trial = 0; trial < 3000; ++trial) {
+    for (int trial = 0; trial < trials; ++trial) {
         const uint64_t n = rng() % 300;
         const uint32_t chunk = chunks[rng() % 5];
         std::vector<uint64_t> s(n), d(n), z(n);
@@ -56,7 +58,43 @@ int main()
                        (unsigned long)pre.bound);
                 return 1;
             }
+            // The checked pass with a short room: same count, same prefix.
+            for (uint64_t cap : {(uint64_t)0, c / 2, c, c + 3}) {
+                std::vector<ChunkRec> part(cap + 1);
+                uint64_t need = ~0ull;
+                const int rc = build_checked(s.data(), d.data(), z.data(), n, merge, chunk,
+                                             part.data(), cap, &need);
+                const uint64_t wrote = cap < c ? cap : c;
+                if (rc != KVCOPY_OK || need != c ||
+                    (wrote && memcmp(ref.data(), part.data(), wrote * sizeof(ChunkRec)) != 0)) {
+                    printf("build_checked: trial %d cap %lu: rc %d need %lu want %lu\n", trial,
+                           (unsigned long)cap, rc, (unsigned long)need, (unsigned long)c);
+                    return 1;
+                }
+            }
             ++cases;
+        }
+        // Broken copies of the list: build_checked rejects them as prescan does.
+        if (n > 0) {
+            const uint64_t i = rng() % n;
+            for (int k = 0; k < 4; ++k) {
+                std::vector<uint64_t> s2 = s, d2 = d, z2 = z;
+                if (k == 0) s2[i] += 4;                       // misaligned source
+                if (k == 1) z2[i] = 12;                       // size not a multiple of 8
+                if (k == 2) d2[i] = ~0ull - 7, z2[i] = 64;    // destination range wraps
+                if (k == 3) z2[i] = ~0ull - 7;                // size wraps the source range
+                Prescan p2;
+                const int want = prescan(s2.data(), d2.data(), z2.data(), n, chunk, &p2);
+                std::vector<ChunkRec> tmp(8);
+                uint64_t need = 0;
+                const int got = build_checked(s2.data(), d2.data(), z2.data(), n, true, chunk,
+                                              tmp.data(), 8, &need);
+                if (want == KVCOPY_OK || got != want) {
+                    printf("build_checked error: trial %d kind %d: %d vs prescan %d\n", trial, k,
+                           got, want);
+                    return 1;
+                }
+            }
         }
     }
     // The default copy-loop choice: pipelined only for D2D grids of at most
