@@ -307,9 +307,11 @@ def bench_kv(c: Ctx, args):
     if not args.skip_extras:
         alone = {}
         for j, name in ((0, "h2d"), (1, "d2h")):
-            s, km = c.timed(res, [j], [sA], args.steps, args.warmup, max_wgs)
+            s, _ = c.timed_bracketed(res, [j], [sA], args.steps, args.warmup, max_wgs)
+            _, km = c.timed(res, [j], [sA], args.steps, 2, max_wgs)
             alone[name] = {"GBps": round(gbs(wl.batches[j].nbytes, s), 3),
-                           "ms_per_call": round(s * 1e3, 4), "kernel_ms": round(km[0], 4)}
+                           "ms_per_call": round(s * 1e3, 4), "kernel_ms": round(km[0], 4),
+                           "latency": c.latency(res, j, max_wgs, k=50, w=5)}
             log(f"  {name} alone: {alone[name]}")
         extras["per_direction_alone"] = alone
         # the startup probe's choice, and the headline step at that cap
@@ -506,7 +508,8 @@ def d2d_results(c: Ctx, args):
                      "kernel_us": round(km[0] * 1e3, 2),
                      "hbm_GBps_kernel": round(gbs(hbm, km[0] / 1e3), 1),
                      "frac_hbm_peak_kernel": round(gbs(hbm, km[0] / 1e3) / HBM_PEAK_GBS, 4),
-                     "latency": c.latency(r, 0, 0, k=50, w=5)}
+                     "latency": c.latency(r, 0, 0, k=200 if name == "1024x4KiB" else 50,
+                                          w=20 if name == "1024x4KiB" else 5)}
         if name == "1024x4KiB":
             out[name]["mall_flushed"] = d2d_flushed(c, r, k=max(20, args.steps))
         c.verify(wld, r, [0], f"d2d {name}")
@@ -653,6 +656,24 @@ def bench_moe(c: Ctx, args):
             log(f"  moe {name} max_wgs={g}: {out[f'{name}/max_wgs={g}']}")
     c.verify(wl, r, list(range(calls)), "moe")     # every call wrote its slots; the last writes win
     r.free()
+    # Context row: 1-8 missed experts per call (one layer's top-8 misses).
+    small = W.moe_gather(seed=1, calls=calls, misses=(1, 8))
+    r = c.Resident(small)
+    t_us, sizes = [], []
+    with no_gc():
+        for i in range(calls):
+            e0, e1 = hiprt.Event(), hiprt.Event()
+            e0.record(c.sA)
+            r.submit(i, 32, c.sA)
+            e1.record(c.sA)
+            t_us.append(e0.elapsed_ms(e1) * 1e3)
+            sizes.append(small.batches[i].nbytes)
+    c.verify(small, r, list(range(calls)), "moe 1-8 misses")
+    r.free()
+    out["context_1_to_8_misses/max_wgs=32"] = {
+        "call_us_p50": round(pct(t_us, 50), 1), "call_us_p99": round(pct(t_us, 99), 1),
+        "GBps_total": round(gbs(sum(sizes), sum(t_us) / 1e6), 2)}
+    log(f"  moe 1-8 misses: {out['context_1_to_8_misses/max_wgs=32']}")
     best = max((v["GBps_total"], k) for k, v in out.items() if k.startswith("byte_balanced"))
     line = base_line(args, best[0], "GB/s", 0.0, {
         "workload": "MoE expert gather: 100 seeded calls, each 26-39 experts x 6 bank rows "
