@@ -674,6 +674,13 @@ def bench_moe(c: Ctx, args):
         "call_us_p50": round(pct(t_us, 50), 1), "call_us_p99": round(pct(t_us, 99), 1),
         "GBps_total": round(gbs(sum(sizes), sum(t_us) / 1e6), 2)}
     log(f"  moe 1-8 misses: {out['context_1_to_8_misses/max_wgs=32']}")
+    # Device-resident miss lists, one HIP graph per call (kvcopy_batch_device):
+    # the decode-side form in which a router kernel leaves the list on the GPU.
+    for name, misses in (("device_graph_26_to_39_misses", (26, 39)),
+                         ("device_graph_1_to_8_misses", (1, 8))):
+        out[f"{name}/max_wgs=32"] = moe_device_graph(c, W.moe_gather(seed=2, calls=calls,
+                                                                    misses=misses), 32)
+        log(f"  moe {name}: {out[f'{name}/max_wgs=32']}")
     best = max((v["GBps_total"], k) for k, v in out.items() if k.startswith("byte_balanced"))
     line = base_line(args, best[0], "GB/s", 0.0, {
         "workload": "MoE expert gather: 100 seeded calls, each 26-39 experts x 6 bank rows "
@@ -685,6 +692,63 @@ def bench_moe(c: Ctx, args):
     line["per_setting"] = out
     line["parity"] = "bit-exact vs oracle"
     return line
+
+
+def moe_device_graph(c: Ctx, wl, max_wgs):
+    """Each call's descriptor list and count are placed in device memory
+    beforehand, and one HIP graph per call captures kvcopy_batch_device on
+    them; the graphs are then replayed in order on one stream, each bracketed
+    by events.  Checked bit-exact against the oracle at the end."""
+    np, torch, K, hiprt = c.np, c.torch, c.K, c.hiprt
+    r = c.Resident(wl)
+    calls = len(wl.batches)
+    max_n = max(b.n for b in wl.batches)
+    lists = []
+    for i, b in enumerate(wl.batches):
+        s_, d_ = r.addrs[i]
+        t = torch.zeros((3, max_n), dtype=torch.int64, device=c.dev)
+        for row, a in enumerate((s_, d_, b.size)):
+            t[row, :b.n].copy_(torch.from_numpy(np.ascontiguousarray(a).view(np.int64)))
+        lists.append((t, torch.tensor([b.n], dtype=torch.int64, device=c.dev)))
+    ws = torch.empty(K.kvcopy_device_workspace_bytes(max_n) + 256, dtype=torch.uint8, device=c.dev)
+    base = (ws.data_ptr() + 255) // 256 * 256
+    st = c.sA
+
+    def call(i):
+        t, n = lists[i]
+        K.kvcopy_batch_device(t[0].data_ptr(), t[1].data_ptr(), t[2].data_ptr(), n.data_ptr(),
+                              max_n, K.H2D, max_wgs, base, stream=st.cuda_stream)
+
+    with torch.cuda.stream(st):
+        call(0)                      # warm-up outside any graph
+    torch.cuda.synchronize()
+    graphs = []
+    for i in range(calls):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=st):
+            call(i)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    r.fill()
+    t_us = []
+    with no_gc(), torch.cuda.stream(st):
+        for i in range(calls):
+            e0, e1 = hiprt.Event(), hiprt.Event()
+            e0.record(st)
+            graphs[i].replay()
+            e1.record(st)
+            t_us.append(e0.elapsed_ms(e1) * 1e3)
+    torch.cuda.synchronize()
+    status = int(ws[base - ws.data_ptr():base - ws.data_ptr() + 8].cpu().numpy().view(np.uint64)[0])
+    if status != 0:
+        log(f"DEVICE BATCH STATUS {status}")
+        sys.exit(3)
+    c.verify(wl, r, list(range(calls)), "moe device graphs")
+    sizes = [b.nbytes for b in wl.batches]
+    del graphs
+    r.free()
+    return {"call_us_p50": round(pct(t_us, 50), 1), "call_us_p99": round(pct(t_us, 99), 1),
+            "GBps_total": round(gbs(sum(sizes), sum(t_us) / 1e6), 2), "calls": calls}
 
 
 # ---------------------------------------------------------------------------
