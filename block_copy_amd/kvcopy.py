@@ -64,7 +64,7 @@ class Opts(ctypes.Structure):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"libkvcopy.so not built ({LIB_PATH}); run "
-                          "`python -c 'import __graft_entry__ as g; g.build()'`")
+                          "`python -m block_copy_amd.build`")
     lib = ctypes.CDLL(LIB_PATH)
     u64p = ctypes.POINTER(ctypes.c_uint64)
     lib.kvcopy_coalesce.restype = ctypes.c_int

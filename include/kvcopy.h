@@ -5,8 +5,10 @@
  * device-visible addresses and byte counts of small, non-contiguous blocks
  * such as KV-cache pages or MoE expert bank rows.  Blocks move between
  * mapped pinned host memory and HBM (H2D, D2H) or within HBM (D2D).  The
- * whole batch costs one descriptor upload and one kernel launch, instead of
- * one DMA memcpy per fragment.
+ * whole batch costs one host planning pass and one kernel launch, instead of
+ * one DMA memcpy per fragment; the planned worklist reaches the GPU through
+ * library-owned pinned memory that the kernel reads in place, or, for a
+ * batch of at most 128 chunks, in the kernel arguments.
  *
  * Sources (cited by page title and section):
  *   [PF]  PegaFlow issue #408, "Kernel transfer backend causes decode TPOT
