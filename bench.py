@@ -95,9 +95,12 @@ def kernel_source_hash():
     return h.hexdigest()
 
 
-def measured_traffic(kernel, path=COUNTERS_KV):
+def measured_traffic(kernel, path=COUNTERS_KV, alg_fetch=None, alg_write=None):
     """Bytes per launch of `kernel` from the committed PMC summary, or None if
-    there is none or the kernel source changed since it was taken."""
+    there is none or the kernel source changed since it was taken.  With the
+    algorithmic bytes each side must move (fetch: payload reads plus the
+    worklist records; write: payload writes), also each side's ratio of
+    measured to algorithmic bytes (1.0 = no re-reads, no extra writes)."""
     try:
         with open(path) as f:
             c = json.load(f)
@@ -109,8 +112,12 @@ def measured_traffic(kernel, path=COUNTERS_KV):
     if not k:
         return None
     f, w = k["fetch_bytes_per_dispatch_scaled"], k["write_bytes_per_dispatch_scaled"]
-    return {"bytes": f + w, "fetch_bytes": f, "write_bytes": w,
-            "source": os.path.relpath(path, ROOT)}
+    out = {"bytes": f + w, "fetch_bytes": f, "write_bytes": w,
+           "source": os.path.relpath(path, ROOT)}
+    if alg_fetch and alg_write:
+        out.update({"algorithmic_fetch_bytes": int(alg_fetch), "algorithmic_write_bytes": int(alg_write),
+                    "fetch_ratio": round(f / alg_fetch, 4), "write_ratio": round(w / alg_write, 4)})
+    return out
 
 
 class Ctx:
@@ -386,7 +393,8 @@ def bench_kv(c: Ctx, args):
     line["roofline"] = {
         "bound": "pcie", "kernel": KERNEL_NAMES[dom], "achieved": round(ach[dom], 3),
         "peak": PCIE_PEAK_GBS, "unit": "GB/s", "frac": round(ach[dom] / PCIE_PEAK_GBS, 4),
-        "traffic": measured_traffic(KERNEL_NAMES[dom]),
+        "traffic": measured_traffic(KERNEL_NAMES[dom], COUNTERS_KV, algo[dom],
+                                    wl.batches[dom].nbytes),
         "kernel_ms": round(kern_ms[dom], 4), "algorithmic_bytes_per_launch": algo[dom],
         "measured_ceiling": meas_ceil,
         "frac_of_measured_ceiling": round(ach[dom] / meas_ceil, 4) if meas_ceil else None,
@@ -502,7 +510,8 @@ def d2d_results(c: Ctx, args):
         _, km = c.timed(r, [0], [c.sA], args.steps, 2, 0)
         pl = K.kvcopy_plan(*r.addrs[0], wld.batches[0].size)
         hbm = 2 * wld.batches[0].nbytes + pl.n_chunks * REC_BYTES
-        out[name] = {"GBps_payload": round(gbs(wld.batches[0].nbytes, s), 2),
+        out[name] = {"payload_bytes": wld.batches[0].nbytes, "records": int(pl.n_chunks),
+                     "GBps_payload": round(gbs(wld.batches[0].nbytes, s), 2),
                      "us_per_call_pipelined": round(s * 1e6, 2),
                      "gpu_us_per_call_back_to_back": round(stream_ms[0] * 1e3, 2),
                      "kernel_us": round(km[0] * 1e3, 2),
@@ -583,7 +592,10 @@ def bench_d2d(c: Ctx, args):
     big = res["65536x4KiB"]
     line["roofline"] = {"bound": "hbm", "kernel": KERNEL_NAMES[2],
                         "achieved": big["hbm_GBps_kernel"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                        "frac": big["frac_hbm_peak_kernel"], "traffic": measured_traffic(KERNEL_NAMES[2], COUNTERS_D2D),
+                        "frac": big["frac_hbm_peak_kernel"],
+                        "traffic": measured_traffic(KERNEL_NAMES[2], COUNTERS_D2D,
+                                                    big["payload_bytes"] + big["records"] * REC_BYTES,
+                                                    big["payload_bytes"]),
                         "workload_of_roofline": "65536x4KiB",
                         "measured_ceiling": res["contiguous_memcpy_hbm_GBps"]["256MiB"]}
     line["d2d"] = res
