@@ -83,3 +83,22 @@ def test_mixed_size_distribution():
     b = wl.batches[0]
     cont = (b.src_off[1:] == b.src_off[:-1] + b.size[:-1]) & (b.dst_off[1:] == b.dst_off[:-1] + b.size[:-1])
     assert int(cont.sum()) == 1024                 # exactly a quarter continue their predecessor
+
+
+def test_random_batches_respect_the_contract():
+    """Random stress batches: 8-byte aligned, inside their arenas, disjoint
+    destinations and sources, and some adjacency for coalescing."""
+    merged_somewhere = False
+    for seed in range(60):
+        wl = W.random_batch(seed)
+        b = wl.batches[0]
+        assert np.all(b.size % 8 == 0) and np.all(b.src_off % 8 == 0) and np.all(b.dst_off % 8 == 0)
+        assert np.all(b.src_off + b.size <= wl.arenas[0].nbytes)
+        assert np.all(b.dst_off + b.size <= wl.arenas[1].nbytes)
+        for off in (b.dst_off, b.src_off):
+            nz = b.size > 0
+            o = np.argsort(off[nz], kind="stable")
+            lo, hi = off[nz][o], (off + b.size)[nz][o]
+            assert np.all(lo[1:] >= hi[:-1])              # no two ranges overlap
+        merged_somewhere |= wl.info["runs"] < b.n
+    assert merged_somewhere

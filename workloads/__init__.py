@@ -331,3 +331,50 @@ def irregular(seed=0, n=64, max_size=40 * KIB, dir_=D2D, src_where="device", dst
               Arena("dst", d_len, dst_where, "sentinel", sentinel=sentinel)]
     b = _batch(dir_, 0, s_off, 1, d_off, size)
     return Workload(f"irregular_{n}", arenas, [b], {"n": n})
+
+
+# ---------------------------------------------------------------------------
+# Randomized batches for stress tests
+# ---------------------------------------------------------------------------
+
+def random_batch(seed, max_n=3000):
+    """One random descriptor list of every shape the contract allows.
+
+    Direction uniform over H2D / D2H / D2D; n log-uniform in [1, max_n];
+    sizes log-uniform over 8-byte multiples from 8 B to 256 KiB, with a
+    random fraction of zeros; descriptors come in runs that are adjacent in
+    both arenas (so coalescing applies) of random length; runs start at
+    independent 8-byte offsets in the two arenas (src and dst differ mod 16
+    about half the time), in shuffled order with small gaps.  Destinations
+    never overlap; sources do not either.
+    """
+    rng = np.random.default_rng(seed)
+    dir_ = int(rng.integers(0, 3))
+    n = max(1, int(round(np.exp(rng.uniform(0, np.log(max_n))))))
+    size = (8 * np.exp(rng.uniform(0, np.log(32768), n)).astype(np.int64)).astype(np.uint64)
+    size[rng.random(n) < rng.uniform(0, 0.2)] = 0
+    cont = rng.random(n) < rng.uniform(0, 0.6)      # descriptor i continues i-1
+    cont[0] = False
+    starts = np.flatnonzero(~cont)
+    runs = [(int(a), int(b)) for a, b in zip(starts, list(starts[1:]) + [n])]
+
+    def place():
+        off = np.zeros(n, np.uint64)
+        cur = 0
+        for r in rng.permutation(len(runs)):
+            a, b = runs[r]
+            cur += 8 * int(rng.integers(0, 16))
+            for i in range(a, b):
+                off[i] = cur
+                cur += int(size[i])
+            cur += 8 * int(rng.integers(1, 8))
+        return off, cur + 64
+
+    s_off, s_len = place()
+    d_off, d_len = place()
+    where = {H2D: ("host", "device"), D2H: ("device", "host"), D2D: ("device", "device")}[dir_]
+    arenas = [Arena("src", s_len, where[0], "random", seed=seed * 1000 + 7),
+              Arena("dst", d_len, where[1], "sentinel")]
+    b = _batch(dir_, 0, s_off, 1, d_off, size)
+    return Workload(f"random_{seed}", arenas, [b], {"n": n, "runs": len(runs)})
+
