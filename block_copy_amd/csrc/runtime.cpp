@@ -175,9 +175,10 @@ uint32_t grid_for(uint64_t n_chunks, int max_wgs)
 // Plans the batch into the staging ring and enqueues the kernel (and, with
 // KVCOPY_F_DESC_UPLOAD, the worklist copy before it).  Called with st->mu
 // held.  One checked pass validates the list and writes its worklist into a
-// region sized for `hint` records (the descriptor count, or the exact chunk
-// count when known); only a batch with more chunks than that (ranges longer
-// than a chunk) is planned a second time into a region of the exact size.
+// region sized for `hint` records (twice the descriptor count, or the exact
+// chunk count when known); only a batch with more chunks than that (many
+// ranges longer than two chunks) is planned a second time into a region of
+// the exact size.
 int run_locked(Staging *st, const uint64_t *src, const uint64_t *dst, const uint64_t *sizes,
                uint64_t n, uint64_t hint, int dir, int max_wgs, hipStream_t stream,
                uint32_t chunk, uint32_t flags, hipEvent_t ev_begin, hipEvent_t ev_end)
@@ -370,7 +371,11 @@ extern "C" int kvcopy_batch_ex(const uint64_t *src_addrs, const uint64_t *dst_ad
         return pre.nnz == 0 ? KVCOPY_OK : hip_fail(e);
     }
     Staging *st = staging_for(device);
-    uint64_t hint = n;   // records per descriptor: exact unless ranges exceed a chunk
+    // Room for the first planning pass: two records per descriptor covers
+    // batches whose ranges are mostly up to two chunks long (mixed 4-28 KiB
+    // sizes with 16 KiB chunks, say), so they are planned once; the region's
+    // unused tail is not committed.
+    uint64_t hint = n <= KVCOPY_MAX_DESCS / 2 ? 2 * n : n;
     if (n <= kInlineRecs && !(flags & (KVCOPY_F_DESC_UPLOAD | KVCOPY_F_PIPELINE | KVCOPY_F_DYNAMIC))) {
         const int rc = run_inline(st, src_addrs, dst_addrs, sizes, n, dir, max_wgs, stream, chunk,
                                   flags, ev_begin, ev_end, &hint);
