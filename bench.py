@@ -201,6 +201,12 @@ class Ctx:
             kern = [(t1 - t0) / k * 1e3] * len(batch_ids)
         return (t1 - t0) / k, kern
 
+    def pair_step(self, r, stream, max_wgs):
+        """One kvcopy_batch_pair call: batch 0 and batch 1 in one launch."""
+        (s0, d0), (s1, d1) = r.addrs[0], r.addrs[1]
+        self.K.kvcopy_batch_pair(s0, d0, r.wl.batches[0].size, s1, d1, r.wl.batches[1].size,
+                                 max_wgs, stream.cuda_stream)
+
     def latency(self, r, bi, max_wgs, k=100, w=10, **kw):
         """Per-call latency of isolated calls: host time inside kvcopy_batch,
         GPU time from an event recorded before the call to one after it, and
@@ -336,6 +342,7 @@ def bench_kv(c: Ctx, args):
             log(f"  DMA baselines {name}: {frag[name]}")
         extras["dma_baselines"] = frag
         extras["dma_baselines_rocm_runtime"] = dma_runtime_baselines()
+        extras["one_launch_pair"] = pair_rates(c, res, args)
 
     if args.counter_calibration:
         counter_calibration(c)
@@ -376,6 +383,16 @@ def bench_kv(c: Ctx, args):
             bad = int(np.flatnonzero(final[i] != imgs[i])[0])
             log(f"PARITY FAILURE in arena {wl.arenas[i].name} at byte {bad}")
             sys.exit(3)
+    if not args.skip_extras:
+        # the one-launch call on the same inputs must leave the same images
+        res.fill()
+        c.pair_step(res, sA, max_wgs)
+        torch.cuda.synchronize()
+        for i in (0, 2):
+            if not np.array_equal(res.image(i), imgs[i]):
+                log(f"PARITY FAILURE (one-launch pair) in arena {wl.arenas[i].name}")
+                sys.exit(3)
+        extras["one_launch_pair"]["parity"] = "bit-exact vs oracle"
     log("  parity: bit-exact against the oracle")
     res.free()
 
@@ -407,6 +424,36 @@ def bench_kv(c: Ctx, args):
     line["parity"] = "bit-exact vs oracle"
     line.update(extras)
     return line
+
+
+def pair_rates(c: Ctx, res, args):
+    """The headline step as one kvcopy_batch_pair call per step (both lists
+    in one launch on one stream), at a few workgroup caps: GB/s of payload
+    over k back-to-back calls bracketed by one event pair."""
+    torch, hiprt = c.torch, c.hiprt
+    step_bytes = res.wl.nbytes
+    out = {}
+    for g in (32, 48, 64, 80, 128, 256, 0):
+        for _ in range(args.warmup):
+            c.pair_step(res, c.sA, g)
+        torch.cuda.synchronize()
+        use_ev = not args.no_events
+        e0, e1 = (hiprt.Event(), hiprt.Event()) if use_ev else (None, None)
+        with no_gc():
+            t0 = time.perf_counter()
+            if use_ev:
+                e0.record(c.sA)
+            for _ in range(args.steps):
+                c.pair_step(res, c.sA, g)
+            if use_ev:
+                e1.record(c.sA)
+            torch.cuda.synchronize()
+            t1 = time.perf_counter()
+        ms = e0.elapsed_ms(e1) / args.steps if use_ev else (t1 - t0) / args.steps * 1e3
+        out[str(g)] = {"GBps": round(gbs(step_bytes, ms / 1e3), 3), "ms_per_step": round(ms, 4),
+                       "wall_GBps": round(gbs(step_bytes, (t1 - t0) / args.steps), 3)}
+        log(f"  one-launch pair max_wgs={g}: {out[str(g)]}")
+    return out
 
 
 def counter_calibration(c: Ctx):
@@ -822,6 +869,9 @@ def bench_interference(c: Ctx, args):
                             time.sleep(20e-6)      # yield the worker while a piece runs
                     for jb in jobs:
                         K.kvcopy_job_destroy(jb)
+                elif isinstance(mode, str) and mode.startswith("pair"):
+                    # both lists in one launch (kvcopy_batch_pair) on one stream
+                    c.pair_step(r, sa, int(mode.split(":")[1]))
                 elif isinstance(mode, str) and mode.startswith("pipe"):
                     # the pipelined loop forced at a small cap
                     g = int(mode.split(":")[1])
@@ -868,7 +918,7 @@ def bench_interference(c: Ctx, args):
         return gpu_ms, wall_ms, moved[0] / dur, bursts[0]
 
     modes = ["none", "direct", 1, 2, 8, 32, 128, 0, "pipe:1", "pipe:4", "job:1024", "job:2048",
-             "job:4096", "cumask:8", "cumask:32"]
+             "job:4096", "cumask:8", "cumask:32", "pair:8", "pair:64"]
     results = {str(m): {"gpu": [], "wall": [], "rate": [], "bursts": 0} for m in modes}
     for rep in range(args.decode_runs):
         order = modes[rep % len(modes):] + modes[:rep % len(modes)]

@@ -113,6 +113,12 @@ hipError_t launch_copy_inline(const InlineWork &w, uint32_t grid, int dir, hipSt
 hipError_t launch_copy(const ChunkRec *recs, uint32_t n_chunks, uint32_t grid, int dir,
                        bool pipelined, hipStream_t stream, hipEvent_t start, hipEvent_t stop);
 
+// kvcopy_batch_pair: two worklists (ra[0..ca), rb[0..cb)) in one kernel;
+// every wavefront alternates between its shares of the two lists in
+// proportion to their chunk counts.  start / stop as for launch_copy.
+hipError_t launch_copy_pair(const ChunkRec *ra, uint32_t ca, const ChunkRec *rb, uint32_t cb,
+                            uint32_t grid, hipStream_t stream, hipEvent_t start, hipEvent_t stop);
+
 // KVCOPY_F_DYNAMIC: the per-chunk loop with chunks claimed at run time.
 // claim points at two zeroed device counters (next chunk, wavefronts done);
 // every wavefront claims `grain` chunks at a time with an atomic add, one

@@ -313,6 +313,51 @@ __device__ __forceinline__ void copy_worklist_dynamic(const ChunkRec *__restrict
     }
 }
 
+// ---- two worklists in one launch -------------------------------------------------
+//
+// kvcopy_batch_pair: two worklists (typically an H2D burst and a D2H burst)
+// in one kernel.  Wavefront w of W owns the shares [w*Ca/W, (w+1)*Ca/W) of
+// list a and [w*Cb/W, (w+1)*Cb/W) of list b and copies them alternately,
+// always taking a chunk of the list that is proportionally behind, so both
+// directions progress together inside every wavefront and the host link
+// carries both until the end.  Records come 64 at a time per list, one batch
+// ahead, as in the per-chunk loop.
+__device__ __forceinline__ void copy_pair(const ChunkRec *__restrict__ ra, uint32_t ca,
+                                          const ChunkRec *__restrict__ rb, uint32_t cb)
+{
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t nw = gridDim.x * kWavesPerWG;
+    const uint32_t w = __builtin_amdgcn_readfirstlane(blockIdx.x * kWavesPerWG + (threadIdx.x >> 6));
+    const uint32_t la = (uint32_t)((uint64_t)w * ca / nw), ha = (uint32_t)((uint64_t)(w + 1) * ca / nw);
+    const uint32_t lb = (uint32_t)((uint64_t)w * cb / nw), hb = (uint32_t)((uint64_t)(w + 1) * cb / nw);
+    const uint32_t na = ha - la, nb = hb - lb;
+    if (na == 0 && nb == 0)
+        return;
+    Rec cur_a = fetch_recs(ra, la, ha, lane), nxt_a = fetch_recs(ra, la + 64u, ha, lane);
+    Rec cur_b = fetch_recs(rb, lb, hb, lane), nxt_b = fetch_recs(rb, lb + 64u, hb, lane);
+    uint32_t ia = 0, ib = 0;   // chunks done in each list
+    while (ia < na || ib < nb) {
+        const bool take_a = ia < na && (ib >= nb || (uint64_t)ia * nb <= (uint64_t)ib * na);
+        if (take_a) {
+            const uint32_t j = ia & 63u;
+            copy_chunk(lane_u64(cur_a.src, j), lane_u64(cur_a.dst, j),
+                       __builtin_amdgcn_readlane(cur_a.bytes, j), lane);
+            if ((++ia & 63u) == 0 && ia < na) {
+                cur_a = nxt_a;
+                nxt_a = fetch_recs(ra, la + ia + 64u, ha, lane);
+            }
+        } else {
+            const uint32_t j = ib & 63u;
+            copy_chunk(lane_u64(cur_b.src, j), lane_u64(cur_b.dst, j),
+                       __builtin_amdgcn_readlane(cur_b.bytes, j), lane);
+            if ((++ib & 63u) == 0 && ib < nb) {
+                cur_b = nxt_b;
+                nxt_b = fetch_recs(rb, lb + ib + 64u, hb, lane);
+            }
+        }
+    }
+}
+
 // ---- inline worklist ----------------------------------------------------------
 //
 // The per-chunk loop over a worklist passed by value in the kernel
@@ -345,6 +390,14 @@ KVC_KERNEL(kvcopy_h2d_pipe_kernel, copy_worklist_pipelined)
 KVC_KERNEL(kvcopy_d2h_pipe_kernel, copy_worklist_pipelined)
 KVC_KERNEL(kvcopy_d2d_pipe_kernel, copy_worklist_pipelined)
 #undef KVC_KERNEL
+
+__global__ __launch_bounds__(kThreadsPerWG) void kvcopy_pair_kernel(const ChunkRec *__restrict__ ra,
+                                                                    uint32_t ca,
+                                                                    const ChunkRec *__restrict__ rb,
+                                                                    uint32_t cb)
+{
+    copy_pair(ra, ca, rb, cb);
+}
 
 #define KVC_INLINE_KERNEL(name)                                                                    \
     __global__ __launch_bounds__(kThreadsPerWG) void name(const InlineWork w)                     \
@@ -383,6 +436,14 @@ hipError_t launch_copy(const ChunkRec *recs, uint32_t n_chunks, uint32_t grid, i
     void *args[] = {(void *)&recs, (void *)&n_chunks};
     return hipExtLaunchKernel(fns[pipelined ? 1 : 0][dir], dim3(grid), dim3(kThreadsPerWG), args, 0,
                               stream, start, stop, 0);
+}
+
+hipError_t launch_copy_pair(const ChunkRec *ra, uint32_t ca, const ChunkRec *rb, uint32_t cb,
+                            uint32_t grid, hipStream_t stream, hipEvent_t start, hipEvent_t stop)
+{
+    void *args[] = {(void *)&ra, (void *)&ca, (void *)&rb, (void *)&cb};
+    return hipExtLaunchKernel(reinterpret_cast<const void *>(&kvcopy_pair_kernel), dim3(grid),
+                              dim3(kThreadsPerWG), args, 0, stream, start, stop, 0);
 }
 
 hipError_t launch_copy_inline(const InlineWork &w, uint32_t grid, int dir, hipStream_t stream,

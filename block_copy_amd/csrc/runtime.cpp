@@ -164,6 +164,11 @@ int resolve_auto(const Staging *st, int dir)
     return dir == KVCOPY_D2D ? KVCOPY_WGS_ALL : 128;
 }
 
+// KVCOPY_WGS_AUTO for kvcopy_batch_pair: with 16,384 x 4 KiB each way, one
+// launch measured 95-96 GB/s on MI355X from 48 to 80 workgroups (93 at 32,
+// 91 at 128, 81 on the full grid), so the middle of that plateau.
+constexpr int kPairAutoWgs = 64;
+
 uint32_t grid_for(uint64_t n_chunks, int max_wgs)
 {
     const uint64_t full = (n_chunks + kWavesPerWG - 1) / kWavesPerWG;   // one wavefront per chunk
@@ -295,6 +300,61 @@ int run_inline(Staging *st, const uint64_t *src, const uint64_t *dst, const uint
     return e == hipSuccess ? KVCOPY_OK : hip_fail(e);
 }
 
+// kvcopy_batch_pair under st->mu: both lists are planned into one staging
+// region, list b's records right after list a's, and one kernel copies both.
+int run_pair_locked(Staging *st, const uint64_t *const src[2], const uint64_t *const dst[2],
+                    const uint64_t *const sizes[2], const uint64_t n[2], bool merge,
+                    int max_wgs, hipStream_t stream)
+{
+    uint64_t hint[2] = {2 * n[0], 2 * n[1]}, cnt[2] = {0, 0}, off = 0;
+    ChunkRec *host = nullptr;
+    int rc;
+    for (int pass = 0; pass < 3; ++pass) {
+        const uint64_t room = (hint[0] + hint[1]) ? hint[0] + hint[1] : 1;
+        const uint64_t need = (room * sizeof(ChunkRec) + kAlign - 1) / kAlign * kAlign;
+        if (4 * need > st->ring.capacity() && (rc = grow(st, need, false, false)) != KVCOPY_OK)
+            return rc;
+        if ((rc = st->ring.reserve(need, &off)) != KVCOPY_OK)
+            return rc;
+        host = reinterpret_cast<ChunkRec *>(st->host + off);
+        if ((rc = build_checked(src[0], dst[0], sizes[0], n[0], merge, KVCOPY_CHUNK_DEFAULT, host,
+                                room, &cnt[0])) != KVCOPY_OK)
+            return rc;   // nothing committed: the region stays free
+        const uint64_t room_b = cnt[0] <= room ? room - cnt[0] : 0;
+        if ((rc = build_checked(src[1], dst[1], sizes[1], n[1], merge, KVCOPY_CHUNK_DEFAULT,
+                                host + (cnt[0] <= room ? cnt[0] : 0), room_b, &cnt[1])) != KVCOPY_OK)
+            return rc;
+        if (cnt[0] + cnt[1] > KVCOPY_MAX_CHUNKS)
+            return KVCOPY_EINVAL;
+        if (cnt[0] + cnt[1] <= room)
+            break;
+        hint[0] = cnt[0];   // plan again into a region of the exact size
+        hint[1] = cnt[1];
+    }
+    const uint64_t total = cnt[0] + cnt[1];
+    if (total == 0)
+        return KVCOPY_OK;   // only zero-size descriptors: nothing to enqueue
+    const uint64_t used = (total * sizeof(ChunkRec) + kAlign - 1) / kAlign * kAlign;
+    if (max_wgs == KVCOPY_WGS_AUTO)
+        max_wgs = kPairAutoWgs;
+    hipError_t e;
+    hipEvent_t done;
+    if (!st->spare.empty()) {
+        done = st->spare.back();
+        st->spare.pop_back();
+    } else if ((e = hipEventCreateWithFlags(&done, hipEventDisableTiming)) != hipSuccess) {
+        return hip_fail(e);
+    }
+    e = launch_copy_pair(host, (uint32_t)cnt[0], host + cnt[0], (uint32_t)cnt[1],
+                         grid_for(total, max_wgs), stream, nullptr, done);
+    if (e != hipSuccess) {
+        st->spare.push_back(done);
+        return hip_fail(e);
+    }
+    st->ring.commit(off, used, done);
+    return KVCOPY_OK;
+}
+
 }  // namespace
 
 void set_tuned_wgs(int device, int dir, int wgs)
@@ -385,6 +445,62 @@ extern "C" int kvcopy_batch_ex(const uint64_t *src_addrs, const uint64_t *dst_ad
     std::lock_guard<std::mutex> g(st->mu);
     return run_locked(st, src_addrs, dst_addrs, sizes, n, hint, dir, max_wgs, stream, chunk, flags,
                       ev_begin, ev_end);
+}
+
+extern "C" int kvcopy_batch_pair(const uint64_t *src_a, const uint64_t *dst_a,
+                                 const uint64_t *sizes_a, uint64_t n_a, const uint64_t *src_b,
+                                 const uint64_t *dst_b, const uint64_t *sizes_b, uint64_t n_b,
+                                 int max_wgs, uint32_t flags, hipStream_t stream)
+{
+    if (max_wgs < KVCOPY_WGS_AUTO || n_a > KVCOPY_MAX_DESCS || n_b > KVCOPY_MAX_DESCS ||
+        (flags & ~(KVCOPY_F_VALIDATE | KVCOPY_F_NO_COALESCE)) != 0)
+        return KVCOPY_EINVAL;
+    if ((n_a && (!src_a || !dst_a || !sizes_a)) || (n_b && (!src_b || !dst_b || !sizes_b)))
+        return KVCOPY_EINVAL;
+    if (n_a + n_b == 0)
+        return KVCOPY_OK;
+    const uint64_t *const src[2] = {src_a, src_b}, *const dst[2] = {dst_a, dst_b};
+    const uint64_t *const sizes[2] = {sizes_a, sizes_b};
+    const uint64_t n[2] = {n_a, n_b};
+    bool bad_env = false;
+    const bool validate = env_validate(&bad_env) || (flags & KVCOPY_F_VALIDATE) != 0;
+    if (bad_env)
+        return KVCOPY_EINVAL;
+    if (validate) {   // the overlap rule spans both lists
+        for (int k = 0; k < 2; ++k) {
+            Prescan pre;
+            const int rc = prescan(src[k], dst[k], sizes[k], n[k], KVCOPY_CHUNK_DEFAULT, &pre);
+            if (rc != KVCOPY_OK)
+                return rc;
+        }
+        std::vector<uint64_t> s(src_a, src_a + n_a), d(dst_a, dst_a + n_a), z(sizes_a, sizes_a + n_a);
+        s.insert(s.end(), src_b, src_b + n_b);
+        d.insert(d.end(), dst_b, dst_b + n_b);
+        z.insert(z.end(), sizes_b, sizes_b + n_b);
+        const int rc = check_overlap(s.data(), d.data(), z.data(), n_a + n_b);
+        if (rc != KVCOPY_OK)
+            return rc;
+    }
+    int device = 0;
+    const hipError_t e = hipGetDevice(&device);
+    if (e != hipSuccess) {
+        uint64_t bound = 0, nnz = 0;
+        for (int k = 0; k < 2; ++k) {   // argument errors keep priority over a failing runtime
+            Prescan pre;
+            const int rc = prescan(src[k], dst[k], sizes[k], n[k], KVCOPY_CHUNK_DEFAULT, &pre);
+            if (rc != KVCOPY_OK)
+                return rc;
+            bound += pre.bound;
+            nnz += pre.nnz;
+        }
+        if (bound > KVCOPY_MAX_CHUNKS)
+            return KVCOPY_EINVAL;
+        return nnz == 0 ? KVCOPY_OK : hip_fail(e);
+    }
+    Staging *st = staging_for(device);
+    std::lock_guard<std::mutex> g(st->mu);
+    return run_pair_locked(st, src, dst, sizes, n, !(flags & KVCOPY_F_NO_COALESCE), max_wgs,
+                           stream);
 }
 
 extern "C" uint64_t kvcopy_device_workspace_bytes(uint64_t max_n)

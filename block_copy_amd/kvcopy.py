@@ -32,7 +32,8 @@ EXPORTS = ("kvcopy_coalesce", "kvcopy_plan", "kvcopy_plan_free", "kvcopy_batch",
            "kvcopy_batch_ex", "kvcopy_strerror", "kvcopy_last_hip_error",
            "kvcopy_host_alloc_mapped", "kvcopy_host_free", "kvcopy_job_create",
            "kvcopy_job_poll", "kvcopy_job_wait", "kvcopy_job_destroy",
-           "kvcopy_device_workspace_bytes", "kvcopy_batch_device", "kvcopy_autotune")
+           "kvcopy_device_workspace_bytes", "kvcopy_batch_device", "kvcopy_autotune",
+           "kvcopy_batch_pair")
 DEVICE_BAD_ALIGN, DEVICE_TOO_MANY_CHUNKS = 1, 2
 
 
@@ -80,6 +81,10 @@ def _load():
     lib.kvcopy_batch_ex.restype = ctypes.c_int
     lib.kvcopy_batch_ex.argtypes = [u64p, u64p, u64p, ctypes.c_uint64, ctypes.c_int,
                                     ctypes.c_int, ctypes.c_void_p, ctypes.POINTER(Opts)]
+    lib.kvcopy_batch_pair.restype = ctypes.c_int
+    lib.kvcopy_batch_pair.argtypes = [u64p, u64p, u64p, ctypes.c_uint64, u64p, u64p, u64p,
+                                      ctypes.c_uint64, ctypes.c_int, ctypes.c_uint32,
+                                      ctypes.c_void_p]
     lib.kvcopy_strerror.restype = ctypes.c_char_p
     lib.kvcopy_strerror.argtypes = [ctypes.c_int]
     lib.kvcopy_last_hip_error.restype = ctypes.c_int
@@ -222,6 +227,23 @@ def kvcopy_batch(src_addrs, dst_addrs, sizes, dir: int, max_wgs: int = WGS_ALL,
         rc = lib.kvcopy_batch(sp, dp, zp, n, int(dir), int(max_wgs), st)
     if check and rc != OK:
         raise KvcopyError(rc, "kvcopy_batch")
+    return rc
+
+
+def kvcopy_batch_pair(src_a, dst_a, sizes_a, src_b, dst_b, sizes_b, max_wgs: int = WGS_ALL,
+                      stream=None, *, flags: int = 0, check: bool = True) -> int:
+    """Two descriptor lists in one launch on `stream` (see include/kvcopy.h)."""
+    sa, sap = _u64(src_a)
+    da, dap = _u64(dst_a)
+    za, zap = _u64(sizes_a)
+    sb, sbp = _u64(src_b)
+    db, dbp = _u64(dst_b)
+    zb, zbp = _u64(sizes_b)
+    na, nb = _n(sa, da, za), _n(sb, db, zb)
+    st = ctypes.c_void_p(int(stream) if stream else 0)
+    rc = lib.kvcopy_batch_pair(sap, dap, zap, na, sbp, dbp, zbp, nb, int(max_wgs), int(flags), st)
+    if check and rc != OK:
+        raise KvcopyError(rc, "kvcopy_batch_pair")
     return rc
 
 

@@ -63,7 +63,7 @@ def test_kernels_have_no_scratch_or_spills(K, src):
     names = set(re.findall(r"\.name:\s+_ZN3kvc12_GLOBAL__N_1\d+(kvcopy_\w+?_kernel)E", txt))
     if src == "kvcopy_kernel.hip":
         want = {f"kvcopy_{d}{v}_kernel" for d in ("h2d", "d2h", "d2d")
-                for v in ("", "_pipe", "_dyn", "_inline")}
+                for v in ("", "_pipe", "_dyn", "_inline")} | {"kvcopy_pair_kernel"}
     else:
         want = {"kvcopy_device_plan_kernel", "kvcopy_device_copy_kernel"}
     assert names == want, names
@@ -169,6 +169,34 @@ def test_batch_argument_errors(K):
     assert call(s, dup, z, K.H2D, flags=K.F_VALIDATE) == K.EOVERLAP  # destinations overlap
     over = np.array([0x30000, 0x10800], np.uint64)
     assert call(s, over, z, K.H2D, flags=K.F_VALIDATE) == K.EOVERLAP  # a destination overlaps a source
+
+
+def test_pair_argument_errors(K):
+    """kvcopy_batch_pair checks both lists before anything touches the GPU."""
+    s = np.array([0x10000, 0x20000], np.uint64)
+    d = np.array([0x30000, 0x40000], np.uint64)
+    z = np.array([4096, 4096], np.uint64)
+    s2, d2 = s + 0x100000, d + 0x100000
+    e = np.zeros(0, np.uint64)
+    call = lambda *a, **k: K.kvcopy_batch_pair(*a, check=False, **k)  # noqa: E731
+    assert call(e, e, e, e, e, e) == K.OK                                  # both lists empty
+    assert call(s, d, np.zeros(2, np.uint64), e, e, e) == K.OK             # only zero sizes
+    assert call(s, d, z, s2 + 4, d2, z) == K.EALIGN                        # list b misaligned
+    assert call(s, d, z + 4, s2, d2, z) == K.EALIGN                        # list a size
+    assert call(s, d, z, s2, d2, z, -2) == K.EINVAL                        # max_wgs below AUTO
+    assert call(s, d, z, s2, d2, z, flags=K.F_PIPELINE) == K.EINVAL        # loop flags: not here
+    assert call(s, d, z, s2, d2, z, flags=K.F_DESC_UPLOAD) == K.EINVAL
+    wrap = np.array([2**64 - 4096], np.uint64)
+    assert call(s, d, z, wrap, d2[:1], z[:1]) == K.EINVAL                  # list b wraps
+    # The overlap rule spans both lists (validate mode only).
+    assert call(s, d, z, s2, d, z, flags=K.F_VALIDATE) == K.EOVERLAP       # same destinations
+    assert call(s, d, z, d + 0x800, d2, z, flags=K.F_VALIDATE) == K.EOVERLAP  # b reads a's dst
+    assert call(s, d, z, s2[:1], s[:1], z[:1], flags=K.F_VALIDATE) == K.EOVERLAP  # b writes a's src
+    import ctypes
+    u = ctypes.POINTER(ctypes.c_uint64)()
+    p = s.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64))
+    assert K.lib.kvcopy_batch_pair(p, p, p, 1, u, u, u, 2, 0, 0, None) == K.EINVAL   # null list b
+    assert K.lib.kvcopy_batch_pair(u, u, u, 0, u, u, u, 0, 0, 0, None) == K.OK
 
 
 def test_null_pointers_and_struct_size(K):

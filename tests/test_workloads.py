@@ -50,6 +50,8 @@ def _check_contract(wl):
     lambda: W.irregular(seed=1, n=300),
     lambda: W.irregular(seed=2, n=300, shared_src=True),
     lambda: W.irregular(seed=3, n=300, zero_frac=0.2, misalign=False),
+    lambda: W.combine("pair", W.irregular(seed=4, n=50, dir_=W.H2D, src_where="host"),
+                      W.irregular(seed=5, n=9, dir_=W.D2H, dst_where="host")),
 ])
 def test_generators_respect_contract(make):
     _check_contract(make())
@@ -102,3 +104,18 @@ def test_random_batches_respect_the_contract():
             assert np.all(lo[1:] >= hi[:-1])              # no two ranges overlap
         merged_somewhere |= wl.info["runs"] < b.n
     assert merged_somewhere
+
+
+def test_combine_renumbers_arenas():
+    a = W.irregular(seed=4, n=50, dir_=W.H2D, src_where="host")
+    b = W.kv_blocks(seed=0, directions="both", n=64, pool_blocks=256)
+    c = W.combine("c", a, b)
+    assert len(c.arenas) == len(a.arenas) + len(b.arenas)
+    assert [x.n for x in c.batches] == [50, 64, 64]
+    assert c.batches[0].src_arena.tolist() == a.batches[0].src_arena.tolist()
+    k = len(a.arenas)
+    for bb, cb in zip(b.batches, c.batches[1:]):
+        assert np.array_equal(cb.src_arena, bb.src_arena + k)
+        assert np.array_equal(cb.dst_arena, bb.dst_arena + k)
+        assert np.array_equal(cb.size, bb.size) and cb.dir == bb.dir
+        assert c.arenas[int(cb.dst_arena[0])] is b.arenas[int(bb.dst_arena[0])]

@@ -378,3 +378,20 @@ def random_batch(seed, max_n=3000):
     b = _batch(dir_, 0, s_off, 1, d_off, size)
     return Workload(f"random_{seed}", arenas, [b], {"n": n, "runs": len(runs)})
 
+
+
+def combine(name, *wls):
+    """One workload holding the arenas and batches of several, in order.
+
+    Each input's arena indices are renumbered past the arenas before it, so
+    the batches of different inputs touch disjoint arenas (no overlap across
+    them); used to hand two unrelated lists to one call.
+    """
+    arenas, batches = [], []
+    for wl in wls:
+        base = len(arenas)
+        arenas.extend(wl.arenas)
+        for b in wl.batches:
+            batches.append(Batch(b.dir, b.src_arena + base, b.src_off.copy(), b.dst_arena + base,
+                                 b.dst_off.copy(), b.size.copy()))
+    return Workload(name, arenas, batches, {"parts": [wl.name for wl in wls]})
