@@ -146,6 +146,25 @@ inline bool pipeline_pays(int dir, uint32_t grid, uint64_t n_chunks)
     return dir == 2 /* KVCOPY_D2D */ && grid <= 256u && n_chunks >= 2ull * grid * kWavesPerWG;
 }
 
+// kvcopy_batch_pair: how many of the launch's nw wavefronts copy list a
+// (the rest copy list b), in proportion to the chunk counts ca and cb,
+// rounded to nearest, and at least one for each non-empty list.  nw >= 2
+// whenever both lists are non-empty (a launch has at least 4 wavefronts).
+inline uint32_t pair_split(uint64_t ca, uint64_t cb, uint32_t nw)
+{
+    if (ca == 0)
+        return 0;
+    if (cb == 0)
+        return nw;
+    const double share = (double)nw * (double)ca / ((double)ca + (double)cb);
+    uint64_t wa = (uint64_t)(share + 0.5);
+    if (wa < 1)
+        wa = 1;
+    if (wa > nw - 1u)
+        wa = nw - 1u;
+    return (uint32_t)wa;
+}
+
 // ---- device-resident batches (device_batch.hip) ---------------------------
 
 uint64_t device_workspace_bytes(uint64_t max_n);

@@ -165,8 +165,8 @@ int resolve_auto(const Staging *st, int dir)
 }
 
 // KVCOPY_WGS_AUTO for kvcopy_batch_pair: with 16,384 x 4 KiB each way, one
-// launch measured 95-96 GB/s on MI355X from 48 to 80 workgroups (93 at 32,
-// 91 at 128, 81 on the full grid), so the middle of that plateau.
+// launch measured its best rate on MI355X at 64 workgroups (96.9 GB/s; 93.6
+// at 32, 92.9 at 128, 87.8 at 256).
 constexpr int kPairAutoWgs = 64;
 
 uint32_t grid_for(uint64_t n_chunks, int max_wgs)

@@ -237,15 +237,15 @@ int kvcopy_batch_ex(const uint64_t *src_addrs, const uint64_t *dst_addrs, const 
  *
  * [PF] "Test setup": KV offload traffic arrives as H2D and D2H bursts at the
  * same time.  When both lists are at hand, this call moves them with one
- * kernel whose wavefronts alternate between their shares of the two lists
- * in proportion to the lists' chunk counts, so every wavefront keeps a read
- * burst and a write burst in flight and both directions of the host link
- * stay busy together until the end.  Measured on MI355X with 16,384 x 4 KiB
- * each way: 95-96 GB/s, where the same bursts as two kernels on two streams
- * reach 85-88 GB/s (and less when the two caps differ: the direction with
- * fewer requests in flight loses its share of the link).  The bytes moved
- * are exactly those of kvcopy_batch(a) followed by kvcopy_batch(b) on
- * `stream`.
+ * kernel whose wavefronts are split between the lists in proportion to
+ * their chunk counts, with every workgroup holding wavefronts of both, so
+ * every CU in use carries both directions and both directions of the host
+ * link stay busy together until the end.  Measured on MI355X with 16,384 x
+ * 4 KiB each way: 96-97 GB/s, where the same bursts as two kernels on two
+ * streams reach 85-88 GB/s (and less when the two caps differ: the
+ * direction with fewer requests in flight loses its share of the link).
+ * The bytes moved are exactly those of kvcopy_batch(a) followed by
+ * kvcopy_batch(b) on `stream`.
  *
  * Each list is validated, coalesced and chunked (16 KiB) as by kvcopy_batch;
  * the overlap rule spans both lists (no destination may overlap another
@@ -254,8 +254,8 @@ int kvcopy_batch_ex(const uint64_t *src_addrs, const uint64_t *dst_addrs, const 
  * list may hold any direction; the usual use is H2D in one and D2H in the
  * other.  n_a or n_b may be 0 (both 0: KVCOPY_OK, nothing enqueued).
  * max_wgs as for kvcopy_batch, except that KVCOPY_WGS_AUTO is 64
- * workgroups, the middle of the measured plateau (95-96 GB/s from 48 to 80
- * workgroups for the burst above; 81 GB/s on the full grid).
+ * workgroups, the best measured cap for the burst above (94-97 GB/s from
+ * 32 to 96 workgroups; 81-87 GB/s above 192).
  * flags: KVCOPY_F_VALIDATE and/or KVCOPY_F_NO_COALESCE, as for
  * kvcopy_batch_ex; any other bit is KVCOPY_EINVAL.  Ownership, threads and
  * errors as for kvcopy_batch; an error in either list enqueues nothing.

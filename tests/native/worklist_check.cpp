@@ -124,6 +124,32 @@ int main(int argc, char **argv)
             return 1;
         }
     }
+    // Pair launches: wavefronts for list a in proportion to the chunk counts,
+    // rounded to nearest, at least one for each non-empty list.
+    struct { uint64_t ca, cb; uint32_t nw, want; } sp[] = {
+        {16384, 16384, 256, 128}, {0, 5, 4, 0}, {5, 0, 4, 4}, {1, 100000, 4, 1},
+        {100000, 1, 4, 3}, {3, 1, 256, 192}, {1, 3, 256, 64}, {1, 1, 4, 2}, {1, 2, 4, 1},
+        {2, 1, 4, 3}, {700, 37, 16, 15}, {37, 700, 16, 1}, {0xFFFFFFFFull, 0xFFFFFFFFull, 8, 4},
+    };
+    for (const auto &c : sp) {
+        if (pair_split(c.ca, c.cb, c.nw) != c.want) {
+            printf("pair_split(%llu, %llu, %u) = %u, want %u\n", (unsigned long long)c.ca,
+                   (unsigned long long)c.cb, c.nw, pair_split(c.ca, c.cb, c.nw), c.want);
+            return 1;
+        }
+    }
+    for (uint32_t nw = 4; nw <= 64; nw += 4)   // every split is a valid partition
+        for (uint64_t ca = 0; ca <= 40; ++ca)
+            for (uint64_t cb = ca == 0 ? 1 : 0; cb <= 40; ++cb) {   // both empty: no launch
+                const uint32_t wa = pair_split(ca, cb, nw);
+                const bool ok = wa <= nw && (ca == 0 || wa >= 1) && (cb == 0 || wa <= nw - 1) &&
+                                (ca != 0 || wa == 0) && (cb != 0 || wa == nw);
+                if (!ok) {
+                    printf("pair_split(%llu, %llu, %u) = %u is not a valid split\n",
+                           (unsigned long long)ca, (unsigned long long)cb, nw, wa);
+                    return 1;
+                }
+            }
     printf("ok %d cases\n", cases);
     return 0;
 }
