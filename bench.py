@@ -19,6 +19,7 @@ checked bit-exact against the oracle images of that leg before the line is
 printed.
 
 Other workloads (``--workload``), one JSON line each:
+  pair          the headline burst as one kvcopy_batch_pair call (one launch)
   d2d           1,024 x 4 KiB D2D gather (and 65,536 x 4 KiB) against HBM
   mixed         H2D with mixed 4-28 KiB sizes, N = 16, 256, 4,096, 65,536
   moe           MoE expert gather, 100 seeded calls of 26-39 experts x 6 banks
@@ -54,6 +55,7 @@ REC_BYTES = 24            # one worklist record per chunk
 KERNEL_NAMES = {0: "kvcopy_h2d_kernel", 1: "kvcopy_d2h_kernel", 2: "kvcopy_d2d_kernel"}
 COUNTERS_KV = os.path.join(ROOT, "profiles", "counters_kv_bidirectional.json")
 COUNTERS_D2D = os.path.join(ROOT, "profiles", "counters_d2d_blocks.json")
+COUNTERS_PAIR = os.path.join(ROOT, "profiles", "counters_kv_pair.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "block_copy_amd", "csrc", f)
                   for f in ("kvcopy_kernel.hip", "copy_chunk.h")]
 
@@ -293,7 +295,7 @@ def bench_kv(c: Ctx, args):
     sA, sB = c.sA, c.sB
     step_bytes = wl.nbytes
     n_desc = sum(b.n for b in wl.batches)
-    max_wgs = args.max_wgs
+    max_wgs = args.max_wgs if args.max_wgs is not None else DEFAULT_MAX_WGS
     log(f"headline: {n_desc} descriptors, {step_bytes} B per step, max_wgs={max_wgs}")
     # No HIP event sits between two kernels (events recorded between the
     # kernels perturb how the two streams overlap): one event pair per stream
@@ -354,44 +356,14 @@ def bench_kv(c: Ctx, args):
     c.run_steps(res, [0, 1], [sA, sB], 1, max_wgs)
     torch.cuda.synchronize()
     final = {i: res.image(i) for i in (0, 2)}        # device pool, host D2H destination
-    import oracle
-    imgs = [a.host_image().copy() if a.fill == "random" else np.full(a.nbytes, a.sentinel, np.uint8)
-            for a in wl.arenas]
-    src_snap = {0: imgs[0].copy(), 1: imgs[1]}
-
-    def oracle_step():
-        moved = 0
-        for j in range(2):
-            b = wl.batches[j]
-            s, d = res.addrs[j]
-            si, di = int(b.src_arena[0]), int(b.dst_arena[0])
-            moved += oracle.copy(s, d, b.size, [(res.bases[si], src_snap[si])],
-                                 [(res.bases[di], imgs[di])])
-        return moved
-
-    reps, moved, t0 = 0, 0, time.perf_counter()
-    while True:
-        moved += oracle_step()
-        reps += 1
-        if time.perf_counter() - t0 >= args.cpu_seconds and reps >= 3:
-            break
-    cpu_s = time.perf_counter() - t0
-    cpu_gbs = gbs(moved, cpu_s)
-    log(f"  cpu oracle: {reps} steps in {cpu_s:.2f} s = {cpu_gbs:.2f} GB/s (1 thread)")
-    for i in (0, 2):
-        if not np.array_equal(final[i], imgs[i]):
-            bad = int(np.flatnonzero(final[i] != imgs[i])[0])
-            log(f"PARITY FAILURE in arena {wl.arenas[i].name} at byte {bad}")
-            sys.exit(3)
+    imgs, cpu = kv_oracle(c, wl, res, args)
+    check_kv_images(wl, final, imgs, "")
     if not args.skip_extras:
         # the one-launch call on the same inputs must leave the same images
         res.fill()
-        c.pair_step(res, sA, max_wgs)
+        c.pair_step(res, sA, K.WGS_AUTO)
         torch.cuda.synchronize()
-        for i in (0, 2):
-            if not np.array_equal(res.image(i), imgs[i]):
-                log(f"PARITY FAILURE (one-launch pair) in arena {wl.arenas[i].name}")
-                sys.exit(3)
+        check_kv_images(wl, {i: res.image(i) for i in (0, 2)}, imgs, " (one-launch pair)")
         extras["one_launch_pair"]["parity"] = "bit-exact vs oracle"
     log("  parity: bit-exact against the oracle")
     res.free()
@@ -419,8 +391,130 @@ def bench_kv(c: Ctx, args):
                          "kernel_ms": round(kern_ms[1 - dom], 4)}}
     line["cpu_baseline"] = {
         "value": round(cpu_gbs, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
-        "sample": f"{reps} full steps (16,384 H2D + 16,384 D2H descriptors of 4 KiB each, "
-                  f"per-descriptor memcpy between host images), {cpu_s:.1f} s"}
+        "sample": f"{cpu['reps']} full steps (16,384 H2D + 16,384 D2H descriptors of 4 KiB each, "
+                  f"per-descriptor memcpy between host images), {cpu['seconds']:.1f} s"}
+    line["parity"] = "bit-exact vs oracle"
+    line.update(extras)
+    return line
+
+
+def kv_oracle(c: Ctx, wl, res, args):
+    """The oracle's images of one bidirectional step (arena index -> uint8
+    array), and the oracle timed over whole steps for about args.cpu_seconds
+    on one host thread."""
+    np = c.np
+    import oracle
+    imgs = [a.host_image().copy() if a.fill == "random" else np.full(a.nbytes, a.sentinel, np.uint8)
+            for a in wl.arenas]
+    src_snap = {0: imgs[0].copy(), 1: imgs[1]}
+
+    def oracle_step():
+        moved = 0
+        for j in range(2):
+            b = wl.batches[j]
+            s, d = res.addrs[j]
+            si, di = int(b.src_arena[0]), int(b.dst_arena[0])
+            moved += oracle.copy(s, d, b.size, [(res.bases[si], src_snap[si])],
+                                 [(res.bases[di], imgs[di])])
+        return moved
+
+    reps, moved, t0 = 0, 0, time.perf_counter()
+    while True:
+        moved += oracle_step()
+        reps += 1
+        if time.perf_counter() - t0 >= args.cpu_seconds and reps >= 3:
+            break
+    cpu_s = time.perf_counter() - t0
+    cpu_gbs = gbs(moved, cpu_s)
+    log(f"  cpu oracle: {reps} steps in {cpu_s:.2f} s = {cpu_gbs:.2f} GB/s (1 thread)")
+    return imgs, {"GBps": cpu_gbs, "reps": reps, "seconds": cpu_s}
+
+
+def check_kv_images(wl, final, imgs, what):
+    """Exits with status 3 unless the device pool and the host D2H
+    destination equal the oracle's images."""
+    np = sys.modules["numpy"]
+    for i in (0, 2):
+        if not np.array_equal(final[i], imgs[i]):
+            bad = int(np.flatnonzero(final[i] != imgs[i])[0])
+            log(f"PARITY FAILURE{what} in arena {wl.arenas[i].name} at byte {bad}")
+            sys.exit(3)
+
+
+# ---------------------------------------------------------------------------
+# The headline burst in one launch (kvcopy_batch_pair)
+# ---------------------------------------------------------------------------
+
+def bench_pair(c: Ctx, args):
+    np, torch, W, K, hiprt = c.np, c.torch, c.W, c.K, c.hiprt
+    wl = W.kv_blocks(seed=0, directions="both")
+    res = c.Resident(wl)
+    step_bytes = wl.nbytes
+    g = args.max_wgs if args.max_wgs is not None else K.WGS_AUTO
+    log(f"pair: {sum(b.n for b in wl.batches)} descriptors in one call, max_wgs={g}")
+    for _ in range(args.warmup):
+        c.pair_step(res, c.sA, g)
+    torch.cuda.synchronize()
+    use_ev = not args.no_events
+    e0, e1 = (hiprt.Event(), hiprt.Event()) if use_ev else (None, None)
+    with no_gc():
+        t0 = time.perf_counter()
+        if use_ev:
+            e0.record(c.sA)
+        for _ in range(args.steps):
+            c.pair_step(res, c.sA, g)
+        if use_ev:
+            e1.record(c.sA)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    step_s = (t1 - t0) / args.steps
+    # The launches run back to back on one stream: the event pair around
+    # them, divided by the steps, is the mean kernel duration.
+    kern_ms = e0.elapsed_ms(e1) / args.steps if use_ev else step_s * 1e3
+    value = gbs(step_bytes, step_s)
+    log(f"  one launch: {step_s * 1e3:.3f} ms/step, {value:.2f} GB/s; kernel {kern_ms:.4f} ms")
+    chunks = sum(K.kvcopy_plan(*res.addrs[j], wl.batches[j].size).n_chunks for j in range(2))
+    alg_fetch = step_bytes + chunks * REC_BYTES       # both payloads read + the worklist records
+    alg_write = step_bytes
+    ach = gbs(alg_fetch, kern_ms / 1e3)   # bytes over the host link: payload both ways + records
+    extras = {}
+    if not args.skip_extras:
+        # the two-stream submission of the same burst first: it also brings
+        # both streams into use before the contiguous ceilings are taken on them
+        extras["two_streams_same_run_GBps"] = round(gbs(step_bytes, c.timed_bracketed(
+            res, [0, 1], [c.sA, c.sB], args.steps, args.warmup, DEFAULT_MAX_WGS)[0]), 3)
+        extras["contiguous_memcpy_ceiling_GBps"] = ceilings(c)
+        log(f"  ceilings {extras['contiguous_memcpy_ceiling_GBps']}, two streams at "
+            f"{DEFAULT_MAX_WGS}: {extras['two_streams_same_run_GBps']} GB/s")
+    if args.counter_calibration:
+        counter_calibration(c)
+    res.fill()
+    c.pair_step(res, c.sA, g)
+    torch.cuda.synchronize()
+    final = {i: res.image(i) for i in (0, 2)}
+    imgs, cpu = kv_oracle(c, wl, res, args)
+    check_kv_images(wl, final, imgs, " (one launch)")
+    log("  parity: bit-exact against the oracle")
+    res.free()
+    meas_ceil = extras.get("contiguous_memcpy_ceiling_GBps", {}).get("both")
+    line = base_line(args, round(value, 3), "GB/s", step_s, {
+        "workload": "bidirectional KV block burst in one launch: 16,384 shuffled 4 KiB H2D + "
+                    "16,384 shuffled 4 KiB D2H per step as one kvcopy_batch_pair call on one "
+                    "stream, 65,536-block device pool, mapped pinned host buffers",
+        "descriptors_per_step": sum(b.n for b in wl.batches), "bytes_per_step": step_bytes,
+        "max_wgs": g, "chunk_bytes": K.CHUNK_DEFAULT, "seed": 0})
+    line["roofline"] = {
+        "bound": "pcie", "kernel": "kvcopy_pair_kernel", "achieved": round(ach, 3),
+        "peak": 2 * PCIE_PEAK_GBS, "unit": "GB/s", "frac": round(ach / (2 * PCIE_PEAK_GBS), 4),
+        "traffic": measured_traffic("kvcopy_pair_kernel", COUNTERS_PAIR, alg_fetch, alg_write),
+        "kernel_ms": round(kern_ms, 4), "algorithmic_bytes_per_launch": alg_fetch,
+        "peak_note": "both directions of PCIe 5.0 x16 (64 GB/s each)",
+        "measured_ceiling": meas_ceil,
+        "frac_of_measured_ceiling": round(ach / meas_ceil, 4) if meas_ceil else None}
+    line["cpu_baseline"] = {
+        "value": round(cpu["GBps"], 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+        "sample": f"{cpu['reps']} full steps (16,384 H2D + 16,384 D2H descriptors of 4 KiB each, "
+                  f"per-descriptor memcpy between host images), {cpu['seconds']:.1f} s"}
     line["parity"] = "bit-exact vs oracle"
     line.update(extras)
     return line
@@ -656,6 +750,7 @@ def bench_d2d(c: Ctx, args):
 
 def bench_mixed(c: Ctx, args):
     W, K, hiprt = c.W, c.K, c.hiprt
+    g = args.max_wgs if args.max_wgs is not None else DEFAULT_MAX_WGS
     rows = {}
     for n in (16, 256, 4096, 65536):
         wl = W.h2d_mixed(seed=0, n=n)
@@ -663,9 +758,9 @@ def bench_mixed(c: Ctx, args):
         b = wl.batches[0]
         pl = K.kvcopy_plan(*r.addrs[0], b.size)
         k = max(5, min(args.steps * 5, 200 if n <= 256 else args.steps))
-        s, _ = c.timed_bracketed(r, [0], [c.sA], k, args.warmup, args.max_wgs)
-        _, km = c.timed(r, [0], [c.sA], k, 2, args.max_wgs)
-        lat = c.latency(r, 0, args.max_wgs, k=50 if n <= 4096 else 10, w=5)
+        s, _ = c.timed_bracketed(r, [0], [c.sA], k, args.warmup, g)
+        _, km = c.timed(r, [0], [c.sA], k, 2, g)
+        lat = c.latency(r, 0, g, k=50 if n <= 4096 else 10, w=5)
         c.verify(wl, r, [0], f"mixed {n}")       # before the DMA baselines write the same bytes
         dma = dma_baselines(c, pl, b.nbytes, hiprt.H2D_KIND, reps=2 if n <= 4096 else 1)
         rows[str(n)] = {"bytes": b.nbytes, "merged": int(pl.n_merged), "chunks": int(pl.n_chunks),
@@ -679,7 +774,7 @@ def bench_mixed(c: Ctx, args):
         "workload": "H2D with mixed sizes (70% in 8-16 KiB, rest 4-8 and 16-28 KiB, 8-byte "
                     "multiples), 25% of descriptors adjacent in both arenas, N = 16 .. 65,536; "
                     "value at N = 65,536",
-        "max_wgs": args.max_wgs, "chunk_bytes": K.CHUNK_DEFAULT, "seed": 0})
+        "max_wgs": g, "chunk_bytes": K.CHUNK_DEFAULT, "seed": 0})
     line["per_n"] = rows
     line["parity"] = "bit-exact vs oracle"
     return line
@@ -967,8 +1062,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--max-wgs", type=int, default=DEFAULT_MAX_WGS)
-    ap.add_argument("--workload", default="kv", choices=["kv", "d2d", "mixed", "moe", "interference"])
+    ap.add_argument("--max-wgs", type=int, default=None,
+                    help=f"workgroup cap (default {DEFAULT_MAX_WGS}; pair: KVCOPY_WGS_AUTO)")
+    ap.add_argument("--workload", default="kv", choices=["kv", "pair", "d2d", "mixed", "moe",
+                                                         "interference"])
     ap.add_argument("--sweep", action="store_true", help="also sweep max_wgs per direction (stderr)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="time budget of the cpu_baseline sample")
@@ -992,7 +1089,7 @@ def main():
               "(the sharding plan is in DESIGN.md); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     c = Ctx(args)
-    fn = {"kv": bench_kv, "d2d": bench_d2d, "mixed": bench_mixed, "moe": bench_moe,
+    fn = {"kv": bench_kv, "pair": bench_pair, "d2d": bench_d2d, "mixed": bench_mixed, "moe": bench_moe,
           "interference": bench_interference}[args.workload]
     line = fn(c, args)
     print(json.dumps(line), flush=True)
