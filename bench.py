@@ -390,7 +390,8 @@ def bench_kv(c: Ctx, args):
         "other_kernel": {"kernel": KERNEL_NAMES[1 - dom], "achieved": round(ach[1 - dom], 3),
                          "kernel_ms": round(kern_ms[1 - dom], 4)}}
     line["cpu_baseline"] = {
-        "value": round(cpu_gbs, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+        "value": round(cpu["GBps"], 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+        "cpu": cpu_model(),
         "sample": f"{cpu['reps']} full steps (16,384 H2D + 16,384 D2H descriptors of 4 KiB each, "
                   f"per-descriptor memcpy between host images), {cpu['seconds']:.1f} s"}
     line["parity"] = "bit-exact vs oracle"
@@ -428,6 +429,18 @@ def kv_oracle(c: Ctx, wl, res, args):
     cpu_gbs = gbs(moved, cpu_s)
     log(f"  cpu oracle: {reps} steps in {cpu_s:.2f} s = {cpu_gbs:.2f} GB/s (1 thread)")
     return imgs, {"GBps": cpu_gbs, "reps": reps, "seconds": cpu_s}
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (for the cpu_baseline record)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def check_kv_images(wl, final, imgs, what):
@@ -513,6 +526,7 @@ def bench_pair(c: Ctx, args):
         "frac_of_measured_ceiling": round(ach / meas_ceil, 4) if meas_ceil else None}
     line["cpu_baseline"] = {
         "value": round(cpu["GBps"], 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+        "cpu": cpu_model(),
         "sample": f"{cpu['reps']} full steps (16,384 H2D + 16,384 D2H descriptors of 4 KiB each, "
                   f"per-descriptor memcpy between host images), {cpu['seconds']:.1f} s"}
     line["parity"] = "bit-exact vs oracle"
