@@ -674,9 +674,11 @@ def d2d_results(c: Ctx, args):
                      "frac_hbm_peak_kernel": round(gbs(hbm, km[0] / 1e3) / HBM_PEAK_GBS, 4),
                      "latency": c.latency(r, 0, 0, k=200 if name == "1024x4KiB" else 50,
                                           w=20 if name == "1024x4KiB" else 5)}
-        if name == "1024x4KiB":
-            out[name]["mall_flushed"] = d2d_flushed(c, r, k=max(20, args.steps))
+        out[name]["mall_flushed"] = d2d_flushed(c, r, k=max(20, args.steps))
         c.verify(wld, r, [0], f"d2d {name}")
+        if name == "65536x4KiB":
+            out[name]["note"] = ("kernel_us: the same call repeated, so most of its 256 MiB of "
+                                 "sources stay in the 256 MB MALL between calls")
         if name == "1024x4KiB":     # after the check: the DMA baselines write the same bytes
             out[name]["dma_baselines"] = dma_baselines(c, pl, wld.batches[0].nbytes,
                                                        hiprt.D2D_KIND, reps=5)
@@ -700,25 +702,51 @@ def d2d_results(c: Ctx, args):
             e2.record(c.sA)
             ms.append(e1.elapsed_ms(e2))
         cont[f"{nbytes >> 20}MiB"] = round(gbs(2 * nbytes, statistics.median(ms) / 1e3), 1)
-    del big
     out["contiguous_memcpy_hbm_GBps"] = cont
     log(f"  contiguous D2D hipMemcpyAsync (HBM GB/s): {cont}")
+    if not args.no_events:
+        # the same kernel on one contiguous range (chunked into 16 KiB pieces):
+        # what scatter/gather costs against a plain copy of the same bytes
+        # (1 GiB also with 2 KiB chunks and the worklist uploaded first, the
+        # fastest contiguous copy measured with this kernel: more, shorter
+        # wavefronts, and 512 Ki records read from HBM instead of the host link)
+        kc = {}
+        for key, nbytes, chunk, flags in (("256MiB", 256 << 20, 0, 0), ("1024MiB", 1 << 30, 0, 0),
+                                          ("1024MiB_chunk2KiB_uploaded", 1 << 30, 2048,
+                                           K.F_DESC_UPLOAD)):
+            s_ = c.np.array([big.data_ptr()], c.np.uint64)
+            d_ = c.np.array([big.data_ptr() + (1 << 30)], c.np.uint64)
+            z_ = c.np.array([nbytes], c.np.uint64)
+            ev = (hiprt.Event(), hiprt.Event())
+            ms = []
+            for i in range(8):
+                K.kvcopy_batch(s_, d_, z_, K.D2D, 0, c.sA.cuda_stream, chunk_bytes=chunk,
+                               flags=flags, kernel_begin=ev[0].h, kernel_end=ev[1].h)
+                if i >= 2:
+                    ms.append(ev[0].elapsed_ms(ev[1]))
+            kc[key] = round(gbs(2 * nbytes, statistics.median(ms) / 1e3), 1)
+        out["kernel_one_contiguous_range_hbm_GBps"] = kc
+        log(f"  the kernel on one contiguous range (HBM GB/s): {kc}")
+    del big
+    out["65536x4KiB"]["distinct_calls"] = d2d_distinct(c, args)
     return out
 
 
 def d2d_flushed(c: Ctx, r, k=20):
-    """The 1,024 x 4 KiB gather with the 256 MB MALL (Infinity Cache) flushed
-    before every call: a 512 MiB scrub kernel runs on the same stream first,
-    outside the kernel's own start/end events.  Returns the median kernel
-    time and the HBM rate it implies, and the per-call GPU time."""
+    """The gather with the 256 MB MALL (Infinity Cache) holding none of its
+    bytes: a kernel that reads 512 MiB of other memory runs on the same stream
+    before every call, outside the kernel's own start/end events.  The scrub
+    only reads, so it leaves no dirty lines whose write-back would land inside
+    the timed kernel.  Returns the median kernel time and the HBM rate it
+    implies, and the per-call GPU time."""
     torch, hiprt = c.torch, c.hiprt
     if c.args.no_events:
         return None
-    scrub = torch.zeros(512 << 20, dtype=torch.uint8, device=c.dev)
+    scrub = torch.zeros(512 << 20, dtype=torch.uint8, device=c.dev).view(torch.int32)
     kern, call = [], []
     with torch.cuda.stream(c.sA):
         for i in range(k + 3):
-            scrub.add_(1)
+            scrub.max()
             e0, e1, k0, k1 = hiprt.Event(), hiprt.Event(), hiprt.Event(), hiprt.Event()
             e0.record(c.sA)
             r.submit(0, 0, c.sA, kernel_begin=k0.h, kernel_end=k1.h)
@@ -732,7 +760,43 @@ def d2d_flushed(c: Ctx, r, k=20):
     kt = statistics.median(kern)
     return {"kernel_us_p50": round(kt, 2), "hbm_GBps_kernel": round(gbs(2 * nbytes, kt / 1e6), 1),
             "gpu_us_p50": round(statistics.median(call), 2), "calls": k,
-            "scrub": "512 MiB written on the same stream before each call"}
+            "scrub": "512 MiB read on the same stream before each call"}
+
+
+def d2d_distinct(c: Ctx, args):
+    """65,536 x 4 KiB D2D calls that cycle through 8 different batches over the
+    same two 1 GiB pools (W.d2d_rotation), so that each call's bytes are
+    mostly not in the MALL and the write-backs of earlier calls land in later
+    ones, as in a long run of distinct calls.  Kernel-only time from each
+    kernel's own events; the final images are checked against the oracle
+    applying the 8 batches in order."""
+    torch, hiprt, W = c.torch, c.hiprt, c.W
+    if args.no_events:
+        return None
+    wl = W.d2d_rotation()
+    r = c.Resident(wl)
+    nb = len(wl.batches)
+    calls = max(4 * nb, args.steps)
+    evs = [(hiprt.Event(), hiprt.Event()) for _ in range(calls)]
+    for i in range(nb):
+        r.submit(i, 0, c.sA)
+    for i in range(calls):
+        r.submit(i % nb, 0, c.sA, kernel_begin=evs[i][0].h, kernel_end=evs[i][1].h)
+    hiprt.stream_sync(c.sA)
+    us = statistics.median(e0.elapsed_ms(e1) * 1e3 for e0, e1 in evs)
+    pl = c.K.kvcopy_plan(*r.addrs[0], wl.batches[0].size)
+    hbm = 2 * wl.batches[0].nbytes + pl.n_chunks * REC_BYTES
+    r.fill()
+    for i in range(nb):
+        r.submit(i, 0, c.sA)
+    hiprt.stream_sync(c.sA)
+    c.verify(wl, r, list(range(nb)), "d2d distinct calls")
+    r.free()
+    out = {"batches": nb, "calls": calls, "kernel_us_p50": round(us, 2),
+           "hbm_GBps_kernel": round(gbs(hbm, us / 1e6), 1),
+           "frac_hbm_peak_kernel": round(gbs(hbm, us / 1e6) / HBM_PEAK_GBS, 4)}
+    log(f"  d2d distinct calls: {out} (bit-exact)")
+    return out
 
 
 def bench_d2d(c: Ctx, args):
@@ -745,14 +809,28 @@ def bench_d2d(c: Ctx, args):
                     "also 65,536 x 4 KiB between two 1 GiB pools",
         "max_wgs": 0, "chunk_bytes": c.K.CHUNK_DEFAULT, "seed": 0})
     big = res["65536x4KiB"]
+    dist = big.get("distinct_calls")
+    # The roofline is taken on calls over distinct blocks: repeating one call
+    # lets the MALL serve most of its sources.  The practical ceiling is a
+    # contiguous copy with a 2 GiB footprint (beyond the MALL), by DMA or by
+    # this kernel on one range.
+    kc = res.get("kernel_one_contiguous_range_hbm_GBps", {})
+    ceil = max(res["contiguous_memcpy_hbm_GBps"]["1024MiB"], kc.get("1024MiB", 0.0),
+               kc.get("1024MiB_chunk2KiB_uploaded", 0.0))
+    ach = dist["hbm_GBps_kernel"] if dist else big["hbm_GBps_kernel"]
     line["roofline"] = {"bound": "hbm", "kernel": KERNEL_NAMES[2],
-                        "achieved": big["hbm_GBps_kernel"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                        "frac": big["frac_hbm_peak_kernel"],
+                        "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(ach / HBM_PEAK_GBS, 4),
                         "traffic": measured_traffic(KERNEL_NAMES[2], COUNTERS_D2D,
                                                     big["payload_bytes"] + big["records"] * REC_BYTES,
                                                     big["payload_bytes"]),
-                        "workload_of_roofline": "65536x4KiB",
-                        "measured_ceiling": res["contiguous_memcpy_hbm_GBps"]["256MiB"]}
+                        "workload_of_roofline": "65536x4KiB, calls cycling over 8 distinct batches"
+                                                if dist else "65536x4KiB, one call repeated",
+                        "achieved_one_call_repeated": big["hbm_GBps_kernel"],
+                        "measured_ceiling": ceil,
+                        "measured_ceiling_what": "contiguous 1 GiB D2D copy (2 GiB footprint): the "
+                                                 "best of hipMemcpyAsync and this kernel on one range",
+                        "frac_of_measured_ceiling": round(ach / ceil, 4) if ceil else None}
     line["d2d"] = res
     line["parity"] = "bit-exact vs oracle"
     return line

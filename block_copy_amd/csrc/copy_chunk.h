@@ -16,10 +16,12 @@ typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 constexpr int kRsrcWord3 = 0x00020000;
 // Cache policy: loads plain, stores nontemporal ("nt", bit 1 of the
 // cache-policy operand on gfx940+).  Measured on MI355X for 65,536 random
-// 4 KiB blocks between two 1 GiB device pools: plain loads with nt stores
-// move 6.4-6.5 TB/s of HBM traffic, against 4.8-4.9 TB/s with nt on both
-// sides or on neither (and 5.3 TB/s for one contiguous hipMemcpy).  For
-// mapped host memory the four combinations are within noise of each other.
+// 4 KiB blocks between two 1 GiB device pools: with one call repeated, plain
+// loads with nt stores move 6.1-6.5 TB/s of HBM traffic (the memory-side
+// cache keeps most sources), against 4.7-4.9 TB/s with nt on both sides or
+// on neither; with calls cycling over 8 different batches every combination
+// tried lands at 4.7-5.0 TB/s and this one at the top.  For mapped host
+// memory the combinations are within noise of each other.
 constexpr int kLoadPolicy = 0;
 constexpr int kStorePolicy = 2;
 constexpr uint32_t kRowBytes = 64u * 16u;          // one wavefront instruction: 1 KiB

@@ -50,6 +50,7 @@ def _check_contract(wl):
     lambda: W.irregular(seed=1, n=300),
     lambda: W.irregular(seed=2, n=300, shared_src=True),
     lambda: W.irregular(seed=3, n=300, zero_frac=0.2, misalign=False),
+    lambda: W.d2d_rotation(seeds=(1, 2, 3), n=512, pool_blocks=2048),
     lambda: W.combine("pair", W.irregular(seed=4, n=50, dir_=W.H2D, src_where="host"),
                       W.irregular(seed=5, n=9, dir_=W.D2H, dst_where="host")),
 ])
@@ -119,3 +120,12 @@ def test_combine_renumbers_arenas():
         assert np.array_equal(cb.dst_arena, bb.dst_arena + k)
         assert np.array_equal(cb.size, bb.size) and cb.dir == bb.dir
         assert c.arenas[int(cb.dst_arena[0])] is b.arenas[int(bb.dst_arena[0])]
+
+
+def test_d2d_rotation_shares_pools():
+    r = W.d2d_rotation(seeds=(1, 2, 3), n=256, pool_blocks=1024)
+    assert len(r.arenas) == 2 and len(r.batches) == 3 and r.info["sequential"]
+    for sd, b in zip((1, 2, 3), r.batches):
+        one = W.d2d_blocks(sd, 256, 1024).batches[0]
+        assert np.array_equal(b.src_off, one.src_off) and np.array_equal(b.dst_off, one.dst_off)
+    assert r.arenas[0].seed == W.d2d_blocks(1, 256, 1024).arenas[0].seed

@@ -118,6 +118,22 @@ def d2d_blocks(seed=0, n=1024, pool_blocks=4096, block=4 * KIB, sentinel=SENTINE
                     {"n": n, "block": block, "pool_blocks": pool_blocks})
 
 
+def d2d_rotation(seeds=tuple(range(1, 9)), n=65536, pool_blocks=262144, block=4 * KIB,
+                 sentinel=SENTINEL_A):
+    """Several D2D batches over the same two pools, applied one after another:
+    batch k draws its n source and n destination blocks as d2d_blocks(seeds[k])
+    does, and the pools are those of d2d_blocks(seeds[0]).  Calls that cycle
+    through the batches touch up to len(seeds) times the blocks of one batch,
+    so a later call finds little of an earlier call's data in the caches.
+    Destinations of different batches may coincide (the batches are
+    sequential: a later batch's bytes win)."""
+    first = d2d_blocks(seeds[0], n, pool_blocks, block, sentinel)
+    batches = [d2d_blocks(sd, n, pool_blocks, block, sentinel).batches[0] for sd in seeds]
+    return Workload(f"d2d_rotation_{len(seeds)}x{n}x{block // KIB}KiB", first.arenas, batches,
+                    {"n": n, "block": block, "pool_blocks": pool_blocks, "seeds": list(seeds),
+                     "sequential": True})
+
+
 def distinct_calls(seed=0, calls=300, n=8192, block=64, src_blocks=65536, sentinel=SENTINEL_A):
     """`calls` D2D batches of n blocks each, every batch writing its own
     destination blocks: batch i scatters n seeded random source blocks (drawn
