@@ -63,8 +63,16 @@ int prescan(const uint64_t *src, const uint64_t *dst, const uint64_t *size, uint
 // of records the batch needs, which may exceed cap: then only the first cap
 // were written, and the caller plans again with room for *n_chunks.  The
 // records are exactly those emit_chunks() gives for merge_ranges()'s output.
+// With `stream`, the records are written with non-temporal stores (for the
+// pinned staging ring, which only the GPU reads): call finish_records()
+// before anything that hands them to the GPU.
 int build_checked(const uint64_t *src, const uint64_t *dst, const uint64_t *size, uint64_t n,
-                  bool merge, uint32_t chunk, ChunkRec *out, uint64_t cap, uint64_t *n_chunks);
+                  bool merge, uint32_t chunk, ChunkRec *out, uint64_t cap, uint64_t *n_chunks,
+                  bool stream = false);
+
+// Orders every record streamed so far before the caller's later stores (the
+// kernel launch's queue packet among them).
+void finish_records();
 
 // build_checked without the checks' result and without a cap (room for
 // Prescan::bound records); returns how many records it wrote.

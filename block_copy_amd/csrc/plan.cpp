@@ -16,6 +16,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <immintrin.h>
+
 #include <algorithm>
 #include <vector>
 
@@ -114,15 +116,39 @@ int prescan(const uint64_t *src, const uint64_t *dst, const uint64_t *size, uint
     return KVCOPY_OK;
 }
 
-int build_checked(const uint64_t *src, const uint64_t *dst, const uint64_t *size, uint64_t n,
-                  bool merge, uint32_t chunk, ChunkRec *out, uint64_t cap, uint64_t *n_chunks)
+namespace {
+
+// One record, written either through the cache or with non-temporal 8-byte
+// stores (three per record).  Records bound for the pinned staging ring are
+// streamed: the GPU reads them over the host link and the CPU never reads
+// them back, so taking each ring line into the cache first (the
+// read-for-ownership of a plain store) only costs memory traffic.  Planning
+// 65,536 descriptors took 91 -> 85 us per call on an MI355X server's host
+// (and 250 -> 125 us on a smaller EPYC host).  The caller orders the
+// streamed stores before the launch (finish_records).
+template <bool Stream>
+inline void put_rec(ChunkRec *r, uint64_t s, uint64_t d, uint32_t bytes)
+{
+    if (Stream) {
+        long long *p = reinterpret_cast<long long *>(r);
+        _mm_stream_si64(p, (long long)s);
+        _mm_stream_si64(p + 1, (long long)d);
+        _mm_stream_si64(p + 2, (long long)bytes);   // bytes, then reserved = 0
+    } else {
+        *r = ChunkRec{s, d, bytes, 0};
+    }
+}
+
+template <bool Stream>
+int build_checked_impl(const uint64_t *src, const uint64_t *dst, const uint64_t *size, uint64_t n,
+                       bool merge, uint32_t chunk, ChunkRec *out, uint64_t cap, uint64_t *n_chunks)
 {
     uint64_t bits = 0, bad = 0, total = 0, w = 0;
     uint64_t cs = 0, cd = 0, cn = 0;   // the open range
     auto close = [&]() {
         if (cn <= chunk) {   // the common case: one chunk per range
             if (w < cap)
-                out[w] = ChunkRec{cs, cd, (uint32_t)cn, 0};
+                put_rec<Stream>(out + w, cs, cd, (uint32_t)cn);
             ++w;
             return;
         }
@@ -134,7 +160,8 @@ int build_checked(const uint64_t *src, const uint64_t *dst, const uint64_t *size
         const uint64_t put = k < room ? k : room;
         for (uint64_t j = 0; j < put; ++j) {
             const uint64_t off = j * chunk, left = cn - off;
-            out[w + j] = ChunkRec{cs + off, cd + off, (uint32_t)(left < chunk ? left : chunk), 0};
+            put_rec<Stream>(out + w + j, cs + off, cd + off,
+                            (uint32_t)(left < chunk ? left : chunk));
         }
         w += k;
     };
@@ -164,6 +191,21 @@ int build_checked(const uint64_t *src, const uint64_t *dst, const uint64_t *size
         return KVCOPY_EINVAL;
     *n_chunks = w;
     return KVCOPY_OK;
+}
+
+}  // namespace
+
+int build_checked(const uint64_t *src, const uint64_t *dst, const uint64_t *size, uint64_t n,
+                  bool merge, uint32_t chunk, ChunkRec *out, uint64_t cap, uint64_t *n_chunks,
+                  bool stream)
+{
+    return stream ? build_checked_impl<true>(src, dst, size, n, merge, chunk, out, cap, n_chunks)
+                  : build_checked_impl<false>(src, dst, size, n, merge, chunk, out, cap, n_chunks);
+}
+
+void finish_records()
+{
+    _mm_sfence();
 }
 
 uint64_t build_worklist(const uint64_t *src, const uint64_t *dst, const uint64_t *size, uint64_t n,

@@ -210,8 +210,8 @@ int run_locked(Staging *st, const uint64_t *src, const uint64_t *dst, const uint
         if ((rc = st->ring.reserve(need, &off)) != KVCOPY_OK)
             return rc;
         host = reinterpret_cast<ChunkRec *>(st->host + off);
-        if ((rc = build_checked(src, dst, sizes, n, merge, chunk, host, room, &n_chunks)) !=
-            KVCOPY_OK)
+        if ((rc = build_checked(src, dst, sizes, n, merge, chunk, host, room, &n_chunks,
+                                true)) != KVCOPY_OK)
             return rc;   // nothing committed: the region stays free
         if (n_chunks == 0)
             return KVCOPY_OK;   // only zero-size descriptors: nothing to enqueue
@@ -222,6 +222,7 @@ int run_locked(Staging *st, const uint64_t *src, const uint64_t *dst, const uint
         hint = n_chunks;   // plan again into a region of the exact size
     }
     const uint64_t used = (n_chunks * sizeof(ChunkRec) + kAlign - 1) / kAlign * kAlign;
+    finish_records();   // the streamed records reach memory before the launch is queued
 
     const ChunkRec *recs = host;   // read in place: mapped at the same address on the device
     hipError_t e;
@@ -323,11 +324,11 @@ int run_pair_locked(Staging *st, const uint64_t *const src[2], const uint64_t *c
             return rc;
         host = reinterpret_cast<ChunkRec *>(st->host + off);
         if ((rc = build_checked(src[0], dst[0], sizes[0], n[0], merge, KVCOPY_CHUNK_DEFAULT, host,
-                                room, &cnt[0])) != KVCOPY_OK)
+                                room, &cnt[0], true)) != KVCOPY_OK)
             return rc;   // nothing committed: the region stays free
         const uint64_t room_b = cnt[0] <= room ? room - cnt[0] : 0;
         if ((rc = build_checked(src[1], dst[1], sizes[1], n[1], merge, KVCOPY_CHUNK_DEFAULT,
-                                host + (cnt[0] <= room ? cnt[0] : 0), room_b, &cnt[1])) != KVCOPY_OK)
+                                host + (cnt[0] <= room ? cnt[0] : 0), room_b, &cnt[1], true)) != KVCOPY_OK)
             return rc;
         if (cnt[0] + cnt[1] > KVCOPY_MAX_CHUNKS)
             return KVCOPY_EINVAL;
@@ -339,6 +340,7 @@ int run_pair_locked(Staging *st, const uint64_t *const src[2], const uint64_t *c
     const uint64_t total = cnt[0] + cnt[1];
     if (total == 0)
         return KVCOPY_OK;   // only zero-size descriptors: nothing to enqueue
+    finish_records();   // the streamed records reach memory before the launch is queued
     const uint64_t used = (total * sizeof(ChunkRec) + kAlign - 1) / kAlign * kAlign;
     if (max_wgs == KVCOPY_WGS_AUTO)
         max_wgs = kPairAutoWgs;

@@ -15,7 +15,7 @@ using namespace kvc;
 
 int main(int argc, char **argv)
 {
-    const int trials = argc > 1 ? atoi(argv[1]) : 3000;   // fewer under the sanitizers
+    const int trials = argc > 1 ? atoi(argv[1]) : 1500;   // fewer under the sanitizers
     std::mt19937_64 rng(12345);
     const uint32_t chunks[] = {16, 64, 4096, 16384, 65536};
     int cases = 0;
@@ -58,19 +58,32 @@ int main(int argc, char **argv)
                        (unsigned long)pre.bound);
                 return 1;
             }
-            // The checked pass with a short room: same count, same prefix.
-            for (uint64_t cap : {(uint64_t)0, c / 2, c, c + 3}) {
+            // The checked pass with a short room: same count, same prefix,
+            // with plain and with streamed stores.
+            for (uint64_t cap : {(uint64_t)0, c / 2, c, c + 3})
+            for (bool streamed : {false, true}) {
                 std::vector<ChunkRec> part(cap + 1);
+                memset(part.data(), 0xA5, part.size() * sizeof(ChunkRec));
                 uint64_t need = ~0ull;
                 const int rc = build_checked(s.data(), d.data(), z.data(), n, merge, chunk,
-                                             part.data(), cap, &need);
+                                             part.data(), cap, &need, streamed);
+                finish_records();
                 const uint64_t wrote = cap < c ? cap : c;
                 if (rc != KVCOPY_OK || need != c ||
                     (wrote && memcmp(ref.data(), part.data(), wrote * sizeof(ChunkRec)) != 0)) {
-                    printf("build_checked: trial %d cap %lu: rc %d need %lu want %lu\n", trial,
-                           (unsigned long)cap, rc, (unsigned long)need, (unsigned long)c);
+                    printf("build_checked: trial %d cap %lu streamed %d: rc %d need %lu want %lu\n",
+                           trial, (unsigned long)cap, (int)streamed, rc, (unsigned long)need,
+                           (unsigned long)c);
                     return 1;
                 }
+                // nothing written past the room
+                const unsigned char *tail = reinterpret_cast<const unsigned char *>(part.data() + wrote);
+                for (size_t b = 0; b < (part.size() - wrote) * sizeof(ChunkRec); ++b)
+                    if (tail[b] != 0xA5) {
+                        printf("build_checked: trial %d cap %lu streamed %d wrote past its room\n",
+                               trial, (unsigned long)cap, (int)streamed);
+                        return 1;
+                    }
             }
             ++cases;
         }

@@ -27,7 +27,7 @@ def test_planner_under_sanitizers(tmp_path):
                     "-I" + os.path.join(ROOT, "include"), "-I" + csrc,
                     os.path.join(ROOT, "tests", "native", "worklist_check.cpp"),
                     os.path.join(csrc, "plan.cpp"), "-o", str(exe)], check=True)
-    out = subprocess.run([str(exe), "400"], capture_output=True, text=True)
+    out = subprocess.run([str(exe), "250"], capture_output=True, text=True)
     assert out.returncode == 0, out.stdout + out.stderr
 
 
