@@ -23,7 +23,7 @@ constexpr uint64_t kBlock = 4096;
 constexpr uint64_t kBytes = kBlocks * kBlock;   // 32 MiB per direction
 constexpr int kWarm = 2;                         // untimed batches per cap
 constexpr int kReps = 6;                         // timed batches per cap
-constexpr int kSweeps = 2;                       // ascending, then descending
+constexpr int kSweeps = 3;                       // ascending, descending, ascending
 const int kCaps[KVCOPY_AUTOTUNE_NCAPS] = KVCOPY_AUTOTUNE_CAPS;
 
 uint64_t splitmix(uint64_t &s)
@@ -119,14 +119,17 @@ extern "C" int kvcopy_autotune(int dir, hipStream_t s0, hipStream_t s1, int *out
                 std::vector<uint64_t>(kBlocks, kBlock), KVCOPY_D2H};
     }
 
-    // Each cap is timed in two sweeps (ascending, then descending) and keeps
-    // its better rate, so one slow window (a fresh stream's first batches,
-    // say) cannot decide the choice.
-    double rate[KVCOPY_AUTOTUNE_NCAPS] = {};
-    double best = 0;
+    // Each cap is timed in three sweeps (ascending, descending, ascending)
+    // and keeps its median rate: neither one slow window (a fresh stream's
+    // first batches, say) nor one lucky window decides.  Two kernels on two
+    // streams can fall into a state where one direction starves the other;
+    // measured on MI355X, a cap of 32 per direction gave 83 GB/s in its best
+    // windows but 72 in a typical one, which the better of two windows hid.
+    double rates[KVCOPY_AUTOTUNE_NCAPS][kSweeps] = {};
     const int ncaps = (int)(sizeof(kCaps) / sizeof(kCaps[0]));
     for (int k = 0; k < kSweeps * ncaps; ++k) {
-        const int c = k < ncaps ? k : 2 * ncaps - 1 - k;
+        const int sweep = k / ncaps, pos = k % ncaps;
+        const int c = sweep % 2 == 0 ? pos : ncaps - 1 - pos;
         for (int rep = -kWarm; rep < kReps; ++rep) {   // negative reps: warm-up, untimed
             if (rep == 0) {
                 if ((e = hipEventRecord(p.ev[0], p.s[0])) != hipSuccess ||
@@ -150,8 +153,15 @@ extern "C" int kvcopy_autotune(int dir, hipStream_t s0, hipStream_t s1, int *out
             (e = hipEventElapsedTime(&ms1, p.ev[0], p.ev[2])) != hipSuccess)
             return kvc::hip_fail(e);
         const double ms = std::max(ms0, nb == 2 ? ms1 : 0.0f);
-        const double r = ms > 0 ? (double)(kBytes * nb * kReps) / (ms * 1e-3) : 0;
-        rate[c] = std::max(rate[c], r);
+        rates[c][sweep] = ms > 0 ? (double)(kBytes * nb * kReps) / (ms * 1e-3) : 0;
+    }
+    double rate[KVCOPY_AUTOTUNE_NCAPS] = {};
+    double best = 0;
+    for (int c = 0; c < ncaps; ++c) {
+        double r[kSweeps];
+        std::copy(rates[c], rates[c] + kSweeps, r);
+        std::sort(r, r + kSweeps);
+        rate[c] = r[kSweeps / 2];
         best = std::max(best, rate[c]);
     }
     int chosen = KVCOPY_WGS_ALL;

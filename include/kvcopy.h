@@ -332,11 +332,11 @@ void kvcopy_job_destroy(kvcopy_job_t *job);
  * direction, freed before it returns), times six batches of 8,192 shuffled
  * 4 KiB blocks per direction at each cap of KVCOPY_AUTOTUNE_CAPS, after two
  * untimed ones (for H2D or D2H both directions run together, H2D on s0 and
- * D2H on s1, as in a KV offload burst; D2D runs on s0), in two sweeps over
- * the caps (ascending, then descending) keeping each cap's better rate, and
- * records the smallest cap within 5% of the best rate as the device's
- * KVCOPY_WGS_AUTO cap for `dir` (for H2D or D2H: for both).  Blocks until
- * done (about a tenth of a second).
+ * D2H on s1, as in a KV offload burst; D2D runs on s0), in three sweeps
+ * over the caps (ascending, descending, ascending) keeping each cap's
+ * median rate, and records the smallest cap within 5% of the best rate as
+ * the device's KVCOPY_WGS_AUTO cap for `dir` (for H2D or D2H: for both).
+ * Blocks until done (about a fifth of a second).
  * s0, s1: the streams the caller will copy on (the hardware queues they map
  *   to matter); NULL = streams created for the probe.
  * out_wgs (may be NULL): the chosen cap (0 = full grid).
