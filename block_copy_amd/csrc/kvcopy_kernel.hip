@@ -72,7 +72,9 @@ __device__ __forceinline__ uint64_t lane_u64(uint64_t v, uint32_t j)
     return ((uint64_t)hi << 32) | lo;
 }
 
-// Wavefront w of nw copies chunks [w*C/nw, (w+1)*C/nw) of the worklist.
+// Wavefront w of nw copies chunks [w*C/nw, (w+1)*C/nw) of the worklist,
+// storing with cache policy SP.
+template <int SP = kStorePolicy>
 __device__ __forceinline__ void copy_share(const ChunkRec *__restrict__ recs, uint32_t n_chunks,
                                            uint32_t w, uint32_t nw)
 {
@@ -87,7 +89,7 @@ __device__ __forceinline__ void copy_share(const ChunkRec *__restrict__ recs, ui
         const uint32_t nb = base + 64u;
         const Rec nxt = load_rec(recs, nb + lane, nb < hi && nb + lane < hi);   // prefetch
         for (uint32_t j = 0; j < cnt; ++j)
-            copy_chunk(lane_u64(cur.src, j), lane_u64(cur.dst, j),
+            copy_chunk<SP>(lane_u64(cur.src, j), lane_u64(cur.dst, j),
                        __builtin_amdgcn_readlane(cur.bytes, j), lane);
         cur = nxt;
     }
@@ -339,9 +341,9 @@ __device__ __forceinline__ void copy_pair(const ChunkRec *__restrict__ ra, uint3
     const uint32_t nw = gridDim.x * kWavesPerWG;
     const uint32_t v = __builtin_amdgcn_readfirstlane((threadIdx.x >> 6) * gridDim.x + blockIdx.x);
     if (v < wa)
-        copy_share(ra, ca, v, wa);
+        copy_share<kPairStorePolicy>(ra, ca, v, wa);
     else
-        copy_share(rb, cb, v - wa, nw - wa);
+        copy_share<kPairStorePolicy>(rb, cb, v - wa, nw - wa);
 }
 
 // ---- inline worklist ----------------------------------------------------------

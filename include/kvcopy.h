@@ -241,7 +241,7 @@ int kvcopy_batch_ex(const uint64_t *src_addrs, const uint64_t *dst_addrs, const 
  * their chunk counts, with every workgroup holding wavefronts of both, so
  * every CU in use carries both directions and both directions of the host
  * link stay busy together until the end.  Measured on MI355X with 16,384 x
- * 4 KiB each way: 96-97 GB/s, where the same bursts as two kernels on two
+ * 4 KiB each way: 98 GB/s, where the same bursts as two kernels on two
  * streams reach 85-88 GB/s (and less when the two caps differ: the
  * direction with fewer requests in flight loses its share of the link).
  * The bytes moved are exactly those of kvcopy_batch(a) followed by
