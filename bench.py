@@ -328,6 +328,22 @@ def bench_kv(c: Ctx, args):
                            "ms_per_call": round(s * 1e3, 4), "kernel_ms": round(km[0], 4),
                            "latency": c.latency(res, j, max_wgs, k=50, w=5)}
             log(f"  {name} alone: {alone[name]}")
+        # a lone D2H list through kvcopy_batch_pair (its kernel stores with
+        # system scope; the single-direction D2H kernel keeps nt alone)
+        e_ = np.zeros(0, np.uint64)
+        s1_, d1_ = res.addrs[1]
+        for _ in range(args.warmup):
+            K.kvcopy_batch_pair(s1_, d1_, wl.batches[1].size, e_, e_, e_, K.WGS_AUTO, sA.cuda_stream)
+        torch.cuda.synchronize()
+        ev0, ev1 = hiprt.Event(), hiprt.Event()
+        ev0.record(sA)
+        for _ in range(args.steps):
+            K.kvcopy_batch_pair(s1_, d1_, wl.batches[1].size, e_, e_, e_, K.WGS_AUTO, sA.cuda_stream)
+        ev1.record(sA)
+        ms_ = ev0.elapsed_ms(ev1) / args.steps
+        alone["d2h_one_list_through_pair"] = {"GBps": round(gbs(wl.batches[1].nbytes, ms_ / 1e3), 3),
+                                              "kernel_ms": round(ms_, 4)}
+        log(f"  d2h alone through kvcopy_batch_pair: {alone['d2h_one_list_through_pair']}")
         extras["per_direction_alone"] = alone
         # the startup probe's choice, and the headline step at that cap
         cap, rates = K.kvcopy_autotune(K.H2D, sA.cuda_stream, sB.cuda_stream)

@@ -170,8 +170,9 @@ int resolve_auto(const Staging *st, int dir)
 }
 
 // KVCOPY_WGS_AUTO for kvcopy_batch_pair: with 16,384 x 4 KiB each way, one
-// launch measured its best rate on MI355X at 64 workgroups (96.9 GB/s; 93.6
-// at 32, 92.9 at 128, 87.8 at 256).
+// launch measured 98.4 GB/s on MI355X at 64 workgroups with no slow window
+// in 30; 96-160 workgroups reached 99.1-99.5 GB/s at the median but had
+// occasional windows below 50 GB/s, and 48 gave 97.9.
 constexpr int kPairAutoWgs = 64;
 
 uint32_t grid_for(uint64_t n_chunks, int max_wgs)

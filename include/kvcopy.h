@@ -252,10 +252,16 @@ int kvcopy_batch_ex(const uint64_t *src_addrs, const uint64_t *dst_addrs, const 
  * destination or any source of either list; checked in validate mode).
  * The kernel reads and writes through the addresses as given, so either
  * list may hold any direction; the usual use is H2D in one and D2H in the
- * other.  n_a or n_b may be 0 (both 0: KVCOPY_OK, nothing enqueued).
+ * other.  n_a or n_b may be 0 (both 0: KVCOPY_OK, nothing enqueued).  The
+ * kernel's stores carry system scope as well as the nontemporal hint; a
+ * lone D2H list given here (n_b = 0) measured 56.7 GB/s for 16,384 x 4 KiB,
+ * against 52.7-55.0 through kvcopy_batch, whose D2H kernel keeps the
+ * nontemporal hint alone because that is faster when an H2D kernel runs
+ * beside it on another stream.
  * max_wgs as for kvcopy_batch, except that KVCOPY_WGS_AUTO is 64
- * workgroups, the best measured cap for the burst above (94-97 GB/s from
- * 32 to 96 workgroups; 81-87 GB/s above 192).
+ * workgroups, the steadiest cap measured for the burst above (98.4 GB/s;
+ * 96-160 workgroups reach 99.1-99.5 at the median with occasional slow
+ * windows; the full grid 84).
  * flags: KVCOPY_F_VALIDATE and/or KVCOPY_F_NO_COALESCE, as for
  * kvcopy_batch_ex; any other bit is KVCOPY_EINVAL.  Ownership, threads and
  * errors as for kvcopy_batch; an error in either list enqueues nothing.

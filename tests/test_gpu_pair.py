@@ -70,19 +70,21 @@ def test_pair_unequal_irregular(K, na, nb, max_wgs):
     res.free()
 
 
+@pytest.mark.parametrize("direction", ["h2d", "d2h"])
 @pytest.mark.parametrize("side", ["a", "b"])
-def test_pair_one_list_empty(K, side):
+def test_pair_one_list_empty(K, side, direction):
+    """One list only: every wavefront of the launch copies it."""
     from block_copy_amd.harness import Resident
-    res = Resident(W.kv_blocks(seed=7, directions="h2d", n=3000))
-    for max_wgs in (1, 16, 0):
-        _say("pair one empty", side, "max_wgs", max_wgs)
+    res = Resident(W.kv_blocks(seed=7, directions=direction, n=3000))
+    for max_wgs in (1, 16, 0, -1):
+        _say("pair one empty", side, direction, "max_wgs", max_wgs)
         res.fill()
         if side == "a":
             _pair(K, res, None, 0, max_wgs)
         else:
             _pair(K, res, 0, None, max_wgs)
         torch.cuda.synchronize()
-        _check(res, [0], f"pair empty {side} max_wgs={max_wgs}")
+        _check(res, [0], f"pair empty {side} {direction} max_wgs={max_wgs}")
     res.free()
 
 
