@@ -1,8 +1,11 @@
 // runtime.cpp -- kvcopy_batch: staging, launch, errors; host allocation helpers.
 //
 // A call plans the batch straight into a library-owned pinned staging ring
-// and launches one copy kernel on the caller's stream (PegaFlow issue #408,
-// "Summary": one descriptor upload and one copy-kernel launch per batch).
+// (with non-temporal stores: only the GPU reads the records) and launches
+// one copy kernel on the caller's stream (PegaFlow issue #408, "Summary":
+// one descriptor upload and one copy-kernel launch per batch).  A batch of
+// at most 128 chunks passes its worklist in the kernel arguments instead,
+// and kvcopy_batch_pair plans two lists into one region for one kernel.
 // The kernel reads its worklist in place from the pinned ring, over the host
 // link, with vector loads of 64 records at a time: the worklist crosses the
 // link once, as part of the kernel's own traffic, with no separate copy and
@@ -15,9 +18,9 @@
 // that they are allocated once and reused.  Here each device has one pinned
 // ring, sized once (it grows only if a single call needs more than a quarter
 // of it).  Each call takes the next free region of the ring; the region is
-// released when an event recorded after the call's kernel has completed.  A
-// call waits on the host only when the ring is full of regions whose kernels
-// are still running.
+// released when the kernel's completion event (the stop event of its own
+// launch) has fired.  A call waits on the host only when the ring is full of
+// regions whose kernels are still running.
 #include <stdlib.h>
 #include <string.h>
 
