@@ -405,6 +405,12 @@ def bench_kv(c: Ctx, args):
         "frac_of_measured_ceiling": round(ach[dom] / meas_ceil, 4) if meas_ceil else None,
         "other_kernel": {"kernel": KERNEL_NAMES[1 - dom], "achieved": round(ach[1 - dom], 3),
                          "kernel_ms": round(kern_ms[1 - dom], 4)}}
+    # the step against the link's measured two-direction ceiling: contiguous
+    # hipMemcpyAsync H2D and D2H of 64 MiB each, concurrent on two streams
+    both_ceil = extras.get("contiguous_memcpy_ceiling_GBps", {}).get("both")
+    if both_ceil:
+        line["roofline"]["measured_ceiling_both_directions"] = both_ceil
+        line["roofline"]["frac_step_of_ceiling_both_directions"] = round(value / both_ceil, 4)
     line["cpu_baseline"] = {
         "value": round(cpu["GBps"], 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
         "cpu": cpu_model(),
@@ -802,6 +808,7 @@ def d2d_distinct(c: Ctx, args):
     us = statistics.median(e0.elapsed_ms(e1) * 1e3 for e0, e1 in evs)
     pl = c.K.kvcopy_plan(*r.addrs[0], wl.batches[0].size)
     hbm = 2 * wl.batches[0].nbytes + pl.n_chunks * REC_BYTES
+    ceiling = random_block_ceiling(c, r, wl, calls)
     r.fill()
     for i in range(nb):
         r.submit(i, 0, c.sA)
@@ -810,9 +817,56 @@ def d2d_distinct(c: Ctx, args):
     r.free()
     out = {"batches": nb, "calls": calls, "kernel_us_p50": round(us, 2),
            "hbm_GBps_kernel": round(gbs(hbm, us / 1e6), 1),
-           "frac_hbm_peak_kernel": round(gbs(hbm, us / 1e6) / HBM_PEAK_GBS, 4)}
+           "frac_hbm_peak_kernel": round(gbs(hbm, us / 1e6) / HBM_PEAK_GBS, 4),
+           "random_block_ceiling": ceiling,
+           "frac_random_block_ceiling": round(ceiling["us"] / us, 4)}
     log(f"  d2d distinct calls: {out} (bit-exact)")
     return out
+
+
+def random_block_ceiling(c: Ctx, r, wl, calls):
+    """What HBM sustains for the rotation's own blocks moved one way at a time:
+    the same source blocks only read, and the same destination blocks only
+    written (libkvload's scattered passes: one wavefront per block, the copy's
+    access shapes), each timed per launch with the kernel's own events, the
+    calls cycling over the batches as the copy's do.  Reads and writes share
+    each HBM channel's data bus, so the copy cannot beat read time + write
+    time; that sum, against 2 x payload, is the random-block ceiling.  Runs
+    after the copy calls and before the refill that precedes the check (the
+    scatter overwrites destination blocks)."""
+    torch, hiprt, np = c.torch, c.hiprt, c.np
+    from block_copy_amd import decode_load as DL
+    sizes = {int(x) for b in wl.batches for x in np.unique(b.size)}
+    if len(sizes) != 1:
+        raise ValueError("the random-block ceiling needs one block size")
+    blk = sizes.pop()
+    nb = len(wl.batches)
+    srcs = [torch.from_numpy(r.addrs[i][0].view(np.int64)).to(c.dev) for i in range(nb)]
+    dsts = [torch.from_numpy(r.addrs[i][1].view(np.int64)).to(c.dev) for i in range(nb)]
+    sink = torch.zeros(64, dtype=torch.int32, device=c.dev)
+    res = {}
+    for kind in ("read", "write"):
+        def launch(i, e0=None, e1=None):
+            if kind == "read":
+                DL.gather_read(srcs[i % nb], blk, sink, c.sA, e0, e1)
+            else:
+                DL.scatter_write(dsts[i % nb], blk, 0xA5A5A5A5, c.sA, e0, e1)
+        for i in range(nb):
+            launch(i)
+        evs = [(hiprt.Event(), hiprt.Event()) for _ in range(calls)]
+        for i in range(calls):
+            launch(i, evs[i][0].h, evs[i][1].h)
+        hiprt.stream_sync(c.sA)
+        res[kind] = statistics.median(e0.elapsed_ms(e1) * 1e3 for e0, e1 in evs)
+    payload = wl.batches[0].nbytes
+    us = res["read"] + res["write"]
+    return {"us": round(us, 2), "GBps": round(gbs(2 * payload, us / 1e6), 1),
+            "read_only_us_p50": round(res["read"], 2),
+            "read_only_GBps": round(gbs(payload, res["read"] / 1e6), 1),
+            "write_only_us_p50": round(res["write"], 2),
+            "write_only_GBps": round(gbs(payload, res["write"] / 1e6), 1),
+            "what": "the same random 4 KiB blocks only read, then only written, each pass "
+                    "timed alone; ceiling = 2 x payload / (read time + write time)"}
 
 
 def bench_d2d(c: Ctx, args):
@@ -847,6 +901,11 @@ def bench_d2d(c: Ctx, args):
                         "measured_ceiling_what": "contiguous 1 GiB D2D copy (2 GiB footprint): the "
                                                  "best of hipMemcpyAsync and this kernel on one range",
                         "frac_of_measured_ceiling": round(ach / ceil, 4) if ceil else None}
+    if dist:
+        rb = dist["random_block_ceiling"]
+        line["roofline"]["random_block_ceiling"] = rb["GBps"]
+        line["roofline"]["frac_of_random_block_ceiling"] = dist["frac_random_block_ceiling"]
+        line["roofline"]["random_block_ceiling_what"] = rb["what"]
     line["d2d"] = res
     line["parity"] = "bit-exact vs oracle"
     return line

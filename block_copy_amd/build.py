@@ -17,9 +17,10 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(PKG, "libkvcopy.so")
 # Measurement-only library: the synthetic decode loop (bf16 GEMV chain) that
-# co-runs with copy bursts in the interference benchmark.
+# co-runs with copy bursts in the interference benchmark, and the scattered
+# read-only and write-only passes that bound the D2D copy.
 LOAD_OUT = os.path.join(PKG, "libkvload.so")
-LOAD_SOURCES = ["gemv_load.hip"]
+LOAD_SOURCES = ["gemv_load.hip", "hbm_probe.hip"]
 BUILD_DIR = os.path.join(ROOT, "_build")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 ARCH = "gfx950"

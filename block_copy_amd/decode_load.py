@@ -1,5 +1,6 @@
-"""ctypes binding of libkvload.so: the synthetic bf16 GEMV decode loop that the
-interference benchmark runs next to copy bursts (measurement only)."""
+"""ctypes binding of libkvload.so (measurement only): the synthetic bf16 GEMV
+decode loop that the interference benchmark runs next to copy bursts, and the
+scattered read-only and write-only passes that bound the D2D copy."""
 from __future__ import annotations
 
 import ctypes
@@ -16,6 +17,14 @@ lib.kvload_chain_bf16.restype = ctypes.c_int
 lib.kvload_chain_bf16.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_int),
                                   ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_void_p),
                                   ctypes.c_int, ctypes.c_void_p]
+
+for _f in (lib.kvload_gather_read, lib.kvload_scatter_write):
+    _f.restype = ctypes.c_int
+lib.kvload_gather_read.argtypes = [ctypes.c_void_p, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32,
+                                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+lib.kvload_scatter_write.argtypes = [ctypes.c_void_p, ctypes.c_uint32, ctypes.c_uint32,
+                                     ctypes.c_uint32, ctypes.c_void_p, ctypes.c_void_p,
+                                     ctypes.c_void_p]
 
 
 def _stream(s):
@@ -57,3 +66,34 @@ class Chain:
         rc = lib.kvload_chain_bf16(self.Ws, self.rows, self.cols, self.acts, self.n, _stream(stream))
         if rc != 0:
             raise RuntimeError(f"kvload_chain_bf16 failed: hipError {rc}")
+
+
+def _blocks(addrs, block_bytes):
+    if addrs.dtype.itemsize != 8 or not addrs.is_cuda or not addrs.is_contiguous():
+        raise ValueError("addrs must be a contiguous 64-bit tensor on the GPU")
+    n = addrs.numel()
+    if n == 0 or n > 1 << 30 or block_bytes <= 0 or block_bytes % 16 or block_bytes > 16384:
+        raise ValueError("need 0 < n <= 2**30 and a block size that is a multiple of 16, <= 16 KiB")
+    return n
+
+
+def gather_read(addrs, block_bytes, sink, stream=None, start=None, stop=None) -> None:
+    """Read the blocks at the device addresses in `addrs` (int64 tensor on the
+    GPU); `sink` is a GPU tensor of at least 256 bytes, written only if the
+    folded data equals a fixed value.  start/stop: raw hipEvent_t handles."""
+    n = _blocks(addrs, block_bytes)
+    if sink.numel() * sink.element_size() < 256 or not sink.is_cuda:
+        raise ValueError("sink must be a GPU tensor of at least 256 bytes")
+    rc = lib.kvload_gather_read(addrs.data_ptr(), n, block_bytes, 0x9E3779B9, sink.data_ptr(),
+                                _stream(stream), start, stop)
+    if rc != 0:
+        raise RuntimeError(f"kvload_gather_read failed: hipError {rc}")
+
+
+def scatter_write(addrs, block_bytes, pattern, stream=None, start=None, stop=None) -> None:
+    """Fill the blocks at the device addresses in `addrs` with a 32-bit pattern."""
+    n = _blocks(addrs, block_bytes)
+    rc = lib.kvload_scatter_write(addrs.data_ptr(), n, block_bytes, pattern & 0xFFFFFFFF,
+                                  _stream(stream), start, stop)
+    if rc != 0:
+        raise RuntimeError(f"kvload_scatter_write failed: hipError {rc}")

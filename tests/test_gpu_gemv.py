@@ -1,5 +1,7 @@
-"""The measurement-only bf16 GEMV (the synthetic decode loop of the
-interference benchmark) against a float32 CPU reference of the same product."""
+"""The measurement-only harness kernels: the bf16 GEMV (the synthetic decode
+loop of the interference benchmark) against a float32 CPU reference of the
+same product, and the scattered read-only and write-only passes that bound
+the D2D copy."""
 import pytest
 
 torch = pytest.importorskip("torch")
@@ -50,3 +52,38 @@ def test_chain_runs_products_in_order(DL):
         got = acts[i + 1].float().cpu()
         tol = ref.abs() * 2.0 ** -8 + 1e-5 * ref.abs().max() + 1e-6
         assert torch.all((got - ref).abs() <= tol), i
+
+
+@pytest.mark.parametrize("blk", [4096, 16, 1040, 16384])
+def test_scattered_passes_touch_exactly_their_blocks(DL, blk):
+    """The D2D ceiling's measurement passes: the write pass fills exactly the
+    listed blocks with its pattern and nothing else; the read pass leaves
+    memory and its sink untouched."""
+    print("[case] scattered passes", blk, flush=True)
+    nblk, n = 64, 23
+    pool = torch.full((nblk * blk + 64,), 0x11, dtype=torch.uint8, device="cuda")
+    g = torch.Generator().manual_seed(blk)
+    idx = torch.randperm(nblk, generator=g)[:n]
+    addrs = (pool.data_ptr() + idx.to(torch.int64) * blk).to("cuda")
+    sink = torch.zeros(64, dtype=torch.int32, device="cuda")
+    DL.gather_read(addrs, blk, sink)
+    torch.cuda.synchronize()
+    assert int(sink.abs().sum()) == 0
+    assert torch.all(pool == 0x11)
+    DL.scatter_write(addrs, blk, 0xA5A5A5A5)
+    torch.cuda.synchronize()
+    want = torch.full((nblk * blk + 64,), 0x11, dtype=torch.uint8)
+    for i in idx.tolist():
+        want[i * blk:(i + 1) * blk] = 0xA5
+    assert torch.equal(pool.cpu(), want)
+
+
+def test_scattered_passes_reject_bad_sizes(DL):
+    print("[case] scattered passes: bad sizes", flush=True)
+    pool = torch.zeros(4096, dtype=torch.uint8, device="cuda")
+    addrs = torch.tensor([pool.data_ptr()], dtype=torch.int64, device="cuda")
+    for blk in (0, 8, 20000):
+        with pytest.raises(ValueError):
+            DL.scatter_write(addrs, blk, 1)
+    with pytest.raises(ValueError):
+        DL.scatter_write(addrs[:0], 16, 1)
