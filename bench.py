@@ -936,6 +936,8 @@ def bench_mixed(c: Ctx, args):
                         "dma_baselines": dma}
         log(f"  mixed N={n}: {rows[str(n)]} (bit-exact)")
         r.free()
+    if args.counter_calibration:
+        counter_calibration(c)
     top = rows["65536"]
     line = base_line(args, top["GBps"], "GB/s", top["bytes"] / top["GBps"] / 1e9, {
         "workload": "H2D with mixed sizes (70% in 8-16 KiB, rest 4-8 and 16-28 KiB, 8-byte "
@@ -1012,6 +1014,8 @@ def bench_moe(c: Ctx, args):
     line["steps"] = calls
     line["per_setting"] = out
     line["parity"] = "bit-exact vs oracle"
+    if args.counter_calibration:
+        counter_calibration(c)
     return line
 
 
