@@ -52,22 +52,22 @@ struct Probe {
     bool own[2] = {false, false};   // streams created here (destroyed at the end)
     hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
     ~Probe()
-    {
+    {   // release path: failures here cannot be reported and change nothing
         for (hipStream_t x : s)
             if (x)
-                hipStreamSynchronize(x);
+                (void)hipStreamSynchronize(x);
         for (void *p : host)
             if (p)
-                hipHostFree(p);
+                (void)hipHostFree(p);
         for (void *p : dev)
             if (p)
-                hipFree(p);
+                (void)hipFree(p);
         for (hipEvent_t e : ev)
             if (e)
-                hipEventDestroy(e);
+                (void)hipEventDestroy(e);
         for (int i = 0; i < 2; ++i)
             if (own[i])
-                hipStreamDestroy(s[i]);
+                (void)hipStreamDestroy(s[i]);
     }
 };
 

@@ -24,13 +24,17 @@ constexpr int kRsrcWord3 = 0x00020000;
 // memory the combinations are within noise of each other.
 constexpr int kLoadPolicy = 0;
 constexpr int kStorePolicy = 2;
-// The one-launch pair kernel stores with sc1 | nt (bits 4 and 1: system
-// scope, nontemporal).  Measured on MI355X with 16,384 x 4 KiB each way:
-// 98.7 GB/s against 96.9 with nt alone; a lone D2H batch also gains (56.7
-// against 52.7 GB/s), but two single-direction kernels on two streams lose
-// with it (84.4 against 87.9 GB/s median, 82.6 with it on the D2H side
-// only), so the single-direction kernels keep nt.
-constexpr int kPairStorePolicy = 18;
+// System-scope stores: sc1 | nt (bits 4 and 1: system scope, nontemporal).
+// The one-launch pair kernel always stores this way.  Measured on MI355X
+// with 16,384 x 4 KiB each way: 98.7 GB/s against 96.9 with nt alone.  A
+// lone D2H batch gains too (56.7 against 52.7 GB/s), but a D2H kernel that
+// runs beside an H2D kernel on another stream loses with it (82-84 against
+// 86.7 GB/s for the two directions at 128 workgroups each), and an H2D
+// kernel gains nothing from it alone (56.9 GB/s either way).  So the D2H
+// per-chunk loop has both forms and the host picks per call (system scope
+// unless one of the library's H2D kernels is still running on another
+// stream); the other kernels keep nt.
+constexpr int kSysStorePolicy = 18;
 constexpr uint32_t kRowBytes = 64u * 16u;          // one wavefront instruction: 1 KiB
 constexpr int kMaxRows = 16;                       // 16 KiB per pass, 64 VGPRs of data
 constexpr uint32_t kPassBytes = kRowBytes * kMaxRows;

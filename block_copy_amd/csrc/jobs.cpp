@@ -138,6 +138,6 @@ extern "C" void kvcopy_job_destroy(kvcopy_job_t *job)
     if (job == nullptr)
         return;
     if (job->ev)
-        hipEventDestroy(job->ev);
+        (void)hipEventDestroy(job->ev);
     delete job;
 }

@@ -113,13 +113,15 @@ hipError_t launch_copy_inline(const InlineWork &w, uint32_t grid, int dir, hipSt
 // Launches the copy kernel for `dir` (one kernel symbol per direction and
 // loop, same result): `grid` workgroups; wavefront w of W copies the chunks
 // [w*C/W, (w+1)*C/W), one chunk at a time or, if `pipelined`, as a stream of
-// 4 KiB pieces with two 16 KiB passes in flight.  recs must be
+// 4 KiB pieces with two 16 KiB passes in flight.  `sys_stores` selects the
+// D2H per-chunk loop's system-scope stores (ignored otherwise).  recs must be
 // device-readable (device memory or mapped host memory).  `start` and `stop`
 // (either may be null) are bound to the kernel's own start and completion
 // (hipExtLaunchKernel's events), which costs no separate marker on the
 // stream.  Returns the launch status.
 hipError_t launch_copy(const ChunkRec *recs, uint32_t n_chunks, uint32_t grid, int dir,
-                       bool pipelined, hipStream_t stream, hipEvent_t start, hipEvent_t stop);
+                       bool pipelined, bool sys_stores, hipStream_t stream, hipEvent_t start,
+                       hipEvent_t stop);
 
 // kvcopy_batch_pair: two worklists (ra[0..ca), rb[0..cb)) in one kernel;
 // every wavefront alternates between its shares of the two lists in

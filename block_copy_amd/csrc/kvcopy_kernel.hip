@@ -95,10 +95,19 @@ __device__ __forceinline__ void copy_share(const ChunkRec *__restrict__ recs, ui
     }
 }
 
+template <int SP = kStorePolicy>
 __device__ __forceinline__ void copy_worklist(const ChunkRec *__restrict__ recs, uint32_t n_chunks)
 {
     const uint32_t w = __builtin_amdgcn_readfirstlane(blockIdx.x * kWavesPerWG + (threadIdx.x >> 6));
-    copy_share(recs, n_chunks, w, gridDim.x * kWavesPerWG);
+    copy_share<SP>(recs, n_chunks, w, gridDim.x * kWavesPerWG);
+}
+
+// The per-chunk loop with system-scope stores (for D2H batches that run
+// with no H2D copy beside them; see kSysStorePolicy).
+__device__ __forceinline__ void copy_worklist_sys(const ChunkRec *__restrict__ recs,
+                                                  uint32_t n_chunks)
+{
+    copy_worklist<kSysStorePolicy>(recs, n_chunks);
 }
 
 // ---- pipelined variant ------------------------------------------------------
@@ -341,9 +350,9 @@ __device__ __forceinline__ void copy_pair(const ChunkRec *__restrict__ ra, uint3
     const uint32_t nw = gridDim.x * kWavesPerWG;
     const uint32_t v = __builtin_amdgcn_readfirstlane((threadIdx.x >> 6) * gridDim.x + blockIdx.x);
     if (v < wa)
-        copy_share<kPairStorePolicy>(ra, ca, v, wa);
+        copy_share<kSysStorePolicy>(ra, ca, v, wa);
     else
-        copy_share<kPairStorePolicy>(rb, cb, v - wa, nw - wa);
+        copy_share<kSysStorePolicy>(rb, cb, v - wa, nw - wa);
 }
 
 // ---- inline worklist ----------------------------------------------------------
@@ -377,6 +386,7 @@ KVC_KERNEL(kvcopy_d2d_kernel, copy_worklist)
 KVC_KERNEL(kvcopy_h2d_pipe_kernel, copy_worklist_pipelined)
 KVC_KERNEL(kvcopy_d2h_pipe_kernel, copy_worklist_pipelined)
 KVC_KERNEL(kvcopy_d2d_pipe_kernel, copy_worklist_pipelined)
+KVC_KERNEL(kvcopy_d2h_sys_kernel, copy_worklist_sys)
 #undef KVC_KERNEL
 
 __global__ __launch_bounds__(kThreadsPerWG) void kvcopy_pair_kernel(const ChunkRec *__restrict__ ra,
@@ -412,7 +422,8 @@ KVC_DYN_KERNEL(kvcopy_d2d_dyn_kernel)
 }  // namespace
 
 hipError_t launch_copy(const ChunkRec *recs, uint32_t n_chunks, uint32_t grid, int dir,
-                       bool pipelined, hipStream_t stream, hipEvent_t start, hipEvent_t stop)
+                       bool pipelined, bool sys_stores, hipStream_t stream, hipEvent_t start,
+                       hipEvent_t stop)
 {
     static const void *const fns[2][3] = {
         {reinterpret_cast<const void *>(&kvcopy_h2d_kernel),
@@ -421,9 +432,11 @@ hipError_t launch_copy(const ChunkRec *recs, uint32_t n_chunks, uint32_t grid, i
         {reinterpret_cast<const void *>(&kvcopy_h2d_pipe_kernel),
          reinterpret_cast<const void *>(&kvcopy_d2h_pipe_kernel),
          reinterpret_cast<const void *>(&kvcopy_d2d_pipe_kernel)}};
+    const void *fn = fns[pipelined ? 1 : 0][dir];
+    if (sys_stores && !pipelined && dir == 1 /* KVCOPY_D2H */)
+        fn = reinterpret_cast<const void *>(&kvcopy_d2h_sys_kernel);
     void *args[] = {(void *)&recs, (void *)&n_chunks};
-    return hipExtLaunchKernel(fns[pipelined ? 1 : 0][dir], dim3(grid), dim3(kThreadsPerWG), args, 0,
-                              stream, start, stop, 0);
+    return hipExtLaunchKernel(fn, dim3(grid), dim3(kThreadsPerWG), args, 0, stream, start, stop, 0);
 }
 
 hipError_t launch_copy_pair(const ChunkRec *ra, uint32_t ca, const ChunkRec *rb, uint32_t cb,

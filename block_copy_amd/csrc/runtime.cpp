@@ -111,12 +111,12 @@ int grow(Staging *st, uint64_t need, bool want_dev, bool want_claims)
         return rc;
     if (resize) {
         if (st->host)
-            hipHostFree(st->host);
+            (void)hipHostFree(st->host);
         if (st->dev)
-            hipFree(st->dev);
+            (void)hipFree(st->dev);
         if (st->claims) {
             want_claims = true;
-            hipFree(st->claims);
+            (void)hipFree(st->claims);
         }
         st->host = nullptr;
         st->dev = nullptr;
@@ -154,7 +154,7 @@ int grow(Staging *st, uint64_t need, bool want_dev, bool want_claims)
         // Once, at allocation (the ring is drained): from here on every
         // kernel leaves its pair at zero.
         if ((e = hipMemset(st->claims, 0, bytes)) != hipSuccess) {
-            hipFree(st->claims);
+            (void)hipFree(st->claims);
             st->claims = nullptr;
             return hip_fail(e);
         }
@@ -262,7 +262,20 @@ int run_locked(Staging *st, const uint64_t *src, const uint64_t *dst, const uint
     } else {
         const bool pipelined = (flags & KVCOPY_F_PIPELINE) != 0 ||
                                (!(flags & KVCOPY_F_PER_CHUNK) && pipeline_pays(dir, grid, n_chunks));
-        e = launch_copy(recs, (uint32_t)n_chunks, grid, dir, pipelined, stream, start, stop);
+        // D2H stores with system scope unless an H2D kernel of this library
+        // is still running on another stream (copy_chunk.h, kSysStorePolicy:
+        // faster alone, slower beside an H2D kernel).  Only the speed depends
+        // on the choice.
+        bool sys = false;
+        if (dir == KVCOPY_D2H && !pipelined) {
+            const int busy = st->ring.running_elsewhere(KVCOPY_H2D, stream);
+            if (busy < 0) {
+                st->spare.push_back(done);
+                return busy;
+            }
+            sys = busy == 0;
+        }
+        e = launch_copy(recs, (uint32_t)n_chunks, grid, dir, pipelined, sys, stream, start, stop);
     }
     if (e == hipSuccess && timed)
         e = hipEventRecord(done, stream);
@@ -270,7 +283,7 @@ int run_locked(Staging *st, const uint64_t *src, const uint64_t *dst, const uint
         st->spare.push_back(done);
         return hip_fail(e);
     }
-    st->ring.commit(off, used, done);
+    st->ring.commit(off, used, done, dir, stream);
     return KVCOPY_OK;
 }
 
@@ -591,7 +604,7 @@ extern "C" int kvcopy_host_alloc_mapped(uint64_t bytes, void **out)
     void *dp = nullptr;
     e = hipHostGetDevicePointer(&dp, p, 0);
     if (e != hipSuccess || dp != p) {
-        hipHostFree(p);
+        (void)hipHostFree(p);
         return hip_fail(e != hipSuccess ? e : hipErrorInvalidValue);
     }
     *out = p;

@@ -63,7 +63,8 @@ def test_kernels_have_no_scratch_or_spills(K, src):
     names = set(re.findall(r"\.name:\s+_ZN3kvc12_GLOBAL__N_1\d+(kvcopy_\w+?_kernel)E", txt))
     if src == "kvcopy_kernel.hip":
         want = {f"kvcopy_{d}{v}_kernel" for d in ("h2d", "d2h", "d2d")
-                for v in ("", "_pipe", "_dyn", "_inline")} | {"kvcopy_pair_kernel"}
+                for v in ("", "_pipe", "_dyn", "_inline")} | {"kvcopy_pair_kernel",
+                                                               "kvcopy_d2h_sys_kernel"}
     else:
         want = {"kvcopy_device_plan_kernel", "kvcopy_device_copy_kernel"}
     assert names == want, names
