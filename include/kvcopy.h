@@ -182,7 +182,10 @@ void kvcopy_plan_free(kvcopy_plan_t *plan);
  * into its own pinned staging ring, and launches one kernel of
  * min(max_wgs, needed) workgroups of 4 wavefronts on `stream`.  Each
  * wavefront takes an equal contiguous share of the chunks and moves them
- * with 16-byte loads and nontemporal 16-byte stores.  The staging region is
+ * with 16-byte loads and nontemporal 16-byte stores (a D2H batch's stores
+ * also carry system scope when none of this library's H2D kernels is still
+ * running on another stream, which is faster alone and slower beside one;
+ * the bytes moved are the same).  The staging region is
  * recycled once an event recorded after the kernel has completed; the call
  * waits on the host only if the whole ring is still in use.  A batch of at
  * most 128 chunks instead passes its worklist in the kernel arguments (no
@@ -253,11 +256,10 @@ int kvcopy_batch_ex(const uint64_t *src_addrs, const uint64_t *dst_addrs, const 
  * The kernel reads and writes through the addresses as given, so either
  * list may hold any direction; the usual use is H2D in one and D2H in the
  * other.  n_a or n_b may be 0 (both 0: KVCOPY_OK, nothing enqueued).  The
- * kernel's stores carry system scope as well as the nontemporal hint; a
- * lone D2H list given here (n_b = 0) measured 56.7 GB/s for 16,384 x 4 KiB,
- * against 52.7-55.0 through kvcopy_batch, whose D2H kernel keeps the
- * nontemporal hint alone because that is faster when an H2D kernel runs
- * beside it on another stream.
+ * kernel's stores carry system scope as well as the nontemporal hint (as
+ * kvcopy_batch's D2H kernel does when none of this library's H2D kernels is
+ * running on another stream; beside one it keeps the nontemporal hint
+ * alone, which is faster there).
  * max_wgs as for kvcopy_batch, except that KVCOPY_WGS_AUTO is 64
  * workgroups, the steadiest cap measured for the burst above (98.4 GB/s;
  * 96-160 workgroups reach 99.1-99.5 at the median with occasional slow
