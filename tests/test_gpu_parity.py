@@ -167,6 +167,34 @@ def test_irregular_chunk_sizes(K, dname, chunk):
     res.free()
 
 
+@pytest.mark.parametrize("beside", ["alone", "h2d_other_stream", "h2d_same_stream"])
+def test_d2h_store_forms(K, beside):
+    """A D2H batch stores with system scope unless one of the library's H2D
+    kernels still runs on another stream, where it keeps the nontemporal
+    form: both forms (and the case of an H2D kernel ahead of it on its own
+    stream) must leave the same bytes.  The D2H batch is irregular
+    (misaligned pairs, 8-byte tails, zero sizes) and larger than the inline
+    limit; the H2D batch is 16,384 x 4 KiB, still running when the D2H batch
+    is submitted."""
+    from block_copy_amd.harness import Resident
+    d2h = W.irregular(seed=61, n=600, dir_=W.D2H, src_where="device", dst_where="host",
+                      misalign=True, zero_frac=0.05)
+    wl = W.combine("d2h_beside_h2d", d2h, W.kv_blocks(seed=3, directions="h2d"))
+    res = Resident(wl)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    for sentinel in (W.SENTINEL_A, W.SENTINEL_B):
+        _say("d2h store forms", beside, "sentinel", hex(sentinel))
+        res.fill(sentinel)
+        if beside == "alone":
+            _run(res, [0], 128, streams=[s2])
+            _check(res, [0], f"d2h alone sentinel={sentinel:#x}", sentinel)
+            continue
+        st = s1 if beside == "h2d_other_stream" else s2
+        _run(res, [1, 0], 128, streams=[st, s2])
+        _check(res, [0, 1], f"d2h {beside} sentinel={sentinel:#x}", sentinel)
+    res.free()
+
+
 @pytest.mark.parametrize("flags", [0, 1, 2, 8, 10, 11])
 def test_irregular_flags(K, flags):
     from block_copy_amd.harness import Resident
