@@ -21,6 +21,8 @@ OUT = os.path.join(PKG, "libkvcopy.so")
 # read-only and write-only passes that bound the D2D copy.
 LOAD_OUT = os.path.join(PKG, "libkvload.so")
 LOAD_SOURCES = ["gemv_load.hip", "hbm_probe.hip"]
+# Measurement-only program: kvcopy_batch's per-call latency from a C caller.
+LATENCY_OUT = os.path.join(PKG, "kvcopy_latency")
 BUILD_DIR = os.path.join(ROOT, "_build")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 ARCH = "gfx950"
@@ -68,8 +70,14 @@ def build(verbose: bool = False) -> str:
     tmp = LOAD_OUT + ".tmp"
     _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *load_objs, "-o", tmp])
     os.replace(tmp, LOAD_OUT)
+    tmp = LATENCY_OUT + ".tmp"
+    _run(["g++", "-O2", "-std=c++17", "-Wall", "-Wextra", "-D__HIP_PLATFORM_AMD__",
+          f"-I{ROCM}/include", f"-I{INCLUDE}", os.path.join(CSRC, "latency_tool.cpp"), "-o", tmp,
+          f"-L{PKG}", "-lkvcopy", f"-L{ROCM}/lib", "-lamdhip64", "-Wl,-rpath,$ORIGIN",
+          f"-Wl,-rpath,{os.path.realpath(os.path.join(ROCM, 'lib'))}"])
+    os.replace(tmp, LATENCY_OUT)
     if verbose:
-        print(f"built {OUT} and {LOAD_OUT}")
+        print(f"built {OUT}, {LOAD_OUT} and {LATENCY_OUT}")
     return OUT
 
 

@@ -87,3 +87,22 @@ def test_scattered_passes_reject_bad_sizes(DL):
             DL.scatter_write(addrs, blk, 1)
     with pytest.raises(ValueError):
         DL.scatter_write(addrs[:0], 16, 1)
+
+
+def test_c_caller_latency_tool(DL):
+    """kvcopy_latency (kvcopy_batch timed from C, in a child process) runs the
+    batches bench.py hands it and finds every destination range equal to its
+    source."""
+    print("[case] kvcopy_latency", flush=True)
+    import bench
+    import workloads as W
+    rows = bench.c_caller_latency([("d2d_small", W.d2d_blocks(seed=3, n=200, pool_blocks=512), 0),
+                                   ("h2d_mixed_16", W.h2d_mixed(seed=1, n=16), -1),
+                                   ("d2h_irregular", W.irregular(seed=5, n=300, dir_=W.D2H,
+                                                                 src_where="device",
+                                                                 dst_where="host"), 8)])
+    assert "error" not in rows, rows
+    for name in ("d2d_small", "h2d_mixed_16", "d2h_irregular"):
+        r = rows[name]
+        assert r["ranges_wrong"] == 0 and r["ranges_checked"] == r["descriptors"], r
+        assert 0 < r["host_us_p50"] <= r["wall_us_p50"], r

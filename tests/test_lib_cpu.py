@@ -290,3 +290,12 @@ def test_autotune_rejects_bad_direction(K):
     import ctypes
     assert K.lib.kvcopy_autotune(3, None, None, None, None) == K.EINVAL
     assert K.lib.kvcopy_autotune(-1, None, None, ctypes.byref(ctypes.c_int()), None) == K.EINVAL
+
+
+def test_latency_tool_is_built_and_checks_its_arguments(K):
+    """The C-caller latency program is built next to the library and refuses
+    to run without batch files (no GPU call is made before that check)."""
+    exe = os.path.join(ROOT, "block_copy_amd", "kvcopy_latency")
+    assert os.access(exe, os.X_OK)
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 1 and "usage" in r.stderr
