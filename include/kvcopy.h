@@ -201,7 +201,9 @@ void kvcopy_plan_free(kvcopy_plan_t *plan);
  *          direction": max_grid_blocks).  KVCOPY_WGS_ALL (0) = one wavefront
  *          per chunk; KVCOPY_WGS_AUTO (-1) = the device's tuned or default
  *          cap.  Below -1 = KVCOPY_EINVAL.
- * stream:  HIP stream (NULL = the null stream).
+ * stream:  HIP stream (NULL = the null stream) of the calling thread's
+ *          current device: the staging ring, the completion events and the
+ *          kernel all belong to that device.
  * Ownership: the descriptor arrays may be reused as soon as the call
  *          returns.  The payload memory must stay valid, and unwritten by
  *          others, until the stream has passed the copy.
