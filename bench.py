@@ -1293,8 +1293,10 @@ def bench_interference(c: Ctx, args):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # 100 steps of the headline burst time about 0.15 s: long enough that a
+    # transient slow window of the two-stream link share does not set the value
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--max-wgs", type=int, default=None,
                     help=f"workgroup cap (default {DEFAULT_MAX_WGS}; pair: KVCOPY_WGS_AUTO)")
     ap.add_argument("--workload", default="kv", choices=["kv", "pair", "d2d", "mixed", "moe",
