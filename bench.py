@@ -328,8 +328,9 @@ def bench_kv(c: Ctx, args):
                            "ms_per_call": round(s * 1e3, 4), "kernel_ms": round(km[0], 4),
                            "latency": c.latency(res, j, max_wgs, k=50, w=5)}
             log(f"  {name} alone: {alone[name]}")
-        # a lone D2H list through kvcopy_batch_pair (its kernel stores with
-        # system scope; the single-direction D2H kernel keeps nt alone)
+        # a lone D2H list through kvcopy_batch_pair (whose kernel always
+        # stores with system scope, as kvcopy_batch's D2H kernel does when no
+        # H2D kernel of the library runs beside it)
         e_ = np.zeros(0, np.uint64)
         s1_, d1_ = res.addrs[1]
         for _ in range(args.warmup):
@@ -344,6 +345,11 @@ def bench_kv(c: Ctx, args):
         alone["d2h_one_list_through_pair"] = {"GBps": round(gbs(wl.batches[1].nbytes, ms_ / 1e3), 3),
                                               "kernel_ms": round(ms_, 4)}
         log(f"  d2h alone through kvcopy_batch_pair: {alone['d2h_one_list_through_pair']}")
+        cl = c_caller_latency([(f"kv_{nm}_16384x4KiB", W.kv_blocks(seed=0, directions=nm), max_wgs)
+                               for nm in ("h2d", "d2h")])
+        for nm in ("h2d", "d2h"):
+            alone[nm]["latency_c_caller"] = cl.get(f"kv_{nm}_16384x4KiB", cl.get("error"))
+        log(f"  each direction alone, C caller: {cl}")
         extras["per_direction_alone"] = alone
         # the startup probe's choice, and the headline step at that cap
         cap, rates = K.kvcopy_autotune(K.H2D, sA.cuda_stream, sB.cuda_stream)
