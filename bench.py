@@ -1252,7 +1252,7 @@ def bench_interference(c: Ctx, args):
         return gpu_ms, wall_ms, moved[0] / dur, bursts[0]
 
     modes = ["none", "direct", 1, 2, 8, 32, 128, 0, "pipe:1", "pipe:4", "job:1024", "job:2048",
-             "job:4096", "cumask:8", "cumask:32", "pair:8", "pair:64"]
+             "job:4096", "cumask:8", "cumask:32", "pair:8", "pair:16", "pair:64"]
     results = {str(m): {"gpu": [], "wall": [], "rate": [], "bursts": 0} for m in modes}
     for rep in range(args.decode_runs):
         order = modes[rep % len(modes):] + modes[:rep % len(modes)]
@@ -1284,6 +1284,14 @@ def bench_interference(c: Ctx, args):
     base = table["none"]["gpu_ms_p99"]
     for m in table:
         table[m]["p99_vs_none"] = round(table[m]["gpu_ms_p99"] / base - 1, 4)
+        # decode time lost per burst: the extra mean step time over all timed
+        # steps, shared out over the bursts that ran meanwhile (p99 and max
+        # show how the loss is spread; this shows how large it is)
+        n_steps = sum(len(x) for x in results[m]["gpu"])
+        if table[m]["bursts"]:
+            table[m]["decode_ms_lost_per_burst"] = round(
+                (table[m]["gpu_ms_mean"] - table["none"]["gpu_ms_mean"]) * n_steps
+                / table[m]["bursts"], 3)
     line = base_line(args, table["32"]["gpu_ms_p99"], "ms", table["none"]["gpu_ms_mean"] / 1e3, {
         "workload": f"decode loop of {n_gemv} bf16 GEMVs ({d_ff}x{d_model} and {d_model}x{d_ff}, "
                     f"{wbytes / 1e9:.2f} GB of distinct weights per step) while a bidirectional "
