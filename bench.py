@@ -142,7 +142,10 @@ class Ctx:
         torch.cuda.set_device(self.dev)
         p = torch.cuda.get_device_properties(self.dev)
         log(f"device: {p.name} ({p.gcnArchName}), {p.multi_processor_count} CUs")
-        self.sA, self.sB = torch.cuda.Stream(), torch.cuda.Stream()
+        # the two copy streams get a hardware queue each (hiprt.QueueStreams):
+        # plain streams may share one and then run the two directions in turn
+        self.queues = hiprt.QueueStreams(2, p.multi_processor_count)
+        self.sA, self.sB = self.queues.streams
 
     def run_steps(self, r, batch_ids, streams, k, max_wgs, events=None, **kw):
         if self.args.desc_upload:
@@ -1161,7 +1164,8 @@ def bench_interference(c: Ctx, args):
         acts.append(torch.empty(shape[0], dtype=torch.bfloat16, device=c.dev))
     chain = Chain(weights, acts)
     wbytes = sum(w.numel() * 2 for w in weights)
-    sD = torch.cuda.Stream()
+    dq = hiprt.QueueStreams(1, torch.cuda.get_device_properties(c.dev).multi_processor_count)
+    sD = dq.streams[0]                 # the decode stream: a hardware queue of its own
     wl = W.kv_blocks(seed=0, directions="both")
     r = c.Resident(wl)
     period = 0.050
@@ -1307,10 +1311,13 @@ def bench_interference(c: Ctx, args):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    # 100 steps of the headline burst time about 0.15 s: long enough that a
-    # transient slow window of the two-stream link share does not set the value
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    # 600 steps of the headline burst time about 0.9 s.  Measured on MI355X,
+    # the rate of two copy kernels on two streams varies over time: 20-step
+    # windows at 68-81 GB/s against 85-88 in between, in stretches of up to
+    # a few hundred ms, so a 0.15 s timed region read 71-82 GB/s in 3 of 8
+    # processes; a longer one averages over those stretches as a long run does
+    ap.add_argument("--steps", type=int, default=600)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--max-wgs", type=int, default=None,
                     help=f"workgroup cap (default {DEFAULT_MAX_WGS}; pair: KVCOPY_WGS_AUTO)")
     ap.add_argument("--workload", default="kv", choices=["kv", "pair", "d2d", "mixed", "moe",
