@@ -144,8 +144,14 @@ class Ctx:
         log(f"device: {p.name} ({p.gcnArchName}), {p.multi_processor_count} CUs")
         # the two copy streams get a hardware queue each (hiprt.QueueStreams):
         # plain streams may share one and then run the two directions in turn
-        self.queues = hiprt.QueueStreams(2, p.multi_processor_count)
-        self.sA, self.sB = self.queues.streams
+        self.stream_kind = "a hardware queue each (full CU mask)"
+        try:
+            self.queues = hiprt.QueueStreams(2, p.multi_processor_count)
+            self.sA, self.sB = self.queues.streams
+        except RuntimeError as e:
+            log(f"  dedicated-queue streams unavailable ({e}); using torch streams")
+            self.stream_kind = "torch streams (dedicated queues unavailable)"
+            self.sA, self.sB = torch.cuda.Stream(), torch.cuda.Stream()
 
     def run_steps(self, r, batch_ids, streams, k, max_wgs, events=None, **kw):
         if self.args.desc_upload:
@@ -403,7 +409,8 @@ def bench_kv(c: Ctx, args):
                     "4 KiB D2H per step, concurrent on two streams, 65,536-block device pool, "
                     "mapped pinned host buffers",
         "descriptors_per_step": n_desc, "bytes_per_step": step_bytes,
-        "max_wgs": max_wgs, "chunk_bytes": K.CHUNK_DEFAULT, "seed": 0})
+        "max_wgs": max_wgs, "chunk_bytes": K.CHUNK_DEFAULT, "seed": 0,
+        "streams": c.stream_kind})
     line["roofline"] = {
         "bound": "pcie", "kernel": KERNEL_NAMES[dom], "achieved": round(ach[dom], 3),
         "peak": PCIE_PEAK_GBS, "unit": "GB/s", "frac": round(ach[dom] / PCIE_PEAK_GBS, 4),
@@ -1164,8 +1171,12 @@ def bench_interference(c: Ctx, args):
         acts.append(torch.empty(shape[0], dtype=torch.bfloat16, device=c.dev))
     chain = Chain(weights, acts)
     wbytes = sum(w.numel() * 2 for w in weights)
-    dq = hiprt.QueueStreams(1, torch.cuda.get_device_properties(c.dev).multi_processor_count)
-    sD = dq.streams[0]                 # the decode stream: a hardware queue of its own
+    try:                               # the decode stream: a hardware queue of its own
+        dq = hiprt.QueueStreams(1, torch.cuda.get_device_properties(c.dev).multi_processor_count)
+        sD = dq.streams[0]
+    except RuntimeError as e:
+        log(f"  dedicated-queue decode stream unavailable ({e}); using a torch stream")
+        sD = torch.cuda.Stream()
     wl = W.kv_blocks(seed=0, directions="both")
     r = c.Resident(wl)
     period = 0.050
