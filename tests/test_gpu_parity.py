@@ -167,6 +167,26 @@ def test_irregular_chunk_sizes(K, dname, chunk):
     res.free()
 
 
+def test_kv_blocks_concurrent_on_dedicated_queues(K):
+    """The headline burst on the streams bench.py uses: a hardware queue each
+    (full CU mask), wrapped as torch streams."""
+    from block_copy_amd import hiprt
+    from block_copy_amd.harness import Resident
+    wl = W.kv_blocks(seed=4, directions="both")
+    res = Resident(wl)
+    q = hiprt.QueueStreams(2, torch.cuda.get_device_properties(0).multi_processor_count)
+    try:
+        for sentinel in (W.SENTINEL_A, W.SENTINEL_B):
+            _say("kv both on dedicated queues, sentinel", hex(sentinel))
+            res.fill(sentinel)
+            _run(res, [0, 1], 128, streams=q.streams)
+            _check(res, [0, 1], f"h2d+d2h dedicated queues sentinel={sentinel:#x}", sentinel)
+    finally:
+        torch.cuda.synchronize()
+        q.destroy()
+        res.free()
+
+
 @pytest.mark.parametrize("beside", ["alone", "h2d_other_stream", "h2d_same_stream"])
 def test_d2h_store_forms(K, beside):
     """A D2H batch stores with system scope unless one of the library's H2D
