@@ -200,7 +200,10 @@ void kvcopy_plan_free(kvcopy_plan_t *plan);
  * max_wgs: workgroup cap ([PF] "Follow-up", item 1: a bounded grid; "Proposed
  *          direction": max_grid_blocks).  KVCOPY_WGS_ALL (0) = one wavefront
  *          per chunk; KVCOPY_WGS_AUTO (-1) = the device's tuned or default
- *          cap.  Below -1 = KVCOPY_EINVAL.
+ *          cap.  Below -1 = KVCOPY_EINVAL.  Measured on MI355X, two copy
+ *          kernels running at once on two streams overlap only while each
+ *          stays within about 256 workgroups (1,024 wavefronts); past that
+ *          they run as if one after the other.
  * stream:  HIP stream (NULL = the null stream) of the calling thread's
  *          current device: the staging ring, the completion events and the
  *          kernel all belong to that device.
