@@ -5,9 +5,20 @@
 // threads.  The vLLM PR #42212 report, section "key source snippet" (the
 // tuned constants), keeps the smallest worker count within 5% of peak.  The
 // probe times shuffled 4 KiB blocks at a ladder of caps and keeps the
-// smallest cap within 5% of the best rate.  For H2D and D2H both directions
+// smallest cap within 2% of the best rate.  For H2D and D2H both directions
 // run together, which is how KV offload bursts arrive (PegaFlow issue #408,
 // "Test setup": H2D and D2H concurrently on separate streams).
+//
+// Window length and tolerance, measured on MI355X over three processes for
+// H2D + D2H on two streams: with 6 timed batches per cap the probe rated
+// 32 or 64 workgroups best (79-85 GB/s against 79-80 at 128), but those
+// caps ran 600-step bursts at 79-81 GB/s against 76-86 at 128; with 24
+// batches it rated 128 best (85-86) and 64 within 5% (83), which ran at
+// 76-83 against 85-89 at 128.  So the windows are 24 batches long (about a
+// second of probing) and only caps within 2% of the best count as ties.
+// The smaller grid that the 5% rule favours does not protect co-running
+// kernels on this part either: they wait on queued host-link traffic, not
+// on compute units.
 #include <stdint.h>
 
 #include <algorithm>
@@ -21,8 +32,9 @@ namespace {
 constexpr uint64_t kBlocks = 8192;
 constexpr uint64_t kBlock = 4096;
 constexpr uint64_t kBytes = kBlocks * kBlock;   // 32 MiB per direction
-constexpr int kWarm = 2;                         // untimed batches per cap
-constexpr int kReps = 6;                         // timed batches per cap
+constexpr int kWarm = 4;                         // untimed batches per cap
+constexpr int kReps = 24;                        // timed batches per cap
+constexpr double kTie = 0.98;                    // a cap this close to the best rate ties
 constexpr int kSweeps = 3;                       // ascending, descending, ascending
 const int kCaps[KVCOPY_AUTOTUNE_NCAPS] = KVCOPY_AUTOTUNE_CAPS;
 
@@ -166,7 +178,7 @@ extern "C" int kvcopy_autotune(int dir, hipStream_t s0, hipStream_t s1, int *out
     }
     int chosen = KVCOPY_WGS_ALL;
     for (int c = 0; c < ncaps; ++c)
-        if (rate[c] >= 0.95 * best) {
+        if (rate[c] >= kTie * best) {
             chosen = kCaps[c];
             break;
         }

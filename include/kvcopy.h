@@ -342,14 +342,16 @@ void kvcopy_job_destroy(kvcopy_job_t *job);
  * picks the smallest number of workers within 5% of peak bandwidth.  This
  * call does both on the current device: it allocates its own probe buffers
  * (32 MiB of mapped pinned host memory and 32 MiB of device memory per
- * direction, freed before it returns), times six batches of 8,192 shuffled
- * 4 KiB blocks per direction at each cap of KVCOPY_AUTOTUNE_CAPS, after two
+ * direction, freed before it returns), times 24 batches of 8,192 shuffled
+ * 4 KiB blocks per direction at each cap of KVCOPY_AUTOTUNE_CAPS, after four
  * untimed ones (for H2D or D2H both directions run together, H2D on s0 and
  * D2H on s1, as in a KV offload burst; D2D runs on s0), in three sweeps
  * over the caps (ascending, descending, ascending) keeping each cap's
- * median rate, and records the smallest cap within 5% of the best rate as
+ * median rate, and records the smallest cap within 2% of the best rate as
  * the device's KVCOPY_WGS_AUTO cap for `dir` (for H2D or D2H: for both).
- * Blocks until done (about a fifth of a second).
+ * On MI355X, shorter windows and the 5% rule picked caps of 32-64 that ran
+ * long H2D + D2H bursts 5-10% slower than 128.
+ * Blocks until done (about a second).
  * s0, s1: the streams the caller will copy on (the hardware queues they map
  *   to matter); NULL = streams created for the probe.
  * out_wgs (may be NULL): the chosen cap (0 = full grid).
