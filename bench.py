@@ -153,9 +153,16 @@ class Ctx:
             self.stream_kind = "torch streams (dedicated queues unavailable)"
             self.sA, self.sB = torch.cuda.Stream(), torch.cuda.Stream()
 
-    def run_steps(self, r, batch_ids, streams, k, max_wgs, events=None, **kw):
+    def run_steps(self, r, batch_ids, streams, k, max_wgs, events=None, joined=False, **kw):
+        """k steps; a step submits each batch on its stream.  With `joined`,
+        every stream waits for the others' batches of the step before its
+        next one, so the batches of a step start together and the step ends
+        when the last one does."""
         if self.args.desc_upload:
             kw["flags"] = kw.get("flags", 0) | self.K.F_DESC_UPLOAD
+        marks = None
+        if joined and len(streams) > 1:
+            marks = [self.hiprt.Event(timing=False) for _ in streams]
         for i in range(k):
             for j, (bi, st) in enumerate(zip(batch_ids, streams)):
                 extra = dict(kw)
@@ -163,6 +170,13 @@ class Ctx:
                     extra.update(kernel_begin=events[i][j][0].h, kernel_end=events[i][j][1].h)
                 g = max_wgs[j] if isinstance(max_wgs, (list, tuple)) else max_wgs
                 r.submit(bi, g, st, **extra)
+            if marks:
+                for m, st in zip(marks, streams):
+                    m.record(st)
+                for j, st in enumerate(streams):
+                    for jj, m in enumerate(marks):
+                        if jj != j:
+                            self.hiprt.stream_wait(st, m)
 
     def timed(self, r, batch_ids, streams, k, w, max_wgs, with_events=True, **kw):
         """Seconds per step over k timed steps (after w warm-up steps), and the
@@ -189,7 +203,8 @@ class Ctx:
     def timed_bracketed(self, r, batch_ids, streams, k, w, max_wgs, **kw):
         """Seconds per step over k timed steps, and each stream's mean kernel
         duration (ms): one HIP event pair per stream brackets its k kernels,
-        which run back to back, so no event sits between two kernels."""
+        which run back to back (joined=True: step by step), so no timing
+        event sits between two kernels."""
         torch, hiprt = self.torch, self.hiprt
         self.run_steps(r, batch_ids, streams, w, max_wgs, **kw)
         torch.cuda.synchronize()
@@ -309,7 +324,11 @@ def bench_kv(c: Ctx, args):
     # No HIP event sits between two kernels (events recorded between the
     # kernels perturb how the two streams overlap): one event pair per stream
     # brackets that stream's back-to-back kernels over the timed steps.
-    step_s, kern_ms = c.timed_bracketed(res, [0, 1], [sA, sB], args.steps, args.warmup, max_wgs)
+    # The step starts both directions together and ends when both are done
+    # (joined): free-running streams drift out of phase over hundreds of
+    # steps and leave stretches with one direction running alone.
+    step_s, kern_ms = c.timed_bracketed(res, [0, 1], [sA, sB], args.steps, args.warmup, max_wgs,
+                                        joined=True)
     value = gbs(step_bytes, step_s)
     log(f"  bidirectional: {step_s * 1e3:.3f} ms/step, {value:.2f} GB/s; mean kernel ms per "
         f"stream {kern_ms}")
@@ -331,7 +350,7 @@ def bench_kv(c: Ctx, args):
     if not args.skip_extras:
         alone = {}
         for j, name in ((0, "h2d"), (1, "d2h")):
-            s, _ = c.timed_bracketed(res, [j], [sA], args.steps, args.warmup, max_wgs)
+            s, _ = c.timed_bracketed(res, [j], [sA], args.steps, args.leg_warmup, max_wgs)
             _, km = c.timed(res, [j], [sA], args.steps, 2, max_wgs)
             alone[name] = {"GBps": round(gbs(wl.batches[j].nbytes, s), 3),
                            "ms_per_call": round(s * 1e3, 4), "kernel_ms": round(km[0], 4),
@@ -342,7 +361,7 @@ def bench_kv(c: Ctx, args):
         # H2D kernel of the library runs beside it)
         e_ = np.zeros(0, np.uint64)
         s1_, d1_ = res.addrs[1]
-        for _ in range(args.warmup):
+        for _ in range(args.leg_warmup):
             K.kvcopy_batch_pair(s1_, d1_, wl.batches[1].size, e_, e_, e_, K.WGS_AUTO, sA.cuda_stream)
         torch.cuda.synchronize()
         ev0, ev1 = hiprt.Event(), hiprt.Event()
@@ -363,7 +382,8 @@ def bench_kv(c: Ctx, args):
         # the startup probe's choice, and the headline step at that cap
         cap, rates = K.kvcopy_autotune(K.H2D, sA.cuda_stream, sB.cuda_stream)
         auto = {"h2d_d2h": cap, "probe_GBps": {str(k): round(v, 2) for k, v in rates.items()}}
-        s_, km = c.timed(res, [0, 1], [sA, sB], args.steps, args.warmup, K.WGS_AUTO)
+        s_, km = c.timed_bracketed(res, [0, 1], [sA, sB], args.steps, args.leg_warmup, K.WGS_AUTO,
+                                   joined=True)
         auto["bidirectional_GBps_at_auto"] = round(gbs(step_bytes, s_), 3)
         extras["autotune"] = auto
         log(f"  autotune: {auto}")
@@ -533,7 +553,8 @@ def bench_pair(c: Ctx, args):
         # the two-stream submission of the same burst first: it also brings
         # both streams into use before the contiguous ceilings are taken on them
         extras["two_streams_same_run_GBps"] = round(gbs(step_bytes, c.timed_bracketed(
-            res, [0, 1], [c.sA, c.sB], args.steps, args.warmup, DEFAULT_MAX_WGS)[0]), 3)
+            res, [0, 1], [c.sA, c.sB], args.steps, args.leg_warmup, DEFAULT_MAX_WGS,
+            joined=True)[0]), 3)
         extras["contiguous_memcpy_ceiling_GBps"] = ceilings(c)
         log(f"  ceilings {extras['contiguous_memcpy_ceiling_GBps']}, two streams at "
             f"{DEFAULT_MAX_WGS}: {extras['two_streams_same_run_GBps']} GB/s")
@@ -580,7 +601,7 @@ def pair_rates(c: Ctx, res, args):
     step_bytes = res.wl.nbytes
     out = {}
     for g in (32, 48, 64, 80, 128, 256, 0):
-        for _ in range(args.warmup):
+        for _ in range(args.leg_warmup):
             c.pair_step(res, c.sA, g)
         torch.cuda.synchronize()
         use_ev = not args.no_events
@@ -741,7 +762,7 @@ def d2d_results(c: Ctx, args):
         r = c.Resident(wld)
         # back-to-back calls with no per-launch event (call rate), then the
         # same calls with the kernel's own start/end events (kernel time)
-        s, stream_ms = c.timed_bracketed(r, [0], [c.sA], args.steps, args.warmup, 0)
+        s, stream_ms = c.timed_bracketed(r, [0], [c.sA], args.steps, args.leg_warmup, 0)
         _, km = c.timed(r, [0], [c.sA], args.steps, 2, 0)
         pl = K.kvcopy_plan(*r.addrs[0], wld.batches[0].size)
         hbm = 2 * wld.batches[0].nbytes + pl.n_chunks * REC_BYTES
@@ -999,7 +1020,7 @@ def bench_mixed(c: Ctx, args):
         b = wl.batches[0]
         pl = K.kvcopy_plan(*r.addrs[0], b.size)
         k = max(5, min(args.steps * 5, 200 if n <= 256 else args.steps))
-        s, _ = c.timed_bracketed(r, [0], [c.sA], k, args.warmup, g)
+        s, _ = c.timed_bracketed(r, [0], [c.sA], k, args.leg_warmup, g)
         _, km = c.timed(r, [0], [c.sA], k, 2, g)
         lat = c.latency(r, 0, g, k=50 if n <= 4096 else 10, w=5)
         c.verify(wl, r, [0], f"mixed {n}")       # before the DMA baselines write the same bytes
@@ -1328,7 +1349,12 @@ def main():
     # a few hundred ms, so a 0.15 s timed region read 71-82 GB/s in 3 of 8
     # processes; a longer one averages over those stretches as a long run does
     ap.add_argument("--steps", type=int, default=600)
-    ap.add_argument("--warmup", type=int, default=100)
+    # The workload's own step warms up for 700 steps (about a second of the
+    # headline burst): measured on MI355X, the first second of bidirectional
+    # traffic in a process runs a few percent slower (two 600-step runs back
+    # to back: 84.4-87.0 GB/s, then 88.0-88.2).  Secondary legs warm up for
+    # at most 100 of their own steps (args.leg_warmup).
+    ap.add_argument("--warmup", type=int, default=700)
     ap.add_argument("--max-wgs", type=int, default=None,
                     help=f"workgroup cap (default {DEFAULT_MAX_WGS}; pair: KVCOPY_WGS_AUTO)")
     ap.add_argument("--workload", default="kv", choices=["kv", "pair", "d2d", "mixed", "moe",
@@ -1350,6 +1376,7 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1536)
     ap.add_argument("--decode-runs", type=int, default=3)
     args = ap.parse_args()
+    args.leg_warmup = min(args.warmup, 100)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: the copy path has no multi-GPU step "

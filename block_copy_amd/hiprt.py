@@ -46,6 +46,8 @@ hip.hipHostFree.argtypes = [ctypes.c_void_p]
 hip.hipMemset.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t]
 hip.hipStreamCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
 hip.hipRuntimeGetVersion.argtypes = [ctypes.POINTER(ctypes.c_int)]
+hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+hip.hipStreamWaitEvent.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint]
 
 
 class _MemLocation(ctypes.Structure):
@@ -71,7 +73,8 @@ if _has_batch:
 for _f in ("hipEventCreate", "hipEventRecord", "hipEventSynchronize", "hipEventElapsedTime",
            "hipEventDestroy", "hipMemcpyAsync", "hipStreamSynchronize", "hipDeviceSynchronize",
            "hipExtStreamCreateWithCUMask", "hipStreamDestroy", "hipMalloc", "hipFree",
-           "hipHostMalloc", "hipHostFree", "hipMemset", "hipStreamCreate", "hipRuntimeGetVersion"):
+           "hipHostMalloc", "hipHostFree", "hipMemset", "hipStreamCreate", "hipRuntimeGetVersion",
+           "hipEventCreateWithFlags", "hipStreamWaitEvent"):
     getattr(hip, _f).restype = ctypes.c_int
 
 
@@ -81,9 +84,12 @@ def check(rc: int, what: str) -> None:
 
 
 class Event:
-    def __init__(self):
+    def __init__(self, timing: bool = True):
         h = ctypes.c_void_p()
-        check(hip.hipEventCreate(ctypes.byref(h)), "hipEventCreate")
+        if timing:
+            check(hip.hipEventCreate(ctypes.byref(h)), "hipEventCreate")
+        else:   # hipEventDisableTiming: an ordering marker only
+            check(hip.hipEventCreateWithFlags(ctypes.byref(h), 2), "hipEventCreateWithFlags")
         self.h = h.value
 
     def record(self, stream) -> None:
@@ -143,6 +149,11 @@ def memcpy_batch_async(dsts, srcs, sizes, stream, src_host: bool, dst_host: bool
 
 def stream_sync(stream) -> None:
     check(hip.hipStreamSynchronize(_s(stream)), "hipStreamSynchronize")
+
+
+def stream_wait(stream, event: "Event") -> None:
+    """Work queued on `stream` after this waits for `event` (hipStreamWaitEvent)."""
+    check(hip.hipStreamWaitEvent(_s(stream), event.h, 0), "hipStreamWaitEvent")
 
 
 class CUMaskStream:
