@@ -161,7 +161,9 @@ class Ctx:
         if self.args.desc_upload:
             kw["flags"] = kw.get("flags", 0) | self.K.F_DESC_UPLOAD
         marks = None
-        if joined and len(streams) > 1:
+        # profiler runs (--no-events) make no event calls at all: rocprofv3 7.2
+        # aborted in its own tool on them, so there the streams run free
+        if joined and len(streams) > 1 and not self.args.no_events:
             marks = [self.hiprt.Event(timing=False) for _ in streams]
         for i in range(k):
             for j, (bi, st) in enumerate(zip(batch_ids, streams)):
@@ -1365,8 +1367,9 @@ def main():
     ap.add_argument("--skip-extras", action="store_true",
                     help="only the headline workload (for profiling runs)")
     ap.add_argument("--no-events", action="store_true",
-                    help="do not bracket kernels with HIP events (profiler runs); the kernel "
-                         "time is then taken as the step time")
+                    help="make no HIP event calls (profiler runs): kernels are not bracketed, "
+                         "the kernel time is taken as the step time, and the two directions "
+                         "of a step are not joined")
     ap.add_argument("--counter-calibration", action="store_true",
                     help="also run a plain 64 MiB elementwise copy kernel 5 times, whose "
                          "known traffic scales the PMC byte counters")
