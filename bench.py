@@ -973,7 +973,7 @@ def bench_d2d(c: Ctx, args):
         "max_wgs": 0, "chunk_bytes": c.K.CHUNK_DEFAULT, "seed": 0})
     line["value_source"] = src
     if src.startswith("C"):
-        line["value_calls"] = cc["calls"]
+        line["value_calls"] = cc.get("pipelined_calls", cc["calls"])
     line["value_python_GBps"] = r1["GBps_payload"]
     big = res["65536x4KiB"]
     dist = big.get("distinct_calls")
