@@ -1054,6 +1054,24 @@ def bench_mixed(c: Ctx, args):
 # MoE expert gather
 # ---------------------------------------------------------------------------
 
+def call_us(c: Ctx, submit, stream):
+    """Microseconds of one call: GPU time between events recorded around it,
+    or, with --no-events (profiler runs, which make no event calls), wall
+    time from a synchronised stream to the call's completion."""
+    hiprt = c.hiprt
+    if c.args.no_events:
+        hiprt.stream_sync(stream)
+        t0 = time.perf_counter()
+        submit()
+        hiprt.stream_sync(stream)
+        return (time.perf_counter() - t0) * 1e6
+    e0, e1 = hiprt.Event(), hiprt.Event()
+    e0.record(stream)
+    submit()
+    e1.record(stream)
+    return e0.elapsed_ms(e1) * 1e3
+
+
 def bench_moe(c: Ctx, args):
     W, K, hiprt = c.W, c.K, c.hiprt
     calls = 100
@@ -1067,11 +1085,7 @@ def bench_moe(c: Ctx, args):
             t_us, sizes = [], []
             with no_gc():
                 for i in range(calls):
-                    e0, e1 = hiprt.Event(), hiprt.Event()
-                    e0.record(c.sA)
-                    r.submit(i, g, c.sA, chunk_bytes=chunk)
-                    e1.record(c.sA)
-                    t_us.append(e0.elapsed_ms(e1) * 1e3)
+                    t_us.append(call_us(c, lambda: r.submit(i, g, c.sA, chunk_bytes=chunk), c.sA))
                     sizes.append(wl.batches[i].nbytes)
             rates = [gbs(z, t / 1e6) for z, t in zip(sizes, t_us)]
             out[f"{name}/max_wgs={g}"] = {
@@ -1086,11 +1100,7 @@ def bench_moe(c: Ctx, args):
     t_us, sizes = [], []
     with no_gc():
         for i in range(calls):
-            e0, e1 = hiprt.Event(), hiprt.Event()
-            e0.record(c.sA)
-            r.submit(i, 32, c.sA)
-            e1.record(c.sA)
-            t_us.append(e0.elapsed_ms(e1) * 1e3)
+            t_us.append(call_us(c, lambda: r.submit(i, 32, c.sA), c.sA))
             sizes.append(small.batches[i].nbytes)
     c.verify(small, r, list(range(calls)), "moe 1-8 misses")
     r.free()
@@ -1100,8 +1110,9 @@ def bench_moe(c: Ctx, args):
     log(f"  moe 1-8 misses: {out['context_1_to_8_misses/max_wgs=32']}")
     # Device-resident miss lists, one HIP graph per call (kvcopy_batch_device):
     # the decode-side form in which a router kernel leaves the list on the GPU.
-    for name, misses in (("device_graph_26_to_39_misses", (26, 39)),
-                         ("device_graph_1_to_8_misses", (1, 8))):
+    for name, misses in (() if args.no_events else
+                         (("device_graph_26_to_39_misses", (26, 39)),
+                          ("device_graph_1_to_8_misses", (1, 8)))):
         out[f"{name}/max_wgs=32"] = moe_device_graph(c, W.moe_gather(seed=2, calls=calls,
                                                                     misses=misses), 32)
         log(f"  moe {name}: {out[f'{name}/max_wgs=32']}")
