@@ -1394,7 +1394,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: the copy path has no multi-GPU step "
-              "(the sharding plan is in DESIGN.md); run with --gpus 1", file=sys.stderr)
+              "(each GPU would run the same kernel on its own share of the descriptors); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     c = Ctx(args)
     fn = {"kv": bench_kv, "pair": bench_pair, "d2d": bench_d2d, "mixed": bench_mixed, "moe": bench_moe,
