@@ -1284,16 +1284,21 @@ def bench_interference(c: Ctx, args):
             th = threading.Thread(target=transfer, daemon=True)
             th.start()
         gpu_ms, wall_ms = [], []
-        evs = [(hiprt.Event(), hiprt.Event()) for _ in range(steps)]
+        # --no-events (profiler runs): no event pairs; the step's wall time
+        # (launches + stream sync) stands in for its GPU time
+        evs = [(None, None) if args.no_events else (hiprt.Event(), hiprt.Event())
+               for _ in range(steps)]
         with no_gc():
             for e0, e1 in evs:
                 t0 = time.perf_counter()
-                e0.record(sD)
+                if e0 is not None:
+                    e0.record(sD)
                 chain.run(sD)
-                e1.record(sD)
+                if e1 is not None:
+                    e1.record(sD)
                 hiprt.stream_sync(sD)
                 wall_ms.append((time.perf_counter() - t0) * 1e3)
-        gpu_ms = [e0.elapsed_ms(e1) for e0, e1 in evs]
+        gpu_ms = wall_ms if args.no_events else [e0.elapsed_ms(e1) for e0, e1 in evs]
         dur = time.perf_counter() - t_start
         if th is not None:
             stop.set()
@@ -1302,6 +1307,14 @@ def bench_interference(c: Ctx, args):
 
     modes = ["none", "direct", 1, 2, 8, 32, 128, 0, "pipe:1", "pipe:4", "job:1024", "job:2048",
              "job:4096", "cumask:8", "cumask:32", "pair:8", "pair:16", "pair:64"]
+    if args.modes:     # a subset, say for a profiler run; "none" (the baseline) always runs
+        pick = [m for m in args.modes.split(",") if m]
+        unknown = [m for m in pick if m not in [str(x) for x in modes]]
+        if unknown:
+            print(f"unknown interference modes {unknown}; known: {[str(x) for x in modes]}",
+                  file=sys.stderr)
+            sys.exit(2)
+        modes = [m for m in modes if str(m) == "none" or str(m) in pick]
     results = {str(m): {"gpu": [], "wall": [], "rate": [], "bursts": 0} for m in modes}
     for rep in range(args.decode_runs):
         order = modes[rep % len(modes):] + modes[:rep % len(modes)]
@@ -1341,11 +1354,14 @@ def bench_interference(c: Ctx, args):
             table[m]["decode_ms_lost_per_burst"] = round(
                 (table[m]["gpu_ms_mean"] - table["none"]["gpu_ms_mean"]) * n_steps
                 / table[m]["bursts"], 3)
-    line = base_line(args, table["32"]["gpu_ms_p99"], "ms", table["none"]["gpu_ms_mean"] / 1e3, {
+    headline_mode = "32" if "32" in table else [m for m in table if m != "none"][0] \
+        if len(table) > 1 else "none"
+    line = base_line(args, table[headline_mode]["gpu_ms_p99"], "ms", table["none"]["gpu_ms_mean"] / 1e3, {
         "workload": f"decode loop of {n_gemv} bf16 GEMVs ({d_ff}x{d_model} and {d_model}x{d_ff}, "
                     f"{wbytes / 1e9:.2f} GB of distinct weights per step) while a bidirectional "
                     "burst (16,384 x 4 KiB H2D + 16,384 x 4 KiB D2H) starts every 50 ms; value = "
-                    "decode step p99 (GPU time) with max_wgs = 32",
+                    f"decode step p99 ({'wall' if args.no_events else 'GPU'} time) in mode "
+                    f"{headline_mode} (an integer mode is max_wgs on two streams)",
         "decode_steps_per_run": steps, "runs_per_mode": args.decode_runs, "seed": 0},
         dtype="bf16", higher=False)
     line["modes"] = table
@@ -1389,6 +1405,8 @@ def main():
                          "instead of reading them in place from pinned staging")
     ap.add_argument("--decode-steps", type=int, default=1536)
     ap.add_argument("--decode-runs", type=int, default=3)
+    ap.add_argument("--modes", default="",
+                    help="interference: comma-separated subset of the modes (default: all)")
     args = ap.parse_args()
     args.leg_warmup = min(args.warmup, 100)
     world = int(os.environ.get("WORLD_SIZE", "1"))
