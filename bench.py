@@ -153,6 +153,19 @@ class Ctx:
             self.stream_kind = "torch streams (dedicated queues unavailable)"
             self.sA, self.sB = torch.cuda.Stream(), torch.cuda.Stream()
 
+    def close(self):
+        """Explicit teardown before the interpreter exits: wait for the GPU,
+        destroy the streams made here, and collect the objects (events,
+        host buffers) whose finalisers make HIP calls while the runtime is
+        still whole (during interpreter shutdown those finalisers skip their
+        HIP calls)."""
+        self.torch.cuda.synchronize()
+        if getattr(self, "queues", None) is not None:
+            self.queues.destroy()
+            self.queues = None
+        gc.collect()
+        self.torch.cuda.synchronize()
+
     def run_steps(self, r, batch_ids, streams, k, max_wgs, events=None, joined=False, **kw):
         """k steps; a step submits each batch on its stream.  With `joined`,
         every stream waits for the others' batches of the step before its
@@ -322,6 +335,24 @@ def bench_kv(c: Ctx, args):
     step_bytes = wl.nbytes
     n_desc = sum(b.n for b in wl.batches)
     max_wgs = args.max_wgs if args.max_wgs is not None else DEFAULT_MAX_WGS
+    extras = {}
+    if not args.skip_extras:
+        # The host link's contiguous ceilings and each direction alone come
+        # first: they are part of the report, and they leave the link in
+        # steady use before the headline's own warm-up (measured on MI355X,
+        # bidirectional traffic in the first quarter second of a process
+        # runs at 51-69 GB/s).
+        extras["contiguous_memcpy_ceiling_GBps"] = ceilings(c)
+        log(f"  contiguous ceilings: {extras['contiguous_memcpy_ceiling_GBps']}")
+        alone = {}
+        for j, name in ((0, "h2d"), (1, "d2h")):
+            s, _ = c.timed_bracketed(res, [j], [sA], args.steps, args.leg_warmup, max_wgs)
+            _, km = c.timed(res, [j], [sA], args.steps, 2, max_wgs)
+            alone[name] = {"GBps": round(gbs(wl.batches[j].nbytes, s), 3),
+                           "ms_per_call": round(s * 1e3, 4), "kernel_ms": round(km[0], 4),
+                           "latency": c.latency(res, j, max_wgs, k=50, w=5)}
+            log(f"  {name} alone: {alone[name]}")
+        extras["per_direction_alone"] = alone
     log(f"headline: {n_desc} descriptors, {step_bytes} B per step, max_wgs={max_wgs}")
     # No HIP event sits between two kernels (events recorded between the
     # kernels perturb how the two streams overlap): one event pair per stream
@@ -338,7 +369,6 @@ def bench_kv(c: Ctx, args):
     algo = [wl.batches[j].nbytes + plans[j].n_chunks * REC_BYTES for j in range(2)]
     ach = [gbs(algo[j], kern_ms[j] / 1e3) for j in range(2)]
 
-    extras = {}
     if args.sweep:
         sweep = {}
         for name, ids, sts in (("h2d", [0], [sA]), ("d2h", [1], [sA]), ("both", [0, 1], [sA, sB])):
@@ -349,18 +379,14 @@ def bench_kv(c: Ctx, args):
                 log(f"  sweep {name} max_wgs={g}: {gbs(nbytes, s_):.2f} GB/s, kernel ms "
                     f"{[round(x, 3) for x in km]}")
         extras["max_wgs_sweep_GBps"] = sweep
+    if not args.skip_extras and not args.no_events:
+        extras["headline_windows"] = headline_windows(c, res, max_wgs)
+        log(f"  headline windows: {dict((k, v) for k, v in extras['headline_windows'].items() if k not in ('GBps', 'kernel_ms_per_stream'))}")
     if not args.skip_extras:
-        alone = {}
-        for j, name in ((0, "h2d"), (1, "d2h")):
-            s, _ = c.timed_bracketed(res, [j], [sA], args.steps, args.leg_warmup, max_wgs)
-            _, km = c.timed(res, [j], [sA], args.steps, 2, max_wgs)
-            alone[name] = {"GBps": round(gbs(wl.batches[j].nbytes, s), 3),
-                           "ms_per_call": round(s * 1e3, 4), "kernel_ms": round(km[0], 4),
-                           "latency": c.latency(res, j, max_wgs, k=50, w=5)}
-            log(f"  {name} alone: {alone[name]}")
-        # a lone D2H list through kvcopy_batch_pair (whose kernel always
-        # stores with system scope, as kvcopy_batch's D2H kernel does when no
-        # H2D kernel of the library runs beside it)
+        alone = extras["per_direction_alone"]
+        # a lone D2H list through kvcopy_batch_pair (whose kernel stores with
+        # the sc1 form, as kvcopy_batch's D2H kernel does when no H2D kernel
+        # of the library runs beside it)
         e_ = np.zeros(0, np.uint64)
         s1_, d1_ = res.addrs[1]
         for _ in range(args.leg_warmup):
@@ -380,17 +406,17 @@ def bench_kv(c: Ctx, args):
         for nm in ("h2d", "d2h"):
             alone[nm]["latency_c_caller"] = cl.get(f"kv_{nm}_16384x4KiB", cl.get("error"))
         log(f"  each direction alone, C caller: {cl}")
-        extras["per_direction_alone"] = alone
         # the startup probe's choice, and the headline step at that cap
         cap, rates = K.kvcopy_autotune(K.H2D, sA.cuda_stream, sB.cuda_stream)
         auto = {"h2d_d2h": cap, "probe_GBps": {str(k): round(v, 2) for k, v in rates.items()}}
         s_, km = c.timed_bracketed(res, [0, 1], [sA, sB], args.steps, args.leg_warmup, K.WGS_AUTO,
                                    joined=True)
         auto["bidirectional_GBps_at_auto"] = round(gbs(step_bytes, s_), 3)
+        if not args.no_events:
+            auto["windows_at_auto"] = headline_windows(c, res, K.WGS_AUTO, n=10)
+            auto["windows_at_auto"].pop("kernel_ms_per_stream")
         extras["autotune"] = auto
         log(f"  autotune: {auto}")
-        extras["contiguous_memcpy_ceiling_GBps"] = ceilings(c)
-        log(f"  contiguous ceilings: {extras['contiguous_memcpy_ceiling_GBps']}")
         frag = {}
         for j, name, kind in ((0, "h2d", hiprt.H2D_KIND), (1, "d2h", hiprt.D2H_KIND)):
             frag[name] = dma_baselines(c, plans[j], wl.batches[j].nbytes, kind)
@@ -422,6 +448,9 @@ def bench_kv(c: Ctx, args):
     res.free()
 
     if not args.skip_extras:
+        ceil_h2d = extras["contiguous_memcpy_ceiling_GBps"]["h2d"]
+        extras["mixed_h2d"] = mixed_compact(c, args, ceil_h2d)
+        extras["moe_gather"] = moe_compact(c, args, ceil_h2d)
         extras["d2d"] = d2d_results(c, args)
 
     dom = 0 if kern_ms[0] >= kern_ms[1] else 1
@@ -449,11 +478,8 @@ def bench_kv(c: Ctx, args):
     if both_ceil:
         line["roofline"]["measured_ceiling_both_directions"] = both_ceil
         line["roofline"]["frac_step_of_ceiling_both_directions"] = round(value / both_ceil, 4)
-    line["cpu_baseline"] = {
-        "value": round(cpu["GBps"], 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
-        "cpu": cpu_model(),
-        "sample": f"{cpu['reps']} full steps (16,384 H2D + 16,384 D2H descriptors of 4 KiB each, "
-                  f"per-descriptor memcpy between host images), {cpu['seconds']:.1f} s"}
+    line["cpu_baseline"] = cpu_baseline_record(
+        cpu, "whole steps of 16,384 H2D + 16,384 D2H descriptors of 4 KiB")
     line["parity"] = "bit-exact vs oracle"
     line.update(extras)
     return line
@@ -461,38 +487,123 @@ def bench_kv(c: Ctx, args):
 
 def kv_oracle(c: Ctx, wl, res, args):
     """The oracle's images of one bidirectional step (arena index -> uint8
-    array), and the oracle timed over whole steps for about args.cpu_seconds
-    on one host thread."""
+    array), and the oracle timed over whole steps on one host thread and on
+    every CPU this process may use (host_cpus)."""
     np = c.np
     import oracle
     imgs = [a.host_image().copy() if a.fill == "random" else np.full(a.nbytes, a.sentinel, np.uint8)
             for a in wl.arenas]
     src_snap = {0: imgs[0].copy(), 1: imgs[1]}
+    parts = []
+    for j in range(2):
+        b = wl.batches[j]
+        s, d = res.addrs[j]
+        si, di = int(b.src_arena[0]), int(b.dst_arena[0])
+        parts.append((s, d, b.size, [(res.bases[si], src_snap[si])], [(res.bases[di], imgs[di])]))
+    for p in parts:                                   # the images of one step
+        oracle.copy(*p)
+    cpus = host_cpus()
+    one = oracle_rate(parts, 1, args.cpu_seconds / 2)
+    many = oracle_rate(parts, cpus["threads"], args.cpu_seconds / 2)
+    log(f"  cpu oracle: 1 thread {one['GBps']:.2f} GB/s, {cpus['threads']} threads "
+        f"{many['GBps']:.2f} GB/s ({cpus})")
+    return imgs, {"one": one, "many": many, "cpus": cpus}
 
-    def oracle_step():
-        moved = 0
-        for j in range(2):
-            b = wl.batches[j]
-            s, d = res.addrs[j]
-            si, di = int(b.src_arena[0]), int(b.dst_arena[0])
-            moved += oracle.copy(s, d, b.size, [(res.bases[si], src_snap[si])],
-                                 [(res.bases[di], imgs[di])])
-        return moved
 
-    reps, moved, t0 = 0, 0, time.perf_counter()
-    while True:
-        moved += oracle_step()
-        reps += 1
-        if time.perf_counter() - t0 >= args.cpu_seconds and reps >= 3:
-            break
-    cpu_s = time.perf_counter() - t0
-    cpu_gbs = gbs(moved, cpu_s)
-    log(f"  cpu oracle: {reps} steps in {cpu_s:.2f} s = {cpu_gbs:.2f} GB/s (1 thread)")
-    return imgs, {"GBps": cpu_gbs, "reps": reps, "seconds": cpu_s}
+def host_cpus() -> dict:
+    """The CPUs this process may use: os.cpu_count() (nproc), the affinity
+    mask, and the cgroup CPU quota (cpu.max, in CPUs) if one is set; the
+    oracle's thread count is the smaller of the last two."""
+    nproc = os.cpu_count() or 1
+    try:
+        aff = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        aff = nproc
+    quota = None
+    try:
+        with open("/sys/fs/cgroup/cpu.max") as f:
+            q, per = f.read().split()[:2]
+            if q != "max":
+                quota = int(q) / int(per)
+    except (OSError, ValueError):
+        pass
+    threads = aff if quota is None else max(1, min(aff, int(quota)))
+    return {"nproc": nproc, "affinity_cpus": aff, "cgroup_cpu_quota": quota, "threads": threads}
+
+
+def oracle_rate(parts, threads, seconds, trials=5):
+    """GB/s of the oracle over whole steps (`parts`: the oracle.copy argument
+    tuples of one step) on `threads` host threads.  Each thread copies a
+    contiguous, byte-balanced share of every part's descriptors, so the
+    threads write disjoint bytes; the oracle releases the interpreter lock
+    while it copies.  Median of `trials` timed runs of about seconds/trials
+    each."""
+    import oracle
+    np = sys.modules["numpy"]
+    shares = [[] for _ in range(threads)]
+    total = 0
+    for s, d, z, sa, da in parts:
+        z = np.ascontiguousarray(z, dtype=np.uint64)
+        cum = np.cumsum(z, dtype=np.uint64)
+        total += int(cum[-1]) if len(cum) else 0
+        cuts = [0] + [int(np.searchsorted(cum, int(cum[-1]) * k // threads, side="right"))
+                      for k in range(1, threads)] + [len(z)]
+        for t in range(threads):
+            a, b = cuts[t], cuts[t + 1]
+            if b > a:
+                shares[t].append((np.ascontiguousarray(s[a:b]), np.ascontiguousarray(d[a:b]),
+                                  z[a:b].copy(), sa, da))
+
+    def run(reps):
+        gate = threading.Barrier(threads + 1)
+
+        def work(t):
+            gate.wait()
+            for _ in range(reps):
+                for args_ in shares[t]:
+                    oracle.copy(*args_)
+        ths = [threading.Thread(target=work, args=(t,)) for t in range(threads)]
+        for th in ths:
+            th.start()
+        gate.wait()
+        t0 = time.perf_counter()
+        for th in ths:
+            th.join()
+        return time.perf_counter() - t0
+
+    t1 = run(1)
+    reps = max(1, int(seconds / trials / max(t1, 1e-6)))
+    times = [run(reps) for _ in range(trials)]
+    dt = statistics.median(times)
+    return {"GBps": gbs(total * reps, dt), "reps_per_trial": reps, "trials": trials,
+            "threads": threads, "seconds": round(sum(times) + t1, 2)}
+
+
+def cpu_baseline_record(cpu, what):
+    """The cpu_baseline object of a JSON line from kv_oracle's timing."""
+    many, one, cpus = cpu["many"], cpu["one"], cpu["cpus"]
+    return {"value": round(many["GBps"], 3), "unit": "GB/s", "cores": many["threads"],
+            "kind": "oracle", "cpu": cpu_model(),
+            "single_thread_GBps": round(one["GBps"], 3), "nproc": cpus["nproc"],
+            "affinity_cpus": cpus["affinity_cpus"], "cgroup_cpu_quota": cpus["cgroup_cpu_quota"],
+            "sample": f"{what}: each thread a contiguous byte-balanced share of both directions' "
+                      f"descriptors, per-descriptor memcpy between host images; median of "
+                      f"{many['trials']} runs of {many['reps_per_trial']} steps on "
+                      f"{many['threads']} threads ({many['seconds']:.1f} s), and of "
+                      f"{one['trials']} runs of {one['reps_per_trial']} steps on 1 thread "
+                      f"({one['seconds']:.1f} s)"}
 
 
 def cpu_model() -> str:
-    """The host CPU's model name (for the cpu_baseline record)."""
+    """The host CPU's model name (lscpu, else /proc/cpuinfo)."""
+    import subprocess
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for ln in out.splitlines():
+            if ln.strip().lower().startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
     try:
         with open("/proc/cpuinfo") as f:
             for ln in f:
@@ -511,6 +622,141 @@ def check_kv_images(wl, final, imgs, what):
         if not np.array_equal(final[i], imgs[i]):
             bad = int(np.flatnonzero(final[i] != imgs[i])[0])
             log(f"PARITY FAILURE{what} in arena {wl.arenas[i].name} at byte {bad}")
+            sys.exit(3)
+
+
+# ---------------------------------------------------------------------------
+# Compact legs of the default run: mixed sizes (H2D) and the MoE gather
+# ---------------------------------------------------------------------------
+
+def mixed_compact(c: Ctx, args, ceil_h2d):
+    """H2D with mixed 4-28 KiB sizes at N = 16, 256, 4,096, 65,536 (the
+    vLLM PR #42212 report's small-block CPU->GPU case): per N the kernel-only
+    rate (the kernel's own events), the rate of back-to-back calls, isolated
+    per-call latency, and the kernel rate against the contiguous H2D
+    ceiling measured in the same run; each N checked bit-exact against the
+    oracle."""
+    W, K = c.W, c.K
+    g = DEFAULT_MAX_WGS
+    rows = {}
+    for n in (16, 256, 4096, 65536):
+        wl = W.h2d_mixed(seed=0, n=n)
+        r = c.Resident(wl)
+        b = wl.batches[0]
+        pl = K.kvcopy_plan(*r.addrs[0], b.size)
+        k = 100 if n <= 256 else 20 if n <= 4096 else 5
+        s, _ = c.timed_bracketed(r, [0], [c.sA], k, min(args.leg_warmup, 10), g)
+        _, km = c.timed(r, [0], [c.sA], k, 2, g)
+        lat = c.latency(r, 0, g, k=30 if n <= 4096 else 5, w=3)
+        c.verify(wl, r, [0], f"mixed {n}")
+        kgb = gbs(b.nbytes, km[0] / 1e3)
+        rows[str(n)] = {"bytes": b.nbytes, "merged": int(pl.n_merged), "chunks": int(pl.n_chunks),
+                        "kernel_us": round(km[0] * 1e3, 2), "kernel_GBps": round(kgb, 2),
+                        "back_to_back_GBps": round(gbs(b.nbytes, s), 2),
+                        "frac_of_h2d_ceiling": round(kgb / ceil_h2d, 4) if ceil_h2d else None,
+                        "latency": lat, "parity": "bit-exact vs oracle"}
+        log(f"  mixed N={n}: {rows[str(n)]}")
+        r.free()
+    return {"max_wgs": g, "per_n": rows,
+            "workload": "H2D, sizes 8-byte multiples in 4-28 KiB (70% in 8-16 KiB), 25% of "
+                        "descriptors adjacent in both arenas, seed 0"}
+
+
+def moe_upstream_order(b):
+    """The descriptors of one MoE call bank-major (stable), for the
+    upstream-style split: with one chunk per row, every wavefront gets the
+    same number of rows and every bank the same number of wavefronts, so the
+    1 MiB rows get a sixth of the workers (FreeToken issue #751, "Problem in
+    upstream today")."""
+    np = sys.modules["numpy"]
+    return np.argsort(b.src_arena, kind="stable")
+
+
+def moe_compact(c: Ctx, args, ceil_h2d, calls=20):
+    """The MoE expert gather (26-39 experts x 6 bank rows per call, 3,164
+    device slots): 20 calls per setting, byte-balanced 16 KiB chunks against
+    the upstream-style split (equal workers per bank, bank-major, one chunk
+    per row) at caps 1-8, plus byte-balanced at 32.  Every destination row
+    written is checked against the oracle at the end, and untouched rows
+    must keep the sentinel."""
+    np, W, K = c.np, c.W, c.K
+    wl = W.moe_gather(seed=0, calls=calls)
+    r = c.Resident(wl)
+    out = {}
+    orders = [moe_upstream_order(b) for b in wl.batches]
+    settings = [("byte_balanced_16KiB", g) for g in (1, 2, 4, 8, 32)] + \
+               [("upstream_equal_workers_per_bank", g) for g in (1, 2, 4, 8)]
+    for name, g in settings:
+        t_us, sizes = [], []
+        with no_gc():
+            for i in range(calls):
+                b = wl.batches[i]
+                s_, d_ = r.addrs[i]
+                if name.startswith("upstream"):
+                    o = orders[i]
+                    sub = lambda: K.kvcopy_batch(s_[o], d_[o], b.size[o], K.H2D, g,  # noqa: E731
+                                                 c.sA.cuda_stream, chunk_bytes=K.CHUNK_MAX,
+                                                 flags=K.F_NO_COALESCE)
+                else:
+                    sub = lambda: K.kvcopy_batch(s_, d_, b.size, K.H2D, g,  # noqa: E731
+                                                 c.sA.cuda_stream)
+                t_us.append(call_us(c, sub, c.sA))
+                sizes.append(b.nbytes)
+        rate = gbs(sum(sizes), sum(t_us) / 1e6)
+        out[f"{name}/max_wgs={g}"] = {
+            "call_us_p50": round(pct(t_us, 50), 1), "call_us_p99": round(pct(t_us, 99), 1),
+            "GBps_total": round(rate, 2),
+            "frac_of_h2d_ceiling": round(rate / ceil_h2d, 4) if ceil_h2d else None}
+        log(f"  moe {name} max_wgs={g}: {out[f'{name}/max_wgs={g}']}")
+    verify_moe_rows(c, wl, r, list(range(calls)))
+    r.free()
+    for g in (1, 2, 4, 8):
+        bb = out[f"byte_balanced_16KiB/max_wgs={g}"]["GBps_total"]
+        up = out[f"upstream_equal_workers_per_bank/max_wgs={g}"]["GBps_total"]
+        out[f"speedup_byte_balanced_over_upstream/max_wgs={g}"] = round(bb / up, 3)
+    out["parity"] = "every written row bit-exact vs oracle; sampled untouched rows keep the sentinel"
+    return out
+
+
+def verify_moe_rows(c: Ctx, wl, r, batch_ids, guard_rows=16):
+    """Checks the MoE slot caches without reading 5.3 GB back: the oracle
+    applies the calls to one image per written slot row (the rows start as
+    the sentinel; later calls overwrite earlier ones as on the GPU), and the
+    GPU's rows are gathered and compared with them; a few rows of each cache
+    that no call wrote must still hold the sentinel.  Exits on mismatch."""
+    import oracle
+    np, torch = c.np, c.torch
+    rows = wl.info["rows"]
+    nb = len(rows)
+    touched = {}                                   # cache arena -> sorted slots
+    for k in batch_ids:
+        b = wl.batches[k]
+        for a, off in zip(b.dst_arena.tolist(), b.dst_off.tolist()):
+            touched.setdefault(a, set()).add(off // rows[a - nb])
+    touched = {a: sorted(v) for a, v in touched.items()}
+    imgs = {(a, sl): np.full(rows[a - nb], wl.arenas[a].sentinel, np.uint8)
+            for a, v in touched.items() for sl in v}
+    srcs = [(r.bases[i], wl.arenas[i].host_image()) for i in range(nb)]
+    dsts = [(r.bases[a] + sl * rows[a - nb], img) for (a, sl), img in imgs.items()]
+    for k in batch_ids:
+        b = wl.batches[k]
+        s, d = r.addrs[k]
+        oracle.copy(s, d, b.size, srcs, dsts)
+    rng = np.random.default_rng(0)
+    for a, slots in touched.items():
+        row = rows[a - nb]
+        view = r.bufs[a].view(-1, row)
+        got = view[torch.tensor(slots, device=view.device)].cpu().numpy()
+        for i, sl in enumerate(slots):
+            if not np.array_equal(got[i], imgs[(a, sl)]):
+                bad = int(np.flatnonzero(got[i] != imgs[(a, sl)])[0])
+                log(f"PARITY FAILURE (moe rows) in {wl.arenas[a].name} slot {sl} at byte {bad}")
+                sys.exit(3)
+        free = np.setdiff1d(np.arange(view.shape[0]), slots)
+        pick = rng.choice(free, size=min(guard_rows, len(free)), replace=False)
+        g = view[torch.tensor(pick, device=view.device)].cpu().numpy()
+        if not np.all(g == wl.arenas[a].sentinel):
+            log(f"PARITY FAILURE (moe rows): an unwritten row of {wl.arenas[a].name} changed")
             sys.exit(3)
 
 
@@ -585,11 +831,8 @@ def bench_pair(c: Ctx, args):
         "peak_note": "both directions of PCIe 5.0 x16 (64 GB/s each)",
         "measured_ceiling": meas_ceil,
         "frac_of_measured_ceiling": round(ach / meas_ceil, 4) if meas_ceil else None}
-    line["cpu_baseline"] = {
-        "value": round(cpu["GBps"], 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
-        "cpu": cpu_model(),
-        "sample": f"{cpu['reps']} full steps (16,384 H2D + 16,384 D2H descriptors of 4 KiB each, "
-                  f"per-descriptor memcpy between host images), {cpu['seconds']:.1f} s"}
+    line["cpu_baseline"] = cpu_baseline_record(
+        cpu, "whole steps of 16,384 H2D + 16,384 D2H descriptors of 4 KiB")
     line["parity"] = "bit-exact vs oracle"
     line.update(extras)
     return line
@@ -699,7 +942,9 @@ def c_caller_latency(named):
         return {"error": "block_copy_amd/kvcopy_latency is not built"}
     with tempfile.TemporaryDirectory() as td:
         files = []
-        for name, wl, max_wgs in named:
+        for entry in named:
+            name, wl, max_wgs = entry[:3]
+            flags = entry[3] if len(entry) > 3 else 0
             b = wl.batches[0]
             if len(set(b.src_arena.tolist())) != 1 or len(set(b.dst_arena.tolist())) != 1:
                 raise ValueError(f"{name}: one source and one destination arena expected")
@@ -707,7 +952,8 @@ def c_caller_latency(named):
             path = os.path.join(td, f"{name}.bin")
             with open(path, "wb") as f:
                 f.write(struct.pack("<64sIIiIQQQ", name.encode()[:63], sa.where == "host",
-                                    da.where == "host", int(max_wgs), 0, sa.nbytes, da.nbytes, b.n))
+                                    da.where == "host", int(max_wgs), int(flags), sa.nbytes,
+                                    da.nbytes, b.n))
                 for a in (b.src_off, b.dst_off, b.size):
                     f.write(a.astype("<u8").tobytes())
             files.append(path)
@@ -783,10 +1029,20 @@ def d2d_results(c: Ctx, args):
             out[name]["note"] = ("kernel_us: the same call repeated, so most of its 256 MiB of "
                                  "sources stay in the 256 MB MALL between calls")
         if name == "1024x4KiB":     # after the check: the DMA baselines write the same bytes
+            if not args.no_events:
+                out[name]["launch_floor_and_caps"] = d2d_launch_floor(c, r)
+                log(f"  d2d {name} kernel vs empty-kernel floor: "
+                    f"{out[name]['launch_floor_and_caps']}")
             out[name]["dma_baselines"] = dma_baselines(c, pl, wld.batches[0].nbytes,
                                                        hiprt.D2D_KIND, reps=5)
             out[name]["latency_c_caller"] = c_caller_latency([("d2d_1024x4KiB", wld, 0)]).get(
                 "d2d_1024x4KiB")
+        else:
+            cl = c_caller_latency([("d2d_65536x4KiB", wld, 0),
+                                   ("d2d_65536x4KiB_dst_order", wld, 0, K.F_DST_ORDER)])
+            out[name]["latency_c_caller"] = cl.get("d2d_65536x4KiB", cl.get("error"))
+            out[name]["latency_c_caller_dst_order"] = cl.get("d2d_65536x4KiB_dst_order",
+                                                             cl.get("error"))
         log(f"  d2d {name}: {out[name]} (bit-exact)")
         r.free()
     big = torch.empty(2 << 30, dtype=torch.uint8, device=c.dev)
@@ -837,6 +1093,52 @@ def d2d_results(c: Ctx, args):
     return out
 
 
+def headline_windows(c: Ctx, res, max_wgs, n=30, k=20, **kw):
+    """n consecutive windows of k joined steps of the headline burst (the
+    step count the headline is timed over), each timed by wall clock around
+    the window and by one event pair per stream around its kernels: the
+    spread of the two-stream rate, and in each window whether both kernels
+    slowed or one stream ran longer than the other."""
+    step_bytes = res.wl.nbytes
+    rates, kern = [], []
+    for _ in range(n):
+        s, km = c.timed_bracketed(res, [0, 1], [c.sA, c.sB], k, 0, max_wgs, joined=True, **kw)
+        rates.append(gbs(step_bytes, s))
+        kern.append([round(x, 4) for x in km])
+    med = statistics.median(rates)
+    within = sum(1 for x in rates if abs(x / med - 1) <= 0.03)
+    return {"windows": n, "steps_per_window": k, "GBps_median": round(med, 3),
+            "GBps_min": round(min(rates), 3), "GBps_max": round(max(rates), 3),
+            "within_3pct_of_median": within, "GBps": [round(x, 2) for x in rates],
+            "kernel_ms_per_stream": kern}
+
+
+def d2d_launch_floor(c: Ctx, r, grids=(16, 32, 64, 128, 256), reps=50):
+    """The 1,024 x 4 KiB call's kernel time at caps 16-256 (the default loop
+    choice: pipelined at 16-128, where every wavefront has 2-16 chunks; at
+    256, the full grid, one chunk per wavefront) beside an empty kernel of
+    the same grid, both from the kernels' own events in this run (median of
+    `reps` launches each)."""
+    from block_copy_amd import decode_load as DL
+    hiprt = c.hiprt
+    out = {}
+    for g in grids:
+        evs = [(hiprt.Event(), hiprt.Event()) for _ in range(reps)]
+        for e0, e1 in evs:
+            DL.empty(g, c.sA, e0.h, e1.h)
+        floor = statistics.median(e0.elapsed_ms(e1) * 1e3 for e0, e1 in evs)
+        evs = [(hiprt.Event(), hiprt.Event()) for _ in range(reps)]
+        for e0, e1 in evs:
+            r.submit(0, g, c.sA, kernel_begin=e0.h, kernel_end=e1.h)
+        us = statistics.median(e0.elapsed_ms(e1) * 1e3 for e0, e1 in evs)
+        out[f"max_wgs={g}"] = {"kernel_us_p50": round(us, 2),
+                               "empty_kernel_us_p50_same_grid": round(floor, 2),
+                               "kernel_minus_floor_us": round(us - floor, 2)}
+    best = min(out, key=lambda k: out[k]["kernel_us_p50"])
+    out["best"] = best
+    return out
+
+
 def d2d_flushed(c: Ctx, r, k=20):
     """The gather with the 256 MB MALL (Infinity Cache) holding none of its
     bytes: a kernel that reads 512 MiB of other memory runs on the same stream
@@ -882,16 +1184,32 @@ def d2d_distinct(c: Ctx, args):
     r = c.Resident(wl)
     nb = len(wl.batches)
     calls = max(4 * nb, args.steps)
-    evs = [(hiprt.Event(), hiprt.Event()) for _ in range(calls)]
-    for i in range(nb):
-        r.submit(i, 0, c.sA)
-    for i in range(calls):
-        r.submit(i % nb, 0, c.sA, kernel_begin=evs[i][0].h, kernel_end=evs[i][1].h)
-    hiprt.stream_sync(c.sA)
-    us = statistics.median(e0.elapsed_ms(e1) * 1e3 for e0, e1 in evs)
+
+    def kernel_us(flags):
+        evs = [(hiprt.Event(), hiprt.Event()) for _ in range(calls)]
+        for i in range(nb):
+            r.submit(i, 0, c.sA, flags=flags)
+        for i in range(calls):
+            r.submit(i % nb, 0, c.sA, flags=flags, kernel_begin=evs[i][0].h,
+                     kernel_end=evs[i][1].h)
+        hiprt.stream_sync(c.sA)
+        return [e0.elapsed_ms(e1) * 1e3 for e0, e1 in evs]
+
+    # list order and destination order, alternating twice so that drift over
+    # the run falls on both alike
+    t_list, t_dst = [], []
+    for _ in range(2):
+        t_list += kernel_us(0)
+        t_dst += kernel_us(c.K.F_DST_ORDER)
+    us, us_dst = statistics.median(t_list), statistics.median(t_dst)
     pl = c.K.kvcopy_plan(*r.addrs[0], wl.batches[0].size)
     hbm = 2 * wl.batches[0].nbytes + pl.n_chunks * REC_BYTES
     ceiling = random_block_ceiling(c, r, wl, calls)
+    r.fill()
+    for i in range(nb):
+        r.submit(i, 0, c.sA, flags=c.K.F_DST_ORDER)
+    hiprt.stream_sync(c.sA)
+    c.verify(wl, r, list(range(nb)), "d2d distinct calls, destination order")
     r.fill()
     for i in range(nb):
         r.submit(i, 0, c.sA)
@@ -901,6 +1219,10 @@ def d2d_distinct(c: Ctx, args):
     out = {"batches": nb, "calls": calls, "kernel_us_p50": round(us, 2),
            "hbm_GBps_kernel": round(gbs(hbm, us / 1e6), 1),
            "frac_hbm_peak_kernel": round(gbs(hbm, us / 1e6) / HBM_PEAK_GBS, 4),
+           "destination_order": {"kernel_us_p50": round(us_dst, 2),
+                                 "hbm_GBps_kernel": round(gbs(hbm, us_dst / 1e6), 1),
+                                 "frac_hbm_peak_kernel": round(gbs(hbm, us_dst / 1e6) / HBM_PEAK_GBS, 4),
+                                 "flag": "KVCOPY_F_DST_ORDER", "parity": "bit-exact vs oracle"},
            "random_block_ceiling": ceiling,
            "frac_random_block_ceiling": round(ceiling["us"] / us, 4)}
     log(f"  d2d distinct calls: {out} (bit-exact)")
@@ -1192,19 +1514,64 @@ def moe_device_graph(c: Ctx, wl, max_wgs):
 # Interference: decode loop vs bidirectional bursts
 # ---------------------------------------------------------------------------
 
+def parse_mode(mode):
+    """(kind, cap, options) of an interference mode.  Modes: "none" (no
+    transfer), "direct" (one hipMemcpyAsync per fragment), an integer cap G
+    (both directions on two streams at G workgroups each; 0 = full grid),
+    "G/sc1" or "G/nt" (the same with the store form forced on both kernels),
+    "duty:ON:PERIOD:G" (the same with time-sliced issue, ON and PERIOD in
+    microseconds), "pair:G" and "pair:G/nt" (both lists in one launch),
+    "pipe:G" (the pipelined loop forced), "job:N" (paced pieces of N
+    descriptors), "h2d:G" and "d2h:G" (one direction alone), "cumask:N" (two
+    streams at the full grid on the first N compute units)."""
+    if isinstance(mode, int):
+        return "streams", mode, {}
+    m = str(mode)
+    if m in ("none", "direct"):
+        return m, 0, {}
+    opt = {}
+    if "/" in m:
+        m, store = m.split("/", 1)
+        if store not in ("sc1", "nt"):
+            raise ValueError(f"unknown store form in interference mode {mode!r}")
+        opt["store"] = store
+    if m.isdigit():
+        return "streams", int(m), opt
+    head, _, rest = m.partition(":")
+    if head == "duty":
+        on, per, cap = rest.split(":")
+        opt["duty"] = (int(round(float(on) * 1000)), int(round(float(per) * 1000)))
+        return "streams", int(cap), opt
+    if head in ("pair", "pipe", "job", "h2d", "d2h", "cumask") and rest.isdigit():
+        return head, int(rest), opt
+    raise ValueError(f"unknown interference mode {mode!r}")
+
+
 def bench_interference(c: Ctx, args):
     torch, W, K, hiprt = c.torch, c.W, c.K, c.hiprt
-    from block_copy_amd.decode_load import Chain
+    from block_copy_amd.decode_load import AluChain, Chain
     d_model, d_ff, n_gemv = 2560, 9728, 36
-    g = torch.Generator(device=c.dev)
-    g.manual_seed(0)
-    weights, acts = [], [torch.randn(d_model, generator=g, device=c.dev).to(torch.bfloat16)]
-    for i in range(n_gemv):
-        shape = (d_ff, d_model) if i % 2 == 0 else (d_model, d_ff)
-        weights.append((torch.randn(shape, generator=g, device=c.dev) * 0.02).to(torch.bfloat16))
-        acts.append(torch.empty(shape[0], dtype=torch.bfloat16, device=c.dev))
-    chain = Chain(weights, acts)
-    wbytes = sum(w.numel() * 2 for w in weights)
+    if args.decode_kind == "alu":
+        # the ALU-only stand-in: 36 kernels that touch memory only in their
+        # last store (one per workgroup)
+        chain = AluChain(torch.zeros(1024, dtype=torch.float32, device=c.dev), n=n_gemv,
+                         grid=args.alu_grid, iters=args.alu_iters)
+        wbytes = 0
+        decode_what = (f"decode stand-in of {n_gemv} ALU-only kernels ({args.alu_grid} workgroups "
+                       f"x 256 threads, {args.alu_iters} dependent FMAs per thread, one store per "
+                       "workgroup)")
+    else:
+        g = torch.Generator(device=c.dev)
+        g.manual_seed(0)
+        weights, acts = [], [torch.randn(d_model, generator=g, device=c.dev).to(torch.bfloat16)]
+        for i in range(n_gemv):
+            shape = (d_ff, d_model) if i % 2 == 0 else (d_model, d_ff)
+            weights.append((torch.randn(shape, generator=g, device=c.dev) * 0.02).to(torch.bfloat16))
+            acts.append(torch.empty(shape[0], dtype=torch.bfloat16, device=c.dev))
+        chain = Chain(weights, acts)
+        wbytes = sum(w.numel() * 2 for w in weights)
+        decode_what = (f"decode loop of {n_gemv} bf16 GEMVs ({d_ff}x{d_model} and {d_model}x{d_ff}, "
+                       f"{wbytes / 1e9:.2f} GB of distinct weights per step)")
     try:                               # the decode stream: a hardware queue of its own
         dq = hiprt.QueueStreams(1, torch.cuda.get_device_properties(c.dev).multi_processor_count)
         sD = dq.streams[0]
@@ -1229,21 +1596,28 @@ def bench_interference(c: Ctx, args):
             if ncu not in masked:
                 masked[ncu] = (hiprt.CUMaskStream(range(ncu)), hiprt.CUMaskStream(range(ncu)))
             sa, sb = masked[ncu]
+            mode = 0          # the full grid, on the masked compute units
+
+        kind, g, opt = parse_mode(mode)
+        copy_kw = {}
+        if opt.get("store"):
+            copy_kw["flags"] = K.F_STORE_SC1 if opt["store"] == "sc1" else K.F_STORE_NT
+        if opt.get("duty"):
+            copy_kw["duty_on_ns"], copy_kw["duty_period_ns"] = opt["duty"]
 
         def transfer():
             nxt = time.perf_counter()
             while not stop.is_set():
-                if mode == "direct":
-                    for j, kind, st in ((0, hiprt.H2D_KIND, c.sA), (1, hiprt.D2H_KIND, c.sB)):
+                if kind == "direct":
+                    for j, kd, st in ((0, hiprt.H2D_KIND, c.sA), (1, hiprt.D2H_KIND, c.sB)):
                         b = wl.batches[j]
                         s_, d_ = r.addrs[j]
                         for x, y, z in zip(s_.tolist(), d_.tolist(), b.size.tolist()):
-                            hiprt.memcpy_async(y, x, z, kind, st)
-                elif isinstance(mode, str) and mode.startswith("job"):
+                            hiprt.memcpy_async(y, x, z, kd, st)
+                elif kind == "job":
                     # paced pieces: the next piece goes only after the previous completed
-                    piece = int(mode.split(":")[1])
                     jobs = [K.kvcopy_job_create(*r.addrs[j], wl.batches[j].size, wl.batches[j].dir,
-                                                0, piece, st.cuda_stream)
+                                                0, g, st.cuda_stream)
                             for j, st in ((0, c.sA), (1, c.sB))]
                     pending = list(jobs)
                     while pending:
@@ -1252,21 +1626,26 @@ def bench_interference(c: Ctx, args):
                             time.sleep(20e-6)      # yield the worker while a piece runs
                     for jb in jobs:
                         K.kvcopy_job_destroy(jb)
-                elif isinstance(mode, str) and mode.startswith("pair"):
+                elif kind == "pair":
                     # both lists in one launch (kvcopy_batch_pair) on one stream
-                    c.pair_step(r, sa, int(mode.split(":")[1]))
-                elif isinstance(mode, str) and mode.startswith("pipe"):
+                    (s0, d0), (s1, d1) = r.addrs[0], r.addrs[1]
+                    K.kvcopy_batch_pair(s0, d0, wl.batches[0].size, s1, d1, wl.batches[1].size, g,
+                                        sa.cuda_stream,
+                                        flags=K.F_STORE_NT if opt.get("store") == "nt" else 0)
+                elif kind == "pipe":
                     # the pipelined loop forced at a small cap
-                    g = int(mode.split(":")[1])
                     r.submit(0, g, sa, flags=K.F_PIPELINE)
                     r.submit(1, g, sb, flags=K.F_PIPELINE)
-                else:
-                    g = K.WGS_ALL if isinstance(mode, str) else mode
-                    r.submit(0, g, sa)
-                    r.submit(1, g, sb)
+                elif kind in ("h2d", "d2h"):
+                    # one direction alone
+                    r.submit(0 if kind == "h2d" else 1, g, sa, **copy_kw)
+                else:                               # two streams at cap g
+                    r.submit(0, g, sa, **copy_kw)
+                    r.submit(1, g, sb, **copy_kw)
                 hiprt.stream_sync(sa)
                 hiprt.stream_sync(sb)
-                moved[0] += wl.nbytes
+                moved[0] += wl.batches[0 if kind == "h2d" else 1].nbytes if kind in ("h2d", "d2h") \
+                    else wl.nbytes
                 bursts[0] += 1
                 nxt += period
                 delay = nxt - time.perf_counter()
@@ -1305,16 +1684,19 @@ def bench_interference(c: Ctx, args):
             th.join()
         return gpu_ms, wall_ms, moved[0] / dur, bursts[0]
 
-    modes = ["none", "direct", 1, 2, 8, 32, 128, 0, "pipe:1", "pipe:4", "job:1024", "job:2048",
-             "job:4096", "cumask:8", "cumask:32", "pair:8", "pair:16", "pair:64"]
-    if args.modes:     # a subset, say for a profiler run; "none" (the baseline) always runs
+    modes = ["none", "direct", 1, 8, 32, 128, 0, "8/sc1", "128/sc1", "8/nt", "h2d:8", "d2h:8",
+             "h2d:128", "d2h:128", "pipe:4", "job:2048", "cumask:8", "pair:8", "pair:16",
+             "pair:64", "pair:8/nt", "pair:16/nt", "duty:2:10:8", "duty:2:20:8", "duty:5:20:32",
+             "duty:2:10:128"]
+    if args.modes:     # a subset or other modes; "none" (the baseline) always runs
         pick = [m for m in args.modes.split(",") if m]
-        unknown = [m for m in pick if m not in [str(x) for x in modes]]
-        if unknown:
-            print(f"unknown interference modes {unknown}; known: {[str(x) for x in modes]}",
-                  file=sys.stderr)
+        try:
+            for m in pick:
+                parse_mode(m)
+        except ValueError as e:
+            print(f"{e}; see parse_mode for the forms", file=sys.stderr)
             sys.exit(2)
-        modes = [m for m in modes if str(m) == "none" or str(m) in pick]
+        modes = ["none"] + [int(m) if m.isdigit() else m for m in pick if m != "none"]
     results = {str(m): {"gpu": [], "wall": [], "rate": [], "bursts": 0} for m in modes}
     for rep in range(args.decode_runs):
         order = modes[rep % len(modes):] + modes[:rep % len(modes)]
@@ -1332,6 +1714,11 @@ def bench_interference(c: Ctx, args):
     hiprt.stream_sync(c.sB)
     c.verify(wl, r, [0, 1], "interference bursts")
     r.free()
+    for pair_ in masked.values():
+        for st in pair_:
+            st.destroy()
+    if isinstance(sD, torch.cuda.ExternalStream):
+        dq.destroy()
     table = {}
     for m, rr in results.items():
         def agg(key, q):
@@ -1357,8 +1744,7 @@ def bench_interference(c: Ctx, args):
     headline_mode = "32" if "32" in table else [m for m in table if m != "none"][0] \
         if len(table) > 1 else "none"
     line = base_line(args, table[headline_mode]["gpu_ms_p99"], "ms", table["none"]["gpu_ms_mean"] / 1e3, {
-        "workload": f"decode loop of {n_gemv} bf16 GEMVs ({d_ff}x{d_model} and {d_model}x{d_ff}, "
-                    f"{wbytes / 1e9:.2f} GB of distinct weights per step) while a bidirectional "
+        "workload": f"{decode_what} while a bidirectional "
                     "burst (16,384 x 4 KiB H2D + 16,384 x 4 KiB D2H) starts every 50 ms; value = "
                     f"decode step p99 ({'wall' if args.no_events else 'GPU'} time) in mode "
                     f"{headline_mode} (an integer mode is max_wgs on two streams)",
@@ -1406,7 +1792,14 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1536)
     ap.add_argument("--decode-runs", type=int, default=3)
     ap.add_argument("--modes", default="",
-                    help="interference: comma-separated subset of the modes (default: all)")
+                    help="interference: comma-separated modes to run (default: a fixed list; "
+                         "see parse_mode)")
+    ap.add_argument("--decode-kind", default="gemv", choices=["gemv", "alu"],
+                    help="interference: the bf16 GEMV chain, or the ALU-only stand-in")
+    ap.add_argument("--alu-iters", type=int, default=4096,
+                    help="interference with --decode-kind alu: dependent FMAs per thread")
+    ap.add_argument("--alu-grid", type=int, default=1024,
+                    help="interference with --decode-kind alu: workgroups per kernel")
     args = ap.parse_args()
     args.leg_warmup = min(args.warmup, 100)
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -1419,6 +1812,7 @@ def main():
           "interference": bench_interference}[args.workload]
     line = fn(c, args)
     print(json.dumps(line), flush=True)
+    c.close()
 
 
 if __name__ == "__main__":

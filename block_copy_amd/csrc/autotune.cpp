@@ -9,16 +9,19 @@
 // run together, which is how KV offload bursts arrive (PegaFlow issue #408,
 // "Test setup": H2D and D2H concurrently on separate streams).
 //
-// Window length and tolerance, measured on MI355X over three processes for
+// Window length and tie rule, measured on MI355X over three processes for
 // H2D + D2H on two streams: with 6 timed batches per cap the probe rated
 // 32 or 64 workgroups best (79-85 GB/s against 79-80 at 128), but those
-// caps ran 600-step bursts at 79-81 GB/s against 76-86 at 128; with 24
-// batches it rated 128 best (85-86) and 64 within 5% (83), which ran at
-// 76-83 against 85-89 at 128.  So the windows are 24 batches long (about a
-// second of probing) and only caps within 2% of the best count as ties.
-// The smaller grid that the 5% rule favours does not protect co-running
-// kernels on this part either: they wait on queued host-link traffic, not
-// on compute units.
+// caps ran 600-step bursts at 79-81 GB/s against 76-86 at 128.  With 24
+// batches of 8,192 blocks and a 2% tie rule it still picked 32 in one run
+// (84.1 GB/s against 85.7 at 128, inside the window-to-window spread), which
+// then ran the burst 3% slower than 128.  So the probe now uses the
+// workload's own batch shape (16,384 blocks of 4 KiB per direction), joins
+// the two directions at every step as a caller's burst does, and lets a
+// smaller cap tie with the best one only if even its slowest sweep reaches
+// the best cap's median rate.  The smaller grid that a tie rule favours does
+// not protect co-running kernels on this part anyway: they wait on queued
+// host-link traffic, not on compute units.
 #include <stdint.h>
 
 #include <algorithm>
@@ -29,12 +32,11 @@
 
 namespace {
 
-constexpr uint64_t kBlocks = 8192;
+constexpr uint64_t kBlocks = 16384;
 constexpr uint64_t kBlock = 4096;
-constexpr uint64_t kBytes = kBlocks * kBlock;   // 32 MiB per direction
+constexpr uint64_t kBytes = kBlocks * kBlock;   // 64 MiB per direction
 constexpr int kWarm = 4;                         // untimed batches per cap
 constexpr int kReps = 24;                        // timed batches per cap
-constexpr double kTie = 0.98;                    // a cap this close to the best rate ties
 constexpr int kSweeps = 3;                       // ascending, descending, ascending
 const int kCaps[KVCOPY_AUTOTUNE_NCAPS] = KVCOPY_AUTOTUNE_CAPS;
 
@@ -63,6 +65,7 @@ struct Probe {
     hipStream_t s[2] = {nullptr, nullptr};
     bool own[2] = {false, false};   // streams created here (destroyed at the end)
     hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
+    hipEvent_t mark[2] = {nullptr, nullptr};   // per-step join of the two streams
     ~Probe()
     {   // release path: failures here cannot be reported and change nothing
         for (hipStream_t x : s)
@@ -75,6 +78,9 @@ struct Probe {
             if (p)
                 (void)hipFree(p);
         for (hipEvent_t e : ev)
+            if (e)
+                (void)hipEventDestroy(e);
+        for (hipEvent_t e : mark)
             if (e)
                 (void)hipEventDestroy(e);
         for (int i = 0; i < 2; ++i)
@@ -113,6 +119,9 @@ extern "C" int kvcopy_autotune(int dir, hipStream_t s0, hipStream_t s1, int *out
     }
     for (hipEvent_t &x : p.ev)
         if ((e = hipEventCreate(&x)) != hipSuccess)
+            return kvc::hip_fail(e);
+    for (hipEvent_t &x : p.mark)
+        if ((e = hipEventCreateWithFlags(&x, hipEventDisableTiming)) != hipSuccess)
             return kvc::hip_fail(e);
 
     // Batches: D2D dev0 -> dev1; otherwise H2D host0 -> dev0 and D2H dev1 -> host1.
@@ -154,6 +163,13 @@ extern "C" int kvcopy_autotune(int dir, hipStream_t s0, hipStream_t s1, int *out
                 if (rc != KVCOPY_OK)
                     return rc;
             }
+            if (nb == 2) {   // the step ends when both directions are done
+                if ((e = hipEventRecord(p.mark[0], p.s[0])) != hipSuccess ||
+                    (e = hipEventRecord(p.mark[1], p.s[1])) != hipSuccess ||
+                    (e = hipStreamWaitEvent(p.s[0], p.mark[1], 0)) != hipSuccess ||
+                    (e = hipStreamWaitEvent(p.s[1], p.mark[0], 0)) != hipSuccess)
+                    return kvc::hip_fail(e);
+            }
         }
         if ((e = hipEventRecord(p.ev[1], p.s[0])) != hipSuccess ||
             (e = hipEventRecord(p.ev[2], p.s[1])) != hipSuccess ||
@@ -167,18 +183,21 @@ extern "C" int kvcopy_autotune(int dir, hipStream_t s0, hipStream_t s1, int *out
         const double ms = std::max(ms0, nb == 2 ? ms1 : 0.0f);
         rates[c][sweep] = ms > 0 ? (double)(kBytes * nb * kReps) / (ms * 1e-3) : 0;
     }
-    double rate[KVCOPY_AUTOTUNE_NCAPS] = {};
-    double best = 0;
+    double rate[KVCOPY_AUTOTUNE_NCAPS] = {}, worst[KVCOPY_AUTOTUNE_NCAPS] = {};
+    int best_c = 0;
     for (int c = 0; c < ncaps; ++c) {
         double r[kSweeps];
         std::copy(rates[c], rates[c] + kSweeps, r);
         std::sort(r, r + kSweeps);
         rate[c] = r[kSweeps / 2];
-        best = std::max(best, rate[c]);
+        worst[c] = r[0];
+        if (rate[c] > rate[best_c])
+            best_c = c;
     }
-    int chosen = KVCOPY_WGS_ALL;
+    // The smallest cap whose slowest sweep still reaches the best cap's median.
+    int chosen = kCaps[best_c];
     for (int c = 0; c < ncaps; ++c)
-        if (rate[c] >= kTie * best) {
+        if (c == best_c || worst[c] >= rate[best_c]) {
             chosen = kCaps[c];
             break;
         }

@@ -24,17 +24,19 @@ constexpr int kRsrcWord3 = 0x00020000;
 // memory the combinations are within noise of each other.
 constexpr int kLoadPolicy = 0;
 constexpr int kStorePolicy = 2;
-// System-scope stores: sc1 | nt (bits 4 and 1: system scope, nontemporal).
-// The one-launch pair kernel always stores this way.  Measured on MI355X
-// with 16,384 x 4 KiB each way: 98.7 GB/s against 96.9 with nt alone.  A
-// lone D2H batch gains too (56.7 against 52.7 GB/s), but a D2H kernel that
-// runs beside an H2D kernel on another stream loses with it (82-84 against
-// 86.7 GB/s for the two directions at 128 workgroups each), and an H2D
-// kernel gains nothing from it alone (56.9 GB/s either way).  So the D2H
-// per-chunk loop has both forms and the host picks per call (system scope
-// unless one of the library's H2D kernels is still running on another
-// stream); the other kernels keep nt.
-constexpr int kSysStorePolicy = 18;
+// The sc1 form: sc1 | nt (bits 4 and 1).  On the gfx940 family the two
+// scope bits SC1:SC0 name the coherence scope of an access (0 wavefront, 1
+// workgroup, 2 device, 3 system), so sc1 alone is a device-scope,
+// nontemporal store.  The one-launch pair kernel stores this way by default.
+// Measured on MI355X with 16,384 x 4 KiB each way: 98.7 GB/s against 96.9
+// with nt alone.  A lone D2H batch gains too (56.7 against 52.7 GB/s), but a
+// D2H kernel that runs beside an H2D kernel on another stream loses with it
+// (82-84 against 86.7 GB/s for the two directions at 128 workgroups each),
+// and an H2D kernel gains nothing from it alone (56.9 GB/s either way).  So
+// by default the D2H per-chunk loop picks the form per call (sc1 unless one
+// of the library's H2D kernels is still running on another stream) and the
+// other kernels keep nt; KVCOPY_F_STORE_SC1 / KVCOPY_F_STORE_NT force one.
+constexpr int kSc1StorePolicy = 18;
 constexpr uint32_t kRowBytes = 64u * 16u;          // one wavefront instruction: 1 KiB
 constexpr int kMaxRows = 16;                       // 16 KiB per pass, 64 VGPRs of data
 constexpr uint32_t kPassBytes = kRowBytes * kMaxRows;

@@ -13,6 +13,7 @@
 // pieces (8 bf16) of the row, 1 KiB per wavefront instruction, multiply with
 // the matching piece of x (read through the caches; every row re-reads the
 // same x), and reduce across the wavefront.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -76,9 +77,56 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_bf16_kernel(const uint16_t *
         y[row] = to_bf16(acc);
 }
 
+// The ALU-only stand-in for a decode kernel: every thread runs `iters`
+// dependent fused multiply-adds on registers and each workgroup stores one
+// value at the end, so the kernel touches memory only in its last store.
+// It tells waits in a kernel's own memory accesses apart from waits that any
+// kernel sees (its dispatch and its end).
+__global__ __launch_bounds__(64 * kWaves) void alu_kernel(float *__restrict__ out, int iters,
+                                                         float seed)
+{
+    float a = seed + (float)threadIdx.x, b = 1.0f + 1e-7f * (float)blockIdx.x;
+    for (int i = 0; i < iters; ++i)
+        a = __builtin_fmaf(a, b, 1e-7f);
+    a += __shfl_xor(a, 1, 64);
+    if (threadIdx.x == 0)
+        out[blockIdx.x & 1023] = a;
+}
+
+// A kernel that does nothing: its duration from the kernel's own events is
+// the launch floor of a grid of that shape.
+__global__ __launch_bounds__(64 * kWaves) void empty_kernel() {}
+
 }  // namespace
 
 extern "C" {
+
+// A chain of n ALU-only kernels of `grid` workgroups and `iters` dependent
+// FMAs per thread on `stream`; `out` holds at least 1,024 floats.  Returns a
+// hipError_t value.
+int kvload_alu_chain(float *out, int n, int grid, int iters, hipStream_t stream)
+{
+    if (!out || n <= 0 || grid <= 0 || grid > (1 << 20) || iters <= 0)
+        return (int)hipErrorInvalidValue;
+    for (int i = 0; i < n; ++i) {
+        hipLaunchKernelGGL(alu_kernel, dim3(grid), dim3(64 * kWaves), 0, stream, out, iters,
+                           (float)i);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return (int)e;
+    }
+    return 0;
+}
+
+// One empty kernel of `grid` workgroups of 256 threads; `start` and `stop`
+// (either may be null) are recorded at the kernel's own start and end.
+int kvload_empty(int grid, hipStream_t stream, hipEvent_t start, hipEvent_t stop)
+{
+    if (grid <= 0 || grid > (1 << 22))
+        return (int)hipErrorInvalidValue;
+    return (int)hipExtLaunchKernel(reinterpret_cast<const void *>(&empty_kernel), dim3(grid),
+                                   dim3(64 * kWaves), nullptr, 0, stream, start, stop, 0);
+}
 
 // One product on `stream`.  Returns a hipError_t value (0 on success);
 // hipErrorInvalidValue for non-positive sizes or cols not a multiple of 8.

@@ -79,6 +79,15 @@ void finish_records();
 uint64_t build_worklist(const uint64_t *src, const uint64_t *dst, const uint64_t *size, uint64_t n,
                         bool merge, uint32_t chunk, ChunkRec *out);
 
+// KVCOPY_F_DST_ORDER: writes in[0..n) to out in order of destination
+// region -- a stable counting sort of the records by (dst >> 22) & 255, so
+// the records of one 4 MiB destination region (and of regions 1 GiB apart)
+// are consecutive, in list order within the region.  With `stream`, out is
+// written with non-temporal stores (call finish_records() before the launch).
+constexpr uint32_t kDstRegionShift = 22;
+constexpr uint32_t kDstBuckets = 256;
+void order_by_dst(const ChunkRec *in, uint64_t n, ChunkRec *out, bool stream);
+
 // True when KVCOPY_VALIDATE=1 in the environment; any value other than
 // unset, "0" or "1" makes *bad true (strict parsing).
 bool env_validate(bool *bad);
@@ -106,28 +115,33 @@ struct InlineWork {
 };
 
 // Launches the per-chunk loop over an inline worklist (w.n_chunks <= kInlineRecs);
-// start / stop as for launch_copy.
-hipError_t launch_copy_inline(const InlineWork &w, uint32_t grid, int dir, hipStream_t stream,
-                              hipEvent_t start, hipEvent_t stop);
+// sc1_stores, start and stop as for launch_copy.
+hipError_t launch_copy_inline(const InlineWork &w, uint32_t grid, int dir, bool sc1_stores,
+                              hipStream_t stream, hipEvent_t start, hipEvent_t stop);
 
-// Launches the copy kernel for `dir` (one kernel symbol per direction and
-// loop, same result): `grid` workgroups; wavefront w of W copies the chunks
-// [w*C/W, (w+1)*C/W), one chunk at a time or, if `pipelined`, as a stream of
-// 4 KiB pieces with two 16 KiB passes in flight.  `sys_stores` selects the
-// D2H per-chunk loop's system-scope stores (ignored otherwise).  recs must be
-// device-readable (device memory or mapped host memory).  `start` and `stop`
-// (either may be null) are bound to the kernel's own start and completion
-// (hipExtLaunchKernel's events), which costs no separate marker on the
-// stream.  Returns the launch status.
+// Launches the copy kernel for `dir` (one kernel symbol per direction, loop
+// and store form, same result): `grid` workgroups; wavefront w of W copies
+// the chunks [w*C/W, (w+1)*C/W), one chunk at a time or, if `pipelined`, as
+// a stream of 4 KiB pieces with two 16 KiB passes in flight.  `sc1_stores`
+// selects the per-chunk loop's sc1|nt store form (copy_chunk.h,
+// kSc1StorePolicy) instead of nt alone; pace_on / pace_period (wall-clock
+// ticks, period 0 = none) time-slice the per-chunk loop's issue.  Both are
+// ignored by the pipelined loop.  recs must be device-readable (device
+// memory or mapped host memory).  `start` and `stop` (either may be null)
+// are bound to the kernel's own start and completion (hipExtLaunchKernel's
+// events), which costs no separate marker on the stream.  Returns the
+// launch status.
 hipError_t launch_copy(const ChunkRec *recs, uint32_t n_chunks, uint32_t grid, int dir,
-                       bool pipelined, bool sys_stores, hipStream_t stream, hipEvent_t start,
-                       hipEvent_t stop);
+                       bool pipelined, bool sc1_stores, uint32_t pace_on, uint32_t pace_period,
+                       hipStream_t stream, hipEvent_t start, hipEvent_t stop);
 
 // kvcopy_batch_pair: two worklists (ra[0..ca), rb[0..cb)) in one kernel;
 // every wavefront alternates between its shares of the two lists in
-// proportion to their chunk counts.  start / stop as for launch_copy.
+// proportion to their chunk counts.  sc1_stores as for launch_copy (the
+// pair's default is the sc1|nt form); start / stop as for launch_copy.
 hipError_t launch_copy_pair(const ChunkRec *ra, uint32_t ca, const ChunkRec *rb, uint32_t cb,
-                            uint32_t grid, hipStream_t stream, hipEvent_t start, hipEvent_t stop);
+                            uint32_t grid, bool sc1_stores, hipStream_t stream, hipEvent_t start,
+                            hipEvent_t stop);
 
 // KVCOPY_F_DYNAMIC: the per-chunk loop with chunks claimed at run time.
 // claim points at two zeroed device counters (next chunk, wavefronts done);
@@ -136,6 +150,28 @@ hipError_t launch_copy_pair(const ChunkRec *ra, uint32_t ca, const ChunkRec *rb,
 hipError_t launch_copy_dynamic(const ChunkRec *recs, uint32_t n_chunks, uint32_t grid, int dir,
                                uint32_t *claim, uint32_t grain, hipStream_t stream,
                                hipEvent_t start, hipEvent_t stop);
+
+// Largest grid of one launch: 2^22 workgroups of 256 work-items (HIP
+// limits a launch to fewer than 2^32 work-items).  A capped grid still
+// copies every chunk, since each wavefront's share is computed from gridDim.
+// With at most 2^24 wavefronts claiming at most 64 chunks each, a dynamic
+// loop's claim counter reaches at most KVCOPY_MAX_CHUNKS + 2^30 < 2^32 (one
+// overshooting claim per wavefront), so the 32-bit counter never wraps.
+constexpr uint32_t kMaxGrid = 1u << 22;
+static_assert((uint64_t)kMaxGrid * kThreadsPerWG < (1ull << 32), "launch too large");
+static_assert(KVCOPY_MAX_CHUNKS + (uint64_t)kMaxGrid * kWavesPerWG * 64 < (1ull << 32),
+              "a dynamic loop's claim counter could wrap");
+
+// Workgroups for a batch of n_chunks under max_wgs (KVCOPY_WGS_ALL or a
+// positive cap; KVCOPY_WGS_AUTO must be resolved first): one wavefront per
+// chunk at most, and at most kMaxGrid.
+inline uint32_t grid_for(uint64_t n_chunks, int max_wgs)
+{
+    uint64_t g = (n_chunks + kWavesPerWG - 1) / kWavesPerWG;   // one wavefront per chunk
+    if (max_wgs != 0 /* KVCOPY_WGS_ALL */ && (uint64_t)max_wgs < g)
+        g = (uint64_t)max_wgs;
+    return (uint32_t)(g < kMaxGrid ? g : kMaxGrid);
+}
 
 // Chunks per claim: about four claims per wavefront, at most 64 (one record
 // per lane), at least 1.

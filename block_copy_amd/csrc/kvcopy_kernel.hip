@@ -72,11 +72,35 @@ __device__ __forceinline__ uint64_t lane_u64(uint64_t v, uint32_t j)
     return ((uint64_t)hi << 32) | lo;
 }
 
+// Time-sliced issue (kvcopy_opts_t duty_on_ns / duty_period_ns): a
+// wavefront starts a chunk only while the device's constant-rate wall clock
+// (s_memrealtime, 100 MHz on MI355X) lies in the first `on` ticks of each
+// `period`.  Every wavefront of every copy kernel reads the same clock, so
+// all of them issue in the same windows and the host link has idle gaps
+// between them.  period == 0: no pacing.  The host guarantees on >= 100
+// ticks and period <= 1,000,000 ticks, and the poll below re-reads the clock
+// every few ticks, so each wait ends within one period.
+struct Pace {
+    uint32_t on, period;   // wall-clock ticks
+};
+
+__device__ __forceinline__ void pace_wait(const Pace p)
+{
+    if (p.period == 0)
+        return;
+    for (;;) {
+        const uint32_t t = (uint32_t)wall_clock64();
+        if (t % p.period < p.on)
+            return;
+        __builtin_amdgcn_s_sleep(2);
+    }
+}
+
 // Wavefront w of nw copies chunks [w*C/nw, (w+1)*C/nw) of the worklist,
 // storing with cache policy SP.
 template <int SP = kStorePolicy>
 __device__ __forceinline__ void copy_share(const ChunkRec *__restrict__ recs, uint32_t n_chunks,
-                                           uint32_t w, uint32_t nw)
+                                           uint32_t w, uint32_t nw, const Pace pace = Pace{0, 0})
 {
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t lo = (uint32_t)((uint64_t)w * n_chunks / nw);
@@ -88,26 +112,21 @@ __device__ __forceinline__ void copy_share(const ChunkRec *__restrict__ recs, ui
         const uint32_t cnt = hi - base < 64u ? hi - base : 64u;
         const uint32_t nb = base + 64u;
         const Rec nxt = load_rec(recs, nb + lane, nb < hi && nb + lane < hi);   // prefetch
-        for (uint32_t j = 0; j < cnt; ++j)
+        for (uint32_t j = 0; j < cnt; ++j) {
+            pace_wait(pace);
             copy_chunk<SP>(lane_u64(cur.src, j), lane_u64(cur.dst, j),
-                       __builtin_amdgcn_readlane(cur.bytes, j), lane);
+                           __builtin_amdgcn_readlane(cur.bytes, j), lane);
+        }
         cur = nxt;
     }
 }
 
-template <int SP = kStorePolicy>
-__device__ __forceinline__ void copy_worklist(const ChunkRec *__restrict__ recs, uint32_t n_chunks)
+template <int SP>
+__device__ __forceinline__ void copy_worklist(const ChunkRec *__restrict__ recs, uint32_t n_chunks,
+                                              const Pace pace)
 {
     const uint32_t w = __builtin_amdgcn_readfirstlane(blockIdx.x * kWavesPerWG + (threadIdx.x >> 6));
-    copy_share<SP>(recs, n_chunks, w, gridDim.x * kWavesPerWG);
-}
-
-// The per-chunk loop with system-scope stores (for D2H batches that run
-// with no H2D copy beside them; see kSysStorePolicy).
-__device__ __forceinline__ void copy_worklist_sys(const ChunkRec *__restrict__ recs,
-                                                  uint32_t n_chunks)
-{
-    copy_worklist<kSysStorePolicy>(recs, n_chunks);
+    copy_share<SP>(recs, n_chunks, w, gridDim.x * kWavesPerWG, pace);
 }
 
 // ---- pipelined variant ------------------------------------------------------
@@ -343,6 +362,7 @@ __device__ __forceinline__ void copy_worklist_dynamic(const ChunkRec *__restrict
 // workgroups: 96.9 GB/s this way, 95.6 GB/s with each wavefront alternating
 // between the lists, 82-85 GB/s with whole workgroups given to one list, and
 // 65 GB/s with each wavefront copying its share of a and then of b.
+template <int SP>
 __device__ __forceinline__ void copy_pair(const ChunkRec *__restrict__ ra, uint32_t ca,
                                           const ChunkRec *__restrict__ rb, uint32_t cb,
                                           uint32_t wa)
@@ -350,9 +370,9 @@ __device__ __forceinline__ void copy_pair(const ChunkRec *__restrict__ ra, uint3
     const uint32_t nw = gridDim.x * kWavesPerWG;
     const uint32_t v = __builtin_amdgcn_readfirstlane((threadIdx.x >> 6) * gridDim.x + blockIdx.x);
     if (v < wa)
-        copy_share<kSysStorePolicy>(ra, ca, v, wa);
+        copy_share<SP>(ra, ca, v, wa);
     else
-        copy_share<kSysStorePolicy>(rb, cb, v - wa, nw - wa);
+        copy_share<SP>(rb, cb, v - wa, nw - wa);
 }
 
 // ---- inline worklist ----------------------------------------------------------
@@ -360,6 +380,7 @@ __device__ __forceinline__ void copy_pair(const ChunkRec *__restrict__ ra, uint3
 // The per-chunk loop over a worklist passed by value in the kernel
 // arguments: the records are read with scalar loads from the kernel-argument
 // segment, so nothing crosses the host link before the first data load.
+template <int SP>
 __device__ __forceinline__ void copy_inline(const InlineWork &w)
 {
     const uint32_t lane = threadIdx.x & 63u;
@@ -369,42 +390,60 @@ __device__ __forceinline__ void copy_inline(const InlineWork &w)
     const uint32_t lo = wv * n / nw, hi = (wv + 1) * n / nw;   // n <= 128: no overflow
     for (uint32_t j = lo; j < hi; ++j) {
         const uint32_t k = __builtin_amdgcn_readfirstlane(j);
-        copy_chunk(w.rec[k].src, w.rec[k].dst, w.rec[k].bytes, lane);
+        copy_chunk<SP>(w.rec[k].src, w.rec[k].dst, w.rec[k].bytes, lane);
     }
 }
 
-// One symbol per direction and loop, so that profiles and counters separate them.
-#define KVC_KERNEL(name, body)                                                                     \
+// One symbol per direction, loop and store form, so that profiles and
+// counters separate them.  "_sc1" kernels store with kSc1StorePolicy, the
+// others with kStorePolicy.
+#define KVC_KERNEL(name, SP)                                                                       \
+    __global__ __launch_bounds__(kThreadsPerWG) void name(const ChunkRec *__restrict__ recs,     \
+                                                          uint32_t n_chunks, const Pace pace)    \
+    {                                                                                              \
+        copy_worklist<SP>(recs, n_chunks, pace);                                                   \
+    }
+KVC_KERNEL(kvcopy_h2d_kernel, kStorePolicy)
+KVC_KERNEL(kvcopy_d2h_kernel, kStorePolicy)
+KVC_KERNEL(kvcopy_d2d_kernel, kStorePolicy)
+KVC_KERNEL(kvcopy_h2d_sc1_kernel, kSc1StorePolicy)
+KVC_KERNEL(kvcopy_d2h_sc1_kernel, kSc1StorePolicy)
+KVC_KERNEL(kvcopy_d2d_sc1_kernel, kSc1StorePolicy)
+#undef KVC_KERNEL
+
+#define KVC_PIPE_KERNEL(name)                                                                      \
     __global__ __launch_bounds__(kThreadsPerWG) void name(const ChunkRec *__restrict__ recs,     \
                                                           uint32_t n_chunks)                     \
     {                                                                                              \
-        body(recs, n_chunks);                                                                      \
+        copy_worklist_pipelined(recs, n_chunks);                                                   \
     }
-KVC_KERNEL(kvcopy_h2d_kernel, copy_worklist)
-KVC_KERNEL(kvcopy_d2h_kernel, copy_worklist)
-KVC_KERNEL(kvcopy_d2d_kernel, copy_worklist)
-KVC_KERNEL(kvcopy_h2d_pipe_kernel, copy_worklist_pipelined)
-KVC_KERNEL(kvcopy_d2h_pipe_kernel, copy_worklist_pipelined)
-KVC_KERNEL(kvcopy_d2d_pipe_kernel, copy_worklist_pipelined)
-KVC_KERNEL(kvcopy_d2h_sys_kernel, copy_worklist_sys)
-#undef KVC_KERNEL
+KVC_PIPE_KERNEL(kvcopy_h2d_pipe_kernel)
+KVC_PIPE_KERNEL(kvcopy_d2h_pipe_kernel)
+KVC_PIPE_KERNEL(kvcopy_d2d_pipe_kernel)
+#undef KVC_PIPE_KERNEL
 
-__global__ __launch_bounds__(kThreadsPerWG) void kvcopy_pair_kernel(const ChunkRec *__restrict__ ra,
-                                                                    uint32_t ca,
-                                                                    const ChunkRec *__restrict__ rb,
-                                                                    uint32_t cb, uint32_t wa)
-{
-    copy_pair(ra, ca, rb, cb, wa);
-}
+#define KVC_PAIR_KERNEL(name, SP)                                                                  \
+    __global__ __launch_bounds__(kThreadsPerWG) void name(                                         \
+        const ChunkRec *__restrict__ ra, uint32_t ca, const ChunkRec *__restrict__ rb, uint32_t cb, \
+        uint32_t wa)                                                                               \
+    {                                                                                              \
+        copy_pair<SP>(ra, ca, rb, cb, wa);                                                         \
+    }
+KVC_PAIR_KERNEL(kvcopy_pair_kernel, kSc1StorePolicy)
+KVC_PAIR_KERNEL(kvcopy_pair_nt_kernel, kStorePolicy)
+#undef KVC_PAIR_KERNEL
 
-#define KVC_INLINE_KERNEL(name)                                                                    \
+#define KVC_INLINE_KERNEL(name, SP)                                                                \
     __global__ __launch_bounds__(kThreadsPerWG) void name(const InlineWork w)                     \
     {                                                                                              \
-        copy_inline(w);                                                                            \
+        copy_inline<SP>(w);                                                                        \
     }
-KVC_INLINE_KERNEL(kvcopy_h2d_inline_kernel)
-KVC_INLINE_KERNEL(kvcopy_d2h_inline_kernel)
-KVC_INLINE_KERNEL(kvcopy_d2d_inline_kernel)
+KVC_INLINE_KERNEL(kvcopy_h2d_inline_kernel, kStorePolicy)
+KVC_INLINE_KERNEL(kvcopy_d2h_inline_kernel, kStorePolicy)
+KVC_INLINE_KERNEL(kvcopy_d2d_inline_kernel, kStorePolicy)
+KVC_INLINE_KERNEL(kvcopy_h2d_inline_sc1_kernel, kSc1StorePolicy)
+KVC_INLINE_KERNEL(kvcopy_d2h_inline_sc1_kernel, kSc1StorePolicy)
+KVC_INLINE_KERNEL(kvcopy_d2d_inline_sc1_kernel, kSc1StorePolicy)
 #undef KVC_INLINE_KERNEL
 
 #define KVC_DYN_KERNEL(name)                                                                       \
@@ -422,41 +461,54 @@ KVC_DYN_KERNEL(kvcopy_d2d_dyn_kernel)
 }  // namespace
 
 hipError_t launch_copy(const ChunkRec *recs, uint32_t n_chunks, uint32_t grid, int dir,
-                       bool pipelined, bool sys_stores, hipStream_t stream, hipEvent_t start,
-                       hipEvent_t stop)
+                       bool pipelined, bool sc1_stores, uint32_t pace_on, uint32_t pace_period,
+                       hipStream_t stream, hipEvent_t start, hipEvent_t stop)
 {
-    static const void *const fns[2][3] = {
+    static const void *const per_chunk[2][3] = {
         {reinterpret_cast<const void *>(&kvcopy_h2d_kernel),
          reinterpret_cast<const void *>(&kvcopy_d2h_kernel),
          reinterpret_cast<const void *>(&kvcopy_d2d_kernel)},
-        {reinterpret_cast<const void *>(&kvcopy_h2d_pipe_kernel),
-         reinterpret_cast<const void *>(&kvcopy_d2h_pipe_kernel),
-         reinterpret_cast<const void *>(&kvcopy_d2d_pipe_kernel)}};
-    const void *fn = fns[pipelined ? 1 : 0][dir];
-    if (sys_stores && !pipelined && dir == 1 /* KVCOPY_D2H */)
-        fn = reinterpret_cast<const void *>(&kvcopy_d2h_sys_kernel);
-    void *args[] = {(void *)&recs, (void *)&n_chunks};
-    return hipExtLaunchKernel(fn, dim3(grid), dim3(kThreadsPerWG), args, 0, stream, start, stop, 0);
+        {reinterpret_cast<const void *>(&kvcopy_h2d_sc1_kernel),
+         reinterpret_cast<const void *>(&kvcopy_d2h_sc1_kernel),
+         reinterpret_cast<const void *>(&kvcopy_d2d_sc1_kernel)}};
+    static const void *const pipe[3] = {reinterpret_cast<const void *>(&kvcopy_h2d_pipe_kernel),
+                                        reinterpret_cast<const void *>(&kvcopy_d2h_pipe_kernel),
+                                        reinterpret_cast<const void *>(&kvcopy_d2d_pipe_kernel)};
+    if (pipelined) {
+        void *args[] = {(void *)&recs, (void *)&n_chunks};
+        return hipExtLaunchKernel(pipe[dir], dim3(grid), dim3(kThreadsPerWG), args, 0, stream,
+                                  start, stop, 0);
+    }
+    Pace pace{pace_on, pace_period};
+    void *args[] = {(void *)&recs, (void *)&n_chunks, (void *)&pace};
+    return hipExtLaunchKernel(per_chunk[sc1_stores ? 1 : 0][dir], dim3(grid), dim3(kThreadsPerWG),
+                              args, 0, stream, start, stop, 0);
 }
 
 hipError_t launch_copy_pair(const ChunkRec *ra, uint32_t ca, const ChunkRec *rb, uint32_t cb,
-                            uint32_t grid, hipStream_t stream, hipEvent_t start, hipEvent_t stop)
+                            uint32_t grid, bool sc1_stores, hipStream_t stream, hipEvent_t start,
+                            hipEvent_t stop)
 {
     uint32_t wa = pair_split(ca, cb, grid * kWavesPerWG);
     void *args[] = {(void *)&ra, (void *)&ca, (void *)&rb, (void *)&cb, (void *)&wa};
-    return hipExtLaunchKernel(reinterpret_cast<const void *>(&kvcopy_pair_kernel), dim3(grid),
-                              dim3(kThreadsPerWG), args, 0, stream, start, stop, 0);
+    const void *fn = sc1_stores ? reinterpret_cast<const void *>(&kvcopy_pair_kernel)
+                                : reinterpret_cast<const void *>(&kvcopy_pair_nt_kernel);
+    return hipExtLaunchKernel(fn, dim3(grid), dim3(kThreadsPerWG), args, 0, stream, start, stop, 0);
 }
 
-hipError_t launch_copy_inline(const InlineWork &w, uint32_t grid, int dir, hipStream_t stream,
-                              hipEvent_t start, hipEvent_t stop)
+hipError_t launch_copy_inline(const InlineWork &w, uint32_t grid, int dir, bool sc1_stores,
+                              hipStream_t stream, hipEvent_t start, hipEvent_t stop)
 {
-    static const void *const fns[3] = {reinterpret_cast<const void *>(&kvcopy_h2d_inline_kernel),
-                                       reinterpret_cast<const void *>(&kvcopy_d2h_inline_kernel),
-                                       reinterpret_cast<const void *>(&kvcopy_d2d_inline_kernel)};
+    static const void *const fns[2][3] = {
+        {reinterpret_cast<const void *>(&kvcopy_h2d_inline_kernel),
+         reinterpret_cast<const void *>(&kvcopy_d2h_inline_kernel),
+         reinterpret_cast<const void *>(&kvcopy_d2d_inline_kernel)},
+        {reinterpret_cast<const void *>(&kvcopy_h2d_inline_sc1_kernel),
+         reinterpret_cast<const void *>(&kvcopy_d2h_inline_sc1_kernel),
+         reinterpret_cast<const void *>(&kvcopy_d2d_inline_sc1_kernel)}};
     void *args[] = {(void *)&w};
-    return hipExtLaunchKernel(fns[dir], dim3(grid), dim3(kThreadsPerWG), args, 0, stream, start,
-                              stop, 0);
+    return hipExtLaunchKernel(fns[sc1_stores ? 1 : 0][dir], dim3(grid), dim3(kThreadsPerWG), args,
+                              0, stream, start, stop, 0);
 }
 
 hipError_t launch_copy_dynamic(const ChunkRec *recs, uint32_t n_chunks, uint32_t grid, int dir,

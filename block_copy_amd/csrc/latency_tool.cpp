@@ -8,7 +8,7 @@
 //   kvcopy_latency FILE...
 //
 // Each FILE describes one batch (written by bench.py from its workloads):
-//   char name[64]; uint32 src_host, dst_host; int32 max_wgs; uint32 reserved;
+//   char name[64]; uint32 src_host, dst_host; int32 max_wgs; uint32 flags;
 //   uint64 src_bytes, dst_bytes, n;  uint64 src_off[n], dst_off[n], size[n]
 // (offsets into a source and a destination arena; an arena is device memory
 // from hipMalloc or mapped pinned host memory from kvcopy_host_alloc_mapped).
@@ -40,7 +40,7 @@ struct Header {
     char name[64];
     uint32_t src_host, dst_host;
     int32_t max_wgs;
-    uint32_t reserved;
+    uint32_t flags;   // KVCOPY_F_* for kvcopy_batch_ex (0: plain kvcopy_batch)
     uint64_t src_bytes, dst_bytes, n;
 };
 
@@ -156,8 +156,14 @@ int run_file(const char *path, hipStream_t st)
     hipEvent_t e0, e1;
     if (!ok(hipEventCreate(&e0), "hipEventCreate") || !ok(hipEventCreate(&e1), "hipEventCreate"))
         return 1;
+    kvcopy_opts_t opts;
+    memset(&opts, 0, sizeof(opts));
+    opts.struct_size = sizeof(opts);
+    opts.flags = h.flags;
     auto call = [&]() {
-        const int rc = kvcopy_batch(s.data(), d.data(), sz.data(), h.n, dir, h.max_wgs, st);
+        const int rc = h.flags ? kvcopy_batch_ex(s.data(), d.data(), sz.data(), h.n, dir, h.max_wgs,
+                                                 st, &opts)
+                               : kvcopy_batch(s.data(), d.data(), sz.data(), h.n, dir, h.max_wgs, st);
         if (rc != KVCOPY_OK)
             fprintf(stderr, "kvcopy_batch: %s\n", kvcopy_strerror(rc));
         return rc == KVCOPY_OK;

@@ -216,6 +216,33 @@ uint64_t build_worklist(const uint64_t *src, const uint64_t *dst, const uint64_t
     return w;
 }
 
+// Destination order for D2D gathers of random blocks: with the worklist in
+// list order, the chunks that the GPU has in flight at any moment write all
+// over HBM; grouped by 4 MiB destination region, the workgroups that the
+// dispatcher starts together write into a narrow band of rows.  A stable
+// counting sort: one pass counts the records per region, a prefix sum places
+// the regions, and a second pass moves every record to its slot.
+void order_by_dst(const ChunkRec *in, uint64_t n, ChunkRec *out, bool stream)
+{
+    uint64_t at[kDstBuckets] = {};
+    for (uint64_t i = 0; i < n; ++i)
+        ++at[(in[i].dst >> kDstRegionShift) & (kDstBuckets - 1)];
+    uint64_t acc = 0;
+    for (uint32_t b = 0; b < kDstBuckets; ++b) {
+        const uint64_t c = at[b];
+        at[b] = acc;
+        acc += c;
+    }
+    for (uint64_t i = 0; i < n; ++i) {
+        const ChunkRec &r = in[i];
+        ChunkRec *o = out + at[(r.dst >> kDstRegionShift) & (kDstBuckets - 1)]++;
+        if (stream)
+            put_rec<true>(o, r.src, r.dst, r.bytes);
+        else
+            put_rec<false>(o, r.src, r.dst, r.bytes);
+    }
+}
+
 uint64_t chunk_prefix(const uint64_t *size, uint64_t m, uint32_t chunk, uint64_t *begin)
 {
     uint64_t acc = 0;

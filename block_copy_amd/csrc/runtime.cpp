@@ -78,6 +78,8 @@ struct Staging {
     // granule, which no other region in flight shares; the call's last
     // wavefront resets the pair to zero.
     uint32_t *claims = nullptr;
+    int clock_khz = 0;             // wall-clock rate (hipDeviceAttributeWallClockRate), 0 = not read yet
+    std::vector<ChunkRec> order_tmp;   // KVCOPY_F_DST_ORDER: the worklist in list order
     std::vector<hipEvent_t> spare;
     StagingRing<hipEvent_t, HipEventOps> ring{HipEventOps{&spare}};
 };
@@ -178,12 +180,53 @@ int resolve_auto(const Staging *st, int dir)
 // occasional windows below 50 GB/s, and 48 gave 97.9.
 constexpr int kPairAutoWgs = 64;
 
-uint32_t grid_for(uint64_t n_chunks, int max_wgs)
+// The per-call options after parsing.
+struct CallOpts {
+    uint32_t chunk = KVCOPY_CHUNK_DEFAULT;
+    uint32_t flags = 0;
+    uint32_t duty_on_ns = 0, duty_period_ns = 0;   // period 0: no pacing
+    hipEvent_t ev_begin = nullptr, ev_end = nullptr;
+};
+
+// KVCOPY_F_STORE_SC1 / KVCOPY_F_STORE_NT: -1 when neither is given.
+int forced_store(uint32_t flags)
 {
-    const uint64_t full = (n_chunks + kWavesPerWG - 1) / kWavesPerWG;   // one wavefront per chunk
-    if (max_wgs == KVCOPY_WGS_ALL || (uint64_t)max_wgs >= full)
-        return (uint32_t)full;
-    return (uint32_t)max_wgs;
+    if (flags & KVCOPY_F_STORE_SC1)
+        return 1;
+    if (flags & KVCOPY_F_STORE_NT)
+        return 0;
+    return -1;
+}
+
+// Duty cycle in wall-clock ticks of `device` (read once per device).
+int pace_ticks(Staging *st, int device, const CallOpts &o, uint32_t *on, uint32_t *period)
+{
+    *on = *period = 0;
+    if (o.duty_period_ns == 0 || o.duty_on_ns == o.duty_period_ns)
+        return KVCOPY_OK;
+    if (st->clock_khz == 0) {
+        int khz = 0;
+        const hipError_t e = hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, device);
+        if (e != hipSuccess)
+            return hip_fail(e);
+        if (khz <= 0)
+            return hip_fail(hipErrorInvalidValue);
+        st->clock_khz = khz;
+    }
+    // ticks = ns * kHz / 1e6, the window rounded up and the period down, at
+    // least 100 ticks on (the kernel polls the clock every few ticks)
+    const uint64_t k = (uint64_t)st->clock_khz;
+    uint64_t t_on = ((uint64_t)o.duty_on_ns * k + 999999) / 1000000;
+    uint64_t t_per = (uint64_t)o.duty_period_ns * k / 1000000;
+    if (t_on < 100)
+        t_on = 100;
+    if (t_per > 1000000)
+        t_per = 1000000;
+    if (t_on >= t_per)
+        return KVCOPY_OK;   // the window covers the period: no pacing
+    *on = (uint32_t)t_on;
+    *period = (uint32_t)t_per;
+    return KVCOPY_OK;
 }
 
 // Plans the batch into the staging ring and enqueues the kernel (and, with
@@ -193,19 +236,45 @@ uint32_t grid_for(uint64_t n_chunks, int max_wgs)
 // chunk count when known); only a batch with more chunks than that (many
 // ranges longer than two chunks) is planned a second time into a region of
 // the exact size.
-int run_locked(Staging *st, const uint64_t *src, const uint64_t *dst, const uint64_t *sizes,
-               uint64_t n, uint64_t hint, int dir, int max_wgs, hipStream_t stream,
-               uint32_t chunk, uint32_t flags, hipEvent_t ev_begin, hipEvent_t ev_end)
+int run_locked(Staging *st, int device, const uint64_t *src, const uint64_t *dst,
+               const uint64_t *sizes, uint64_t n, uint64_t hint, int dir, int max_wgs,
+               hipStream_t stream, const CallOpts &o)
 {
+    const uint32_t flags = o.flags, chunk = o.chunk;
     const bool upload = (flags & KVCOPY_F_DESC_UPLOAD) != 0;
     const bool dynamic = (flags & KVCOPY_F_DYNAMIC) != 0;
     const bool merge = !(flags & KVCOPY_F_NO_COALESCE);
+    const bool dst_order = (flags & KVCOPY_F_DST_ORDER) != 0;
+    uint32_t pace_on = 0, pace_period = 0;
+    int rc = pace_ticks(st, device, o, &pace_on, &pace_period);
+    if (rc != KVCOPY_OK)
+        return rc;
     uint64_t off = 0, n_chunks = 0;
     ChunkRec *host = nullptr;
-    int rc;
-    for (int pass = 0; pass < 2; ++pass) {
-        const uint64_t room = hint ? hint : 1;
-        const uint64_t need = (room * sizeof(ChunkRec) + kAlign - 1) / kAlign * kAlign;
+    if (dst_order) {
+        // Plan in list order into host memory of the library's own, then
+        // place the records into the ring in destination order.
+        std::vector<ChunkRec> &tmp = st->order_tmp;
+        for (int pass = 0; pass < 2; ++pass) {
+            const uint64_t room = hint ? hint : 1;
+            try {
+                if (tmp.size() < room)
+                    tmp.resize(room);
+            } catch (...) {
+                return KVCOPY_ENOMEM;
+            }
+            if ((rc = build_checked(src, dst, sizes, n, merge, chunk, tmp.data(), room,
+                                    &n_chunks)) != KVCOPY_OK)
+                return rc;
+            if (n_chunks == 0)
+                return KVCOPY_OK;   // only zero-size descriptors: nothing to enqueue
+            if (n_chunks > KVCOPY_MAX_CHUNKS)
+                return KVCOPY_EINVAL;
+            if (n_chunks <= room)
+                break;
+            hint = n_chunks;   // plan again with room for every record
+        }
+        const uint64_t need = (n_chunks * sizeof(ChunkRec) + kAlign - 1) / kAlign * kAlign;
         if (4 * need > st->ring.capacity() || (upload && st->dev == nullptr) ||
             (dynamic && st->claims == nullptr)) {
             if ((rc = grow(st, need, upload, dynamic)) != KVCOPY_OK)
@@ -214,16 +283,30 @@ int run_locked(Staging *st, const uint64_t *src, const uint64_t *dst, const uint
         if ((rc = st->ring.reserve(need, &off)) != KVCOPY_OK)
             return rc;
         host = reinterpret_cast<ChunkRec *>(st->host + off);
-        if ((rc = build_checked(src, dst, sizes, n, merge, chunk, host, room, &n_chunks,
-                                true)) != KVCOPY_OK)
-            return rc;   // nothing committed: the region stays free
-        if (n_chunks == 0)
-            return KVCOPY_OK;   // only zero-size descriptors: nothing to enqueue
-        if (n_chunks > KVCOPY_MAX_CHUNKS)
-            return KVCOPY_EINVAL;
-        if (n_chunks <= room)
-            break;
-        hint = n_chunks;   // plan again into a region of the exact size
+        order_by_dst(st->order_tmp.data(), n_chunks, host, true);
+    } else {
+        for (int pass = 0; pass < 2; ++pass) {
+            const uint64_t room = hint ? hint : 1;
+            const uint64_t need = (room * sizeof(ChunkRec) + kAlign - 1) / kAlign * kAlign;
+            if (4 * need > st->ring.capacity() || (upload && st->dev == nullptr) ||
+                (dynamic && st->claims == nullptr)) {
+                if ((rc = grow(st, need, upload, dynamic)) != KVCOPY_OK)
+                    return rc;
+            }
+            if ((rc = st->ring.reserve(need, &off)) != KVCOPY_OK)
+                return rc;
+            host = reinterpret_cast<ChunkRec *>(st->host + off);
+            if ((rc = build_checked(src, dst, sizes, n, merge, chunk, host, room, &n_chunks,
+                                    true)) != KVCOPY_OK)
+                return rc;   // nothing committed: the region stays free
+            if (n_chunks == 0)
+                return KVCOPY_OK;   // only zero-size descriptors: nothing to enqueue
+            if (n_chunks > KVCOPY_MAX_CHUNKS)
+                return KVCOPY_EINVAL;
+            if (n_chunks <= room)
+                break;
+            hint = n_chunks;   // plan again into a region of the exact size
+        }
     }
     const uint64_t used = (n_chunks * sizeof(ChunkRec) + kAlign - 1) / kAlign * kAlign;
     finish_records();   // the streamed records reach memory before the launch is queued
@@ -245,7 +328,7 @@ int run_locked(Staging *st, const uint64_t *src, const uint64_t *dst, const uint
     // caller asks for the kernel's own start and end (timing), those take
     // the launch's event slots and the completion event is recorded after
     // the kernel instead.
-    const bool timed = ev_begin != nullptr || ev_end != nullptr;
+    const bool timed = o.ev_begin != nullptr || o.ev_end != nullptr;
     hipEvent_t done;
     if (!st->spare.empty()) {
         done = st->spare.back();
@@ -254,28 +337,35 @@ int run_locked(Staging *st, const uint64_t *src, const uint64_t *dst, const uint
         return hip_fail(e);
     }
     const uint32_t grid = grid_for(n_chunks, max_wgs);
-    hipEvent_t start = timed ? ev_begin : nullptr, stop = timed ? ev_end : done;
+    hipEvent_t start = timed ? o.ev_begin : nullptr, stop = timed ? o.ev_end : done;
     if (dynamic) {
         uint32_t *claim = st->claims + off / kAlign * 2;
         e = launch_copy_dynamic(recs, (uint32_t)n_chunks, grid, dir, claim,
                                 claim_grain(n_chunks, grid), stream, start, stop);
     } else {
+        // A forced store form or pacing selects the per-chunk loop.
+        const bool per_chunk = (flags & (KVCOPY_F_PER_CHUNK | KVCOPY_F_STORE_SC1 |
+                                         KVCOPY_F_STORE_NT)) != 0 || pace_period != 0;
         const bool pipelined = (flags & KVCOPY_F_PIPELINE) != 0 ||
-                               (!(flags & KVCOPY_F_PER_CHUNK) && pipeline_pays(dir, grid, n_chunks));
-        // D2H stores with system scope unless an H2D kernel of this library
-        // is still running on another stream (copy_chunk.h, kSysStorePolicy:
-        // faster alone, slower beside an H2D kernel).  Only the speed depends
-        // on the choice.
-        bool sys = false;
-        if (dir == KVCOPY_D2H && !pipelined) {
-            const int busy = st->ring.running_elsewhere(KVCOPY_H2D, stream);
-            if (busy < 0) {
-                st->spare.push_back(done);
-                return busy;
+                               (!per_chunk && pipeline_pays(dir, grid, n_chunks));
+        // D2H stores with the sc1 form unless an H2D kernel of this library
+        // is still running on another stream (copy_chunk.h, kSc1StorePolicy:
+        // faster alone, slower beside an H2D kernel), unless a flag forces a
+        // form.  Only the speed depends on the choice.
+        int sc1 = forced_store(flags);
+        if (sc1 < 0) {
+            sc1 = 0;
+            if (dir == KVCOPY_D2H && !pipelined) {
+                const int busy = st->ring.running_elsewhere(KVCOPY_H2D, stream);
+                if (busy < 0) {
+                    st->spare.push_back(done);
+                    return busy;
+                }
+                sc1 = busy == 0;
             }
-            sys = busy == 0;
         }
-        e = launch_copy(recs, (uint32_t)n_chunks, grid, dir, pipelined, sys, stream, start, stop);
+        e = launch_copy(recs, (uint32_t)n_chunks, grid, dir, pipelined, sc1 != 0, pace_on,
+                        pace_period, stream, start, stop);
     }
     if (e == hipSuccess && timed)
         e = hipEventRecord(done, stream);
@@ -296,14 +386,14 @@ constexpr int kNotInline = 1;   // run_inline's "use the staging ring instead"
 // chunk count, when the worklist does not fit or the default policy would
 // pick the pipelined loop for this grid (small D2D grids).
 int run_inline(Staging *st, const uint64_t *src, const uint64_t *dst, const uint64_t *sizes,
-               uint64_t n, int dir, int max_wgs, hipStream_t stream, uint32_t chunk,
-               uint32_t flags, hipEvent_t ev_begin, hipEvent_t ev_end, uint64_t *chunks)
+               uint64_t n, int dir, int max_wgs, hipStream_t stream, const CallOpts &o,
+               uint64_t *chunks)
 {
     InlineWork w;
     w.reserved = 0;
     uint64_t need = 0;
-    const int rc = build_checked(src, dst, sizes, n, !(flags & KVCOPY_F_NO_COALESCE), chunk, w.rec,
-                                 kInlineRecs, &need);
+    const int rc = build_checked(src, dst, sizes, n, !(o.flags & KVCOPY_F_NO_COALESCE), o.chunk,
+                                 w.rec, kInlineRecs, &need);
     if (rc != KVCOPY_OK)
         return rc;
     if (need == 0)
@@ -317,9 +407,11 @@ int run_inline(Staging *st, const uint64_t *src, const uint64_t *dst, const uint
         max_wgs = resolve_auto(st, dir);
     }
     const uint32_t grid = grid_for(w.n_chunks, max_wgs);
-    if (!(flags & KVCOPY_F_PER_CHUNK) && pipeline_pays(dir, grid, w.n_chunks))
+    const int forced = forced_store(o.flags);
+    if (!(o.flags & KVCOPY_F_PER_CHUNK) && forced < 0 && pipeline_pays(dir, grid, w.n_chunks))
         return kNotInline;
-    const hipError_t e = launch_copy_inline(w, grid, dir, stream, ev_begin, ev_end);
+    const hipError_t e =
+        launch_copy_inline(w, grid, dir, forced == 1, stream, o.ev_begin, o.ev_end);
     return e == hipSuccess ? KVCOPY_OK : hip_fail(e);
 }
 
@@ -327,7 +419,7 @@ int run_inline(Staging *st, const uint64_t *src, const uint64_t *dst, const uint
 // region, list b's records right after list a's, and one kernel copies both.
 int run_pair_locked(Staging *st, const uint64_t *const src[2], const uint64_t *const dst[2],
                     const uint64_t *const sizes[2], const uint64_t n[2], bool merge,
-                    int max_wgs, hipStream_t stream)
+                    bool sc1_stores, int max_wgs, hipStream_t stream)
 {
     uint64_t hint[2] = {2 * n[0], 2 * n[1]}, cnt[2] = {0, 0}, off = 0;
     ChunkRec *host = nullptr;
@@ -370,7 +462,7 @@ int run_pair_locked(Staging *st, const uint64_t *const src[2], const uint64_t *c
         return hip_fail(e);
     }
     e = launch_copy_pair(host, (uint32_t)cnt[0], host + cnt[0], (uint32_t)cnt[1],
-                         grid_for(total, max_wgs), stream, nullptr, done);
+                         grid_for(total, max_wgs), sc1_stores, stream, nullptr, done);
     if (e != hipSuccess) {
         st->spare.push_back(done);
         return hip_fail(e);
@@ -396,25 +488,38 @@ extern "C" int kvcopy_batch_ex(const uint64_t *src_addrs, const uint64_t *dst_ad
                                const uint64_t *sizes, uint64_t n, int dir, int max_wgs,
                                hipStream_t stream, const kvcopy_opts_t *opts)
 {
-    uint32_t chunk = KVCOPY_CHUNK_DEFAULT, flags = 0;
-    hipEvent_t ev_begin = nullptr, ev_end = nullptr;
+    CallOpts o;
     if (opts) {
-        if (opts->struct_size != sizeof(kvcopy_opts_t))
+        if (opts->struct_size != sizeof(kvcopy_opts_t) && opts->struct_size != KVCOPY_OPTS_V1_SIZE)
             return KVCOPY_EINVAL;
         if (opts->chunk_bytes) {
             if ((opts->chunk_bytes & 15u) || opts->chunk_bytes > KVCOPY_CHUNK_MAX)
                 return KVCOPY_EINVAL;
-            chunk = opts->chunk_bytes;
+            o.chunk = opts->chunk_bytes;
         }
-        if (opts->flags & ~(KVCOPY_F_VALIDATE | KVCOPY_F_NO_COALESCE | KVCOPY_F_DESC_UPLOAD |
-                            KVCOPY_F_PIPELINE | KVCOPY_F_PER_CHUNK | KVCOPY_F_DYNAMIC))
+        const uint32_t known = KVCOPY_F_VALIDATE | KVCOPY_F_NO_COALESCE | KVCOPY_F_DESC_UPLOAD |
+                               KVCOPY_F_PIPELINE | KVCOPY_F_PER_CHUNK | KVCOPY_F_DYNAMIC |
+                               KVCOPY_F_STORE_SC1 | KVCOPY_F_STORE_NT | KVCOPY_F_DST_ORDER;
+        if (opts->flags & ~known)
             return KVCOPY_EINVAL;
         const uint32_t loops = opts->flags & (KVCOPY_F_PIPELINE | KVCOPY_F_PER_CHUNK | KVCOPY_F_DYNAMIC);
         if (loops & (loops - 1))   // more than one loop forced
             return KVCOPY_EINVAL;
-        flags = opts->flags;
-        ev_begin = opts->kernel_begin;
-        ev_end = opts->kernel_end;
+        const uint32_t stores = opts->flags & (KVCOPY_F_STORE_SC1 | KVCOPY_F_STORE_NT);
+        if (stores == (KVCOPY_F_STORE_SC1 | KVCOPY_F_STORE_NT) ||
+            (stores && (opts->flags & (KVCOPY_F_PIPELINE | KVCOPY_F_DYNAMIC))))
+            return KVCOPY_EINVAL;   // store forms exist for the per-chunk loop only
+        if (opts->struct_size == sizeof(kvcopy_opts_t) && opts->duty_period_ns != 0) {
+            if (opts->duty_on_ns < 1000 || opts->duty_on_ns > opts->duty_period_ns ||
+                opts->duty_period_ns > 10000000u ||
+                (opts->flags & (KVCOPY_F_PIPELINE | KVCOPY_F_DYNAMIC)))
+                return KVCOPY_EINVAL;
+            o.duty_on_ns = opts->duty_on_ns;
+            o.duty_period_ns = opts->duty_period_ns;
+        }
+        o.flags = opts->flags;
+        o.ev_begin = opts->kernel_begin;
+        o.ev_end = opts->kernel_end;
     }
     if (dir != KVCOPY_H2D && dir != KVCOPY_D2H && dir != KVCOPY_D2D)
         return KVCOPY_EINVAL;
@@ -425,7 +530,7 @@ extern "C" int kvcopy_batch_ex(const uint64_t *src_addrs, const uint64_t *dst_ad
     if (!src_addrs || !dst_addrs || !sizes)
         return KVCOPY_EINVAL;
     bool bad_env = false;
-    const bool validate = env_validate(&bad_env) || (flags & KVCOPY_F_VALIDATE);
+    const bool validate = env_validate(&bad_env) || (o.flags & KVCOPY_F_VALIDATE);
     if (bad_env)
         return KVCOPY_EINVAL;
 
@@ -435,7 +540,7 @@ extern "C" int kvcopy_batch_ex(const uint64_t *src_addrs, const uint64_t *dst_ad
     // overlap check.
     if (validate) {
         Prescan pre;
-        int rc = prescan(src_addrs, dst_addrs, sizes, n, chunk, &pre);
+        int rc = prescan(src_addrs, dst_addrs, sizes, n, o.chunk, &pre);
         if (rc != KVCOPY_OK)
             return rc;
         if ((rc = check_overlap(src_addrs, dst_addrs, sizes, n)) != KVCOPY_OK)
@@ -447,7 +552,7 @@ extern "C" int kvcopy_batch_ex(const uint64_t *src_addrs, const uint64_t *dst_ad
     if (e != hipSuccess) {
         // Argument errors keep priority over a failing runtime.
         Prescan pre;
-        const int rc = prescan(src_addrs, dst_addrs, sizes, n, chunk, &pre);
+        const int rc = prescan(src_addrs, dst_addrs, sizes, n, o.chunk, &pre);
         if (rc != KVCOPY_OK)
             return rc;
         if (pre.bound > KVCOPY_MAX_CHUNKS)
@@ -460,15 +565,16 @@ extern "C" int kvcopy_batch_ex(const uint64_t *src_addrs, const uint64_t *dst_ad
     // sizes with 16 KiB chunks, say), so they are planned once; the region's
     // unused tail is not committed.
     uint64_t hint = n <= KVCOPY_MAX_DESCS / 2 ? 2 * n : n;
-    if (n <= kInlineRecs && !(flags & (KVCOPY_F_DESC_UPLOAD | KVCOPY_F_PIPELINE | KVCOPY_F_DYNAMIC))) {
-        const int rc = run_inline(st, src_addrs, dst_addrs, sizes, n, dir, max_wgs, stream, chunk,
-                                  flags, ev_begin, ev_end, &hint);
+    const uint32_t ring_only = KVCOPY_F_DESC_UPLOAD | KVCOPY_F_PIPELINE | KVCOPY_F_DYNAMIC |
+                               KVCOPY_F_DST_ORDER;
+    if (n <= kInlineRecs && !(o.flags & ring_only) && o.duty_period_ns == 0) {
+        const int rc = run_inline(st, src_addrs, dst_addrs, sizes, n, dir, max_wgs, stream, o,
+                                  &hint);
         if (rc != kNotInline)
             return rc;
     }
     std::lock_guard<std::mutex> g(st->mu);
-    return run_locked(st, src_addrs, dst_addrs, sizes, n, hint, dir, max_wgs, stream, chunk, flags,
-                      ev_begin, ev_end);
+    return run_locked(st, device, src_addrs, dst_addrs, sizes, n, hint, dir, max_wgs, stream, o);
 }
 
 extern "C" int kvcopy_batch_pair(const uint64_t *src_a, const uint64_t *dst_a,
@@ -477,7 +583,7 @@ extern "C" int kvcopy_batch_pair(const uint64_t *src_a, const uint64_t *dst_a,
                                  int max_wgs, uint32_t flags, hipStream_t stream)
 {
     if (max_wgs < KVCOPY_WGS_AUTO || n_a > KVCOPY_MAX_DESCS || n_b > KVCOPY_MAX_DESCS ||
-        (flags & ~(KVCOPY_F_VALIDATE | KVCOPY_F_NO_COALESCE)) != 0)
+        (flags & ~(KVCOPY_F_VALIDATE | KVCOPY_F_NO_COALESCE | KVCOPY_F_STORE_NT)) != 0)
         return KVCOPY_EINVAL;
     if ((n_a && (!src_a || !dst_a || !sizes_a)) || (n_b && (!src_b || !dst_b || !sizes_b)))
         return KVCOPY_EINVAL;
@@ -523,8 +629,8 @@ extern "C" int kvcopy_batch_pair(const uint64_t *src_a, const uint64_t *dst_a,
     }
     Staging *st = staging_for(device);
     std::lock_guard<std::mutex> g(st->mu);
-    return run_pair_locked(st, src, dst, sizes, n, !(flags & KVCOPY_F_NO_COALESCE), max_wgs,
-                           stream);
+    return run_pair_locked(st, src, dst, sizes, n, !(flags & KVCOPY_F_NO_COALESCE),
+                           !(flags & KVCOPY_F_STORE_NT), max_wgs, stream);
 }
 
 extern "C" uint64_t kvcopy_device_workspace_bytes(uint64_t max_n)
@@ -559,7 +665,7 @@ extern "C" int kvcopy_batch_device(const uint64_t *d_src, const uint64_t *d_dst,
         std::lock_guard<std::mutex> g(st->mu);
         max_wgs = resolve_auto(st, dir);
     }
-    const uint32_t grid = max_wgs ? (uint32_t)max_wgs : 1024u;
+    const uint32_t grid = max_wgs == 0 ? 1024u : (uint32_t)max_wgs < kMaxGrid ? (uint32_t)max_wgs : kMaxGrid;
     const hipError_t e =
         launch_device_batch(d_src, d_dst, d_sizes, d_n, max_n, chunk_bytes, grid, workspace, stream);
     return e == hipSuccess ? KVCOPY_OK : hip_fail(e);

@@ -1,6 +1,7 @@
 """ctypes binding of libkvload.so (measurement only): the synthetic bf16 GEMV
-decode loop that the interference benchmark runs next to copy bursts, and the
-scattered read-only and write-only passes that bound the D2D copy."""
+decode loop that the interference benchmark runs next to copy bursts (and an
+ALU-only stand-in for it), the scattered read-only and write-only passes
+that bound the D2D copy, and an empty kernel for launch floors."""
 from __future__ import annotations
 
 import ctypes
@@ -17,6 +18,12 @@ lib.kvload_chain_bf16.restype = ctypes.c_int
 lib.kvload_chain_bf16.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_int),
                                   ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_void_p),
                                   ctypes.c_int, ctypes.c_void_p]
+
+lib.kvload_alu_chain.restype = ctypes.c_int
+lib.kvload_alu_chain.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                 ctypes.c_void_p]
+lib.kvload_empty.restype = ctypes.c_int
+lib.kvload_empty.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
 
 for _f in (lib.kvload_gather_read, lib.kvload_scatter_write):
     _f.restype = ctypes.c_int
@@ -66,6 +73,29 @@ class Chain:
         rc = lib.kvload_chain_bf16(self.Ws, self.rows, self.cols, self.acts, self.n, _stream(stream))
         if rc != 0:
             raise RuntimeError(f"kvload_chain_bf16 failed: hipError {rc}")
+
+
+class AluChain:
+    """The ALU-only stand-in for a decode step: n kernels of `grid`
+    workgroups, each thread running `iters` dependent FMAs, one store per
+    workgroup at the end (`out`: a GPU float tensor of at least 1,024)."""
+
+    def __init__(self, out, n=36, grid=1024, iters=4096):
+        if out.numel() < 1024 or not out.is_cuda or out.element_size() != 4:
+            raise ValueError("out must be a float32 GPU tensor of at least 1,024 elements")
+        self.out, self.n, self.grid, self.iters = out, int(n), int(grid), int(iters)
+
+    def run(self, stream=None) -> None:
+        rc = lib.kvload_alu_chain(self.out.data_ptr(), self.n, self.grid, self.iters, _stream(stream))
+        if rc != 0:
+            raise RuntimeError(f"kvload_alu_chain failed: hipError {rc}")
+
+
+def empty(grid, stream=None, start=None, stop=None) -> None:
+    """One empty kernel of `grid` workgroups (its events give the launch floor)."""
+    rc = lib.kvload_empty(int(grid), _stream(stream), start, stop)
+    if rc != 0:
+        raise RuntimeError(f"kvload_empty failed: hipError {rc}")
 
 
 def _blocks(addrs, block_bytes):

@@ -11,6 +11,7 @@ from __future__ import annotations
 import ctypes
 import ctypes.util
 import os
+import sys
 
 _CANDIDATES = [os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "lib", "libamdhip64.so"),
                "libamdhip64.so"]
@@ -101,10 +102,19 @@ class Event:
         check(hip.hipEventElapsedTime(ctypes.byref(ms), self.h, end.h), "hipEventElapsedTime")
         return float(ms.value)
 
+    def destroy(self) -> None:
+        if self.h:
+            h, self.h = self.h, None
+            check(hip.hipEventDestroy(h), "hipEventDestroy")
+
     def __del__(self):
+        # No HIP call from a finaliser that runs while the interpreter shuts
+        # down: by then the runtime (or a profiler wrapped around it) may be
+        # tearing itself down.  The process's exit releases the event.
+        if sys.is_finalizing():
+            return
         try:
-            if self.h:
-                hip.hipEventDestroy(self.h)
+            self.destroy()
         except Exception:
             pass
 

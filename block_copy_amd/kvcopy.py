@@ -13,6 +13,7 @@ from __future__ import annotations
 
 import ctypes
 import os
+import sys
 from dataclasses import dataclass
 
 import numpy as np
@@ -24,6 +25,8 @@ CHUNK_DEFAULT = 16384
 CHUNK_MAX = 1 << 20
 F_VALIDATE, F_NO_COALESCE, F_DESC_UPLOAD = 0x1, 0x2, 0x8
 F_PIPELINE, F_PER_CHUNK, F_DYNAMIC = 0x10, 0x20, 0x40
+F_STORE_SC1, F_STORE_NT, F_DST_ORDER = 0x80, 0x100, 0x200
+OPTS_V1_SIZE = 32
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvcopy.so")
 
@@ -59,7 +62,8 @@ class Opts(ctypes.Structure):
     """kvcopy_opts_t."""
     _fields_ = [("struct_size", ctypes.c_uint32), ("chunk_bytes", ctypes.c_uint32),
                 ("flags", ctypes.c_uint32), ("reserved", ctypes.c_uint32),
-                ("kernel_begin", ctypes.c_void_p), ("kernel_end", ctypes.c_void_p)]
+                ("kernel_begin", ctypes.c_void_p), ("kernel_end", ctypes.c_void_p),
+                ("duty_on_ns", ctypes.c_uint32), ("duty_period_ns", ctypes.c_uint32)]
 
 
 def _load():
@@ -206,22 +210,25 @@ def kvcopy_plan(src, dst, sizes, chunk_bytes: int = 0) -> Plan:
 
 def kvcopy_batch(src_addrs, dst_addrs, sizes, dir: int, max_wgs: int = WGS_ALL,
                  stream=None, *, chunk_bytes: int = 0, flags: int = 0,
-                 kernel_begin=None, kernel_end=None, check: bool = True) -> int:
+                 kernel_begin=None, kernel_end=None, duty_on_ns: int = 0,
+                 duty_period_ns: int = 0, opts_size: int = 0, check: bool = True) -> int:
     """Enqueue the batch on `stream` (see include/kvcopy.h).
 
     With any option given, calls kvcopy_batch_ex.  kernel_begin/kernel_end
-    are raw hipEvent_t handles (ints).  Raises KvcopyError on failure unless
-    check=False, in which case the status code is returned.
+    are raw hipEvent_t handles (ints).  opts_size overrides struct_size
+    (say OPTS_V1_SIZE).  Raises KvcopyError on failure unless check=False,
+    in which case the status code is returned.
     """
     s, sp = _u64(src_addrs)
     d, dp = _u64(dst_addrs)
     z, zp = _u64(sizes)
     n = _n(s, d, z)
     st = ctypes.c_void_p(int(stream) if stream else 0)
-    if chunk_bytes or flags or kernel_begin or kernel_end:
-        o = Opts(ctypes.sizeof(Opts), int(chunk_bytes), int(flags), 0,
+    if chunk_bytes or flags or kernel_begin or kernel_end or duty_period_ns or opts_size:
+        o = Opts(int(opts_size) or ctypes.sizeof(Opts), int(chunk_bytes), int(flags), 0,
                  ctypes.c_void_p(int(kernel_begin) if kernel_begin else 0),
-                 ctypes.c_void_p(int(kernel_end) if kernel_end else 0))
+                 ctypes.c_void_p(int(kernel_end) if kernel_end else 0),
+                 int(duty_on_ns), int(duty_period_ns))
         rc = lib.kvcopy_batch_ex(sp, dp, zp, n, int(dir), int(max_wgs), st, ctypes.byref(o))
     else:
         rc = lib.kvcopy_batch(sp, dp, zp, n, int(dir), int(max_wgs), st)
@@ -277,6 +284,11 @@ class HostBuffer:
             self.ptr = 0
 
     def __del__(self):
+        # Free explicitly (free()); a finaliser that runs during interpreter
+        # shutdown makes no HIP call and leaves the memory to the process's
+        # exit.
+        if sys.is_finalizing():
+            return
         try:
             self.free()
         except Exception:

@@ -118,6 +118,25 @@ enum {
  * reset by each kernel's last wavefront).  Exclusive with the two flags
  * above. */
 #define KVCOPY_F_DYNAMIC 0x40u
+/* Store form of the per-chunk loop.  Two forms give the same bytes: the
+ * nontemporal hint alone ("nt"), and nt with the sc1 scope bit ("sc1", a
+ * device-scope store on the gfx940 family).  By default D2H batches use sc1
+ * unless one of this library's H2D kernels is still running on another
+ * stream, and H2D and D2D batches use nt (measured on MI355X: sc1 is faster
+ * for a lone D2H batch, slower for a D2H batch beside an H2D kernel, the
+ * same for H2D).  These flags force one form, for any direction; they select
+ * the per-chunk loop (KVCOPY_F_PIPELINE or KVCOPY_F_DYNAMIC with either is
+ * KVCOPY_EINVAL, and so are both).  kvcopy_batch_pair takes
+ * KVCOPY_F_STORE_NT (its default is sc1). */
+#define KVCOPY_F_STORE_SC1 0x80u
+#define KVCOPY_F_STORE_NT 0x100u
+/* Destination order: the worklist handed to the kernel is ordered by 4 MiB
+ * destination region ((dst >> 22) mod 256; list order within a region)
+ * instead of list order, so that the chunks in flight at any moment write a
+ * narrow band of memory.  It costs one more pass over the records on the
+ * host.  Results do not depend on it.  Meant for D2D gathers of many random
+ * blocks. */
+#define KVCOPY_F_DST_ORDER 0x200u
 
 /*
  * kvcopy_coalesce -- merge list-consecutive adjacent ranges.
@@ -183,9 +202,9 @@ void kvcopy_plan_free(kvcopy_plan_t *plan);
  * min(max_wgs, needed) workgroups of 4 wavefronts on `stream`.  Each
  * wavefront takes an equal contiguous share of the chunks and moves them
  * with 16-byte loads and nontemporal 16-byte stores (a D2H batch's stores
- * also carry system scope when none of this library's H2D kernels is still
- * running on another stream, which is faster alone and slower beside one;
- * the bytes moved are the same).  The staging region is
+ * also carry the sc1 scope bit when none of this library's H2D kernels is
+ * still running on another stream, which is faster alone and slower beside
+ * one; the bytes moved are the same; see KVCOPY_F_STORE_SC1).  The staging region is
  * recycled once an event recorded after the kernel has completed; the call
  * waits on the host only if the whole ring is still in use.  A batch of at
  * most 128 chunks instead passes its worklist in the kernel arguments (no
@@ -218,15 +237,32 @@ void kvcopy_plan_free(kvcopy_plan_t *plan);
 int kvcopy_batch(const uint64_t *src_addrs, const uint64_t *dst_addrs, const uint64_t *sizes,
                  uint64_t n, int dir, int max_wgs, hipStream_t stream);
 
-/* Options for kvcopy_batch_ex.  Zero-initialise, then set struct_size. */
+/* Options for kvcopy_batch_ex.  Zero-initialise, then set struct_size.
+ * struct_size may also be KVCOPY_OPTS_V1_SIZE (the layout without the
+ * duty-cycle fields, which then count as zero). */
 typedef struct {
-    uint32_t struct_size;   /* sizeof(kvcopy_opts_t) */
+    uint32_t struct_size;   /* sizeof(kvcopy_opts_t) or KVCOPY_OPTS_V1_SIZE */
     uint32_t chunk_bytes;   /* 0 = default; else a multiple of 16, <= KVCOPY_CHUNK_MAX */
     uint32_t flags;         /* KVCOPY_F_* */
     uint32_t reserved;
     hipEvent_t kernel_begin; /* if non-NULL: bound to the copy kernel's start (hipExtLaunchKernel) */
     hipEvent_t kernel_end;   /* if non-NULL: bound to the copy kernel's completion */
+    /* Time-sliced issue ([PF] "Proposed direction": a tail-bounded policy
+     * that trades transfer speed for co-running kernels' latency).  When
+     * duty_period_ns is non-zero, every wavefront starts a chunk only in the
+     * first duty_on_ns of each duty_period_ns of the device's wall clock
+     * (hipDeviceAttributeWallClockRate), so all copy kernels issue in the
+     * same windows and leave the host link idle in between.  Requires
+     * 1,000 <= duty_on_ns <= duty_period_ns <= 10,000,000 (else
+     * KVCOPY_EINVAL); on == period means no pacing.  Applies to the
+     * per-chunk loop (with KVCOPY_F_PIPELINE or KVCOPY_F_DYNAMIC:
+     * KVCOPY_EINVAL).  A chunk started at the end of a window still
+     * completes after it, so the link carries traffic for somewhat longer
+     * than duty_on_ns per period. */
+    uint32_t duty_on_ns;
+    uint32_t duty_period_ns;
 } kvcopy_opts_t;
+#define KVCOPY_OPTS_V1_SIZE 32u
 
 /*
  * kvcopy_batch_ex -- kvcopy_batch with options (chunk size, flags, and
@@ -260,17 +296,17 @@ int kvcopy_batch_ex(const uint64_t *src_addrs, const uint64_t *dst_addrs, const 
  * destination or any source of either list; checked in validate mode).
  * The kernel reads and writes through the addresses as given, so either
  * list may hold any direction; the usual use is H2D in one and D2H in the
- * other.  n_a or n_b may be 0 (both 0: KVCOPY_OK, nothing enqueued).  The
- * kernel's stores carry system scope as well as the nontemporal hint (as
- * kvcopy_batch's D2H kernel does when none of this library's H2D kernels is
- * running on another stream; beside one it keeps the nontemporal hint
- * alone, which is faster there).
+ * other.  n_a or n_b may be 0 (both 0: KVCOPY_OK, nothing enqueued).  By
+ * default the kernel's stores carry the sc1 scope bit as well as the
+ * nontemporal hint (as kvcopy_batch's D2H kernel does when none of this
+ * library's H2D kernels is running on another stream); KVCOPY_F_STORE_NT
+ * selects the nontemporal hint alone.
  * max_wgs as for kvcopy_batch, except that KVCOPY_WGS_AUTO is 64
  * workgroups, the steadiest cap measured for the burst above (98.4 GB/s;
  * 96-160 workgroups reach 99.1-99.5 at the median with occasional slow
  * windows; the full grid 84).
- * flags: KVCOPY_F_VALIDATE and/or KVCOPY_F_NO_COALESCE, as for
- * kvcopy_batch_ex; any other bit is KVCOPY_EINVAL.  Ownership, threads and
+ * flags: KVCOPY_F_VALIDATE, KVCOPY_F_NO_COALESCE and KVCOPY_F_STORE_NT, as
+ * for kvcopy_batch_ex; any other bit is KVCOPY_EINVAL.  Ownership, threads and
  * errors as for kvcopy_batch; an error in either list enqueues nothing.
  */
 int kvcopy_batch_pair(const uint64_t *src_a, const uint64_t *dst_a, const uint64_t *sizes_a,
@@ -339,24 +375,26 @@ void kvcopy_job_destroy(kvcopy_job_t *job);
  * [FT] "Proposal", question 1, suggests choosing the worker count from a
  * small startup probe and targeting bytes in flight rather than threads;
  * the vLLM PR #42212 report ("key source snippet", the tuned constants)
- * picks the smallest number of workers within 5% of peak bandwidth.  This
- * call does both on the current device: it allocates its own probe buffers
- * (32 MiB of mapped pinned host memory and 32 MiB of device memory per
- * direction, freed before it returns), times 24 batches of 8,192 shuffled
- * 4 KiB blocks per direction at each cap of KVCOPY_AUTOTUNE_CAPS, after four
- * untimed ones (for H2D or D2H both directions run together, H2D on s0 and
- * D2H on s1, as in a KV offload burst; D2D runs on s0), in three sweeps
- * over the caps (ascending, descending, ascending) keeping each cap's
- * median rate, and records the smallest cap within 2% of the best rate as
- * the device's KVCOPY_WGS_AUTO cap for `dir` (for H2D or D2H: for both).
- * On MI355X, shorter windows and the 5% rule picked caps of 32-64 that ran
- * long H2D + D2H bursts 5-10% slower than 128.
- * Blocks until done (about a second).
+ * picks the smallest number of workers within a tolerance of peak
+ * bandwidth.  This call does both on the current device: it allocates its
+ * own probe buffers (64 MiB of mapped pinned host memory and 64 MiB of
+ * device memory per direction, freed before it returns), times 24 batches
+ * of 16,384 shuffled 4 KiB blocks per direction at each cap of
+ * KVCOPY_AUTOTUNE_CAPS, after four untimed ones (for H2D or D2H both
+ * directions run together, H2D on s0 and D2H on s1, joined at every step
+ * as in a KV offload burst; D2D runs on s0), in three sweeps over the caps
+ * (ascending, descending, ascending), and rates each cap by its median
+ * sweep.  It records as the device's KVCOPY_WGS_AUTO cap for `dir` (for H2D
+ * or D2H: for both) the smallest cap whose slowest sweep still reaches the
+ * best cap's median rate.  On MI355X a 2% tolerance on the medians picked
+ * 32 workgroups inside the window-to-window spread of two streams, which
+ * then ran the burst 3% slower than 128.
+ * Blocks until done (one to two seconds).
  * s0, s1: the streams the caller will copy on (the hardware queues they map
  *   to matter); NULL = streams created for the probe.
  * out_wgs (may be NULL): the chosen cap (0 = full grid).
  * out_rates (may be NULL): KVCOPY_AUTOTUNE_NCAPS doubles, bytes per second
- *   at each cap, in the order of KVCOPY_AUTOTUNE_CAPS.
+ *   at each cap (median sweep), in the order of KVCOPY_AUTOTUNE_CAPS.
  * errors: KVCOPY_EINVAL (bad dir), KVCOPY_ENOMEM, KVCOPY_EHIP.
  */
 #define KVCOPY_AUTOTUNE_NCAPS 10

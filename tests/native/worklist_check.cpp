@@ -163,6 +163,86 @@ int main(int argc, char **argv)
                     return 1;
                 }
             }
+    // Grid sizes at the documented limits: one wavefront per chunk, never
+    // more than kMaxGrid workgroups (a launch must stay under 2^32
+    // work-items), and a dynamic loop's claim counter cannot wrap: its
+    // largest value is (claims below n + one overshooting claim per
+    // wavefront) x grain.
+    struct { uint64_t chunks; int cap; uint32_t want; } gf[] = {
+        {1, 0, 1}, {4, 0, 1}, {5, 0, 2}, {1024, 0, 256}, {1024, 16, 16}, {1024, 300, 256},
+        {1ull << 24, 0, 1u << 22}, {(1ull << 24) + 4, 0, 1u << 22}, {1ull << 26, 0, 1u << 22},
+        {KVCOPY_MAX_CHUNKS, 0, 1u << 22}, {KVCOPY_MAX_CHUNKS, 0x7fffffff, 1u << 22},
+        {KVCOPY_MAX_CHUNKS, 1000, 1000}, {KVCOPY_MAX_CHUNKS, 1, 1},
+    };
+    for (const auto &c : gf) {
+        const uint32_t g = grid_for(c.chunks, c.cap);
+        if (g != c.want) {
+            printf("grid_for(%llu, %d) = %u, want %u\n", (unsigned long long)c.chunks, c.cap, g,
+                   c.want);
+            return 1;
+        }
+    }
+    for (uint64_t chunks : {(uint64_t)1, (uint64_t)1000, (uint64_t)1 << 20, (uint64_t)1 << 26,
+                            KVCOPY_MAX_CHUNKS})
+        for (int cap : {0, 1, 7, 256, 65536, 0x7fffffff}) {
+            const uint32_t g = grid_for(chunks, cap);
+            const uint64_t nw = (uint64_t)g * kWavesPerWG;
+            const uint64_t grain = claim_grain(chunks, g);
+            const uint64_t top = ((chunks + grain - 1) / grain + nw) * grain;
+            if (g == 0 || g > kMaxGrid || (uint64_t)g * kThreadsPerWG >= (1ull << 32) ||
+                grain < 1 || grain > 64 || top >= (1ull << 32)) {
+                printf("limits: chunks %llu cap %d: grid %u grain %llu top %llu\n",
+                       (unsigned long long)chunks, cap, g, (unsigned long long)grain,
+                       (unsigned long long)top);
+                return 1;
+            }
+        }
+    // Destination order: a permutation of the records, grouped by 4 MiB
+    // destination region in bucket order, list order kept within a bucket,
+    // the same with plain and with streamed stores.
+    for (int trial = 0; trial < 200; ++trial) {
+        const uint64_t n = rng() % 3000;
+        std::vector<ChunkRec> in(n), out(n + 1), out2(n + 1);
+        for (uint64_t i = 0; i < n; ++i)
+            in[i] = ChunkRec{rng() & ~7ull, (rng() % (3ull << 30)) & ~7ull,
+                             (uint32_t)(8 * (1 + rng() % 2048)), 0};
+        for (uint64_t i = 0; i < n; ++i)   // tag each record by its list position
+            in[i].src = (in[i].src & ~0xFFFFFull) | (i << 3);
+        memset(out.data(), 0x5A, out.size() * sizeof(ChunkRec));
+        order_by_dst(in.data(), n, out.data(), false);
+        order_by_dst(in.data(), n, out2.data(), true);
+        finish_records();
+        if (n && memcmp(out.data(), out2.data(), n * sizeof(ChunkRec)) != 0) {
+            printf("order_by_dst: streamed and plain stores differ\n");
+            return 1;
+        }
+        std::vector<int> seen(n, 0);
+        for (uint64_t k = 0; k < n; ++k) {
+            const uint64_t i = (out[k].src & 0xFFFFFull) >> 3;
+            const uint32_t b = (uint32_t)((out[k].dst >> kDstRegionShift) & (kDstBuckets - 1));
+            if (i >= n || seen[i]++ || memcmp(&out[k], &in[i], sizeof(ChunkRec)) != 0) {
+                printf("order_by_dst: trial %d slot %llu is not a distinct input record\n", trial,
+                       (unsigned long long)k);
+                return 1;
+            }
+            if (k > 0) {
+                const uint64_t ip = (out[k - 1].src & 0xFFFFFull) >> 3;
+                const uint32_t bp =
+                    (uint32_t)((out[k - 1].dst >> kDstRegionShift) & (kDstBuckets - 1));
+                if (bp > b || (bp == b && ip > i)) {
+                    printf("order_by_dst: trial %d slots %llu-%llu out of order\n", trial,
+                           (unsigned long long)k - 1, (unsigned long long)k);
+                    return 1;
+                }
+            }
+        }
+        const unsigned char *tail = reinterpret_cast<const unsigned char *>(out.data() + n);
+        for (size_t b = 0; b < sizeof(ChunkRec); ++b)
+            if (tail[b] != 0x5A) {
+                printf("order_by_dst wrote past its output\n");
+                return 1;
+            }
+    }
     printf("ok %d cases\n", cases);
     return 0;
 }

@@ -436,3 +436,127 @@ def test_auto_cap_and_autotune(K):
     _run(res, [0, 1], K.WGS_AUTO, streams=[s1, s2])
     _check(res, [0, 1], "WGS_AUTO tuned")
     res.free()
+
+
+# ---------------------------------------------------------------------------
+# CU-masked streams: the copy confined to a few compute units (the ROCm
+# analogue of the Green Context SM limit in PegaFlow issue #408,
+# "Follow-up", item 4)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n_cus", [8, 32])
+def test_copies_on_cu_masked_streams(K, n_cus):
+    """The headline burst (16,384 x 4 KiB each way, both directions on two
+    streams) and an irregular D2D batch (misaligned pairs, 8-byte tails,
+    zero sizes), each on streams whose kernels may use only the first
+    n_cus compute units."""
+    from block_copy_amd import hiprt
+    from block_copy_amd.harness import Resident
+    kv = Resident(W.kv_blocks(seed=6, directions="both"))
+    irr = Resident(W.irregular(seed=7, n=3000, dir_=W.D2D, misalign=True, zero_frac=0.05))
+    sa, sb = hiprt.CUMaskStream(range(n_cus)), hiprt.CUMaskStream(range(n_cus))
+    try:
+        for sentinel in (W.SENTINEL_A, W.SENTINEL_B):
+            for max_wgs in (8, 128):
+                _say("cu-masked streams", n_cus, "CUs, max_wgs", max_wgs, "sentinel", hex(sentinel))
+                kv.fill(sentinel)
+                kv.submit(0, max_wgs, sa.cuda_stream)
+                kv.submit(1, max_wgs, sb.cuda_stream)
+                hiprt.stream_sync(sa)
+                hiprt.stream_sync(sb)
+                _check(kv, [0, 1], f"kv both on {n_cus} CUs max_wgs={max_wgs}", sentinel)
+            irr.fill(sentinel)
+            irr.submit(0, 0, sa.cuda_stream)
+            hiprt.stream_sync(sa)
+            _check(irr, [0], f"irregular d2d on {n_cus} CUs", sentinel)
+    finally:
+        torch.cuda.synchronize()
+        sa.destroy()
+        sb.destroy()
+        kv.free()
+        irr.free()
+
+
+# ---------------------------------------------------------------------------
+# Forced store forms, time-sliced issue, destination order
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("form", ["sc1", "nt"])
+@pytest.mark.parametrize("dname", sorted(DIRS))
+def test_forced_store_forms(K, dname, form):
+    """KVCOPY_F_STORE_SC1 / KVCOPY_F_STORE_NT in every direction, through the
+    staging ring (600 descriptors) and the inline worklist (40)."""
+    from block_copy_amd.harness import Resident
+    d, sw, dw = DIRS[dname]
+    flag = K.F_STORE_SC1 if form == "sc1" else K.F_STORE_NT
+    for n in (600, 40):
+        wl = W.irregular(seed=100 + n + d, n=n, max_size=20000, dir_=d, src_where=sw, dst_where=dw,
+                         misalign=True, zero_frac=0.05)
+        res = Resident(wl)
+        for sentinel in (W.SENTINEL_A, W.SENTINEL_B):
+            for max_wgs in (1, 16, 0):
+                _say("store form", form, dname, "n", n, "max_wgs", max_wgs, "sentinel", hex(sentinel))
+                res.fill(sentinel)
+                _run(res, [0], max_wgs, flags=flag)
+                _check(res, [0], f"{form} {dname} n={n} max_wgs={max_wgs}", sentinel)
+        res.free()
+
+
+def test_pair_nt_stores(K):
+    from block_copy_amd.harness import Resident
+    wl = W.kv_blocks(seed=8, directions="both", n=4096, pool_blocks=16384)
+    res = Resident(wl)
+    (s0, d0), (s1, d1) = res.addrs
+    for sentinel in (W.SENTINEL_A, W.SENTINEL_B):
+        for max_wgs in (8, K.WGS_AUTO):
+            _say("pair nt stores max_wgs", max_wgs, "sentinel", hex(sentinel))
+            res.fill(sentinel)
+            K.kvcopy_batch_pair(s0, d0, wl.batches[0].size, s1, d1, wl.batches[1].size, max_wgs,
+                                flags=K.F_STORE_NT)
+            torch.cuda.synchronize()
+            _check(res, [0, 1], f"pair nt max_wgs={max_wgs}", sentinel)
+    res.free()
+
+
+@pytest.mark.parametrize("duty", [(2000, 10000), (1000, 50000), (10000, 10000)])
+def test_duty_cycle(K, duty):
+    """Time-sliced issue: both directions on two streams, and an irregular
+    D2H batch with 8-byte tails, each kernel starting chunks only inside
+    the on-windows.  (10 us of 10 us: the window covers the period.)"""
+    from block_copy_amd.harness import Resident
+    on, period = duty
+    kv = Resident(W.kv_blocks(seed=9, directions="both", n=2048, pool_blocks=8192))
+    irr = Resident(W.irregular(seed=10, n=500, dir_=W.D2H, src_where="device", dst_where="host",
+                               misalign=True, zero_frac=0.05))
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    for sentinel in (W.SENTINEL_A, W.SENTINEL_B):
+        for max_wgs in (2, 32):
+            _say("duty cycle", on, period, "max_wgs", max_wgs, "sentinel", hex(sentinel))
+            kv.fill(sentinel)
+            _run(kv, [0, 1], max_wgs, streams=[s1, s2], duty_on_ns=on, duty_period_ns=period)
+            _check(kv, [0, 1], f"duty {on}/{period} max_wgs={max_wgs}", sentinel)
+        irr.fill(sentinel)
+        _run(irr, [0], 4, duty_on_ns=on, duty_period_ns=period, flags=K.F_STORE_NT)
+        _check(irr, [0], f"duty {on}/{period} irregular d2h", sentinel)
+    kv.free()
+    irr.free()
+
+
+@pytest.mark.parametrize("max_wgs", [1, 64, 0])
+def test_destination_order(K, max_wgs):
+    """KVCOPY_F_DST_ORDER: the D2D block gather, an irregular batch whose
+    ranges span several chunks (planned twice: more records than the first
+    pass has room for), and an H2D batch."""
+    from block_copy_amd.harness import Resident
+    cases = [(W.d2d_blocks(seed=11), 0),
+             (W.irregular(seed=12, n=700, max_size=80 * 1024, dir_=W.D2D, misalign=True,
+                          zero_frac=0.05), 4096),
+             (W.kv_blocks(seed=13, directions="h2d", n=4096, pool_blocks=16384), 0)]
+    for wl, chunk in cases:
+        res = Resident(wl)
+        for sentinel in (W.SENTINEL_A, W.SENTINEL_B):
+            _say("destination order", wl.name, "max_wgs", max_wgs, "sentinel", hex(sentinel))
+            res.fill(sentinel)
+            _run(res, [0], max_wgs, flags=K.F_DST_ORDER, chunk_bytes=chunk)
+            _check(res, [0], f"dst order {wl.name} max_wgs={max_wgs}", sentinel)
+        res.free()

@@ -63,8 +63,8 @@ def test_kernels_have_no_scratch_or_spills(K, src):
     names = set(re.findall(r"\.name:\s+_ZN3kvc12_GLOBAL__N_1\d+(kvcopy_\w+?_kernel)E", txt))
     if src == "kvcopy_kernel.hip":
         want = {f"kvcopy_{d}{v}_kernel" for d in ("h2d", "d2h", "d2d")
-                for v in ("", "_pipe", "_dyn", "_inline")} | {"kvcopy_pair_kernel",
-                                                               "kvcopy_d2h_sys_kernel"}
+                for v in ("", "_sc1", "_pipe", "_dyn", "_inline", "_inline_sc1")} | {
+                    "kvcopy_pair_kernel", "kvcopy_pair_nt_kernel"}
     else:
         want = {"kvcopy_device_plan_kernel", "kvcopy_device_copy_kernel"}
     assert names == want, names
@@ -159,11 +159,25 @@ def test_batch_argument_errors(K):
     assert call(s, d, z, K.H2D, -2) == K.EINVAL
     assert call(s, d, z, K.H2D, chunk_bytes=24) == K.EINVAL        # chunk not a multiple of 16
     assert call(s, d, z, K.H2D, chunk_bytes=(1 << 20) + 16) == K.EINVAL
-    assert call(s, d, z, K.H2D, flags=0x100) == K.EINVAL          # unknown flag
+    assert call(s, d, z, K.H2D, flags=0x400) == K.EINVAL          # unknown flag
     assert call(s, d, z, K.H2D, flags=0x4) == K.EINVAL            # a retired flag value
     assert call(s, d, z, K.H2D, flags=K.F_PIPELINE | K.F_PER_CHUNK) == K.EINVAL  # two loops forced
     assert call(s, d, z, K.H2D, flags=K.F_DYNAMIC | K.F_PIPELINE) == K.EINVAL
     assert call(s, d, z, K.H2D, flags=K.F_DYNAMIC | K.F_PER_CHUNK) == K.EINVAL
+    # store forms: one at a time, for the per-chunk loop only
+    assert call(s, d, z, K.H2D, flags=K.F_STORE_SC1 | K.F_STORE_NT) == K.EINVAL
+    assert call(s, d, z, K.H2D, flags=K.F_STORE_SC1 | K.F_PIPELINE) == K.EINVAL
+    assert call(s, d, z, K.H2D, flags=K.F_STORE_NT | K.F_DYNAMIC) == K.EINVAL
+    # duty cycle: 1 us <= on <= period <= 10 ms, per-chunk loop only
+    assert call(s, d, z, K.H2D, duty_on_ns=999, duty_period_ns=10000) == K.EINVAL
+    assert call(s, d, z, K.H2D, duty_on_ns=20000, duty_period_ns=10000) == K.EINVAL
+    assert call(s, d, z, K.H2D, duty_on_ns=5000, duty_period_ns=10000001) == K.EINVAL
+    assert call(s, d, z, K.H2D, duty_on_ns=5000, duty_period_ns=20000,
+                flags=K.F_PIPELINE) == K.EINVAL
+    assert call(s, d, z, K.H2D, duty_on_ns=5000, duty_period_ns=20000,
+                flags=K.F_DYNAMIC) == K.EINVAL
+    assert call(s, d, z, K.H2D, opts_size=24) == K.EINVAL          # unknown struct size
+    assert call(s, d, z + 4, K.H2D, opts_size=K.OPTS_V1_SIZE) == K.EALIGN   # v1 layout accepted
     wrap = np.array([2**64 - 4096], np.uint64)
     assert call(wrap, d[:1], z[:1], K.H2D) == K.EINVAL             # address range wraps
     dup = np.array([0x30000, 0x30800], np.uint64)
@@ -187,6 +201,8 @@ def test_pair_argument_errors(K):
     assert call(s, d, z, s2, d2, z, -2) == K.EINVAL                        # max_wgs below AUTO
     assert call(s, d, z, s2, d2, z, flags=K.F_PIPELINE) == K.EINVAL        # loop flags: not here
     assert call(s, d, z, s2, d2, z, flags=K.F_DESC_UPLOAD) == K.EINVAL
+    assert call(s, d, z, s2, d2, z, flags=K.F_STORE_SC1) == K.EINVAL       # sc1 is its default
+    assert call(s, d, z, s2 + 4, d2, z, flags=K.F_STORE_NT) == K.EALIGN    # nt accepted
     wrap = np.array([2**64 - 4096], np.uint64)
     assert call(s, d, z, wrap, d2[:1], z[:1]) == K.EINVAL                  # list b wraps
     # The overlap rule spans both lists (validate mode only).
@@ -205,7 +221,7 @@ def test_null_pointers_and_struct_size(K):
     u = ctypes.POINTER(ctypes.c_uint64)()
     assert K.lib.kvcopy_batch(u, u, u, 3, 0, 0, None) == K.EINVAL
     assert K.lib.kvcopy_batch(u, u, u, 0, 0, 0, None) == K.OK
-    o = K.Opts(ctypes.sizeof(K.Opts) - 8, 0, 0, 0, None, None)
+    o = K.Opts(ctypes.sizeof(K.Opts) - 4, 0, 0, 0, None, None)   # neither known size
     s = np.array([0], np.uint64)
     p = s.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64))
     assert K.lib.kvcopy_batch_ex(p, p, p, 1, 0, 0, None, ctypes.byref(o)) == K.EINVAL
