@@ -139,57 +139,174 @@ inline void put_rec(ChunkRec *r, uint64_t s, uint64_t d, uint32_t bytes)
     }
 }
 
+// The planning pass's state: validity accumulators, records written, and
+// the open range (the last range, not yet written, which the next
+// descriptor may still extend).
+struct PassState {
+    uint64_t bits = 0, bad = 0, total = 0, w = 0;
+    uint64_t cs = 0, cd = 0, cn = 0;
+};
+
+// Fast path of the planning pass for the common case: a run of descriptors
+// each of size 1..chunk, none continuing the one before it, none wrapping.
+// Four descriptors at a time, entered with no open range: AVX2 compares
+// check the sizes, the wrap and the merge rule for all four (and that the
+// descriptor after them is non-empty and does not continue the fourth, so
+// the fourth's range is closed too); the four records are transposed in
+// registers (two unpacks, a blend and three lane permutes) and written as
+// three 32-byte stores, where the scalar path makes twelve 8-byte ones.
+// Returns the index of the first descriptor it did not consume; the scalar
+// pass takes over from there with no open range.
+template <bool Stream>
+__attribute__((target("avx2"))) uint64_t fast_groups_avx2(const uint64_t *src, const uint64_t *dst,
+                                                          const uint64_t *size, uint64_t i,
+                                                          uint64_t n, bool merge, uint32_t chunk,
+                                                          ChunkRec *out, uint64_t cap, PassState &st)
+{
+    const __m256i flip = _mm256_set1_epi64x((long long)0x8000000000000000ull);
+    const __m256i lim = _mm256_xor_si256(_mm256_set1_epi64x((long long)chunk), flip);
+    const __m256i one = _mm256_set1_epi64x(1);
+    const __m256i zero = _mm256_setzero_si256();
+    __m256i vbits = zero, vtotal = zero;
+    // total + 4 * chunk per group must not overflow (else the scalar pass flags it)
+    const uint64_t total_max = ~0ull - 4ull * chunk * (n / 4 + 1);
+    uint64_t w = st.w;
+    if (st.total > total_max)
+        return i;
+    while (i + 5 <= n && w + 4 <= cap) {
+        const __m256i S = _mm256_loadu_si256(reinterpret_cast<const __m256i *>(src + i));
+        const __m256i D = _mm256_loadu_si256(reinterpret_cast<const __m256i *>(dst + i));
+        const __m256i Z = _mm256_loadu_si256(reinterpret_cast<const __m256i *>(size + i));
+        // every size in [1, chunk]: z - 1 < chunk, unsigned
+        const __m256i zok = _mm256_cmpgt_epi64(lim, _mm256_xor_si256(_mm256_sub_epi64(Z, one), flip));
+        const __m256i SE = _mm256_add_epi64(S, Z), DE = _mm256_add_epi64(D, Z);
+        // no wrap: s + z >= s and d + z >= d, unsigned
+        __m256i bad =
+            _mm256_or_si256(_mm256_cmpgt_epi64(_mm256_xor_si256(S, flip), _mm256_xor_si256(SE, flip)),
+                            _mm256_cmpgt_epi64(_mm256_xor_si256(D, flip), _mm256_xor_si256(DE, flip)));
+        // the descriptor after each of the four: non-empty (the fourth's
+        // successor; a zero size would hide which one follows) and, with
+        // merging, not continuing it in both arenas
+        const __m256i Zn = _mm256_loadu_si256(reinterpret_cast<const __m256i *>(size + i + 1));
+        bad = _mm256_or_si256(bad, _mm256_cmpeq_epi64(Zn, zero));
+        if (merge) {
+            const __m256i Sn = _mm256_loadu_si256(reinterpret_cast<const __m256i *>(src + i + 1));
+            const __m256i Dn = _mm256_loadu_si256(reinterpret_cast<const __m256i *>(dst + i + 1));
+            bad = _mm256_or_si256(bad, _mm256_and_si256(_mm256_cmpeq_epi64(SE, Sn),
+                                                        _mm256_cmpeq_epi64(DE, Dn)));
+        }
+        if (_mm256_movemask_epi8(zok) != -1 || !_mm256_testz_si256(bad, bad))
+            break;
+        vbits = _mm256_or_si256(vbits, _mm256_or_si256(_mm256_or_si256(S, D), Z));
+        vtotal = _mm256_add_epi64(vtotal, Z);
+        // records [s0 d0 z0] [s1 d1 z1] [s2 d2 z2] [s3 d3 z3] as 16-byte
+        // pairs [s0 d0][z0 s1][d1 z1] [s2 d2][z2 s3][d3 z3]
+        const __m256i y0 = _mm256_unpacklo_epi64(S, D);        // [s0 d0 | s2 d2]
+        const __m256i y1 = _mm256_blend_epi32(Z, S, 0xCC);     // [z0 s1 | z2 s3]
+        const __m256i y2 = _mm256_unpackhi_epi64(D, Z);        // [d1 z1 | d3 z3]
+        const __m256i r0 = _mm256_permute2x128_si256(y0, y1, 0x20);
+        const __m256i r1 = _mm256_permute2x128_si256(y2, y0, 0x30);
+        const __m256i r2 = _mm256_permute2x128_si256(y1, y2, 0x31);
+        __m256i *o = reinterpret_cast<__m256i *>(out + w);
+        if (Stream && (reinterpret_cast<uintptr_t>(o) & 31u) == 0) {
+            _mm256_stream_si256(o, r0);
+            _mm256_stream_si256(o + 1, r1);
+            _mm256_stream_si256(o + 2, r2);
+        } else {
+            _mm256_storeu_si256(o, r0);
+            _mm256_storeu_si256(o + 1, r1);
+            _mm256_storeu_si256(o + 2, r2);
+        }
+        w += 4;
+        i += 4;
+    }
+    alignas(32) uint64_t b[4], t[4];
+    _mm256_store_si256(reinterpret_cast<__m256i *>(b), vbits);
+    _mm256_store_si256(reinterpret_cast<__m256i *>(t), vtotal);
+    st.bits |= b[0] | b[1] | b[2] | b[3];
+    st.total += t[0] + t[1] + t[2] + t[3];
+    st.w = w;
+    return i;
+}
+
+bool have_avx2()
+{
+    static const bool yes = __builtin_cpu_supports("avx2");
+    return yes;
+}
+
 template <bool Stream>
 int build_checked_impl(const uint64_t *src, const uint64_t *dst, const uint64_t *size, uint64_t n,
                        bool merge, uint32_t chunk, ChunkRec *out, uint64_t cap, uint64_t *n_chunks)
 {
-    uint64_t bits = 0, bad = 0, total = 0, w = 0;
-    uint64_t cs = 0, cd = 0, cn = 0;   // the open range
+    PassState st;
     auto close = [&]() {
-        if (cn <= chunk) {   // the common case: one chunk per range
-            if (w < cap)
-                put_rec<Stream>(out + w, cs, cd, (uint32_t)cn);
-            ++w;
+        if (st.cn <= chunk) {   // the common case: one chunk per range
+            if (st.w < cap)
+                put_rec<Stream>(out + st.w, st.cs, st.cd, (uint32_t)st.cn);
+            ++st.w;
             return;
         }
         // Count arithmetically and write only what fits: an invalid list (a
         // size that wraps, say) is rejected after the pass, and must not cost
         // a loop over its chunks first.
-        const uint64_t k = cn / chunk + (cn % chunk != 0);
-        const uint64_t room = w < cap ? cap - w : 0;
+        const uint64_t k = st.cn / chunk + (st.cn % chunk != 0);
+        const uint64_t room = st.w < cap ? cap - st.w : 0;
         const uint64_t put = k < room ? k : room;
         for (uint64_t j = 0; j < put; ++j) {
-            const uint64_t off = j * chunk, left = cn - off;
-            put_rec<Stream>(out + w + j, cs + off, cd + off,
+            const uint64_t off = j * chunk, left = st.cn - off;
+            put_rec<Stream>(out + st.w + j, st.cs + off, st.cd + off,
                             (uint32_t)(left < chunk ? left : chunk));
         }
-        w += k;
+        st.w += k;
     };
-    for (uint64_t i = 0; i < n; ++i) {
+    const bool fast = have_avx2();
+    uint64_t retry = 0;   // after a group the fast path declined, go on scalar for a while
+    for (uint64_t i = 0; i < n;) {
+        if (fast && i >= retry) {
+            // Close the open range early when descriptor i (non-empty) does
+            // not continue it, so the fast path starts with no open range.
+            const uint64_t zi = size[i];
+            if (st.cn != 0 && zi != 0 &&
+                !(merge && st.cs + st.cn == src[i] && st.cd + st.cn == dst[i])) {
+                close();
+                st.cn = 0;
+            }
+            if (st.cn == 0) {
+                const uint64_t j = fast_groups_avx2<Stream>(src, dst, size, i, n, merge, chunk, out,
+                                                            cap, st);
+                if (j == i)
+                    retry = i + 4;
+                i = j;
+                if (i >= n)
+                    break;
+            }
+        }
         const uint64_t s = src[i], d = dst[i], z = size[i];
-        const uint64_t t = total + z;
-        bits |= s | d | z;
-        bad |= (uint64_t)(s + z < s) | (uint64_t)(d + z < d) | (uint64_t)(t < total);
-        total = t;
+        ++i;
+        const uint64_t t = st.total + z;
+        st.bits |= s | d | z;
+        st.bad |= (uint64_t)(s + z < s) | (uint64_t)(d + z < d) | (uint64_t)(t < st.total);
+        st.total = t;
         if (z == 0)
             continue;
-        if (merge && cn != 0 && cs + cn == s && cd + cn == d) {
-            cn += z;
+        if (merge && st.cn != 0 && st.cs + st.cn == s && st.cd + st.cn == d) {
+            st.cn += z;
             continue;
         }
-        if (cn != 0)
+        if (st.cn != 0)
             close();
-        cs = s;
-        cd = d;
-        cn = z;
+        st.cs = s;
+        st.cd = d;
+        st.cn = z;
     }
-    if (cn != 0)
+    if (st.cn != 0)
         close();
-    if (bits & 7u)
+    if (st.bits & 7u)
         return KVCOPY_EALIGN;
-    if (bad)
+    if (st.bad)
         return KVCOPY_EINVAL;
-    *n_chunks = w;
+    *n_chunks = st.w;
     return KVCOPY_OK;
 }
 

@@ -110,6 +110,73 @@ int main(int argc, char **argv)
             }
         }
     }
+    // Runs of block descriptors (the planner's vector fast path): mostly
+    // non-adjacent 4 KiB blocks, with rare zero sizes, chains of adjacent
+    // blocks, ranges longer than a chunk and misaligned entries, planned
+    // into outputs at every 8-byte offset within 32 bytes and with rooms
+    // that end mid-list, plain and streamed; the records must equal the
+    // step-by-step planner's.
+    for (int trial = 0; trial < trials; ++trial) {
+        const uint64_t n = 5 + rng() % 2000;
+        const uint32_t chunk = (rng() % 3 == 0) ? 4096 : 16384;
+        std::vector<uint64_t> s(n), d(n), z(n);
+        const int rare = 1 + (int)(rng() % 200);
+        for (uint64_t i = 0; i < n; ++i) {
+            z[i] = 4096;
+            const int r = (int)(rng() % 1000);
+            if (r < rare / 4)
+                z[i] = 0;
+            else if (r < rare / 2)
+                z[i] = 8 * (1 + rng() % 8000);
+            if (i > 0 && r >= rare / 2 && r < rare) {
+                s[i] = s[i - 1] + z[i - 1];
+                d[i] = d[i - 1] + z[i - 1];
+            } else {
+                s[i] = (1ull << 36) + (rng() % (1u << 20)) * 4096 + (r == 999 ? 12 : 0);
+                d[i] = (1ull << 40) + (rng() % (1u << 20)) * 4096;
+            }
+        }
+        for (int merge = 0; merge < 2; ++merge) {
+            std::vector<uint64_t> ms(n + 1), md(n + 1), mz(n + 1), mb(n + 2);
+            uint64_t m = 0, total = 0;
+            const int mrc = merge_ranges(s.data(), d.data(), z.data(), n, merge, ms.data(), md.data(),
+                                         mz.data(), &m, &total);
+            const uint64_t c = chunk_prefix(mz.data(), m, chunk, mb.data());
+            std::vector<ChunkRec> ref(c + 1);
+            emit_chunks(ms.data(), md.data(), mz.data(), mb.data(), m, chunk, ref.data());
+            for (int shift = 0; shift < 4; ++shift)
+            for (uint64_t cap : {c, c / 3, c + 5})
+            for (bool streamed : {false, true}) {
+                std::vector<unsigned char> raw((cap + 8) * sizeof(ChunkRec) + 64, 0xA5);
+                uintptr_t base = (reinterpret_cast<uintptr_t>(raw.data()) + 31) & ~(uintptr_t)31;
+                ChunkRec *part = reinterpret_cast<ChunkRec *>(base + 8 * shift);
+                uint64_t need = ~0ull;
+                const int rc = build_checked(s.data(), d.data(), z.data(), n, merge, chunk, part, cap,
+                                             &need, streamed);
+                finish_records();
+                if (rc != mrc) {
+                    printf("fast path: trial %d: rc %d, merge_ranges %d\n", trial, rc, mrc);
+                    return 1;
+                }
+                if (rc != KVCOPY_OK)
+                    continue;
+                const uint64_t wrote = cap < c ? cap : c;
+                if (need != c || (wrote && memcmp(ref.data(), part, wrote * sizeof(ChunkRec)) != 0)) {
+                    printf("fast path: trial %d merge %d shift %d cap %llu streamed %d: %llu records,"
+                           " want %llu\n", trial, merge, shift, (unsigned long long)cap, (int)streamed,
+                           (unsigned long long)need, (unsigned long long)c);
+                    return 1;
+                }
+                const unsigned char *tail = reinterpret_cast<const unsigned char *>(part + wrote);
+                for (size_t b = 0; b < 8 * sizeof(ChunkRec); ++b)
+                    if (tail[b] != 0xA5) {
+                        printf("fast path: trial %d wrote past its room\n", trial);
+                        return 1;
+                    }
+            }
+            ++cases;
+        }
+    }
     // The default copy-loop choice: pipelined only for D2D grids of at most
     // 256 workgroups in which every wavefront has at least two chunks.
     struct { int dir; uint32_t grid; uint64_t chunks; bool want; } pol[] = {
