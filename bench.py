@@ -174,8 +174,8 @@ class Ctx:
         if self.args.desc_upload:
             kw["flags"] = kw.get("flags", 0) | self.K.F_DESC_UPLOAD
         marks = None
-        # profiler runs (--no-events) make no event calls at all: rocprofv3 7.2
-        # aborted in its own tool on them, so there the streams run free
+        # profiler runs (--no-events) make no event calls at all (rocprofv3 7.2
+        # aborted in its own tool on them): there the host joins the steps
         if joined and len(streams) > 1 and not self.args.no_events:
             marks = [self.hiprt.Event(timing=False) for _ in streams]
         for i in range(k):
@@ -192,6 +192,11 @@ class Ctx:
                     for jj, m in enumerate(marks):
                         if jj != j:
                             self.hiprt.stream_wait(st, m)
+            elif joined and len(streams) > 1:
+                # profiler runs (no event calls): the host waits for both
+                # streams, so the next step's kernels again start together
+                for st in streams:
+                    self.hiprt.stream_sync(st)
 
     def timed(self, r, batch_ids, streams, k, w, max_wgs, with_events=True, **kw):
         """Seconds per step over k timed steps (after w warm-up steps), and the
@@ -1519,6 +1524,7 @@ def parse_mode(mode):
     transfer), "direct" (one hipMemcpyAsync per fragment), an integer cap G
     (both directions on two streams at G workgroups each; 0 = full grid),
     "G/sc1" or "G/nt" (the same with the store form forced on both kernels),
+    "tail" (two streams with KVCOPY_F_TAIL_BOUNDED; "tail/nt" with nt stores),
     "duty:ON:PERIOD:G" (the same with time-sliced issue, ON and PERIOD in
     microseconds), "pair:G" and "pair:G/nt" (both lists in one launch),
     "pipe:G" (the pipelined loop forced), "job:N" (paced pieces of N
@@ -1538,6 +1544,9 @@ def parse_mode(mode):
     if m.isdigit():
         return "streams", int(m), opt
     head, _, rest = m.partition(":")
+    if head == "tail":
+        opt["tail"] = True
+        return "streams", 0, opt
     if head == "duty":
         on, per, cap = rest.split(":")
         opt["duty"] = (int(round(float(on) * 1000)), int(round(float(per) * 1000)))
@@ -1602,6 +1611,8 @@ def bench_interference(c: Ctx, args):
         copy_kw = {}
         if opt.get("store"):
             copy_kw["flags"] = K.F_STORE_SC1 if opt["store"] == "sc1" else K.F_STORE_NT
+        if opt.get("tail"):
+            copy_kw["flags"] = copy_kw.get("flags", 0) | K.F_TAIL_BOUNDED
         if opt.get("duty"):
             copy_kw["duty_on_ns"], copy_kw["duty_period_ns"] = opt["duty"]
 
@@ -1686,8 +1697,8 @@ def bench_interference(c: Ctx, args):
 
     modes = ["none", "direct", 1, 8, 32, 128, 0, "8/sc1", "128/sc1", "8/nt", "h2d:8", "d2h:8",
              "h2d:128", "d2h:128", "pipe:4", "job:2048", "cumask:8", "pair:8", "pair:16",
-             "pair:64", "pair:8/nt", "pair:16/nt", "duty:2:10:8", "duty:2:20:8", "duty:5:20:32",
-             "duty:2:10:128"]
+             "pair:64", "pair:8/nt", "pair:16/nt", "duty:2:20:8", "duty:2:20:4", "duty:2:20:4/sc1",
+             "duty:2:40:4/sc1", "duty:2:10:128", "tail"]
     if args.modes:     # a subset or other modes; "none" (the baseline) always runs
         pick = [m for m in args.modes.split(",") if m]
         try:

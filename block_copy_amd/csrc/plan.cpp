@@ -335,11 +335,16 @@ uint64_t build_worklist(const uint64_t *src, const uint64_t *dst, const uint64_t
 
 // Destination order for D2D gathers of random blocks: with the worklist in
 // list order, the chunks that the GPU has in flight at any moment write all
-// over HBM; grouped by 4 MiB destination region, the workgroups that the
-// dispatcher starts together write into a narrow band of rows.  A stable
-// counting sort: one pass counts the records per region, a prefix sum places
-// the regions, and a second pass moves every record to its slot.
-void order_by_dst(const ChunkRec *in, uint64_t n, ChunkRec *out, bool stream)
+// over HBM; grouped by destination region, the workgroups that the
+// dispatcher starts together write into a narrow band of rows.  Measured on
+// MI355X (65,536 random 4 KiB blocks between two 1 GiB pools, calls over 8
+// distinct batches): regions of 1, 4, 16 and 64 MiB and a full sort by
+// destination all gave 100.8-103 us against 107 us in list order, so the
+// regions are 64 MiB, 16 of them: a stable counting sort with 16 output
+// streams.  The records are written with ordinary (cached) stores:
+// non-temporal stores scattered over the streams each flush a partly filled
+// write-combining buffer, which measured 20 times slower.
+void order_by_dst(const ChunkRec *in, uint64_t n, ChunkRec *out)
 {
     uint64_t at[kDstBuckets] = {};
     for (uint64_t i = 0; i < n; ++i)
@@ -352,11 +357,7 @@ void order_by_dst(const ChunkRec *in, uint64_t n, ChunkRec *out, bool stream)
     }
     for (uint64_t i = 0; i < n; ++i) {
         const ChunkRec &r = in[i];
-        ChunkRec *o = out + at[(r.dst >> kDstRegionShift) & (kDstBuckets - 1)]++;
-        if (stream)
-            put_rec<true>(o, r.src, r.dst, r.bytes);
-        else
-            put_rec<false>(o, r.src, r.dst, r.bytes);
+        out[at[(r.dst >> kDstRegionShift) & (kDstBuckets - 1)]++] = r;
     }
 }
 

@@ -180,6 +180,14 @@ int resolve_auto(const Staging *st, int dir)
 // occasional windows below 50 GB/s, and 48 gave 97.9.
 constexpr int kPairAutoWgs = 64;
 
+// KVCOPY_F_TAIL_BOUNDED: measured on MI355X (a bf16 GEMV decode loop beside
+// H2D + D2H bursts of 16,384 x 4 KiB every 50 ms): 4 workgroups per stream
+// issuing in 2 us of every 20 us with sc1 stores held the decode's p99 to
+// +4.9% and its worst step to 0.44 ms (0.41 ms alone); a 40 us period gave
+// +2.8% and 0.41 ms at half the transfer rate, 8 workgroups +6.1% / 0.43 ms.
+constexpr uint32_t kTailDutyOnNs = 2000, kTailDutyPeriodNs = 20000;
+constexpr int kTailMaxWgs = 4;
+
 // The per-call options after parsing.
 struct CallOpts {
     uint32_t chunk = KVCOPY_CHUNK_DEFAULT;
@@ -283,7 +291,7 @@ int run_locked(Staging *st, int device, const uint64_t *src, const uint64_t *dst
         if ((rc = st->ring.reserve(need, &off)) != KVCOPY_OK)
             return rc;
         host = reinterpret_cast<ChunkRec *>(st->host + off);
-        order_by_dst(st->order_tmp.data(), n_chunks, host, true);
+        order_by_dst(st->order_tmp.data(), n_chunks, host);
     } else {
         for (int pass = 0; pass < 2; ++pass) {
             const uint64_t room = hint ? hint : 1;
@@ -340,8 +348,9 @@ int run_locked(Staging *st, int device, const uint64_t *src, const uint64_t *dst
     hipEvent_t start = timed ? o.ev_begin : nullptr, stop = timed ? o.ev_end : done;
     if (dynamic) {
         uint32_t *claim = st->claims + off / kAlign * 2;
-        e = launch_copy_dynamic(recs, (uint32_t)n_chunks, grid, dir, claim,
-                                claim_grain(n_chunks, grid), stream, start, stop);
+        const uint32_t g = grid < kDynMaxGrid ? grid : kDynMaxGrid;
+        e = launch_copy_dynamic(recs, (uint32_t)n_chunks, g, dir, claim, claim_grain(n_chunks, g),
+                                stream, start, stop);
     } else {
         // A forced store form or pacing selects the per-chunk loop.
         const bool per_chunk = (flags & (KVCOPY_F_PER_CHUNK | KVCOPY_F_STORE_SC1 |
@@ -499,7 +508,8 @@ extern "C" int kvcopy_batch_ex(const uint64_t *src_addrs, const uint64_t *dst_ad
         }
         const uint32_t known = KVCOPY_F_VALIDATE | KVCOPY_F_NO_COALESCE | KVCOPY_F_DESC_UPLOAD |
                                KVCOPY_F_PIPELINE | KVCOPY_F_PER_CHUNK | KVCOPY_F_DYNAMIC |
-                               KVCOPY_F_STORE_SC1 | KVCOPY_F_STORE_NT | KVCOPY_F_DST_ORDER;
+                               KVCOPY_F_STORE_SC1 | KVCOPY_F_STORE_NT | KVCOPY_F_DST_ORDER |
+                               KVCOPY_F_TAIL_BOUNDED;
         if (opts->flags & ~known)
             return KVCOPY_EINVAL;
         const uint32_t loops = opts->flags & (KVCOPY_F_PIPELINE | KVCOPY_F_PER_CHUNK | KVCOPY_F_DYNAMIC);
@@ -520,6 +530,18 @@ extern "C" int kvcopy_batch_ex(const uint64_t *src_addrs, const uint64_t *dst_ad
         o.flags = opts->flags;
         o.ev_begin = opts->kernel_begin;
         o.ev_end = opts->kernel_end;
+        if (o.flags & KVCOPY_F_TAIL_BOUNDED) {
+            if (o.flags & (KVCOPY_F_PIPELINE | KVCOPY_F_DYNAMIC))
+                return KVCOPY_EINVAL;
+            if (!(o.flags & KVCOPY_F_STORE_NT))
+                o.flags |= KVCOPY_F_STORE_SC1;
+            if (o.duty_period_ns == 0) {
+                o.duty_on_ns = kTailDutyOnNs;
+                o.duty_period_ns = kTailDutyPeriodNs;
+            }
+            if (max_wgs == KVCOPY_WGS_ALL || max_wgs == KVCOPY_WGS_AUTO || max_wgs > kTailMaxWgs)
+                max_wgs = kTailMaxWgs;
+        }
     }
     if (dir != KVCOPY_H2D && dir != KVCOPY_D2H && dir != KVCOPY_D2D)
         return KVCOPY_EINVAL;

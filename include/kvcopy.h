@@ -115,8 +115,10 @@ enum {
  * (about a quarter of its fair share, at most 64) with an atomic add on a
  * counter in device memory, one batch ahead, so faster wavefronts take more
  * chunks.  The library owns the counters (allocated and zeroed on first use,
- * reset by each kernel's last wavefront).  Exclusive with the two flags
- * above. */
+ * reset by each kernel's last wavefront).  Every claim hits one counter, so
+ * this loop runs at most 128 workgroups whatever max_wgs allows (measured
+ * on MI355X: 65,536 chunks at the full grid took 2.2 ms, the claims
+ * serialising).  Exclusive with the two flags above. */
 #define KVCOPY_F_DYNAMIC 0x40u
 /* Store form of the per-chunk loop.  Two forms give the same bytes: the
  * nontemporal hint alone ("nt"), and nt with the sc1 scope bit ("sc1", a
@@ -130,13 +132,28 @@ enum {
  * KVCOPY_F_STORE_NT (its default is sc1). */
 #define KVCOPY_F_STORE_SC1 0x80u
 #define KVCOPY_F_STORE_NT 0x100u
-/* Destination order: the worklist handed to the kernel is ordered by 4 MiB
- * destination region ((dst >> 22) mod 256; list order within a region)
+/* Destination order: the worklist handed to the kernel is ordered by 64 MiB
+ * destination region ((dst >> 26) mod 16; list order within a region)
  * instead of list order, so that the chunks in flight at any moment write a
- * narrow band of memory.  It costs one more pass over the records on the
+ * narrow band of memory.  It costs two more passes over the records on the
  * host.  Results do not depend on it.  Meant for D2D gathers of many random
- * blocks. */
+ * blocks: measured on MI355X, calls of 65,536 random 4 KiB blocks between
+ * two 1 GiB pools run 6% faster on the GPU (100.8 against 107 us). */
 #define KVCOPY_F_DST_ORDER 0x200u
+/* Tail-bounded policy ([PF] "Proposed direction": a tail-bounded policy
+ * beside the throughput-oriented one, for transfers that share the GPU with
+ * latency-sensitive kernels).  A preset of the options above: the sc1 store
+ * form (unless KVCOPY_F_STORE_NT is given), a 2 us issue window in every
+ * 20 us (unless duty_on_ns / duty_period_ns are given), and at most 4
+ * workgroups per call (max_wgs above 4, KVCOPY_WGS_ALL and KVCOPY_WGS_AUTO
+ * become 4).  It moves about 3.3 GB/s of 4 KiB blocks per call in flight.
+ * Measured on MI355X with a batch-1 decode loop of 36 bf16 GEMVs (0.38 ms
+ * per step) beside an H2D + D2H burst of 16,384 x 4 KiB each way every
+ * 50 ms on two streams: decode step p99 +4.9% and worst step 0.44 ms
+ * (0.41 ms with no transfer) at 2.56 GiB/s sustained, where the default
+ * (128 workgroups per stream) gives p99 +2% but a worst step near 2 ms.
+ * With KVCOPY_F_PIPELINE or KVCOPY_F_DYNAMIC: KVCOPY_EINVAL. */
+#define KVCOPY_F_TAIL_BOUNDED 0x400u
 
 /*
  * kvcopy_coalesce -- merge list-consecutive adjacent ranges.

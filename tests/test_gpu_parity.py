@@ -560,3 +560,27 @@ def test_destination_order(K, max_wgs):
             _run(res, [0], max_wgs, flags=K.F_DST_ORDER, chunk_bytes=chunk)
             _check(res, [0], f"dst order {wl.name} max_wgs={max_wgs}", sentinel)
         res.free()
+
+
+def test_tail_bounded_preset(K):
+    """KVCOPY_F_TAIL_BOUNDED (sc1 stores, time-sliced issue, at most 4
+    workgroups): the KV burst on two streams, an irregular D2H batch, and
+    the preset with the nt store form and with its own duty cycle."""
+    from block_copy_amd.harness import Resident
+    kv = Resident(W.kv_blocks(seed=14, directions="both", n=2048, pool_blocks=8192))
+    irr = Resident(W.irregular(seed=15, n=400, dir_=W.D2H, src_where="device", dst_where="host",
+                               misalign=True, zero_frac=0.05))
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    cases = [dict(flags=K.F_TAIL_BOUNDED), dict(flags=K.F_TAIL_BOUNDED | K.F_STORE_NT),
+             dict(flags=K.F_TAIL_BOUNDED, duty_on_ns=1000, duty_period_ns=5000)]
+    for sentinel in (W.SENTINEL_A, W.SENTINEL_B):
+        for kw in cases:
+            _say("tail-bounded", kw, "sentinel", hex(sentinel))
+            kv.fill(sentinel)
+            _run(kv, [0, 1], K.WGS_AUTO, streams=[s1, s2], **kw)
+            _check(kv, [0, 1], f"tail-bounded {kw}", sentinel)
+            irr.fill(sentinel)
+            _run(irr, [0], 0, **kw)
+            _check(irr, [0], f"tail-bounded irregular {kw}", sentinel)
+    kv.free()
+    irr.free()

@@ -159,7 +159,11 @@ def test_batch_argument_errors(K):
     assert call(s, d, z, K.H2D, -2) == K.EINVAL
     assert call(s, d, z, K.H2D, chunk_bytes=24) == K.EINVAL        # chunk not a multiple of 16
     assert call(s, d, z, K.H2D, chunk_bytes=(1 << 20) + 16) == K.EINVAL
-    assert call(s, d, z, K.H2D, flags=0x400) == K.EINVAL          # unknown flag
+    assert call(s, d, z, K.H2D, flags=0x800) == K.EINVAL          # unknown flag
+    assert call(s, d, z, K.H2D, flags=K.F_TAIL_BOUNDED | K.F_PIPELINE) == K.EINVAL
+    assert call(s, d, z, K.H2D, flags=K.F_TAIL_BOUNDED | K.F_DYNAMIC) == K.EINVAL
+    assert call(s, d, z, K.H2D, -5, flags=K.F_TAIL_BOUNDED) == K.EINVAL
+    assert call(s, d, z + 4, K.H2D, flags=K.F_TAIL_BOUNDED) == K.EALIGN   # preset accepted
     assert call(s, d, z, K.H2D, flags=0x4) == K.EINVAL            # a retired flag value
     assert call(s, d, z, K.H2D, flags=K.F_PIPELINE | K.F_PER_CHUNK) == K.EINVAL  # two loops forced
     assert call(s, d, z, K.H2D, flags=K.F_DYNAMIC | K.F_PIPELINE) == K.EINVAL
