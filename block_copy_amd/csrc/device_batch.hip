@@ -14,6 +14,9 @@
 //      binary search over the prefix and walking forward from there.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+#include <vector>
+
 #include "kvcopy.h"
 #include "kvcopy_internal.h"
 
@@ -45,7 +48,7 @@ __device__ __forceinline__ uint64_t wave_incl_scan(uint64_t v, uint32_t lane)
 __global__ __launch_bounds__(kPlanThreads) void kvcopy_device_plan_kernel(
     const uint64_t *__restrict__ src, const uint64_t *__restrict__ dst,
     const uint64_t *__restrict__ size, const uint64_t *__restrict__ d_n, uint64_t max_n,
-    uint32_t chunk, DevWorkspace *__restrict__ ws)
+    uint32_t chunk, DevWorkspace *__restrict__ ws, uint64_t *__restrict__ status_out)
 {
     __shared__ uint64_t wave_tot[kPlanThreads / 64];
     __shared__ uint64_t carry_s;
@@ -93,6 +96,8 @@ __global__ __launch_bounds__(kPlanThreads) void kvcopy_device_plan_kernel(
             status = KVCOPY_DEVICE_TOO_MANY_CHUNKS;
         ws->status = status;
         ws->total = status ? 0 : total;
+        if (status_out)
+            *status_out = status;
     }
 }
 
@@ -143,12 +148,12 @@ uint64_t device_workspace_bytes(uint64_t max_n)
 
 hipError_t launch_device_batch(const uint64_t *src, const uint64_t *dst, const uint64_t *size,
                                const uint64_t *d_n, uint64_t max_n, uint32_t chunk, uint32_t grid,
-                               void *workspace, hipStream_t stream)
+                               void *workspace, uint64_t *status_out, hipStream_t stream)
 {
     DevWorkspace *ws = reinterpret_cast<DevWorkspace *>(workspace);
     {
         void *args[] = {(void *)&src, (void *)&dst, (void *)&size, (void *)&d_n, (void *)&max_n,
-                        (void *)&chunk, (void *)&ws};
+                        (void *)&chunk, (void *)&ws, (void *)&status_out};
         const hipError_t e =
             hipLaunchKernel(reinterpret_cast<const void *>(&kvcopy_device_plan_kernel), dim3(1),
                             dim3(kPlanThreads), args, 0, stream);
@@ -159,6 +164,52 @@ hipError_t launch_device_batch(const uint64_t *src, const uint64_t *dst, const u
     void *args[] = {(void *)&src, (void *)&dst, (void *)&size, (void *)&chunk, (void *)&cws};
     return hipLaunchKernel(reinterpret_cast<const void *>(&kvcopy_device_copy_kernel), dim3(grid),
                            dim3(kThreadsPerWG), args, 0, stream);
+}
+
+// ---- the library's own workspace (kvcopy_batch_device_noalloc) -------------
+//
+// A workspace for KVCOPY_NOALLOC_MAX_N descriptors in a file-scope device
+// array, so that a call needs no allocation at all.  Each GPU the library
+// runs on holds its own copy until the process ends.  In host code `scratch`
+// names a host-side stand-in, not device memory: its device address comes
+// from hipGetSymbolAddress, once per device (with that device current), and
+// only that address is ever handed to a kernel.  Every call on a device uses
+// the same array; the plan kernel rewrites every word the copy kernel reads,
+// so nothing in it needs clearing between calls.
+constexpr uint64_t kNoallocBytes = (32 + 8 * (KVCOPY_NOALLOC_MAX_N + 1) + 255) / 256 * 256;
+static_assert(offsetof(DevWorkspace, begin) == 32, "workspace header layout");
+static __device__ __align__(256) uint8_t scratch[kNoallocBytes];
+
+namespace {
+
+std::mutex g_scratch_mu;
+std::vector<void *> g_scratch_ptr;   // device ordinal -> device address of `scratch`
+
+}  // namespace
+
+uint64_t noalloc_workspace_bytes()
+{
+    return kNoallocBytes;
+}
+
+hipError_t noalloc_workspace(int device, void **out)
+{
+    std::lock_guard<std::mutex> g(g_scratch_mu);
+    if ((size_t)device < g_scratch_ptr.size() && g_scratch_ptr[device] != nullptr) {
+        *out = g_scratch_ptr[device];
+        return hipSuccess;
+    }
+    void *ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess)
+        return e;
+    if (ptr == nullptr || (reinterpret_cast<uintptr_t>(ptr) & 255u))
+        return hipErrorInvalidSymbol;
+    if ((size_t)device >= g_scratch_ptr.size())
+        g_scratch_ptr.resize((size_t)device + 1, nullptr);
+    g_scratch_ptr[device] = ptr;
+    *out = ptr;
+    return hipSuccess;
 }
 
 }  // namespace kvc

@@ -222,9 +222,16 @@ inline uint32_t pair_split(uint64_t ca, uint64_t cb, uint32_t nw)
 uint64_t device_workspace_bytes(uint64_t max_n);
 
 // Enqueues the plan kernel (one workgroup) and the copy kernel (`grid`
-// workgroups) on `stream`.
+// workgroups) on `stream`.  status_out (device memory, may be null) also
+// receives the workspace's status word.
 hipError_t launch_device_batch(const uint64_t *src, const uint64_t *dst, const uint64_t *size,
                                const uint64_t *d_n, uint64_t max_n, uint32_t chunk, uint32_t grid,
-                               void *workspace, hipStream_t stream);
+                               void *workspace, uint64_t *status_out, hipStream_t stream);
+
+// kvcopy_batch_device_noalloc: the device address of the library's own
+// workspace array on `device` (which must be the current device), looked up
+// on the first call per device.
+hipError_t noalloc_workspace(int device, void **out);
+uint64_t noalloc_workspace_bytes();
 
 }  // namespace kvc

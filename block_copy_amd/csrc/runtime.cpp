@@ -660,23 +660,25 @@ extern "C" uint64_t kvcopy_device_workspace_bytes(uint64_t max_n)
     return device_workspace_bytes(max_n);
 }
 
-extern "C" int kvcopy_batch_device(const uint64_t *d_src, const uint64_t *d_dst,
-                                   const uint64_t *d_sizes, const uint64_t *d_n, uint64_t max_n,
-                                   int dir, int max_wgs, uint32_t chunk_bytes, void *workspace,
-                                   hipStream_t stream)
+namespace {
+
+// Argument checks and grid of kvcopy_batch_device and its no-allocation
+// variant (KVCOPY_OK, or the error; nothing enqueued on error).
+int device_call_args(const uint64_t *d_src, const uint64_t *d_dst, const uint64_t *d_sizes,
+                     const uint64_t *d_n, uint64_t max_n, int dir, int max_wgs,
+                     uint32_t *chunk_bytes, uint32_t *grid)
 {
     if (dir != KVCOPY_H2D && dir != KVCOPY_D2H && dir != KVCOPY_D2D)
         return KVCOPY_EINVAL;
     if (max_wgs < KVCOPY_WGS_AUTO || max_n > KVCOPY_MAX_DESCS)
         return KVCOPY_EINVAL;
-    if (chunk_bytes == 0)
-        chunk_bytes = KVCOPY_CHUNK_DEFAULT;
-    if ((chunk_bytes & 15u) || chunk_bytes > KVCOPY_CHUNK_MAX)
+    if (*chunk_bytes == 0)
+        *chunk_bytes = KVCOPY_CHUNK_DEFAULT;
+    if ((*chunk_bytes & 15u) || *chunk_bytes > KVCOPY_CHUNK_MAX)
         return KVCOPY_EINVAL;
     if (max_n == 0)
         return KVCOPY_OK;
-    if (!d_src || !d_dst || !d_sizes || !d_n || !workspace ||
-        (reinterpret_cast<uintptr_t>(workspace) & 255u))
+    if (!d_src || !d_dst || !d_sizes || !d_n)
         return KVCOPY_EINVAL;
     if (max_wgs == KVCOPY_WGS_AUTO) {
         int device = 0;
@@ -687,9 +689,51 @@ extern "C" int kvcopy_batch_device(const uint64_t *d_src, const uint64_t *d_dst,
         std::lock_guard<std::mutex> g(st->mu);
         max_wgs = resolve_auto(st, dir);
     }
-    const uint32_t grid = max_wgs == 0 ? 1024u : (uint32_t)max_wgs < kMaxGrid ? (uint32_t)max_wgs : kMaxGrid;
-    const hipError_t e =
-        launch_device_batch(d_src, d_dst, d_sizes, d_n, max_n, chunk_bytes, grid, workspace, stream);
+    *grid = max_wgs == 0 ? 1024u : (uint32_t)max_wgs < kMaxGrid ? (uint32_t)max_wgs : kMaxGrid;
+    return KVCOPY_OK;
+}
+
+}  // namespace
+
+extern "C" int kvcopy_batch_device(const uint64_t *d_src, const uint64_t *d_dst,
+                                   const uint64_t *d_sizes, const uint64_t *d_n, uint64_t max_n,
+                                   int dir, int max_wgs, uint32_t chunk_bytes, void *workspace,
+                                   hipStream_t stream)
+{
+    uint32_t grid = 0;
+    int rc = device_call_args(d_src, d_dst, d_sizes, d_n, max_n, dir, max_wgs, &chunk_bytes, &grid);
+    if (rc != KVCOPY_OK || max_n == 0)
+        return rc;
+    if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u))
+        return KVCOPY_EINVAL;
+    const hipError_t e = launch_device_batch(d_src, d_dst, d_sizes, d_n, max_n, chunk_bytes, grid,
+                                             workspace, nullptr, stream);
+    return e == hipSuccess ? KVCOPY_OK : hip_fail(e);
+}
+
+extern "C" int kvcopy_batch_device_noalloc(const uint64_t *d_src, const uint64_t *d_dst,
+                                           const uint64_t *d_sizes, const uint64_t *d_n,
+                                           uint64_t max_n, int dir, int max_wgs,
+                                           uint32_t chunk_bytes, uint64_t *d_status,
+                                           hipStream_t stream)
+{
+    if (max_n > KVCOPY_NOALLOC_MAX_N)
+        return KVCOPY_EINVAL;
+    uint32_t grid = 0;
+    int rc = device_call_args(d_src, d_dst, d_sizes, d_n, max_n, dir, max_wgs, &chunk_bytes, &grid);
+    if (rc != KVCOPY_OK || max_n == 0)
+        return rc;
+    int device = 0;
+    hipError_t e = hipGetDevice(&device);
+    if (e != hipSuccess)
+        return hip_fail(e);
+    void *ws = nullptr;
+    if ((e = noalloc_workspace(device, &ws)) != hipSuccess)
+        return hip_fail(e);
+    if (device_workspace_bytes(max_n) > noalloc_workspace_bytes())
+        return KVCOPY_EINVAL;   // cannot happen for max_n <= KVCOPY_NOALLOC_MAX_N
+    e = launch_device_batch(d_src, d_dst, d_sizes, d_n, max_n, chunk_bytes, grid, ws, d_status,
+                            stream);
     return e == hipSuccess ? KVCOPY_OK : hip_fail(e);
 }
 

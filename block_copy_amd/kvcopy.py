@@ -36,8 +36,9 @@ EXPORTS = ("kvcopy_coalesce", "kvcopy_plan", "kvcopy_plan_free", "kvcopy_batch",
            "kvcopy_host_alloc_mapped", "kvcopy_host_free", "kvcopy_job_create",
            "kvcopy_job_poll", "kvcopy_job_wait", "kvcopy_job_destroy",
            "kvcopy_device_workspace_bytes", "kvcopy_batch_device", "kvcopy_autotune",
-           "kvcopy_batch_pair")
+           "kvcopy_batch_pair", "kvcopy_batch_device_noalloc")
 DEVICE_BAD_ALIGN, DEVICE_TOO_MANY_CHUNKS = 1, 2
+NOALLOC_MAX_N = 131072
 
 
 class KvcopyError(RuntimeError):
@@ -117,6 +118,11 @@ def _load():
                                         ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int,
                                         ctypes.c_int, ctypes.c_uint32, ctypes.c_void_p,
                                         ctypes.c_void_p]
+    lib.kvcopy_batch_device_noalloc.restype = ctypes.c_int
+    lib.kvcopy_batch_device_noalloc.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                                ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int,
+                                                ctypes.c_int, ctypes.c_uint32, ctypes.c_void_p,
+                                                ctypes.c_void_p]
     return lib
 
 
@@ -345,6 +351,21 @@ def kvcopy_batch_device(d_src: int, d_dst: int, d_sizes: int, d_n: int, max_n: i
                                  int(max_wgs), int(chunk_bytes), p(workspace), st)
     if check and rc != OK:
         raise KvcopyError(rc, "kvcopy_batch_device")
+    return rc
+
+
+def kvcopy_batch_device_noalloc(d_src: int, d_dst: int, d_sizes: int, d_n: int, max_n: int,
+                                dir: int, max_wgs: int, d_status: int = 0, stream=None,
+                                chunk_bytes: int = 0, check: bool = True) -> int:
+    """kvcopy_batch_device with the library's own workspace (see
+    include/kvcopy.h): no allocation; max_n <= NOALLOC_MAX_N; d_status is
+    an optional device address that receives the status word."""
+    st = ctypes.c_void_p(int(stream) if stream else 0)
+    p = lambda x: ctypes.c_void_p(int(x) if x else 0)  # noqa: E731
+    rc = lib.kvcopy_batch_device_noalloc(p(d_src), p(d_dst), p(d_sizes), p(d_n), int(max_n),
+                                         int(dir), int(max_wgs), int(chunk_bytes), p(d_status), st)
+    if check and rc != OK:
+        raise KvcopyError(rc, "kvcopy_batch_device_noalloc")
     return rc
 
 

@@ -461,6 +461,39 @@ int kvcopy_batch_device(const uint64_t *d_src, const uint64_t *d_dst, const uint
                         const uint64_t *d_n, uint64_t max_n, int dir, int max_wgs,
                         uint32_t chunk_bytes, void *workspace, hipStream_t stream);
 
+/*
+ * kvcopy_batch_device_noalloc -- kvcopy_batch_device with the library's own
+ * workspace instead of a caller-allocated one.
+ *
+ * For callers that cannot allocate memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  The call allocates
+ * nothing (no hipMalloc, hipFree or allocating library routine): the
+ * workspace is a file-scope device array of the library, of
+ * kvcopy_device_workspace_bytes(KVCOPY_NOALLOC_MAX_N) bytes (1 MiB + 256 B),
+ * which each GPU that the library runs on holds until the process ends.
+ * Its device address is looked up on the first call on each device.
+ *
+ * Arguments and behaviour as for kvcopy_batch_device, except:
+ *   max_n:    at most KVCOPY_NOALLOC_MAX_N (else KVCOPY_EINVAL, nothing
+ *             enqueued).
+ *   d_status: device uint64 (may be NULL) that receives the status word
+ *             (0, KVCOPY_DEVICE_BAD_ALIGN or KVCOPY_DEVICE_TOO_MANY_CHUNKS)
+ *             once the plan kernel has run; the workspace itself is not
+ *             visible to the caller.
+ * Every call on one GPU shares the one array: calls that may run at the
+ * same time on one GPU (unordered streams) race and must not be made; calls
+ * ordered on one stream are safe.  The array keeps the last call's
+ * contents; each call rewrites everything it reads, so nothing needs
+ * clearing.
+ * errors: as kvcopy_batch_device; KVCOPY_EHIP also if the array's address
+ *   cannot be looked up.
+ */
+#define KVCOPY_NOALLOC_MAX_N 131072u
+int kvcopy_batch_device_noalloc(const uint64_t *d_src, const uint64_t *d_dst,
+                                const uint64_t *d_sizes, const uint64_t *d_n, uint64_t max_n,
+                                int dir, int max_wgs, uint32_t chunk_bytes, uint64_t *d_status,
+                                hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif
