@@ -173,6 +173,9 @@ class Ctx:
         when the last one does."""
         if self.args.desc_upload:
             kw["flags"] = kw.get("flags", 0) | self.K.F_DESC_UPLOAD
+        if self.args.store != "auto":
+            kw["flags"] = kw.get("flags", 0) | (self.K.F_STORE_SC1 if self.args.store == "sc1"
+                                                else self.K.F_STORE_NT)
         marks = None
         # profiler runs (--no-events) make no event calls at all (rocprofv3 7.2
         # aborted in its own tool on them): there the host joins the steps
@@ -466,7 +469,7 @@ def bench_kv(c: Ctx, args):
                     "mapped pinned host buffers",
         "descriptors_per_step": n_desc, "bytes_per_step": step_bytes,
         "max_wgs": max_wgs, "chunk_bytes": K.CHUNK_DEFAULT, "seed": 0,
-        "streams": c.stream_kind})
+        "streams": c.stream_kind, "store_form": args.store})
     line["roofline"] = {
         "bound": "pcie", "kernel": KERNEL_NAMES[dom], "achieved": round(ach[dom], 3),
         "peak": PCIE_PEAK_GBS, "unit": "GB/s", "frac": round(ach[dom] / PCIE_PEAK_GBS, 4),
@@ -1800,6 +1803,9 @@ def main():
     ap.add_argument("--desc-upload", action="store_true",
                     help="upload worklists to device memory before each kernel (KVCOPY_F_DESC_UPLOAD) "
                          "instead of reading them in place from pinned staging")
+    ap.add_argument("--store", default="auto", choices=["auto", "sc1", "nt"],
+                    help="store form of the copy kernels in the timed steps (KVCOPY_F_STORE_SC1 / "
+                         "KVCOPY_F_STORE_NT); auto = the library's choice")
     ap.add_argument("--decode-steps", type=int, default=1536)
     ap.add_argument("--decode-runs", type=int, default=3)
     ap.add_argument("--modes", default="",
