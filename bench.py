@@ -52,7 +52,7 @@ HBM_PEAK_GBS = 8000.0     # MI355X HBM3E
 # link; the full grid oversubscribes it (see the max_wgs sweep, --sweep).
 DEFAULT_MAX_WGS = 128
 REC_BYTES = 24            # one worklist record per chunk
-KERNEL_NAMES = {0: "kvcopy_h2d_kernel", 1: "kvcopy_d2h_kernel", 2: "kvcopy_d2d_kernel"}
+DIR_NAMES = ("h2d", "d2h", "d2d")
 COUNTERS_KV = os.path.join(ROOT, "profiles", "counters_kv_bidirectional.json")
 COUNTERS_D2D = os.path.join(ROOT, "profiles", "counters_d2d_blocks.json")
 COUNTERS_PAIR = os.path.join(ROOT, "profiles", "counters_kv_pair.json")
@@ -173,9 +173,7 @@ class Ctx:
         when the last one does."""
         if self.args.desc_upload:
             kw["flags"] = kw.get("flags", 0) | self.K.F_DESC_UPLOAD
-        if self.args.store != "auto":
-            kw["flags"] = kw.get("flags", 0) | (self.K.F_STORE_SC1 if self.args.store == "sc1"
-                                                else self.K.F_STORE_NT)
+        forms = store_forms(self.args.store)
         marks = None
         # profiler runs (--no-events) make no event calls at all (rocprofv3 7.2
         # aborted in its own tool on them): there the host joins the steps
@@ -187,6 +185,10 @@ class Ctx:
                 if events is not None:
                     extra.update(kernel_begin=events[i][j][0].h, kernel_end=events[i][j][1].h)
                 g = max_wgs[j] if isinstance(max_wgs, (list, tuple)) else max_wgs
+                form = forms.get(r.wl.batches[bi].dir)
+                if form:
+                    extra["flags"] = extra.get("flags", 0) | (
+                        self.K.F_STORE_SC1 if form == "sc1" else self.K.F_STORE_NT)
                 r.submit(bi, g, st, **extra)
             if marks:
                 for m, st in zip(marks, streams):
@@ -324,6 +326,31 @@ class Ctx:
                 sys.exit(3)
 
 
+def kernel_name(dir_, spec="auto"):
+    """The per-chunk copy kernel's symbol for a direction under --store
+    (the library stores D2H in the sc1 form and the rest nt by default)."""
+    form = store_forms(spec).get(dir_) or ("sc1" if dir_ == 1 else "nt")
+    return f"kvcopy_{DIR_NAMES[dir_]}{'_sc1' if form == 'sc1' else ''}_kernel"
+
+
+def store_forms(spec):
+    """Direction (0 H2D, 1 D2H, 2 D2D) -> "sc1" or "nt" from --store: "auto"
+    (the library's choice for every direction), "sc1" or "nt" (every
+    direction), or per direction as "h2d:sc1,d2h:nt"."""
+    if spec == "auto":
+        return {}
+    if spec in ("sc1", "nt"):
+        return {0: spec, 1: spec, 2: spec}
+    out = {}
+    for part in spec.split(","):
+        d, _, f = part.partition(":")
+        if d not in ("h2d", "d2h", "d2d") or f not in ("sc1", "nt", "auto"):
+            raise ValueError(f"bad --store part {part!r}")
+        if f != "auto":
+            out[("h2d", "d2h", "d2d").index(d)] = f
+    return out
+
+
 def base_line(args, value, unit, step_s, config, dtype="u8", higher=True):
     return {"metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": round(step_s * 1e3, 4), "higher_is_better": higher,
@@ -344,14 +371,14 @@ def bench_kv(c: Ctx, args):
     n_desc = sum(b.n for b in wl.batches)
     max_wgs = args.max_wgs if args.max_wgs is not None else DEFAULT_MAX_WGS
     extras = {}
+    # The host link's contiguous ceilings (DMA, no copy kernel) and, in the
+    # full run, each direction alone come first: they are part of the report,
+    # and they leave the link in steady use before the headline's own warm-up
+    # (measured on MI355X, bidirectional traffic in the first quarter second
+    # of a process runs at 51-69 GB/s).
+    extras["contiguous_memcpy_ceiling_GBps"] = ceilings(c)
+    log(f"  contiguous ceilings: {extras['contiguous_memcpy_ceiling_GBps']}")
     if not args.skip_extras:
-        # The host link's contiguous ceilings and each direction alone come
-        # first: they are part of the report, and they leave the link in
-        # steady use before the headline's own warm-up (measured on MI355X,
-        # bidirectional traffic in the first quarter second of a process
-        # runs at 51-69 GB/s).
-        extras["contiguous_memcpy_ceiling_GBps"] = ceilings(c)
-        log(f"  contiguous ceilings: {extras['contiguous_memcpy_ceiling_GBps']}")
         alone = {}
         for j, name in ((0, "h2d"), (1, "d2h")):
             s, _ = c.timed_bracketed(res, [j], [sA], args.steps, args.leg_warmup, max_wgs)
@@ -471,14 +498,15 @@ def bench_kv(c: Ctx, args):
         "max_wgs": max_wgs, "chunk_bytes": K.CHUNK_DEFAULT, "seed": 0,
         "streams": c.stream_kind, "store_form": args.store})
     line["roofline"] = {
-        "bound": "pcie", "kernel": KERNEL_NAMES[dom], "achieved": round(ach[dom], 3),
+        "bound": "pcie", "kernel": kernel_name(dom, args.store), "achieved": round(ach[dom], 3),
         "peak": PCIE_PEAK_GBS, "unit": "GB/s", "frac": round(ach[dom] / PCIE_PEAK_GBS, 4),
-        "traffic": measured_traffic(KERNEL_NAMES[dom], COUNTERS_KV, algo[dom],
+        "traffic": measured_traffic(kernel_name(dom, args.store), COUNTERS_KV, algo[dom],
                                     wl.batches[dom].nbytes),
         "kernel_ms": round(kern_ms[dom], 4), "algorithmic_bytes_per_launch": algo[dom],
         "measured_ceiling": meas_ceil,
         "frac_of_measured_ceiling": round(ach[dom] / meas_ceil, 4) if meas_ceil else None,
-        "other_kernel": {"kernel": KERNEL_NAMES[1 - dom], "achieved": round(ach[1 - dom], 3),
+        "other_kernel": {"kernel": kernel_name(1 - dom, args.store),
+                         "achieved": round(ach[1 - dom], 3),
                          "kernel_ms": round(kern_ms[1 - dom], 4)}}
     # the step against the link's measured two-direction ceiling: contiguous
     # hipMemcpyAsync H2D and D2H of 64 MiB each, concurrent on two streams
@@ -1315,10 +1343,10 @@ def bench_d2d(c: Ctx, args):
     ceil = max(res["contiguous_memcpy_hbm_GBps"]["1024MiB"], kc.get("1024MiB", 0.0),
                kc.get("1024MiB_chunk2KiB_uploaded", 0.0))
     ach = dist["hbm_GBps_kernel"] if dist else big["hbm_GBps_kernel"]
-    line["roofline"] = {"bound": "hbm", "kernel": KERNEL_NAMES[2],
+    line["roofline"] = {"bound": "hbm", "kernel": kernel_name(2, args.store),
                         "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                         "frac": round(ach / HBM_PEAK_GBS, 4),
-                        "traffic": measured_traffic(KERNEL_NAMES[2], COUNTERS_D2D,
+                        "traffic": measured_traffic(kernel_name(2, args.store), COUNTERS_D2D,
                                                     big["payload_bytes"] + big["records"] * REC_BYTES,
                                                     big["payload_bytes"]),
                         "workload_of_roofline": "65536x4KiB, calls cycling over 8 distinct batches"
@@ -1803,9 +1831,10 @@ def main():
     ap.add_argument("--desc-upload", action="store_true",
                     help="upload worklists to device memory before each kernel (KVCOPY_F_DESC_UPLOAD) "
                          "instead of reading them in place from pinned staging")
-    ap.add_argument("--store", default="auto", choices=["auto", "sc1", "nt"],
+    ap.add_argument("--store", default="auto",
                     help="store form of the copy kernels in the timed steps (KVCOPY_F_STORE_SC1 / "
-                         "KVCOPY_F_STORE_NT); auto = the library's choice")
+                         "KVCOPY_F_STORE_NT): auto (the library's choice), sc1, nt, or per "
+                         "direction as h2d:sc1,d2h:nt")
     ap.add_argument("--decode-steps", type=int, default=1536)
     ap.add_argument("--decode-runs", type=int, default=3)
     ap.add_argument("--modes", default="",
@@ -1819,6 +1848,11 @@ def main():
                     help="interference with --decode-kind alu: workgroups per kernel")
     args = ap.parse_args()
     args.leg_warmup = min(args.warmup, 100)
+    try:
+        store_forms(args.store)
+    except ValueError as e:
+        print(e, file=sys.stderr)
+        sys.exit(2)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: the copy path has no multi-GPU step "

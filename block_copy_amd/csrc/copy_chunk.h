@@ -27,15 +27,16 @@ constexpr int kStorePolicy = 2;
 // The sc1 form: sc1 | nt (bits 4 and 1).  On the gfx940 family the two
 // scope bits SC1:SC0 name the coherence scope of an access (0 wavefront, 1
 // workgroup, 2 device, 3 system), so sc1 alone is a device-scope,
-// nontemporal store.  The one-launch pair kernel stores this way by default.
-// Measured on MI355X with 16,384 x 4 KiB each way: 98.7 GB/s against 96.9
-// with nt alone.  A lone D2H batch gains too (56.7 against 52.7 GB/s), but a
-// D2H kernel that runs beside an H2D kernel on another stream loses with it
-// (82-84 against 86.7 GB/s for the two directions at 128 workgroups each),
-// and an H2D kernel gains nothing from it alone (56.9 GB/s either way).  So
-// by default the D2H per-chunk loop picks the form per call (sc1 unless one
-// of the library's H2D kernels is still running on another stream) and the
-// other kernels keep nt; KVCOPY_F_STORE_SC1 / KVCOPY_F_STORE_NT force one.
+// nontemporal store.  D2H kernels and the one-launch pair store this way by
+// default.  Measured on MI355X (16,384 x 4 KiB each way, 300 steps after
+// 300 warm-up steps, three processes per setting in alternating order): H2D
+// and D2H on two streams at 128 workgroups each move 94.2-94.6 GB/s with the
+// D2H kernel's stores in this form and 87.9-88.4 GB/s with nt alone, whatever
+// form the H2D kernel's stores take; a lone D2H batch moves 56.7 against
+// 52.7 GB/s.  The nt form also wrote 65.66 MiB per 64 MiB D2H launch
+// (FETCH/WRITE_SIZE counters), this one exactly 64.00 MiB.  H2D and D2D
+// stores, which land in HBM, keep nt; KVCOPY_F_STORE_SC1 / KVCOPY_F_STORE_NT
+// force one form.
 constexpr int kSc1StorePolicy = 18;
 constexpr uint32_t kRowBytes = 64u * 16u;          // one wavefront instruction: 1 KiB
 constexpr int kMaxRows = 16;                       // 16 KiB per pass, 64 VGPRs of data

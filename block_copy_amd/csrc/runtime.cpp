@@ -357,22 +357,12 @@ int run_locked(Staging *st, int device, const uint64_t *src, const uint64_t *dst
                                          KVCOPY_F_STORE_NT)) != 0 || pace_period != 0;
         const bool pipelined = (flags & KVCOPY_F_PIPELINE) != 0 ||
                                (!per_chunk && pipeline_pays(dir, grid, n_chunks));
-        // D2H stores with the sc1 form unless an H2D kernel of this library
-        // is still running on another stream (copy_chunk.h, kSc1StorePolicy:
-        // faster alone, slower beside an H2D kernel), unless a flag forces a
-        // form.  Only the speed depends on the choice.
+        // D2H stores take the sc1 form and the other directions nt
+        // (copy_chunk.h, kSc1StorePolicy), unless a flag forces one.  Only
+        // the speed depends on the choice.
         int sc1 = forced_store(flags);
-        if (sc1 < 0) {
-            sc1 = 0;
-            if (dir == KVCOPY_D2H && !pipelined) {
-                const int busy = st->ring.running_elsewhere(KVCOPY_H2D, stream);
-                if (busy < 0) {
-                    st->spare.push_back(done);
-                    return busy;
-                }
-                sc1 = busy == 0;
-            }
-        }
+        if (sc1 < 0)
+            sc1 = dir == KVCOPY_D2H;
         e = launch_copy(recs, (uint32_t)n_chunks, grid, dir, pipelined, sc1 != 0, pace_on,
                         pace_period, stream, start, stop);
     }
@@ -382,7 +372,7 @@ int run_locked(Staging *st, int device, const uint64_t *src, const uint64_t *dst
         st->spare.push_back(done);
         return hip_fail(e);
     }
-    st->ring.commit(off, used, done, dir, stream);
+    st->ring.commit(off, used, done);
     return KVCOPY_OK;
 }
 
@@ -419,8 +409,8 @@ int run_inline(Staging *st, const uint64_t *src, const uint64_t *dst, const uint
     const int forced = forced_store(o.flags);
     if (!(o.flags & KVCOPY_F_PER_CHUNK) && forced < 0 && pipeline_pays(dir, grid, w.n_chunks))
         return kNotInline;
-    const hipError_t e =
-        launch_copy_inline(w, grid, dir, forced == 1, stream, o.ev_begin, o.ev_end);
+    const bool sc1 = forced < 0 ? dir == KVCOPY_D2H : forced == 1;
+    const hipError_t e = launch_copy_inline(w, grid, dir, sc1, stream, o.ev_begin, o.ev_end);
     return e == hipSuccess ? KVCOPY_OK : hip_fail(e);
 }
 

@@ -23,8 +23,6 @@ public:
     struct Region {
         uint64_t begin, end;
         Ev ev;
-        int kind;            // caller's label (the copy direction)
-        const void *owner;   // caller's label (the stream)
     };
 
     explicit StagingRing(Ops ops = Ops()) : ops_(ops) {}
@@ -94,28 +92,10 @@ public:
 
     // Records that [off, off + used) is in use until `ev` completes.
     // `off` must come from the last reserve() and used <= the size reserved.
-    // `kind` and `owner` only label the region for running_elsewhere().
-    void commit(uint64_t off, uint64_t used, Ev ev, int kind = -1, const void *owner = nullptr)
+    void commit(uint64_t off, uint64_t used, Ev ev)
     {
-        inflight_.push_back(Region{off, off + used, ev, kind, owner});
+        inflight_.push_back(Region{off, off + used, ev});
         head_ = off + used;
-    }
-
-    // 1 if a region labelled `kind` by an owner other than `owner` is still
-    // running, 0 if not, < 0 an error code from poll.  Polls without waiting,
-    // newest region first, at most `look` matching regions (older ones have
-    // most likely completed; the answer only steers a performance choice).
-    int running_elsewhere(int kind, const void *owner, int look = 4)
-    {
-        for (auto it = inflight_.rbegin(); it != inflight_.rend() && look > 0; ++it) {
-            if (it->kind != kind || it->owner == owner)
-                continue;
-            --look;
-            const int rc = ops_.poll(it->ev);
-            if (rc != 1)
-                return rc < 0 ? rc : 1;
-        }
-        return 0;
     }
 
 private:

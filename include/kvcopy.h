@@ -123,13 +123,13 @@ enum {
 /* Store form of the per-chunk loop.  Two forms give the same bytes: the
  * nontemporal hint alone ("nt"), and nt with the sc1 scope bit ("sc1", a
  * device-scope store on the gfx940 family).  By default D2H batches use sc1
- * unless one of this library's H2D kernels is still running on another
- * stream, and H2D and D2D batches use nt (measured on MI355X: sc1 is faster
- * for a lone D2H batch, slower for a D2H batch beside an H2D kernel, the
- * same for H2D).  These flags force one form, for any direction; they select
- * the per-chunk loop (KVCOPY_F_PIPELINE or KVCOPY_F_DYNAMIC with either is
- * KVCOPY_EINVAL, and so are both).  kvcopy_batch_pair takes
- * KVCOPY_F_STORE_NT (its default is sc1). */
+ * and H2D and D2D batches nt.  Measured on MI355X with 16,384 x 4 KiB each
+ * way on two streams: 94.2-94.6 GB/s with the D2H kernel's stores in the
+ * sc1 form, 87.9-88.4 with nt, whatever the H2D kernel's form; a lone D2H
+ * batch 56.7 against 52.7 GB/s.  These flags force one form, for any
+ * direction; they select the per-chunk loop (KVCOPY_F_PIPELINE or
+ * KVCOPY_F_DYNAMIC with either is KVCOPY_EINVAL, and so are both).
+ * kvcopy_batch_pair takes KVCOPY_F_STORE_NT (its default is sc1). */
 #define KVCOPY_F_STORE_SC1 0x80u
 #define KVCOPY_F_STORE_NT 0x100u
 /* Destination order: the worklist handed to the kernel is ordered by 64 MiB
@@ -219,9 +219,8 @@ void kvcopy_plan_free(kvcopy_plan_t *plan);
  * min(max_wgs, needed) workgroups of 4 wavefronts on `stream`.  Each
  * wavefront takes an equal contiguous share of the chunks and moves them
  * with 16-byte loads and nontemporal 16-byte stores (a D2H batch's stores
- * also carry the sc1 scope bit when none of this library's H2D kernels is
- * still running on another stream, which is faster alone and slower beside
- * one; the bytes moved are the same; see KVCOPY_F_STORE_SC1).  The staging region is
+ * also carry the sc1 scope bit, which is faster over the host link; the
+ * bytes moved are the same; see KVCOPY_F_STORE_SC1).  The staging region is
  * recycled once an event recorded after the kernel has completed; the call
  * waits on the host only if the whole ring is still in use.  A batch of at
  * most 128 chunks instead passes its worklist in the kernel arguments (no
@@ -302,8 +301,8 @@ int kvcopy_batch_ex(const uint64_t *src_addrs, const uint64_t *dst_addrs, const 
  * their chunk counts, with every workgroup holding wavefronts of both, so
  * every CU in use carries both directions and both directions of the host
  * link stay busy together until the end.  Measured on MI355X with 16,384 x
- * 4 KiB each way: 98 GB/s, where the same bursts as two kernels on two
- * streams reach 85-88 GB/s (and less when the two caps differ: the
+ * 4 KiB each way: 98-99 GB/s, where the same bursts as two kernels on two
+ * streams reach 93-94 GB/s (and less when the two caps differ: the
  * direction with fewer requests in flight loses its share of the link).
  * The bytes moved are exactly those of kvcopy_batch(a) followed by
  * kvcopy_batch(b) on `stream`.
@@ -315,8 +314,7 @@ int kvcopy_batch_ex(const uint64_t *src_addrs, const uint64_t *dst_addrs, const 
  * list may hold any direction; the usual use is H2D in one and D2H in the
  * other.  n_a or n_b may be 0 (both 0: KVCOPY_OK, nothing enqueued).  By
  * default the kernel's stores carry the sc1 scope bit as well as the
- * nontemporal hint (as kvcopy_batch's D2H kernel does when none of this
- * library's H2D kernels is running on another stream); KVCOPY_F_STORE_NT
+ * nontemporal hint (as kvcopy_batch's D2H kernel does); KVCOPY_F_STORE_NT
  * selects the nontemporal hint alone.
  * max_wgs as for kvcopy_batch, except that KVCOPY_WGS_AUTO is 64
  * workgroups, the steadiest cap measured for the burst above (98.4 GB/s;

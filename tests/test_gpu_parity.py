@@ -189,13 +189,11 @@ def test_kv_blocks_concurrent_on_dedicated_queues(K):
 
 @pytest.mark.parametrize("beside", ["alone", "h2d_other_stream", "h2d_same_stream"])
 def test_d2h_store_forms(K, beside):
-    """A D2H batch stores with system scope unless one of the library's H2D
-    kernels still runs on another stream, where it keeps the nontemporal
-    form: both forms (and the case of an H2D kernel ahead of it on its own
-    stream) must leave the same bytes.  The D2H batch is irregular
-    (misaligned pairs, 8-byte tails, zero sizes) and larger than the inline
-    limit; the H2D batch is 16,384 x 4 KiB, still running when the D2H batch
-    is submitted."""
+    """A D2H batch (sc1 stores) alone, beside an H2D kernel still running on
+    another stream, and behind one on its own stream must leave the same
+    bytes.  The D2H batch is irregular (misaligned pairs, 8-byte tails, zero
+    sizes) and larger than the inline limit; the H2D batch is 16,384 x
+    4 KiB, still running when the D2H batch is submitted."""
     from block_copy_amd.harness import Resident
     d2h = W.irregular(seed=61, n=600, dir_=W.D2H, src_where="device", dst_where="host",
                       misalign=True, zero_frac=0.05)
