@@ -144,9 +144,17 @@ class Ctx:
         log(f"device: {p.name} ({p.gcnArchName}), {p.multi_processor_count} CUs")
         # the two copy streams get a hardware queue each (hiprt.QueueStreams):
         # plain streams may share one and then run the two directions in turn
+        ncu = p.multi_processor_count
+        cus = None
         self.stream_kind = "a hardware queue each (full CU mask)"
+        if getattr(args, "copy_cus", "all") == "halves":
+            # mask bits [0, ncu/2) for the first stream, the rest for the
+            # second: every XCD keeps CUs for both (bit i is a CU of XCD i % 8)
+            cus = [range(ncu // 2), range(ncu // 2, ncu)]
+            self.stream_kind = ("a hardware queue each; first stream on CU mask bits 0-"
+                                f"{ncu // 2 - 1}, second on {ncu // 2}-{ncu - 1}")
         try:
-            self.queues = hiprt.QueueStreams(2, p.multi_processor_count)
+            self.queues = hiprt.QueueStreams(2, ncu, cus)
             self.sA, self.sB = self.queues.streams
         except RuntimeError as e:
             log(f"  dedicated-queue streams unavailable ({e}); using torch streams")
@@ -326,6 +334,16 @@ class Ctx:
                 sys.exit(3)
 
 
+def parse_wgs(text):
+    """--max-wgs: one cap, or "H2D,D2H" (two caps, headline only)."""
+    vals = [int(x) for x in text.split(",")]
+    if len(vals) == 1:
+        return vals[0]
+    if len(vals) != 2:
+        raise argparse.ArgumentTypeError("expected N or H2D,D2H")
+    return vals
+
+
 def kernel_name(dir_, spec="auto"):
     """The per-chunk copy kernel's symbol for a direction under --store
     (the library stores D2H in the sc1 form and the rest nt by default)."""
@@ -370,6 +388,10 @@ def bench_kv(c: Ctx, args):
     step_bytes = wl.nbytes
     n_desc = sum(b.n for b in wl.batches)
     max_wgs = args.max_wgs if args.max_wgs is not None else DEFAULT_MAX_WGS
+
+    def cap_of(j):     # direction j's cap (--max-wgs H2D,D2H gives one per direction)
+        return max_wgs[j] if isinstance(max_wgs, list) else max_wgs
+
     extras = {}
     # The host link's contiguous ceilings (DMA, no copy kernel) and, in the
     # full run, each direction alone come first: they are part of the report,
@@ -381,11 +403,11 @@ def bench_kv(c: Ctx, args):
     if not args.skip_extras:
         alone = {}
         for j, name in ((0, "h2d"), (1, "d2h")):
-            s, _ = c.timed_bracketed(res, [j], [sA], args.steps, args.leg_warmup, max_wgs)
-            _, km = c.timed(res, [j], [sA], args.steps, 2, max_wgs)
+            s, _ = c.timed_bracketed(res, [j], [sA], args.steps, args.leg_warmup, cap_of(j))
+            _, km = c.timed(res, [j], [sA], args.steps, 2, cap_of(j))
             alone[name] = {"GBps": round(gbs(wl.batches[j].nbytes, s), 3),
                            "ms_per_call": round(s * 1e3, 4), "kernel_ms": round(km[0], 4),
-                           "latency": c.latency(res, j, max_wgs, k=50, w=5)}
+                           "latency": c.latency(res, j, cap_of(j), k=50, w=5)}
             log(f"  {name} alone: {alone[name]}")
         extras["per_direction_alone"] = alone
     log(f"headline: {n_desc} descriptors, {step_bytes} B per step, max_wgs={max_wgs}")
@@ -436,8 +458,8 @@ def bench_kv(c: Ctx, args):
         alone["d2h_one_list_through_pair"] = {"GBps": round(gbs(wl.batches[1].nbytes, ms_ / 1e3), 3),
                                               "kernel_ms": round(ms_, 4)}
         log(f"  d2h alone through kvcopy_batch_pair: {alone['d2h_one_list_through_pair']}")
-        cl = c_caller_latency([(f"kv_{nm}_16384x4KiB", W.kv_blocks(seed=0, directions=nm), max_wgs)
-                               for nm in ("h2d", "d2h")])
+        cl = c_caller_latency([(f"kv_{nm}_16384x4KiB", W.kv_blocks(seed=0, directions=nm), cap_of(j))
+                               for j, nm in enumerate(("h2d", "d2h"))])
         for nm in ("h2d", "d2h"):
             alone[nm]["latency_c_caller"] = cl.get(f"kv_{nm}_16384x4KiB", cl.get("error"))
         log(f"  each direction alone, C caller: {cl}")
@@ -1812,8 +1834,12 @@ def main():
     # to back: 84.4-87.0 GB/s, then 88.0-88.2).  Secondary legs warm up for
     # at most 100 of their own steps (args.leg_warmup).
     ap.add_argument("--warmup", type=int, default=700)
-    ap.add_argument("--max-wgs", type=int, default=None,
-                    help=f"workgroup cap (default {DEFAULT_MAX_WGS}; pair: KVCOPY_WGS_AUTO)")
+    ap.add_argument("--max-wgs", type=parse_wgs, default=None,
+                    help=f"workgroup cap (default {DEFAULT_MAX_WGS}; pair: KVCOPY_WGS_AUTO); "
+                         "kv only: H2D,D2H for a cap per direction")
+    ap.add_argument("--copy-cus", default="all", choices=["all", "halves"],
+                    help="CU masks of the two copy streams: every CU, or disjoint halves "
+                         "(each XCD keeps CUs for both)")
     ap.add_argument("--workload", default="kv", choices=["kv", "pair", "d2d", "mixed", "moe",
                                                          "interference"])
     ap.add_argument("--sweep", action="store_true", help="also sweep max_wgs per direction (stderr)")
@@ -1848,6 +1874,10 @@ def main():
                     help="interference with --decode-kind alu: workgroups per kernel")
     args = ap.parse_args()
     args.leg_warmup = min(args.warmup, 100)
+    if isinstance(args.max_wgs, list) and args.workload != "kv":
+        print("a cap per direction (--max-wgs H2D,D2H) applies to --workload kv only",
+              file=sys.stderr)
+        sys.exit(2)
     try:
         store_forms(args.store)
     except ValueError as e:

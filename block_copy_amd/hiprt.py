@@ -107,11 +107,13 @@ class Event:
             h, self.h = self.h, None
             check(hip.hipEventDestroy(h), "hipEventDestroy")
 
-    def __del__(self):
+    def __del__(self, _finalizing=sys.is_finalizing):
         # No HIP call from a finaliser that runs while the interpreter shuts
         # down: by then the runtime (or a profiler wrapped around it) may be
         # tearing itself down.  The process's exit releases the event.
-        if sys.is_finalizing():
+        # (sys.is_finalizing is bound as a default: module globals may
+        # already be cleared when a late finaliser runs)
+        if _finalizing():
             return
         try:
             self.destroy()
@@ -197,11 +199,18 @@ class QueueStreams:
     the two streams, 3 processes in 8 ran at 75-80 GB/s.  A CU mask is a
     property of the hardware queue, so a stream created with one gets a
     queue of its own; with every CU in the mask it runs like any other
-    stream (default priority).  torch.cuda.ExternalStream wraps them."""
+    stream (default priority).  torch.cuda.ExternalStream wraps them.
 
-    def __init__(self, n: int, total_cus: int):
+    `cus` (optional): one iterable of CU mask bits per stream instead of
+    every CU.  Mask bit i is a CU of XCD i % 8, and a mask that leaves an
+    XCD without CUs is refused."""
+
+    def __init__(self, n: int, total_cus: int, cus=None):
         import torch
-        self._masked = [CUMaskStream(range(total_cus), total_cus) for _ in range(n)]
+        if cus is not None and len(cus) != n:
+            raise ValueError("cus must give one CU set per stream")
+        sets = cus if cus is not None else [range(total_cus)] * n
+        self._masked = [CUMaskStream(c, total_cus) for c in sets]
         self.streams = [torch.cuda.ExternalStream(m.cuda_stream) for m in self._masked]
 
     def destroy(self):

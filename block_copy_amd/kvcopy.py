@@ -289,11 +289,13 @@ class HostBuffer:
             kvcopy_host_free(self.ptr)
             self.ptr = 0
 
-    def __del__(self):
+    def __del__(self, _finalizing=sys.is_finalizing):
         # Free explicitly (free()); a finaliser that runs during interpreter
         # shutdown makes no HIP call and leaves the memory to the process's
         # exit.
-        if sys.is_finalizing():
+        # (sys.is_finalizing is bound as a default: module globals may
+        # already be cleared when a late finaliser runs)
+        if _finalizing():
             return
         try:
             self.free()

@@ -12,6 +12,14 @@
          traffic in the same process (bench.py --counter-calibration: torch.neg
          over 64 MiB of int32, which reads 64 MiB and writes 64 MiB).
 
+  python -m block_copy_amd.profile_summary bursts DIR --name NAME --command CMD [--workload TEXT]
+         [--decode gemv_bf16_kernel] [--per-step 36]
+      -> markdown table of a --kernel-trace run of bench.py's interference
+         leg: decode steps (each run of --per-step decode kernels, first
+         start to last end) and decode kernels outside every copy burst and
+         overlapping the bursts of each copy configuration (copy kernels
+         that overlap in time form one burst).
+
 DIR is rocprofv3's output directory (-d); the CSV files are found below it.
 """
 from __future__ import annotations
@@ -89,6 +97,77 @@ def trace(args):
         print(f"| {name} | {grid} | {g['wg']} | {len(d)} | {statistics.mean(d):.1f} | "
               f"{statistics.median(d):.1f} | {min(d):.1f} | {max(d):.1f} | {g['vgpr']} | "
               f"{g['scratch']} | {g['lds']} |")
+
+
+def _p99(v):
+    v = sorted(v)
+    return v[max(0, -(-99 * len(v) // 100) - 1)]
+
+
+def bursts(args):
+    rows = _rows(args.dir, "kernel_trace.csv")
+
+    def iv(r):
+        return int(r["Start_Timestamp"]), int(r["End_Timestamp"])
+
+    dec = sorted(iv(r) for r in rows if args.decode in r["Kernel_Name"])
+    per = args.per_step
+    steps = [(dec[i][0], dec[i + per - 1][1]) for i in range(0, len(dec) - per + 1, per)]
+    copies = []
+    for r in rows:
+        name = short_name(r["Kernel_Name"])
+        if name.startswith("kvcopy_") and "plan" not in name:
+            wg = int(float(_get(r, "Workgroup_Size", "Workgroup_Size_X", default=1)))
+            copies.append((iv(r), name, _grid(r) // max(wg, 1), _get(r, "Queue_Id", default="?")))
+    copies.sort()
+    groups = []   # copy kernels that overlap in time form one burst
+    for (s0, e0), name, wgs, q in copies:
+        if groups and s0 <= groups[-1]["end"]:
+            groups[-1]["end"] = max(groups[-1]["end"], e0)
+            groups[-1]["k"].add((name, wgs, q))
+        else:
+            groups.append({"start": s0, "end": e0, "k": {(name, wgs, q)}})
+    for g in groups:
+        g["label"] = " + ".join(f"{n} x{w} WGs (queue {q})" for n, w, q in sorted(g["k"]))
+
+    def owner(a, b):
+        """The burst that the interval [a, b] overlaps, or None."""
+        for g in groups:
+            if g["start"] <= b and a <= g["end"]:
+                return g["label"]
+        return None
+
+    by = {}
+    for what, items in (("steps", steps), ("gemvs", dec)):
+        for a, b in items:
+            by.setdefault(owner(a, b), {"steps": [], "gemvs": []})[what].append((b - a) / 1e3)
+    print(f"# Kernel trace: {args.name}\n")
+    print("Command (run from the repository root on one MI355X):\n")
+    print(f"```\n{args.command}\n```\n")
+    if args.workload:
+        print(args.workload + "\n")
+    queues = sorted({_get(r, "Queue_Id", default="?") for r in rows if args.decode in r["Kernel_Name"]})
+    print(f"{len(dec)} decode kernels ({len(steps)} steps of {per}) on queue(s) {queues}; "
+          f"{len(copies)} copy kernels in {len(groups)} bursts.\n")
+    print("Decode steps (first decode kernel's start to the last one's end) and decode kernels, "
+          "outside every burst and overlapping the bursts of each copy configuration:\n")
+    print("| where | bursts | burst length median (us) | steps | step median (us) | step p99 (us) | "
+          "step max (us) | decode kernels | kernel median (us) | kernel max (us) |")
+    print("|---|---|---|---|---|---|---|---|---|---|")
+
+    def cells(v):
+        return (f"{len(v)} | {statistics.median(v):.1f} | {_p99(v):.1f} | {max(v):.1f}" if v
+                else "0 | — | — | —")
+
+    labels = [None] + sorted({g["label"] for g in groups})
+    for lab in labels:
+        d = by.get(lab, {"steps": [], "gemvs": []})
+        gl = [(g["end"] - g["start"]) / 1e3 for g in groups if g["label"] == lab]
+        head = (f"| outside every burst | — | —" if lab is None else
+                f"| bursts of {lab} | {len(gl)} | {statistics.median(gl):.0f}")
+        gv = d["gemvs"]
+        gcell = (f"{len(gv)} | {statistics.median(gv):.1f} | {max(gv):.1f}" if gv else "0 | — | —")
+        print(f"{head} | {cells(d['steps'])} | {gcell} |")
 
 
 def _counter(d, counter):
@@ -173,6 +252,13 @@ def main():
     t.add_argument("--name", required=True)
     t.add_argument("--command", required=True)
     t.add_argument("--workload", default="")
+    b = sub.add_parser("bursts")
+    b.add_argument("dir")
+    b.add_argument("--name", required=True)
+    b.add_argument("--command", required=True)
+    b.add_argument("--workload", default="")
+    b.add_argument("--decode", default="gemv_bf16_kernel")
+    b.add_argument("--per-step", type=int, default=36)
     c = sub.add_parser("counters")
     c.add_argument("--fetch", required=True)
     c.add_argument("--write", required=True)
@@ -180,7 +266,7 @@ def main():
     c.add_argument("--fetch-command", required=True)
     c.add_argument("--write-command", required=True)
     a = ap.parse_args()
-    trace(a) if a.what == "trace" else counters(a)
+    {"trace": trace, "bursts": bursts, "counters": counters}[a.what](a)
 
 
 if __name__ == "__main__":
