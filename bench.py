@@ -47,10 +47,16 @@ sys.path.insert(0, ROOT)
 METRIC = "GB/s for batched 4–16 KiB descriptor copies (H2D/D2H/D2D), % of link/HBM peak"
 PCIE_PEAK_GBS = 64.0      # PCIe 5.0 x16, per direction (MI355X host interface)
 HBM_PEAK_GBS = 8000.0     # MI355X HBM3E
-# Workgroup cap of the headline: with H2D and D2H running together, a few
-# dozen workgroups per direction keep enough bytes in flight to fill the
-# link; the full grid oversubscribes it (see the max_wgs sweep, --sweep).
-DEFAULT_MAX_WGS = 128
+# Workgroup cap per stream of the headline.  Measured on MI355X with the
+# headline burst on streams over disjoint CU halves (Ctx.headline_streams),
+# two processes per cap: 8 -> 96.4-97.2 GB/s, 12-32 -> 69-87, 48 -> 96.3,
+# 64 -> 96.7-96.8, 96 -> 96.7-97.1, 128 -> 90.6-90.9, 256 -> 85.7-86.3.
+# 64 sits inside the broad plateau; the peak at 8 is a narrow one (7 or 9
+# workgroups per stream on streams over every CU: 84-90 GB/s).
+DEFAULT_MAX_WGS = 64
+# Workgroup cap of the one-direction legs (mixed sizes): the library's
+# default grid for H2D and D2H.
+ONE_WAY_MAX_WGS = 128
 REC_BYTES = 24            # one worklist record per chunk
 DIR_NAMES = ("h2d", "d2h", "d2d")
 COUNTERS_KV = os.path.join(ROOT, "profiles", "counters_kv_bidirectional.json")
@@ -144,22 +150,34 @@ class Ctx:
         log(f"device: {p.name} ({p.gcnArchName}), {p.multi_processor_count} CUs")
         # the two copy streams get a hardware queue each (hiprt.QueueStreams):
         # plain streams may share one and then run the two directions in turn
-        ncu = p.multi_processor_count
-        cus = None
+        self.ncu = p.multi_processor_count
+        self._halves = None
         self.stream_kind = "a hardware queue each (full CU mask)"
-        if getattr(args, "copy_cus", "all") == "halves":
-            # mask bits [0, ncu/2) for the first stream, the rest for the
-            # second: every XCD keeps CUs for both (bit i is a CU of XCD i % 8)
-            cus = [range(ncu // 2), range(ncu // 2, ncu)]
-            self.stream_kind = ("a hardware queue each; first stream on CU mask bits 0-"
-                                f"{ncu // 2 - 1}, second on {ncu // 2}-{ncu - 1}")
         try:
-            self.queues = hiprt.QueueStreams(2, ncu, cus)
+            self.queues = hiprt.QueueStreams(2, self.ncu)
             self.sA, self.sB = self.queues.streams
         except RuntimeError as e:
             log(f"  dedicated-queue streams unavailable ({e}); using torch streams")
             self.stream_kind = "torch streams (dedicated queues unavailable)"
             self.sA, self.sB = torch.cuda.Stream(), torch.cuda.Stream()
+
+    def headline_streams(self):
+        """The two copy streams of the headline step and their description.
+        With --copy-cus halves (the default) each has a hardware queue of its
+        own on one half of the CU mask bits, [0, n/2) and [n/2, n): every XCD
+        keeps CUs for both (bit i is a CU of XCD i % 8).  Measured on MI355X
+        with the headline burst: 96.3-97.1 GB/s at 48-96 workgroups per
+        stream against 94.5-95.8 at 64 on streams over every CU.  With
+        --copy-cus all they are sA and sB."""
+        if self.args.copy_cus != "halves" or getattr(self, "queues", None) is None:
+            return self.sA, self.sB, self.stream_kind
+        if self._halves is None:
+            n = self.ncu
+            self._halves = self.hiprt.QueueStreams(2, n, [range(n // 2), range(n // 2, n)])
+        n = self.ncu
+        return (*self._halves.streams,
+                f"a hardware queue each; H2D on CU mask bits 0-{n // 2 - 1}, D2H on "
+                f"{n // 2}-{n - 1} (every XCD keeps CUs for both)")
 
     def close(self):
         """Explicit teardown before the interpreter exits: wait for the GPU,
@@ -168,9 +186,10 @@ class Ctx:
         still whole (during interpreter shutdown those finalisers skip their
         HIP calls)."""
         self.torch.cuda.synchronize()
-        if getattr(self, "queues", None) is not None:
-            self.queues.destroy()
-            self.queues = None
+        for q in ("queues", "_halves"):
+            if getattr(self, q, None) is not None:
+                getattr(self, q).destroy()
+                setattr(self, q, None)
         gc.collect()
         self.torch.cuda.synchronize()
 
@@ -385,6 +404,7 @@ def bench_kv(c: Ctx, args):
     wl = W.kv_blocks(seed=0, directions="both")
     res = c.Resident(wl)
     sA, sB = c.sA, c.sB
+    hA, hB, stream_kind = c.headline_streams()     # the headline step's two streams
     step_bytes = wl.nbytes
     n_desc = sum(b.n for b in wl.batches)
     max_wgs = args.max_wgs if args.max_wgs is not None else DEFAULT_MAX_WGS
@@ -417,7 +437,7 @@ def bench_kv(c: Ctx, args):
     # The step starts both directions together and ends when both are done
     # (joined): free-running streams drift out of phase over hundreds of
     # steps and leave stretches with one direction running alone.
-    step_s, kern_ms = c.timed_bracketed(res, [0, 1], [sA, sB], args.steps, args.warmup, max_wgs,
+    step_s, kern_ms = c.timed_bracketed(res, [0, 1], [hA, hB], args.steps, args.warmup, max_wgs,
                                         joined=True)
     value = gbs(step_bytes, step_s)
     log(f"  bidirectional: {step_s * 1e3:.3f} ms/step, {value:.2f} GB/s; mean kernel ms per "
@@ -428,7 +448,7 @@ def bench_kv(c: Ctx, args):
 
     if args.sweep:
         sweep = {}
-        for name, ids, sts in (("h2d", [0], [sA]), ("d2h", [1], [sA]), ("both", [0, 1], [sA, sB])):
+        for name, ids, sts in (("h2d", [0], [sA]), ("d2h", [1], [sA]), ("both", [0, 1], [hA, hB])):
             for g in (1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 0):
                 s_, km = c.timed(res, ids, sts, max(3, args.steps // 2), 2, g)
                 nbytes = sum(wl.batches[i].nbytes for i in ids)
@@ -437,7 +457,7 @@ def bench_kv(c: Ctx, args):
                     f"{[round(x, 3) for x in km]}")
         extras["max_wgs_sweep_GBps"] = sweep
     if not args.skip_extras and not args.no_events:
-        extras["headline_windows"] = headline_windows(c, res, max_wgs)
+        extras["headline_windows"] = headline_windows(c, res, max_wgs, streams=(hA, hB))
         log(f"  headline windows: {dict((k, v) for k, v in extras['headline_windows'].items() if k not in ('GBps', 'kernel_ms_per_stream'))}")
     if not args.skip_extras:
         alone = extras["per_direction_alone"]
@@ -464,13 +484,13 @@ def bench_kv(c: Ctx, args):
             alone[nm]["latency_c_caller"] = cl.get(f"kv_{nm}_16384x4KiB", cl.get("error"))
         log(f"  each direction alone, C caller: {cl}")
         # the startup probe's choice, and the headline step at that cap
-        cap, rates = K.kvcopy_autotune(K.H2D, sA.cuda_stream, sB.cuda_stream)
+        cap, rates = K.kvcopy_autotune(K.H2D, hA.cuda_stream, hB.cuda_stream)
         auto = {"h2d_d2h": cap, "probe_GBps": {str(k): round(v, 2) for k, v in rates.items()}}
-        s_, km = c.timed_bracketed(res, [0, 1], [sA, sB], args.steps, args.leg_warmup, K.WGS_AUTO,
+        s_, km = c.timed_bracketed(res, [0, 1], [hA, hB], args.steps, args.leg_warmup, K.WGS_AUTO,
                                    joined=True)
         auto["bidirectional_GBps_at_auto"] = round(gbs(step_bytes, s_), 3)
         if not args.no_events:
-            auto["windows_at_auto"] = headline_windows(c, res, K.WGS_AUTO, n=10)
+            auto["windows_at_auto"] = headline_windows(c, res, K.WGS_AUTO, n=10, streams=(hA, hB))
             auto["windows_at_auto"].pop("kernel_ms_per_stream")
         extras["autotune"] = auto
         log(f"  autotune: {auto}")
@@ -489,7 +509,7 @@ def bench_kv(c: Ctx, args):
     # The DMA baselines above wrote the same destination arenas, so refill
     # them and run one more kernel step before reading the images back.
     res.fill()
-    c.run_steps(res, [0, 1], [sA, sB], 1, max_wgs)
+    c.run_steps(res, [0, 1], [hA, hB], 1, max_wgs)
     torch.cuda.synchronize()
     final = {i: res.image(i) for i in (0, 2)}        # device pool, host D2H destination
     imgs, cpu = kv_oracle(c, wl, res, args)
@@ -518,7 +538,7 @@ def bench_kv(c: Ctx, args):
                     "mapped pinned host buffers",
         "descriptors_per_step": n_desc, "bytes_per_step": step_bytes,
         "max_wgs": max_wgs, "chunk_bytes": K.CHUNK_DEFAULT, "seed": 0,
-        "streams": c.stream_kind, "store_form": args.store})
+        "streams": stream_kind, "store_form": args.store})
     line["roofline"] = {
         "bound": "pcie", "kernel": kernel_name(dom, args.store), "achieved": round(ach[dom], 3),
         "peak": PCIE_PEAK_GBS, "unit": "GB/s", "frac": round(ach[dom] / PCIE_PEAK_GBS, 4),
@@ -695,7 +715,7 @@ def mixed_compact(c: Ctx, args, ceil_h2d):
     ceiling measured in the same run; each N checked bit-exact against the
     oracle."""
     W, K = c.W, c.K
-    g = DEFAULT_MAX_WGS
+    g = ONE_WAY_MAX_WGS
     rows = {}
     for n in (16, 256, 4096, 65536):
         wl = W.h2d_mixed(seed=0, n=n)
@@ -858,8 +878,9 @@ def bench_pair(c: Ctx, args):
     if not args.skip_extras:
         # the two-stream submission of the same burst first: it also brings
         # both streams into use before the contiguous ceilings are taken on them
+        hA, hB, _ = c.headline_streams()
         extras["two_streams_same_run_GBps"] = round(gbs(step_bytes, c.timed_bracketed(
-            res, [0, 1], [c.sA, c.sB], args.steps, args.leg_warmup, DEFAULT_MAX_WGS,
+            res, [0, 1], [hA, hB], args.steps, args.leg_warmup, DEFAULT_MAX_WGS,
             joined=True)[0]), 3)
         extras["contiguous_memcpy_ceiling_GBps"] = ceilings(c)
         log(f"  ceilings {extras['contiguous_memcpy_ceiling_GBps']}, two streams at "
@@ -1151,16 +1172,18 @@ def d2d_results(c: Ctx, args):
     return out
 
 
-def headline_windows(c: Ctx, res, max_wgs, n=30, k=20, **kw):
+def headline_windows(c: Ctx, res, max_wgs, n=30, k=20, streams=None, **kw):
     """n consecutive windows of k joined steps of the headline burst (the
-    step count the headline is timed over), each timed by wall clock around
-    the window and by one event pair per stream around its kernels: the
-    spread of the two-stream rate, and in each window whether both kernels
-    slowed or one stream ran longer than the other."""
+    step count the headline is timed over) on `streams` (default sA, sB),
+    each timed by wall clock around the window and by one event pair per
+    stream around its kernels: the spread of the two-stream rate, and in
+    each window whether both kernels slowed or one stream ran longer than
+    the other."""
     step_bytes = res.wl.nbytes
+    st = list(streams) if streams is not None else [c.sA, c.sB]
     rates, kern = [], []
     for _ in range(n):
-        s, km = c.timed_bracketed(res, [0, 1], [c.sA, c.sB], k, 0, max_wgs, joined=True, **kw)
+        s, km = c.timed_bracketed(res, [0, 1], st, k, 0, max_wgs, joined=True, **kw)
         rates.append(gbs(step_bytes, s))
         kern.append([round(x, 4) for x in km])
     med = statistics.median(rates)
@@ -1394,7 +1417,7 @@ def bench_d2d(c: Ctx, args):
 
 def bench_mixed(c: Ctx, args):
     W, K, hiprt = c.W, c.K, c.hiprt
-    g = args.max_wgs if args.max_wgs is not None else DEFAULT_MAX_WGS
+    g = args.max_wgs if args.max_wgs is not None else ONE_WAY_MAX_WGS
     rows = {}
     for n in (16, 256, 4096, 65536):
         wl = W.h2d_mixed(seed=0, n=n)
@@ -1426,6 +1449,86 @@ def bench_mixed(c: Ctx, args):
                     "value at N = 65,536",
         "max_wgs": g, "chunk_bytes": K.CHUNK_DEFAULT, "seed": 0})
     line["per_n"] = rows
+    line["parity"] = "bit-exact vs oracle"
+    return line
+
+
+# ---------------------------------------------------------------------------
+# Kernel or the runtime's copy, per batch shape
+# ---------------------------------------------------------------------------
+
+# (descriptors, bytes each): lone small blocks, bursts of 4 KiB blocks, 64 KiB
+# blocks, 1 MiB rows, and large single ranges
+CROSSOVER_SHAPES = ((1, 4 << 10), (4, 4 << 10), (16, 4 << 10), (16384, 4 << 10), (4, 64 << 10),
+                    (1024, 64 << 10), (1, 1 << 20), (64, 1 << 20), (1, 4 << 20), (4, 16 << 20),
+                    (1, 64 << 20))
+
+
+def bench_crossover(c: Ctx, args):
+    """Kernel or the runtime's copy, per batch shape.  The vLLM PR #42212
+    report ("implementation breakdown") routes batches of fewer than 16
+    descriptors, or of descriptors above 28 KiB, to DMA.  Here: shuffled
+    blocks of one size between mapped pinned memory and HBM, each direction
+    alone; the GPU time between events recorded around one call (median of
+    several calls, after 3 untimed ones) for one kvcopy_batch at max_wgs
+    (default 8) and for one hipMemcpyAsync per range; every shape checked
+    bit-exact against the oracle."""
+    W, K, hiprt, torch = c.W, c.K, c.hiprt, c.torch
+    if args.no_events:
+        print("the crossover workload times calls with HIP events; run it without --no-events",
+              file=sys.stderr)
+        sys.exit(2)
+    g = args.max_wgs if args.max_wgs is not None else 8
+    st = c.sA
+
+    def median_ms(fn, reps):
+        out = []
+        for i in range(reps + 3):
+            e0, e1 = hiprt.Event(), hiprt.Event()
+            e0.record(st)
+            fn()
+            e1.record(st)
+            ms = e0.elapsed_ms(e1)
+            if i >= 3:
+                out.append(ms)
+        return statistics.median(out)
+
+    rows, wins = {}, 0
+    for n, size in CROSSOVER_SHAPES:
+        for dname in ("h2d", "d2h"):
+            wl = W.kv_blocks(seed=0, directions=dname, n=n, pool_blocks=n, block=size)
+            r = c.Resident(wl)
+            nbytes = wl.batches[0].nbytes
+            reps = 20 if n <= 64 else 5
+            kern = median_ms(lambda: r.submit(0, g, st), reps)
+            r.fill()
+            r.submit(0, g, st)
+            torch.cuda.synchronize()
+            c.verify(wl, r, [0], f"crossover {n} x {size} {dname}")
+            pl = K.kvcopy_plan(*r.addrs[0], wl.batches[0].size)
+            kind = hiprt.H2D_KIND if dname == "h2d" else hiprt.D2H_KIND
+            ranges = list(zip(pl.src.tolist(), pl.dst.tolist(), pl.size.tolist()))
+
+            def per_range():
+                for s_, d_, z_ in ranges:
+                    hiprt.memcpy_async(d_, s_, z_, kind, st)
+
+            rt = median_ms(per_range, reps)
+            key = f"{n}x{size}/{dname}"
+            rows[key] = {"kernel_us": round(kern * 1e3, 2), "kernel_GBps": round(gbs(nbytes, kern / 1e3), 3),
+                         "runtime_copy_us": round(rt * 1e3, 2),
+                         "runtime_copy_GBps": round(gbs(nbytes, rt / 1e3), 3),
+                         "runtime_copies": len(ranges)}
+            wins += kern <= rt
+            log(f"  crossover {key}: {rows[key]}")
+            r.free()
+    line = base_line(args, wins, "shapes", 0.0, {
+        "workload": "one kvcopy_batch against one hipMemcpyAsync per range, shuffled blocks "
+                    "between mapped pinned memory and HBM, each direction alone, "
+                    f"{len(CROSSOVER_SHAPES)} shapes from 1 x 4 KiB to 1 x 64 MiB; value = shapes "
+                    "(of both directions) where the kernel call takes no longer",
+        "max_wgs": g, "chunk_bytes": K.CHUNK_DEFAULT, "seed": 0}, dtype="u8")
+    line["shapes"] = rows
     line["parity"] = "bit-exact vs oracle"
     return line
 
@@ -1805,13 +1908,16 @@ def bench_interference(c: Ctx, args):
             table[m]["decode_ms_lost_per_burst"] = round(
                 (table[m]["gpu_ms_mean"] - table["none"]["gpu_ms_mean"]) * n_steps
                 / table[m]["bursts"], 3)
-    headline_mode = "32" if "32" in table else [m for m in table if m != "none"][0] \
-        if len(table) > 1 else "none"
+    # the line's value: the tail-bounded preset (the library's setting for
+    # copies beside latency-sensitive kernels) when it ran, else 32 per stream
+    headline_mode = next((m for m in ("tail", "32") if m in table),
+                         next((m for m in table if m != "none"), "none"))
     line = base_line(args, table[headline_mode]["gpu_ms_p99"], "ms", table["none"]["gpu_ms_mean"] / 1e3, {
         "workload": f"{decode_what} while a bidirectional "
                     "burst (16,384 x 4 KiB H2D + 16,384 x 4 KiB D2H) starts every 50 ms; value = "
                     f"decode step p99 ({'wall' if args.no_events else 'GPU'} time) in mode "
-                    f"{headline_mode} (an integer mode is max_wgs on two streams)",
+                    f"{headline_mode} (an integer mode is max_wgs on two streams; tail is "
+                    "KVCOPY_F_TAIL_BOUNDED on two streams)",
         "decode_steps_per_run": steps, "runs_per_mode": args.decode_runs, "seed": 0},
         dtype="bf16", higher=False)
     line["modes"] = table
@@ -1835,13 +1941,14 @@ def main():
     # at most 100 of their own steps (args.leg_warmup).
     ap.add_argument("--warmup", type=int, default=700)
     ap.add_argument("--max-wgs", type=parse_wgs, default=None,
-                    help=f"workgroup cap (default {DEFAULT_MAX_WGS}; pair: KVCOPY_WGS_AUTO); "
+                    help=f"workgroup cap (kv: {DEFAULT_MAX_WGS} per stream; mixed: {ONE_WAY_MAX_WGS}; "
+                         "pair: KVCOPY_WGS_AUTO); "
                          "kv only: H2D,D2H for a cap per direction")
-    ap.add_argument("--copy-cus", default="all", choices=["all", "halves"],
-                    help="CU masks of the two copy streams: every CU, or disjoint halves "
-                         "(each XCD keeps CUs for both)")
+    ap.add_argument("--copy-cus", default="halves", choices=["all", "halves"],
+                    help="kv: CU masks of the headline's two copy streams, disjoint halves "
+                         "(default; each XCD keeps CUs for both) or every CU")
     ap.add_argument("--workload", default="kv", choices=["kv", "pair", "d2d", "mixed", "moe",
-                                                         "interference"])
+                                                         "interference", "crossover"])
     ap.add_argument("--sweep", action="store_true", help="also sweep max_wgs per direction (stderr)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="time budget of the cpu_baseline sample")
@@ -1890,7 +1997,7 @@ def main():
         sys.exit(2)
     c = Ctx(args)
     fn = {"kv": bench_kv, "pair": bench_pair, "d2d": bench_d2d, "mixed": bench_mixed, "moe": bench_moe,
-          "interference": bench_interference}[args.workload]
+          "interference": bench_interference, "crossover": bench_crossover}[args.workload]
     line = fn(c, args)
     print(json.dumps(line), flush=True)
     c.close()

@@ -391,7 +391,8 @@ void kvcopy_job_destroy(kvcopy_job_t *job);
  * small startup probe and targeting bytes in flight rather than threads;
  * the vLLM PR #42212 report ("key source snippet", the tuned constants)
  * picks the smallest number of workers within a tolerance of peak
- * bandwidth.  This call does both on the current device: it allocates its
+ * bandwidth.  This call probes the current device and keeps a tolerance,
+ * but breaks ties the other way (below): it allocates its
  * own probe buffers (64 MiB of mapped pinned host memory and 64 MiB of
  * device memory per direction, freed before it returns), times 24 batches
  * of 16,384 shuffled 4 KiB blocks per direction at each cap of
@@ -400,10 +401,11 @@ void kvcopy_job_destroy(kvcopy_job_t *job);
  * as in a KV offload burst; D2D runs on s0), in three sweeps over the caps
  * (ascending, descending, ascending), and rates each cap by its median
  * sweep.  It records as the device's KVCOPY_WGS_AUTO cap for `dir` (for H2D
- * or D2H: for both) the smallest cap whose slowest sweep still reaches the
- * best cap's median rate.  On MI355X a 2% tolerance on the medians picked
- * 32 workgroups inside the window-to-window spread of two streams, which
- * then ran the burst 3% slower than 128.
+ * or D2H: for both) the largest cap whose median is within 1% of the best
+ * cap's and whose slowest sweep is within 3% of it.  Near-ties go to the
+ * larger grid: on MI355X, with two streams, 8 and 64 workgroups per stream
+ * rated within 0.6% of each other, but 8 later ran some 20-step windows of
+ * the burst 5-9% slower, 64 none.
  * Blocks until done (one to two seconds).
  * s0, s1: the streams the caller will copy on (the hardware queues they map
  *   to matter); NULL = streams created for the probe.
