@@ -1266,13 +1266,30 @@ def d2d_distinct(c: Ctx, args):
     nb = len(wl.batches)
     calls = max(4 * nb, args.steps)
 
-    def kernel_us(flags):
+    K = c.K
+    # each batch's descriptors sorted by destination address on the caller's
+    # side (the copy's result does not depend on the order: no destination
+    # overlaps another within a batch)
+    by_dst = []
+    for i in range(nb):
+        s_, d_ = r.addrs[i]
+        o = c.np.argsort(d_, kind="stable")
+        by_dst.append((s_[o], d_[o], wl.batches[i].size[o]))
+
+    def kernel_us(flags, sorted_=False):
         evs = [(hiprt.Event(), hiprt.Event()) for _ in range(calls)]
+
+        def call(i, **kw):
+            if sorted_:
+                s_, d_, z_ = by_dst[i]
+                K.kvcopy_batch(s_, d_, z_, W.D2D, 0, c.sA.cuda_stream, flags=flags, **kw)
+            else:
+                r.submit(i, 0, c.sA, flags=flags, **kw)
+
         for i in range(nb):
-            r.submit(i, 0, c.sA, flags=flags)
+            call(i)
         for i in range(calls):
-            r.submit(i % nb, 0, c.sA, flags=flags, kernel_begin=evs[i][0].h,
-                     kernel_end=evs[i][1].h)
+            call(i % nb, kernel_begin=evs[i][0].h, kernel_end=evs[i][1].h)
         hiprt.stream_sync(c.sA)
         return [e0.elapsed_ms(e1) * 1e3 for e0, e1 in evs]
 
@@ -1281,8 +1298,20 @@ def d2d_distinct(c: Ctx, args):
     t_list, t_dst = [], []
     for _ in range(2):
         t_list += kernel_us(0)
-        t_dst += kernel_us(c.K.F_DST_ORDER)
+        t_dst += kernel_us(K.F_DST_ORDER)
     us, us_dst = statistics.median(t_list), statistics.median(t_dst)
+    # where the records live and how the caller orders the list: records
+    # uploaded to device memory before each kernel (KVCOPY_F_DESC_UPLOAD),
+    # the list sorted by destination, and both, with either store form
+    variants = {"list_order_records_in_device_memory": (K.F_DESC_UPLOAD, False),
+                "sorted_by_destination": (0, True),
+                "sorted_by_destination_records_in_device_memory": (K.F_DESC_UPLOAD, True),
+                "sorted_by_destination_records_in_device_memory_sc1_stores":
+                    (K.F_DESC_UPLOAD | K.F_STORE_SC1, True)}
+    var_us = {name: [] for name in variants}
+    for _ in range(2):
+        for name, (fl, srt) in variants.items():
+            var_us[name] += kernel_us(fl, srt)
     pl = c.K.kvcopy_plan(*r.addrs[0], wl.batches[0].size)
     hbm = 2 * wl.batches[0].nbytes + pl.n_chunks * REC_BYTES
     ceiling = random_block_ceiling(c, r, wl, calls)
@@ -1291,6 +1320,13 @@ def d2d_distinct(c: Ctx, args):
         r.submit(i, 0, c.sA, flags=c.K.F_DST_ORDER)
     hiprt.stream_sync(c.sA)
     c.verify(wl, r, list(range(nb)), "d2d distinct calls, destination order")
+    r.fill()
+    for i in range(nb):
+        s_, d_, z_ = by_dst[i]
+        K.kvcopy_batch(s_, d_, z_, W.D2D, 0, c.sA.cuda_stream,
+                       flags=K.F_DESC_UPLOAD | K.F_STORE_SC1)
+    hiprt.stream_sync(c.sA)
+    c.verify(wl, r, list(range(nb)), "d2d distinct calls, sorted, uploaded records, sc1 stores")
     r.fill()
     for i in range(nb):
         r.submit(i, 0, c.sA)
@@ -1306,6 +1342,10 @@ def d2d_distinct(c: Ctx, args):
                                  "flag": "KVCOPY_F_DST_ORDER", "parity": "bit-exact vs oracle"},
            "random_block_ceiling": ceiling,
            "frac_random_block_ceiling": round(ceiling["us"] / us, 4)}
+    for name, v in var_us.items():
+        u = statistics.median(v)
+        out[name] = {"kernel_us_p50": round(u, 2), "hbm_GBps_kernel": round(gbs(hbm, u / 1e6), 1),
+                     "frac_hbm_peak_kernel": round(gbs(hbm, u / 1e6) / HBM_PEAK_GBS, 4)}
     log(f"  d2d distinct calls: {out} (bit-exact)")
     return out
 

@@ -74,6 +74,12 @@ int build_checked(const uint64_t *src, const uint64_t *dst, const uint64_t *size
 // kernel launch's queue packet among them).
 void finish_records();
 
+// Whether build_checked plans this list with its AVX2 path (runs of
+// single-chunk, non-adjacent descriptors four at a time): the host has AVX2
+// and the list's first 64 descriptors are mostly such runs.
+bool planner_vector_path(const uint64_t *src, const uint64_t *dst, const uint64_t *size, uint64_t n,
+                         bool merge, uint32_t chunk);
+
 // build_checked without the checks' result and without a cap (room for
 // Prescan::bound records); returns how many records it wrote.
 uint64_t build_worklist(const uint64_t *src, const uint64_t *dst, const uint64_t *size, uint64_t n,

@@ -116,6 +116,7 @@ int main(int argc, char **argv)
     // into outputs at every 8-byte offset within 32 bytes and with rooms
     // that end mid-list, plain and streamed; the records must equal the
     // step-by-step planner's.
+    int vector_lists = 0, block_lists = 0;
     for (int trial = 0; trial < trials; ++trial) {
         const uint64_t n = 5 + rng() % 2000;
         const uint32_t chunk = (rng() % 3 == 0) ? 4096 : 16384;
@@ -137,6 +138,8 @@ int main(int argc, char **argv)
             }
         }
         for (int merge = 0; merge < 2; ++merge) {
+            ++block_lists;
+            vector_lists += planner_vector_path(s.data(), d.data(), z.data(), n, merge, chunk);
             std::vector<uint64_t> ms(n + 1), md(n + 1), mz(n + 1), mb(n + 2);
             uint64_t m = 0, total = 0;
             const int mrc = merge_ranges(s.data(), d.data(), z.data(), n, merge, ms.data(), md.data(),
@@ -175,6 +178,28 @@ int main(int argc, char **argv)
                     }
             }
             ++cases;
+        }
+    }
+    // On an AVX2 host most of these lists must take the vector path, or the
+    // block above would not test it.
+    if (__builtin_cpu_supports("avx2") && vector_lists * 2 < block_lists) {
+        printf("fast path: only %d of %d block lists took the vector path\n", vector_lists,
+               block_lists);
+        return 1;
+    }
+    // Mixed sizes with merges (the H2D mixed-size workload's shape) take the
+    // scalar pass.
+    {
+        std::vector<uint64_t> s(4096), d(4096), z(4096);
+        for (uint64_t i = 0; i < 4096; ++i) {
+            z[i] = 8 * (512 + rng() % 3072);                  // 4-28 KiB
+            const bool cont = i > 0 && rng() % 4 == 0;
+            s[i] = cont ? s[i - 1] + z[i - 1] : (1ull << 36) + (rng() % (1u << 20)) * 32768;
+            d[i] = cont ? d[i - 1] + z[i - 1] : (1ull << 40) + (rng() % (1u << 20)) * 32768;
+        }
+        if (planner_vector_path(s.data(), d.data(), z.data(), 4096, true, 16384)) {
+            printf("fast path: a mixed-size list with merges took the vector path\n");
+            return 1;
         }
     }
     // The default copy-loop choice: pipelined only for D2D grids of at most
