@@ -1118,10 +1118,14 @@ def d2d_results(c: Ctx, args):
                 "d2d_1024x4KiB")
         else:
             cl = c_caller_latency([("d2d_65536x4KiB", wld, 0),
-                                   ("d2d_65536x4KiB_dst_order", wld, 0, K.F_DST_ORDER)])
+                                   ("d2d_65536x4KiB_dst_order", wld, 0, K.F_DST_ORDER),
+                                   ("d2d_65536x4KiB_wg_dst_order_upload", wld, 0,
+                                    K.F_DST_ORDER | K.F_DESC_UPLOAD | K.F_WG_PER_CHUNK)])
             out[name]["latency_c_caller"] = cl.get("d2d_65536x4KiB", cl.get("error"))
             out[name]["latency_c_caller_dst_order"] = cl.get("d2d_65536x4KiB_dst_order",
                                                              cl.get("error"))
+            out[name]["latency_c_caller_wg_dst_order_upload"] = cl.get(
+                "d2d_65536x4KiB_wg_dst_order_upload", cl.get("error"))
         log(f"  d2d {name}: {out[name]} (bit-exact)")
         r.free()
     big = torch.empty(2 << 30, dtype=torch.uint8, device=c.dev)
@@ -1303,11 +1307,19 @@ def d2d_distinct(c: Ctx, args):
     # where the records live and how the caller orders the list: records
     # uploaded to device memory before each kernel (KVCOPY_F_DESC_UPLOAD),
     # the list sorted by destination, and both, with either store form
+    # and the workgroup-per-chunk loop (KVCOPY_F_WG_PER_CHUNK), which reads
+    # each chunk's record in its workgroup and so wants them in device memory
+    WG = K.F_WG_PER_CHUNK | K.F_DESC_UPLOAD
     variants = {"list_order_records_in_device_memory": (K.F_DESC_UPLOAD, False),
                 "sorted_by_destination": (0, True),
                 "sorted_by_destination_records_in_device_memory": (K.F_DESC_UPLOAD, True),
                 "sorted_by_destination_records_in_device_memory_sc1_stores":
-                    (K.F_DESC_UPLOAD | K.F_STORE_SC1, True)}
+                    (K.F_DESC_UPLOAD | K.F_STORE_SC1, True),
+                "wg_per_chunk_records_in_device_memory": (WG, False),
+                "wg_per_chunk_destination_order_records_in_device_memory": (WG | K.F_DST_ORDER, False),
+                "wg_per_chunk_sorted_by_destination_records_in_device_memory": (WG, True),
+                "wg_per_chunk_sorted_by_destination_records_in_device_memory_sc1_stores":
+                    (WG | K.F_STORE_SC1, True)}
     var_us = {name: [] for name in variants}
     for _ in range(2):
         for name, (fl, srt) in variants.items():
@@ -1329,6 +1341,24 @@ def d2d_distinct(c: Ctx, args):
     c.verify(wl, r, list(range(nb)), "d2d distinct calls, sorted, uploaded records, sc1 stores")
     r.fill()
     for i in range(nb):
+        r.submit(i, 0, c.sA, flags=WG | K.F_DST_ORDER)
+    hiprt.stream_sync(c.sA)
+    c.verify(wl, r, list(range(nb)), "d2d distinct calls, workgroup per chunk, destination order")
+    # back-to-back calls in the workgroup mode, the record upload included:
+    # GPU time per call between two events around all calls
+    e0, e1 = hiprt.Event(), hiprt.Event()
+    per_call = {}
+    for name, fl in (("list_order_default", 0),
+                     ("wg_per_chunk_destination_order_records_uploaded", WG | K.F_DST_ORDER)):
+        for i in range(nb):
+            r.submit(i, 0, c.sA, flags=fl)
+        e0.record(c.sA)
+        for i in range(calls):
+            r.submit(i % nb, 0, c.sA, flags=fl)
+        e1.record(c.sA)
+        per_call[name] = round(e0.elapsed_ms(e1) * 1e3 / calls, 2)
+    r.fill()
+    for i in range(nb):
         r.submit(i, 0, c.sA)
     hiprt.stream_sync(c.sA)
     c.verify(wl, r, list(range(nb)), "d2d distinct calls")
@@ -1342,6 +1372,7 @@ def d2d_distinct(c: Ctx, args):
                                  "flag": "KVCOPY_F_DST_ORDER", "parity": "bit-exact vs oracle"},
            "random_block_ceiling": ceiling,
            "frac_random_block_ceiling": round(ceiling["us"] / us, 4)}
+    out["gpu_us_per_call_back_to_back"] = per_call
     for name, v in var_us.items():
         u = statistics.median(v)
         out[name] = {"kernel_us_p50": round(u, 2), "hbm_GBps_kernel": round(gbs(hbm, u / 1e6), 1),

@@ -148,6 +148,12 @@ hipError_t launch_copy_pair(const ChunkRec *ra, uint32_t ca, const ChunkRec *rb,
                             uint32_t grid, bool sc1_stores, hipStream_t stream, hipEvent_t start,
                             hipEvent_t stop);
 
+// KVCOPY_F_WG_PER_CHUNK: `grid` workgroups; workgroup g copies chunks g,
+// g + grid, ..., its four wavefronts sharing each chunk.  sc1_stores, start
+// and stop as for launch_copy.
+hipError_t launch_copy_wg(const ChunkRec *recs, uint32_t n_chunks, uint32_t grid, int dir,
+                          bool sc1_stores, hipStream_t stream, hipEvent_t start, hipEvent_t stop);
+
 // KVCOPY_F_DYNAMIC: the per-chunk loop with chunks claimed at run time.
 // claim points at two zeroed device counters (next chunk, wavefronts done);
 // every wavefront claims `grain` chunks at a time with an atomic add, one
@@ -173,6 +179,17 @@ static_assert(KVCOPY_MAX_CHUNKS + (uint64_t)kMaxGrid * kWavesPerWG * 64 < (1ull 
 inline uint32_t grid_for(uint64_t n_chunks, int max_wgs)
 {
     uint64_t g = (n_chunks + kWavesPerWG - 1) / kWavesPerWG;   // one wavefront per chunk
+    if (max_wgs != 0 /* KVCOPY_WGS_ALL */ && (uint64_t)max_wgs < g)
+        g = (uint64_t)max_wgs;
+    return (uint32_t)(g < kMaxGrid ? g : kMaxGrid);
+}
+
+// Workgroups for the workgroup-per-chunk loop: one per chunk at most, and at
+// most kMaxGrid (workgroups then stride over the chunks, so a capped grid
+// still copies every chunk; c + grid stays below 2^32 for c < 2^31).
+inline uint32_t grid_for_wg(uint64_t n_chunks, int max_wgs)
+{
+    uint64_t g = n_chunks;
     if (max_wgs != 0 /* KVCOPY_WGS_ALL */ && (uint64_t)max_wgs < g)
         g = (uint64_t)max_wgs;
     return (uint32_t)(g < kMaxGrid ? g : kMaxGrid);

@@ -349,6 +349,76 @@ __device__ __forceinline__ void copy_worklist_dynamic(const ChunkRec *__restrict
     }
 }
 
+// ---- one workgroup per chunk ------------------------------------------------------
+//
+// Workgroup g of G copies chunks g, g + G, g + 2G, ...; its four wavefronts
+// share each chunk: thread t moves the 16-byte words at t*16 + k*4 KiB, so a
+// 4 KiB chunk is one load and one store per thread and a 16 KiB chunk four
+// of each, all loads first.  The chunk's record is read by the workgroup
+// itself (wave-uniform), just before its data: with the worklist in device
+// memory and in destination order, the workgroups that the dispatcher
+// starts together move whole blocks of a narrow band of memory.  Measured
+// on MI355X with 65,536 random 4 KiB blocks between two 1 GiB pools (calls
+// over 8 distinct batches, records in device memory): 95.6 us per kernel
+// sorted by destination against 102.7 us with one wavefront per chunk.
+constexpr uint32_t kWgRowBytes = kThreadsPerWG * 16u;   // one access per thread: 4 KiB
+constexpr int kWgMaxRows = 4;                           // 16 KiB per pass
+
+template <int R, int SP>
+__device__ __forceinline__ void copy_wg_rows(__amdgpu_buffer_rsrc_t rs, __amdgpu_buffer_rsrc_t rd,
+                                             uint32_t voff)
+{
+    v4u v[R];
+#pragma unroll
+    for (int j = 0; j < R; ++j)
+        v[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(voff + j * kWgRowBytes), 0,
+                                                     kLoadPolicy);
+#pragma unroll
+    for (int j = 0; j < R; ++j)
+        __builtin_amdgcn_raw_buffer_store_b128(v[j], rd, (int)(voff + j * kWgRowBytes), 0, SP);
+}
+
+// The whole workgroup copies one chunk.  src, dst and bytes are uniform.  As
+// in copy_chunk, the buffer ranges end at the chunk's last whole 16-byte
+// word, so the threads past the end of a short row need no masking, and an
+// odd trailing 8-byte word is moved by thread 0.
+template <int SP>
+__device__ __forceinline__ void copy_chunk_wg(uint64_t src, uint64_t dst, uint32_t bytes)
+{
+    const uint32_t body = bytes & ~15u;
+    const __amdgpu_buffer_rsrc_t rs = rsrc_u(src, body);
+    const __amdgpu_buffer_rsrc_t rd = rsrc_u(dst, body);
+    const uint32_t t16 = threadIdx.x * 16u;
+    for (uint32_t off = 0; off < body; off += kWgRowBytes * kWgMaxRows) {
+        const uint32_t left = body - off;
+        switch (left >= kWgRowBytes * (kWgMaxRows - 1) + 1 ? kWgMaxRows
+                                                           : (left + kWgRowBytes - 1) / kWgRowBytes) {
+        case 1: copy_wg_rows<1, SP>(rs, rd, off + t16); break;
+        case 2: copy_wg_rows<2, SP>(rs, rd, off + t16); break;
+        case 3: copy_wg_rows<3, SP>(rs, rd, off + t16); break;
+        default: copy_wg_rows<4, SP>(rs, rd, off + t16); break;
+        }
+    }
+    if ((bytes & 8u) && threadIdx.x == 0) {   // a range that ends in an odd 8-byte word
+        const uint64_t w = *reinterpret_cast<KVC_GLOBAL const uint64_t *>(src + body);
+        __builtin_nontemporal_store(w, reinterpret_cast<KVC_GLOBAL uint64_t *>(dst + body));
+    }
+}
+
+template <int SP>
+__device__ __forceinline__ void copy_worklist_wg(const ChunkRec *__restrict__ recs,
+                                                 uint32_t n_chunks)
+{
+    // c + gridDim.x cannot wrap: n_chunks <= 2^31 and gridDim.x <= 2^22
+    for (uint32_t c = blockIdx.x; c < n_chunks; c += gridDim.x) {
+        const KVC_GLOBAL uint64_t *p =
+            (const KVC_GLOBAL uint64_t *)reinterpret_cast<uintptr_t>(recs + c);
+        const uint64_t s = uniform64(p[0]), d = uniform64(p[1]);
+        const uint32_t b = __builtin_amdgcn_readfirstlane((uint32_t)p[2]);
+        copy_chunk_wg<SP>(s, d, b);
+    }
+}
+
 // ---- two worklists in one launch -------------------------------------------------
 //
 // kvcopy_batch_pair: two worklists (typically an H2D burst and a D2H burst)
@@ -422,6 +492,20 @@ KVC_PIPE_KERNEL(kvcopy_d2h_pipe_kernel)
 KVC_PIPE_KERNEL(kvcopy_d2d_pipe_kernel)
 #undef KVC_PIPE_KERNEL
 
+#define KVC_WG_KERNEL(name, SP)                                                                    \
+    __global__ __launch_bounds__(kThreadsPerWG) void name(const ChunkRec *__restrict__ recs,     \
+                                                          uint32_t n_chunks)                     \
+    {                                                                                              \
+        copy_worklist_wg<SP>(recs, n_chunks);                                                      \
+    }
+KVC_WG_KERNEL(kvcopy_h2d_wg_kernel, kStorePolicy)
+KVC_WG_KERNEL(kvcopy_d2h_wg_kernel, kStorePolicy)
+KVC_WG_KERNEL(kvcopy_d2d_wg_kernel, kStorePolicy)
+KVC_WG_KERNEL(kvcopy_h2d_wg_sc1_kernel, kSc1StorePolicy)
+KVC_WG_KERNEL(kvcopy_d2h_wg_sc1_kernel, kSc1StorePolicy)
+KVC_WG_KERNEL(kvcopy_d2d_wg_sc1_kernel, kSc1StorePolicy)
+#undef KVC_WG_KERNEL
+
 #define KVC_PAIR_KERNEL(name, SP)                                                                  \
     __global__ __launch_bounds__(kThreadsPerWG) void name(                                         \
         const ChunkRec *__restrict__ ra, uint32_t ca, const ChunkRec *__restrict__ rb, uint32_t cb, \
@@ -483,6 +567,21 @@ hipError_t launch_copy(const ChunkRec *recs, uint32_t n_chunks, uint32_t grid, i
     void *args[] = {(void *)&recs, (void *)&n_chunks, (void *)&pace};
     return hipExtLaunchKernel(per_chunk[sc1_stores ? 1 : 0][dir], dim3(grid), dim3(kThreadsPerWG),
                               args, 0, stream, start, stop, 0);
+}
+
+hipError_t launch_copy_wg(const ChunkRec *recs, uint32_t n_chunks, uint32_t grid, int dir,
+                          bool sc1_stores, hipStream_t stream, hipEvent_t start, hipEvent_t stop)
+{
+    static const void *const fns[2][3] = {
+        {reinterpret_cast<const void *>(&kvcopy_h2d_wg_kernel),
+         reinterpret_cast<const void *>(&kvcopy_d2h_wg_kernel),
+         reinterpret_cast<const void *>(&kvcopy_d2d_wg_kernel)},
+        {reinterpret_cast<const void *>(&kvcopy_h2d_wg_sc1_kernel),
+         reinterpret_cast<const void *>(&kvcopy_d2h_wg_sc1_kernel),
+         reinterpret_cast<const void *>(&kvcopy_d2d_wg_sc1_kernel)}};
+    void *args[] = {(void *)&recs, (void *)&n_chunks};
+    return hipExtLaunchKernel(fns[sc1_stores ? 1 : 0][dir], dim3(grid), dim3(kThreadsPerWG), args,
+                              0, stream, start, stop, 0);
 }
 
 hipError_t launch_copy_pair(const ChunkRec *ra, uint32_t ca, const ChunkRec *rb, uint32_t cb,

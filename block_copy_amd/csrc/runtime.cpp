@@ -346,7 +346,13 @@ int run_locked(Staging *st, int device, const uint64_t *src, const uint64_t *dst
     }
     const uint32_t grid = grid_for(n_chunks, max_wgs);
     hipEvent_t start = timed ? o.ev_begin : nullptr, stop = timed ? o.ev_end : done;
-    if (dynamic) {
+    if (flags & KVCOPY_F_WG_PER_CHUNK) {
+        int sc1 = forced_store(flags);
+        if (sc1 < 0)
+            sc1 = dir == KVCOPY_D2H;
+        e = launch_copy_wg(recs, (uint32_t)n_chunks, grid_for_wg(n_chunks, max_wgs), dir, sc1 != 0,
+                           stream, start, stop);
+    } else if (dynamic) {
         uint32_t *claim = st->claims + off / kAlign * 2;
         const uint32_t g = grid < kDynMaxGrid ? grid : kDynMaxGrid;
         e = launch_copy_dynamic(recs, (uint32_t)n_chunks, g, dir, claim, claim_grain(n_chunks, g),
@@ -499,20 +505,21 @@ extern "C" int kvcopy_batch_ex(const uint64_t *src_addrs, const uint64_t *dst_ad
         const uint32_t known = KVCOPY_F_VALIDATE | KVCOPY_F_NO_COALESCE | KVCOPY_F_DESC_UPLOAD |
                                KVCOPY_F_PIPELINE | KVCOPY_F_PER_CHUNK | KVCOPY_F_DYNAMIC |
                                KVCOPY_F_STORE_SC1 | KVCOPY_F_STORE_NT | KVCOPY_F_DST_ORDER |
-                               KVCOPY_F_TAIL_BOUNDED;
+                               KVCOPY_F_TAIL_BOUNDED | KVCOPY_F_WG_PER_CHUNK;
         if (opts->flags & ~known)
             return KVCOPY_EINVAL;
-        const uint32_t loops = opts->flags & (KVCOPY_F_PIPELINE | KVCOPY_F_PER_CHUNK | KVCOPY_F_DYNAMIC);
+        const uint32_t loops = opts->flags & (KVCOPY_F_PIPELINE | KVCOPY_F_PER_CHUNK |
+                                              KVCOPY_F_DYNAMIC | KVCOPY_F_WG_PER_CHUNK);
         if (loops & (loops - 1))   // more than one loop forced
             return KVCOPY_EINVAL;
         const uint32_t stores = opts->flags & (KVCOPY_F_STORE_SC1 | KVCOPY_F_STORE_NT);
         if (stores == (KVCOPY_F_STORE_SC1 | KVCOPY_F_STORE_NT) ||
             (stores && (opts->flags & (KVCOPY_F_PIPELINE | KVCOPY_F_DYNAMIC))))
-            return KVCOPY_EINVAL;   // store forms exist for the per-chunk loop only
+            return KVCOPY_EINVAL;   // store forms exist for the per-chunk and workgroup loops
         if (opts->struct_size == sizeof(kvcopy_opts_t) && opts->duty_period_ns != 0) {
             if (opts->duty_on_ns < 1000 || opts->duty_on_ns > opts->duty_period_ns ||
                 opts->duty_period_ns > 10000000u ||
-                (opts->flags & (KVCOPY_F_PIPELINE | KVCOPY_F_DYNAMIC)))
+                (opts->flags & (KVCOPY_F_PIPELINE | KVCOPY_F_DYNAMIC | KVCOPY_F_WG_PER_CHUNK)))
                 return KVCOPY_EINVAL;
             o.duty_on_ns = opts->duty_on_ns;
             o.duty_period_ns = opts->duty_period_ns;
@@ -521,7 +528,7 @@ extern "C" int kvcopy_batch_ex(const uint64_t *src_addrs, const uint64_t *dst_ad
         o.ev_begin = opts->kernel_begin;
         o.ev_end = opts->kernel_end;
         if (o.flags & KVCOPY_F_TAIL_BOUNDED) {
-            if (o.flags & (KVCOPY_F_PIPELINE | KVCOPY_F_DYNAMIC))
+            if (o.flags & (KVCOPY_F_PIPELINE | KVCOPY_F_DYNAMIC | KVCOPY_F_WG_PER_CHUNK))
                 return KVCOPY_EINVAL;
             if (!(o.flags & KVCOPY_F_STORE_NT))
                 o.flags |= KVCOPY_F_STORE_SC1;
@@ -578,7 +585,7 @@ extern "C" int kvcopy_batch_ex(const uint64_t *src_addrs, const uint64_t *dst_ad
     // unused tail is not committed.
     uint64_t hint = n <= KVCOPY_MAX_DESCS / 2 ? 2 * n : n;
     const uint32_t ring_only = KVCOPY_F_DESC_UPLOAD | KVCOPY_F_PIPELINE | KVCOPY_F_DYNAMIC |
-                               KVCOPY_F_DST_ORDER;
+                               KVCOPY_F_DST_ORDER | KVCOPY_F_WG_PER_CHUNK;
     if (n <= kInlineRecs && !(o.flags & ring_only) && o.duty_period_ns == 0) {
         const int rc = run_inline(st, src_addrs, dst_addrs, sizes, n, dir, max_wgs, stream, o,
                                   &hint);

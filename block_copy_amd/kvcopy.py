@@ -26,6 +26,7 @@ CHUNK_MAX = 1 << 20
 F_VALIDATE, F_NO_COALESCE, F_DESC_UPLOAD = 0x1, 0x2, 0x8
 F_PIPELINE, F_PER_CHUNK, F_DYNAMIC = 0x10, 0x20, 0x40
 F_STORE_SC1, F_STORE_NT, F_DST_ORDER, F_TAIL_BOUNDED = 0x80, 0x100, 0x200, 0x400
+F_WG_PER_CHUNK = 0x800
 OPTS_V1_SIZE = 32
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvcopy.so")

@@ -7,6 +7,8 @@
 - per-chunk forced where the default would pick the pipelined loop;
 - dynamic claims (KVCOPY_F_DYNAMIC): chunks claimed with device atomics,
   counters reset by each kernel's last wavefront;
+- one workgroup per chunk (KVCOPY_F_WG_PER_CHUNK): the four wavefronts of a
+  workgroup share each chunk;
 - inline worklists (the default for batches of at most 128 chunks): the
   records travel in the kernel arguments.
 Every case reads the touched arenas back whole (guard bytes included) and
@@ -191,6 +193,74 @@ def test_dynamic_d2d_large(K):
         res.fill()
         _run(res, [0], max_wgs, flags=K.F_DYNAMIC)
         _check(res, [0], f"dynamic d2d 65536 max_wgs={max_wgs}")
+    res.free()
+
+
+# ---------------------------------------------------------------------------
+# One workgroup per chunk (KVCOPY_F_WG_PER_CHUNK): the four wavefronts of a
+# workgroup share each chunk, 4 KiB rows, the record read by the workgroup
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dname", sorted(DIRS))
+@pytest.mark.parametrize("chunk", [16, 1024, 4096, 16384, 1 << 20])
+def test_wg_per_chunk_irregular(K, dname, chunk):
+    """Chunks shorter than a 4 KiB row, rows cut short, passes of 16 KiB,
+    8-byte tails, src != dst mod 16, zero sizes; grids below and at the chunk
+    count, the worklist in pinned memory, uploaded and in destination order,
+    in both store forms."""
+    from block_copy_amd.harness import Resident
+    d, sw, dw = DIRS[dname]
+    wl = W.irregular(seed=chunk % 97 + 5, n=300, max_size=min(80 * 1024, 256 * chunk), dir_=d,
+                     src_where=sw, dst_where=dw, misalign=True, zero_frac=0.05)
+    res = Resident(wl)
+    for max_wgs, extra in ((1, 0), (7, K.F_DESC_UPLOAD), (0, 0),
+                           (0, K.F_DESC_UPLOAD | K.F_STORE_SC1), (5, K.F_DST_ORDER | K.F_STORE_NT)):
+        _say("wg-per-chunk irregular", dname, "chunk", chunk, "max_wgs", max_wgs, "flags", extra)
+        res.fill()
+        _run(res, [0], max_wgs, chunk_bytes=chunk, flags=K.F_WG_PER_CHUNK | extra)
+        _check(res, [0], f"wg-per-chunk irregular {dname} chunk={chunk} max_wgs={max_wgs} "
+                         f"flags={extra}")
+    res.free()
+
+
+@pytest.mark.parametrize("max_wgs", [1, 64, 0])
+def test_wg_per_chunk_d2d_blocks(K, max_wgs):
+    from block_copy_amd.harness import Resident
+    wl = W.d2d_blocks(seed=0)
+    res = Resident(wl)
+    for sentinel in (W.SENTINEL_A, W.SENTINEL_B):
+        for extra in (0, K.F_DESC_UPLOAD | K.F_DST_ORDER):
+            _say("wg-per-chunk d2d 1024x4KiB max_wgs", max_wgs, "flags", extra, "sentinel",
+                 hex(sentinel))
+            res.fill(sentinel)
+            _run(res, [0], max_wgs, flags=K.F_WG_PER_CHUNK | extra)
+            _check(res, [0], f"wg-per-chunk d2d max_wgs={max_wgs} flags={extra}", sentinel)
+    res.free()
+
+
+def test_wg_per_chunk_d2d_large(K):
+    """65,536 x 4 KiB between two 1 GiB pools: one workgroup per chunk, and a
+    capped grid whose workgroups stride over the chunks."""
+    from block_copy_amd.harness import Resident
+    wl = W.d2d_blocks(seed=1, n=65536, pool_blocks=262144)
+    res = Resident(wl)
+    for max_wgs in (0, 4096):
+        _say("wg-per-chunk d2d 65536x4KiB max_wgs", max_wgs)
+        res.fill()
+        _run(res, [0], max_wgs, flags=K.F_WG_PER_CHUNK | K.F_DESC_UPLOAD | K.F_DST_ORDER)
+        _check(res, [0], f"wg-per-chunk d2d 65536 max_wgs={max_wgs}")
+    res.free()
+
+
+@pytest.mark.parametrize("max_wgs", [8, 0])
+def test_wg_per_chunk_kv_concurrent(K, max_wgs):
+    from block_copy_amd.harness import Resident
+    wl = W.kv_blocks(seed=6, directions="both")
+    res = Resident(wl)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    _say("wg-per-chunk kv both max_wgs", max_wgs)
+    _run(res, [0, 1], max_wgs, streams=[s1, s2], flags=K.F_WG_PER_CHUNK)
+    _check(res, [0, 1], f"wg-per-chunk h2d+d2h max_wgs={max_wgs}")
     res.free()
 
 

@@ -26,7 +26,8 @@ def K():
 def test_random_batches(K, block):
     from block_copy_amd.harness import Resident
     flag_set = [0, 0, K.F_PIPELINE, K.F_PER_CHUNK, K.F_DYNAMIC, K.F_DESC_UPLOAD,
-                K.F_NO_COALESCE, K.F_VALIDATE, K.F_DYNAMIC | K.F_DESC_UPLOAD]
+                K.F_NO_COALESCE, K.F_VALIDATE, K.F_DYNAMIC | K.F_DESC_UPLOAD, K.F_WG_PER_CHUNK,
+                K.F_WG_PER_CHUNK | K.F_DESC_UPLOAD | K.F_DST_ORDER]
     streams = [None, torch.cuda.Stream()]
     for seed in range(block * 30, block * 30 + 30):
         rng = np.random.default_rng(10_000 + seed)

@@ -63,7 +63,8 @@ def test_kernels_have_no_scratch_or_spills(K, src):
     names = set(re.findall(r"\.name:\s+_ZN3kvc12_GLOBAL__N_1\d+(kvcopy_\w+?_kernel)E", txt))
     if src == "kvcopy_kernel.hip":
         want = {f"kvcopy_{d}{v}_kernel" for d in ("h2d", "d2h", "d2d")
-                for v in ("", "_sc1", "_pipe", "_dyn", "_inline", "_inline_sc1")} | {
+                for v in ("", "_sc1", "_pipe", "_dyn", "_inline", "_inline_sc1", "_wg",
+                          "_wg_sc1")} | {
                     "kvcopy_pair_kernel", "kvcopy_pair_nt_kernel"}
     else:
         want = {"kvcopy_device_plan_kernel", "kvcopy_device_copy_kernel"}
@@ -159,7 +160,7 @@ def test_batch_argument_errors(K):
     assert call(s, d, z, K.H2D, -2) == K.EINVAL
     assert call(s, d, z, K.H2D, chunk_bytes=24) == K.EINVAL        # chunk not a multiple of 16
     assert call(s, d, z, K.H2D, chunk_bytes=(1 << 20) + 16) == K.EINVAL
-    assert call(s, d, z, K.H2D, flags=0x800) == K.EINVAL          # unknown flag
+    assert call(s, d, z, K.H2D, flags=0x1000) == K.EINVAL         # unknown flag
     assert call(s, d, z, K.H2D, flags=K.F_TAIL_BOUNDED | K.F_PIPELINE) == K.EINVAL
     assert call(s, d, z, K.H2D, flags=K.F_TAIL_BOUNDED | K.F_DYNAMIC) == K.EINVAL
     assert call(s, d, z, K.H2D, -5, flags=K.F_TAIL_BOUNDED) == K.EINVAL
@@ -168,6 +169,13 @@ def test_batch_argument_errors(K):
     assert call(s, d, z, K.H2D, flags=K.F_PIPELINE | K.F_PER_CHUNK) == K.EINVAL  # two loops forced
     assert call(s, d, z, K.H2D, flags=K.F_DYNAMIC | K.F_PIPELINE) == K.EINVAL
     assert call(s, d, z, K.H2D, flags=K.F_DYNAMIC | K.F_PER_CHUNK) == K.EINVAL
+    assert call(s, d, z, K.D2D, flags=K.F_WG_PER_CHUNK | K.F_PIPELINE) == K.EINVAL
+    assert call(s, d, z, K.D2D, flags=K.F_WG_PER_CHUNK | K.F_DYNAMIC) == K.EINVAL
+    assert call(s, d, z, K.D2D, flags=K.F_WG_PER_CHUNK | K.F_PER_CHUNK) == K.EINVAL
+    assert call(s, d, z, K.D2D, flags=K.F_WG_PER_CHUNK | K.F_TAIL_BOUNDED) == K.EINVAL
+    assert call(s, d, z, K.D2D, duty_on_ns=5000, duty_period_ns=20000,
+                flags=K.F_WG_PER_CHUNK) == K.EINVAL
+    assert call(s, d, z + 4, K.D2D, flags=K.F_WG_PER_CHUNK | K.F_STORE_SC1) == K.EALIGN  # accepted
     # store forms: one at a time, for the per-chunk loop only
     assert call(s, d, z, K.H2D, flags=K.F_STORE_SC1 | K.F_STORE_NT) == K.EINVAL
     assert call(s, d, z, K.H2D, flags=K.F_STORE_SC1 | K.F_PIPELINE) == K.EINVAL
