@@ -10,8 +10,8 @@
 // link, with vector loads of 64 records at a time: the worklist crosses the
 // link once, as part of the kernel's own traffic, with no separate copy and
 // no copy-engine latency in front of the kernel.  (KVCOPY_F_DESC_UPLOAD
-// instead copies it into a device twin of the ring with hipMemcpyAsync on
-// the caller's stream.)
+// instead copies it into a device twin of the ring with hipMemcpyAsync on a
+// stream of the library's own, which the caller's stream waits for.)
 //
 // The vLLM PR #42212 report, section "review highlights", points out that
 // descriptor buffers must be pinned for the transfer to be asynchronous, and
@@ -80,6 +80,11 @@ struct Staging {
     uint32_t *claims = nullptr;
     int clock_khz = 0;             // wall-clock rate (hipDeviceAttributeWallClockRate), 0 = not read yet
     std::vector<ChunkRec> order_tmp;   // KVCOPY_F_DST_ORDER: the worklist in list order
+    // KVCOPY_F_DESC_UPLOAD: the worklist copies run on a stream of the
+    // library's own (default priority), created on first use; the caller's
+    // stream waits for each copy through `up_done` before its kernel.
+    hipStream_t up_stream = nullptr;
+    hipEvent_t up_done = nullptr;
     std::vector<hipEvent_t> spare;
     StagingRing<hipEvent_t, HipEventOps> ring{HipEventOps{&spare}};
 };
@@ -322,9 +327,27 @@ int run_locked(Staging *st, int device, const uint64_t *src, const uint64_t *dst
     const ChunkRec *recs = host;   // read in place: mapped at the same address on the device
     hipError_t e;
     if (upload) {
+        // The copy depends only on the host having written the region, so it
+        // runs on the library's own stream and overlaps whatever the caller's
+        // stream is still running (the previous call's kernel, in a train of
+        // calls); the caller's stream waits for it before the kernel.  The
+        // region's device twin is free: the ring hands a region out again
+        // only after its last kernel, which waited for its copy, completed.
+        if (st->up_stream == nullptr) {
+            if ((e = hipStreamCreateWithFlags(&st->up_stream, hipStreamNonBlocking)) != hipSuccess) {
+                st->up_stream = nullptr;
+                return hip_fail(e);
+            }
+            if ((e = hipEventCreateWithFlags(&st->up_done, hipEventDisableTiming)) != hipSuccess) {
+                st->up_done = nullptr;
+                return hip_fail(e);
+            }
+        }
         ChunkRec *dev = reinterpret_cast<ChunkRec *>(st->dev + off);
         if ((e = hipMemcpyAsync(dev, host, n_chunks * sizeof(ChunkRec), hipMemcpyHostToDevice,
-                                stream)) != hipSuccess)
+                                st->up_stream)) != hipSuccess ||
+            (e = hipEventRecord(st->up_done, st->up_stream)) != hipSuccess ||
+            (e = hipStreamWaitEvent(stream, st->up_done, 0)) != hipSuccess)
             return hip_fail(e);
         recs = dev;
     }
