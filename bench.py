@@ -1275,22 +1275,31 @@ def d2d_distinct(c: Ctx, args):
     r = c.Resident(wl)
     nb = len(wl.batches)
     if args.no_events:
-        # profiler runs: the workgroup-per-chunk mode with uploaded records in
-        # destination order over the rotation, timed by the kernel trace (its
-        # kernel runs nowhere else in a profiled D2D leg), parity-checked
-        fl = c.K.F_WG_PER_CHUNK | c.K.F_DESC_UPLOAD | c.K.F_DST_ORDER
+        # profiler runs: the fastest mode of the timed runs over the rotation
+        # (each batch sorted by destination, one workgroup per chunk, records
+        # uploaded, sc1 stores), timed by the kernel trace (its kernel,
+        # kvcopy_d2d_wg_sc1_kernel, runs nowhere else in a profiled D2D leg),
+        # parity-checked
+        K = c.K
+        fl = K.F_WG_PER_CHUNK | K.F_DESC_UPLOAD | K.F_STORE_SC1
         calls = max(4 * nb, args.steps)
+        srt = []
+        for i in range(nb):
+            s_, d_ = r.addrs[i]
+            o = c.np.argsort(d_, kind="stable")
+            srt.append((s_[o], d_[o], wl.batches[i].size[o]))
         r.fill()
         for i in range(nb):
-            r.submit(i, 0, c.sA, flags=fl)
+            K.kvcopy_batch(*srt[i], W.D2D, 0, c.sA.cuda_stream, flags=fl)
         hiprt.stream_sync(c.sA)
         c.verify(wl, r, list(range(nb)), "d2d distinct calls, workgroup per chunk")
         for i in range(calls):
-            r.submit(i % nb, 0, c.sA, flags=fl)
+            K.kvcopy_batch(*srt[i % nb], W.D2D, 0, c.sA.cuda_stream, flags=fl)
         hiprt.stream_sync(c.sA)
         r.free()
-        return {"calls": calls, "mode": "KVCOPY_F_WG_PER_CHUNK | KVCOPY_F_DESC_UPLOAD | "
-                "KVCOPY_F_DST_ORDER", "timed_by": "the kernel trace (kvcopy_d2d_wg_kernel)"}
+        return {"calls": calls, "mode": "each batch sorted by destination; KVCOPY_F_WG_PER_CHUNK | "
+                "KVCOPY_F_DESC_UPLOAD | KVCOPY_F_STORE_SC1",
+                "timed_by": "the kernel trace (kvcopy_d2d_wg_sc1_kernel)"}
     calls = max(4 * nb, args.steps)
 
     K = c.K
