@@ -200,6 +200,8 @@ class Ctx:
         when the last one does."""
         if self.args.desc_upload:
             kw["flags"] = kw.get("flags", 0) | self.K.F_DESC_UPLOAD
+        if getattr(self.args, "flags", 0):
+            kw["flags"] = kw.get("flags", 0) | self.args.flags
         forms = store_forms(self.args.store)
         marks = None
         # profiler runs (--no-events) make no event calls at all (rocprofv3 7.2
@@ -2093,6 +2095,9 @@ def main():
     ap.add_argument("--desc-upload", action="store_true",
                     help="upload worklists to device memory before each kernel (KVCOPY_F_DESC_UPLOAD) "
                          "instead of reading them in place from pinned staging")
+    ap.add_argument("--flags", type=lambda x: int(x, 0), default=0,
+                    help="kvcopy_batch_ex flags added to every call of the timed steps "
+                         "(measurement only; e.g. 0x800 = KVCOPY_F_WG_PER_CHUNK)")
     ap.add_argument("--store", default="auto",
                     help="store form of the copy kernels in the timed steps (KVCOPY_F_STORE_SC1 / "
                          "KVCOPY_F_STORE_NT): auto (the library's choice), sc1, nt, or per "
