@@ -334,14 +334,16 @@ int run_locked(Staging *st, int device, const uint64_t *src, const uint64_t *dst
         // region's device twin is free: the ring hands a region out again
         // only after its last kernel, which waited for its copy, completed.
         if (st->up_stream == nullptr) {
-            if ((e = hipStreamCreateWithFlags(&st->up_stream, hipStreamNonBlocking)) != hipSuccess) {
-                st->up_stream = nullptr;
+            hipStream_t us = nullptr;
+            hipEvent_t ue = nullptr;
+            if ((e = hipStreamCreateWithFlags(&us, hipStreamNonBlocking)) != hipSuccess)
+                return hip_fail(e);
+            if ((e = hipEventCreateWithFlags(&ue, hipEventDisableTiming)) != hipSuccess) {
+                (void)hipStreamDestroy(us);
                 return hip_fail(e);
             }
-            if ((e = hipEventCreateWithFlags(&st->up_done, hipEventDisableTiming)) != hipSuccess) {
-                st->up_done = nullptr;
-                return hip_fail(e);
-            }
+            st->up_stream = us;   // both or neither
+            st->up_done = ue;
         }
         ChunkRec *dev = reinterpret_cast<ChunkRec *>(st->dev + off);
         if ((e = hipMemcpyAsync(dev, host, n_chunks * sizeof(ChunkRec), hipMemcpyHostToDevice,

@@ -252,6 +252,29 @@ def test_wg_per_chunk_d2d_large(K):
     res.free()
 
 
+@pytest.mark.parametrize("loop", ["per_chunk", "wg"])
+def test_upload_train_wraps_the_ring(K, loop):
+    """48 uploaded calls back to back on one stream, cycling over 8 batches
+    of 16,384 random 4 KiB blocks (393 KiB of worklist each: the 16 MiB
+    staging ring and its device twin wrap), so each call's worklist copy,
+    on the library's upload stream, runs while earlier kernels still read
+    their own regions.  The pools' sources are never written, so the final
+    images are those of the 8 batches applied once, in order."""
+    from block_copy_amd.harness import Resident
+    wl = W.d2d_rotation(n=16384, pool_blocks=65536)
+    res = Resident(wl)
+    fl = K.F_DESC_UPLOAD | (K.F_WG_PER_CHUNK if loop == "wg" else 0)
+    st = torch.cuda.Stream()
+    for sentinel in (W.SENTINEL_A, W.SENTINEL_B):
+        _say("upload train", loop, "sentinel", hex(sentinel))
+        res.fill(sentinel)
+        for i in range(48):
+            res.submit(i % 8, 0, st, flags=fl)
+        torch.cuda.synchronize()
+        _check(res, list(range(8)), f"upload train {loop}", sentinel)
+    res.free()
+
+
 @pytest.mark.parametrize("max_wgs", [8, 0])
 def test_wg_per_chunk_kv_concurrent(K, max_wgs):
     from block_copy_amd.harness import Resident

@@ -475,6 +475,34 @@ def test_copies_on_cu_masked_streams(K, n_cus):
         irr.free()
 
 
+def test_kv_burst_on_cu_half_streams(K):
+    """The headline's setting: H2D on a stream over the first half of the CU
+    mask bits and D2H on one over the second half (each XCD keeps CUs for
+    both), at the headline cap and at 8 and 128, several bursts back to back
+    with the two streams joined per burst."""
+    from block_copy_amd import hiprt
+    from block_copy_amd.harness import Resident
+    n = torch.cuda.get_device_properties(0).multi_processor_count
+    kv = Resident(W.kv_blocks(seed=9, directions="both"))
+    sa, sb = hiprt.CUMaskStream(range(n // 2), n), hiprt.CUMaskStream(range(n // 2, n), n)
+    try:
+        for sentinel in (W.SENTINEL_A, W.SENTINEL_B):
+            for max_wgs in (64, 8, 128):
+                _say("cu-half streams, max_wgs", max_wgs, "sentinel", hex(sentinel))
+                kv.fill(sentinel)
+                for _ in range(5):
+                    kv.submit(0, max_wgs, sa.cuda_stream)
+                    kv.submit(1, max_wgs, sb.cuda_stream)
+                    hiprt.stream_sync(sa)
+                    hiprt.stream_sync(sb)
+                _check(kv, [0, 1], f"kv both on CU halves max_wgs={max_wgs}", sentinel)
+    finally:
+        torch.cuda.synchronize()
+        sa.destroy()
+        sb.destroy()
+        kv.free()
+
+
 # ---------------------------------------------------------------------------
 # Forced store forms, time-sliced issue, destination order
 # ---------------------------------------------------------------------------
