@@ -1006,6 +1006,11 @@ def per_fragment(c: Ctx, plan, kind, reps=2):
     return (time.perf_counter() - t0) / reps
 
 
+# The C-caller tool's header flag that makes it time one hipMemcpyAsync per
+# range instead of kvcopy_batch (latency_tool.cpp, kRuntimeCopy).
+RUNTIME_COPY_FLAG = 0x80000000
+
+
 def c_caller_latency(named):
     """Per-call latency of kvcopy_batch from a C caller: block_copy_amd/kvcopy_latency
     (built with the library) in a child process without torch, so the figures
@@ -1653,6 +1658,26 @@ def bench_crossover(c: Ctx, args):
             wins += kern <= rt
             log(f"  crossover {key}: {rows[key]}")
             r.free()
+    # Both calls above are issued from Python, where kvcopy_batch carries a few
+    # microseconds more marshalling (three arrays) than one hipMemcpyAsync
+    # call; for the small batches the same kernel calls are also timed from C
+    # (the C-caller tool: events around the call, host time inside it).
+    named = [(f"{n}x{size}_{dname}", W.kv_blocks(seed=0, directions=dname, n=n, pool_blocks=n,
+                                                block=size), g)
+             for n, size in CROSSOVER_SHAPES if n <= 16 and size <= (64 << 10)
+             for dname in ("h2d", "d2h")]
+    cl = c_caller_latency(named + [(f"{nm}_runtime", wl_, g_, RUNTIME_COPY_FLAG)
+                                   for nm, wl_, g_ in named])
+    for key, row in rows.items():
+        crow = cl.get(key.replace("/", "_"))
+        rrow = cl.get(key.replace("/", "_") + "_runtime")
+        if crow:
+            row["kernel_call_gpu_us_from_c"] = crow.get("gpu_us_p50")
+            row["kernel_call_host_us_from_c"] = crow.get("host_us_p50")
+        if rrow:
+            row["runtime_copy_gpu_us_from_c"] = rrow.get("gpu_us_p50")
+    if "error" in cl:
+        log(f"  crossover, C caller: {cl['error']}")
     line = base_line(args, wins, "shapes", 0.0, {
         "workload": "one kvcopy_batch against one hipMemcpyAsync per range, shuffled blocks "
                     "between mapped pinned memory and HBM, each direction alone, "

@@ -19,7 +19,8 @@
 //   pipelined_us  back-to-back calls with no sync in between, per call
 //            (after 50 untimed ones; at least 20 ms of calls);
 // then checks that every destination range holds its source bytes, and
-// prints one JSON object per file on stdout.
+// prints one JSON object per file on stdout.  With the header flag bit
+// kRuntimeCopy the calls are one hipMemcpyAsync per descriptor instead.
 #include <stdint.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -43,6 +44,10 @@ struct Header {
     uint32_t flags;   // KVCOPY_F_* for kvcopy_batch_ex (0: plain kvcopy_batch)
     uint64_t src_bytes, dst_bytes, n;
 };
+
+// A header flag bit outside the library's flags: time one hipMemcpyAsync per
+// descriptor instead of kvcopy_batch (the runtime's copy, also from C).
+constexpr uint32_t kRuntimeCopy = 0x80000000u;
 
 bool ok(hipError_t e, const char *what)
 {
@@ -159,11 +164,23 @@ int run_file(const char *path, hipStream_t st)
     kvcopy_opts_t opts;
     memset(&opts, 0, sizeof(opts));
     opts.struct_size = sizeof(opts);
-    opts.flags = h.flags;
+    const bool runtime_copy = (h.flags & kRuntimeCopy) != 0;
+    opts.flags = h.flags & ~kRuntimeCopy;
+    const hipMemcpyKind kind = dir == KVCOPY_H2D   ? hipMemcpyHostToDevice
+                               : dir == KVCOPY_D2H ? hipMemcpyDeviceToHost
+                                                   : hipMemcpyDeviceToDevice;
     auto call = [&]() {
-        const int rc = h.flags ? kvcopy_batch_ex(s.data(), d.data(), sz.data(), h.n, dir, h.max_wgs,
-                                                 st, &opts)
-                               : kvcopy_batch(s.data(), d.data(), sz.data(), h.n, dir, h.max_wgs, st);
+        if (runtime_copy) {
+            for (uint64_t i = 0; i < h.n; ++i)
+                if (!ok(hipMemcpyAsync(reinterpret_cast<void *>(d[i]),
+                                       reinterpret_cast<const void *>(s[i]), sz[i], kind, st),
+                        "hipMemcpyAsync"))
+                    return false;
+            return true;
+        }
+        const int rc = opts.flags ? kvcopy_batch_ex(s.data(), d.data(), sz.data(), h.n, dir,
+                                                    h.max_wgs, st, &opts)
+                                  : kvcopy_batch(s.data(), d.data(), sz.data(), h.n, dir, h.max_wgs, st);
         if (rc != KVCOPY_OK)
             fprintf(stderr, "kvcopy_batch: %s\n", kvcopy_strerror(rc));
         return rc == KVCOPY_OK;
@@ -226,12 +243,13 @@ int run_file(const char *path, hipStream_t st)
         bad += memcmp(si.data() + so[i], di.data() + dof[i], sz[i]) != 0;
     (void)hipEventDestroy(e0);
     (void)hipEventDestroy(e1);
-    printf("{\"name\": \"%s\", \"descriptors\": %llu, \"bytes\": %llu, \"max_wgs\": %d, "
+    printf("{\"name\": \"%s\", \"call\": \"%s\", \"descriptors\": %llu, \"bytes\": %llu, \"max_wgs\": %d, "
            "\"calls\": %d, \"host_us_p50\": %.2f, \"host_us_p99\": %.2f, \"wall_us_p50\": %.2f, "
            "\"wall_us_p99\": %.2f, \"gpu_us_p50\": %.2f, \"gpu_us_p99\": %.2f, "
            "\"pipelined_us_per_call\": %.2f, \"pipelined_calls\": %d, \"ranges_checked\": %llu, "
            "\"ranges_wrong\": %llu}\n",
-           h.name, (unsigned long long)h.n, (unsigned long long)bytes, h.max_wgs, reps,
+           h.name, runtime_copy ? "hipMemcpyAsync per range" : "kvcopy_batch",
+           (unsigned long long)h.n, (unsigned long long)bytes, h.max_wgs, reps,
            pct(host_us, 50), pct(host_us, 99), pct(wall_us, 50), pct(wall_us, 99), pct(gpu_us, 50),
            pct(gpu_us, 99), pipelined, bb, (unsigned long long)h.n, (unsigned long long)bad);
     fflush(stdout);
