@@ -220,7 +220,8 @@ def counters(args):
                            "write_scale": sw},
            "commands": {"fetch": args.fetch_command, "write": args.write_command},
            "kernels": by_name, "by_grid": kernels}
-    jpath = os.path.join(ROOT, "profiles", f"counters_{args.name}.json")
+    out_dir = getattr(args, "out_dir", None) or os.path.join(ROOT, "profiles")
+    jpath = os.path.join(out_dir, f"counters_{args.name}.json")
     with open(jpath, "w") as fh:
         json.dump(out, fh, indent=1)
     lines = [f"# Counters: {args.name}\n",
@@ -239,7 +240,7 @@ def counters(args):
                      f"{k['write_bytes_per_dispatch_scaled'] / 2**20:.2f} |")
     lines.append(f"\nKernel source sha256 at the time of the passes: `{out['kernel_source_sha256']}` "
                  "(bench.py reports `traffic` only while it matches).")
-    with open(os.path.join(ROOT, "profiles", f"counters_{args.name}.md"), "w") as fh:
+    with open(os.path.join(out_dir, f"counters_{args.name}.md"), "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print(f"wrote {jpath}")
 
@@ -265,6 +266,7 @@ def main():
     c.add_argument("--name", required=True)
     c.add_argument("--fetch-command", required=True)
     c.add_argument("--write-command", required=True)
+    c.add_argument("--out-dir", default=None, help="default: profiles/")
     a = ap.parse_args()
     {"trace": trace, "bursts": bursts, "counters": counters}[a.what](a)
 
