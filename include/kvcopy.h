@@ -131,8 +131,9 @@ enum {
  * way on two streams: 94.2-94.6 GB/s with the D2H kernel's stores in the
  * sc1 form, 87.9-88.4 with nt, whatever the H2D kernel's form; a lone D2H
  * batch 56.7 against 52.7 GB/s.  These flags force one form, for any
- * direction; they select the per-chunk loop (KVCOPY_F_PIPELINE or
- * KVCOPY_F_DYNAMIC with either is KVCOPY_EINVAL, and so are both).
+ * direction; they select the per-chunk loop unless KVCOPY_F_WG_PER_CHUNK
+ * is given (KVCOPY_F_PIPELINE or KVCOPY_F_DYNAMIC with either is
+ * KVCOPY_EINVAL, and so are both).
  * kvcopy_batch_pair takes KVCOPY_F_STORE_NT (its default is sc1). */
 #define KVCOPY_F_STORE_SC1 0x80u
 #define KVCOPY_F_STORE_NT 0x100u
@@ -142,7 +143,9 @@ enum {
  * narrow band of memory.  It costs two more passes over the records on the
  * host.  Results do not depend on it.  Meant for D2D gathers of many random
  * blocks: measured on MI355X, calls of 65,536 random 4 KiB blocks between
- * two 1 GiB pools run 6% faster on the GPU (100.8 against 107 us). */
+ * two 1 GiB pools run 3-5% faster on the GPU (101.6-103.8 against 106-107
+ * us), at 66-70 us more host time per call; a caller's list sorted by
+ * destination with KVCOPY_F_WG_PER_CHUNK does better (below). */
 #define KVCOPY_F_DST_ORDER 0x200u
 /* Tail-bounded policy ([PF] "Proposed direction": a tail-bounded policy
  * beside the throughput-oriented one, for transfers that share the GPU with
@@ -153,10 +156,11 @@ enum {
  * become 4).  It moves about 3.3 GB/s of 4 KiB blocks per call in flight.
  * Measured on MI355X with a batch-1 decode loop of 36 bf16 GEMVs (0.38 ms
  * per step) beside an H2D + D2H burst of 16,384 x 4 KiB each way every
- * 50 ms on two streams: decode step p99 +4.9% and worst step 0.44 ms
- * (0.41 ms with no transfer) at 2.56 GiB/s sustained, where the default
+ * 50 ms on two streams: decode step p99 +4.9% and worst step 0.43 ms
+ * (0.41 ms with no transfer) at 2.61 GiB/s sustained, where the default
  * (128 workgroups per stream) gives p99 +2% but a worst step near 2 ms.
- * With KVCOPY_F_PIPELINE or KVCOPY_F_DYNAMIC: KVCOPY_EINVAL. */
+ * With KVCOPY_F_PIPELINE, KVCOPY_F_DYNAMIC or KVCOPY_F_WG_PER_CHUNK:
+ * KVCOPY_EINVAL. */
 #define KVCOPY_F_TAIL_BOUNDED 0x400u
 /* One workgroup per chunk: the four wavefronts of a workgroup share each
  * chunk (thread t moves the 16-byte words at t*16 + k*4 KiB), and workgroup
@@ -293,8 +297,8 @@ typedef struct {
      * same windows and leave the host link idle in between.  Requires
      * 1,000 <= duty_on_ns <= duty_period_ns <= 10,000,000 (else
      * KVCOPY_EINVAL); on == period means no pacing.  Applies to the
-     * per-chunk loop (with KVCOPY_F_PIPELINE or KVCOPY_F_DYNAMIC:
-     * KVCOPY_EINVAL).  A chunk started at the end of a window still
+     * per-chunk loop (with KVCOPY_F_PIPELINE, KVCOPY_F_DYNAMIC or
+     * KVCOPY_F_WG_PER_CHUNK: KVCOPY_EINVAL).  A chunk started at the end of a window still
      * completes after it, so the link carries traffic for somewhat longer
      * than duty_on_ns per period. */
     uint32_t duty_on_ns;
