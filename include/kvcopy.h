@@ -428,10 +428,9 @@ void kvcopy_job_destroy(kvcopy_job_t *job);
  * (ascending, descending, ascending), and rates each cap by its median
  * sweep.  It records as the device's KVCOPY_WGS_AUTO cap for `dir` (for H2D
  * or D2H: for both) the largest cap whose median is within 2% of the best
- * cap's and whose slowest sweep is within 4% of it.  Near-ties go to the
- * larger grid: on MI355X, with two streams, 8 and 64 workgroups per stream
- * rated within 0.6-1.1% of each other, but 8 later ran some 20-step windows
- * of the burst 5-9% slower, 64 none.
+ * cap's.  Near-ties go to the larger grid: on MI355X, with two streams, 8
+ * and 64 workgroups per stream rated within 0.5-1.1% of each other, but 8
+ * later ran some 20-step windows of the burst 5-9% slower, 64 none.
  * Blocks until done (one to two seconds).
  * s0, s1: the streams the caller will copy on (the hardware queues they map
  *   to matter); NULL = streams created for the probe.
