@@ -449,14 +449,17 @@ def bench_kv(c: Ctx, args):
     ach = [gbs(algo[j], kern_ms[j] / 1e3) for j in range(2)]
 
     if args.sweep:
+        # each direction alone on one stream, and both on the headline's two
+        # streams with the steps joined, each point timed as the headline is
+        # (one event pair per stream around its back-to-back kernels)
         sweep = {}
         for name, ids, sts in (("h2d", [0], [sA]), ("d2h", [1], [sA]), ("both", [0, 1], [hA, hB])):
             for g in (1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 0):
-                s_, km = c.timed(res, ids, sts, max(3, args.steps // 2), 2, g)
+                s_, km = c.timed_bracketed(res, ids, sts, max(3, args.steps // 2), args.leg_warmup,
+                                           g, joined=len(ids) > 1)
                 nbytes = sum(wl.batches[i].nbytes for i in ids)
                 sweep[f"{name}/{g}"] = round(gbs(nbytes, s_), 2)
-                log(f"  sweep {name} max_wgs={g}: {gbs(nbytes, s_):.2f} GB/s, kernel ms "
-                    f"{[round(x, 3) for x in km]}")
+                log(f"  sweep {name} max_wgs={g}: {gbs(nbytes, s_):.2f} GB/s")
         extras["max_wgs_sweep_GBps"] = sweep
     if not args.skip_extras and not args.no_events:
         extras["headline_windows"] = headline_windows(c, res, max_wgs, streams=(hA, hB))
