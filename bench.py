@@ -367,7 +367,8 @@ def parse_wgs(text):
 
 def kernel_name(dir_, spec="auto"):
     """The per-chunk copy kernel's symbol for a direction under --store
-    (the library stores D2H in the sc1 form and the rest nt by default)."""
+    (the library stores D2H in the sc1 form on grids of three or more
+    workgroups, as every leg that names a kernel runs, and the rest nt)."""
     form = store_forms(spec).get(dir_) or ("sc1" if dir_ == 1 else "nt")
     return f"kvcopy_{DIR_NAMES[dir_]}{'_sc1' if form == 'sc1' else ''}_kernel"
 
@@ -466,9 +467,8 @@ def bench_kv(c: Ctx, args):
         log(f"  headline windows: {dict((k, v) for k, v in extras['headline_windows'].items() if k not in ('GBps', 'kernel_ms_per_stream'))}")
     if not args.skip_extras:
         alone = extras["per_direction_alone"]
-        # a lone D2H list through kvcopy_batch_pair (whose kernel stores with
-        # the sc1 form, as kvcopy_batch's D2H kernel does when no H2D kernel
-        # of the library runs beside it)
+        # a lone D2H list through kvcopy_batch_pair (whose kernel stores in
+        # the sc1 form, as kvcopy_batch's D2H kernel does on such grids)
         e_ = np.zeros(0, np.uint64)
         s1_, d1_ = res.addrs[1]
         for _ in range(args.leg_warmup):

@@ -195,6 +195,19 @@ inline uint32_t grid_for_wg(uint64_t n_chunks, int max_wgs)
     return (uint32_t)(g < kMaxGrid ? g : kMaxGrid);
 }
 
+// The default store form (copy_chunk.h): sc1 for D2H batches on grids of
+// three or more workgroups, nt otherwise.  Measured on MI355X with 16,384 x
+// 4 KiB, a lone D2H batch moves 12.9 / 25.6 / 50.1 / 56.2 GB/s at 1 / 2 / 4
+// / 8 workgroups with sc1 stores and 26.4 / 52.5 / 55.1 / 54.6 with nt;
+// beside an H2D batch on another stream the two forms tie at 1-2
+// workgroups per stream (19.5-19.9 and 37.0-37.3 GB/s for both), and sc1
+// wins from 4 up (65.2 against 55.4 at 4, 96.7 against 67.5 at 8).
+constexpr uint32_t kSc1MinGrid = 3;
+inline bool default_sc1(int dir, uint32_t grid)
+{
+    return dir == 1 /* KVCOPY_D2H */ && grid >= kSc1MinGrid;
+}
+
 // Largest grid of the dynamic loop.  Every claim is an atomic add on one
 // device word: measured on MI355X, 65,536 chunks at the full grid (16,384
 // workgroups, one chunk per claim) took 2.2 ms instead of 0.1 ms, the

@@ -372,11 +372,11 @@ int run_locked(Staging *st, int device, const uint64_t *src, const uint64_t *dst
     const uint32_t grid = grid_for(n_chunks, max_wgs);
     hipEvent_t start = timed ? o.ev_begin : nullptr, stop = timed ? o.ev_end : done;
     if (flags & KVCOPY_F_WG_PER_CHUNK) {
+        const uint32_t g = grid_for_wg(n_chunks, max_wgs);
         int sc1 = forced_store(flags);
         if (sc1 < 0)
-            sc1 = dir == KVCOPY_D2H;
-        e = launch_copy_wg(recs, (uint32_t)n_chunks, grid_for_wg(n_chunks, max_wgs), dir, sc1 != 0,
-                           stream, start, stop);
+            sc1 = default_sc1(dir, g);
+        e = launch_copy_wg(recs, (uint32_t)n_chunks, g, dir, sc1 != 0, stream, start, stop);
     } else if (dynamic) {
         uint32_t *claim = st->claims + off / kAlign * 2;
         const uint32_t g = grid < kDynMaxGrid ? grid : kDynMaxGrid;
@@ -388,12 +388,13 @@ int run_locked(Staging *st, int device, const uint64_t *src, const uint64_t *dst
                                          KVCOPY_F_STORE_NT)) != 0 || pace_period != 0;
         const bool pipelined = (flags & KVCOPY_F_PIPELINE) != 0 ||
                                (!per_chunk && pipeline_pays(dir, grid, n_chunks));
-        // D2H stores take the sc1 form and the other directions nt
-        // (copy_chunk.h, kSc1StorePolicy), unless a flag forces one.  Only
-        // the speed depends on the choice.
+        // D2H stores take the sc1 form on grids of three or more workgroups
+        // and the other cases nt (copy_chunk.h, kSc1StorePolicy;
+        // default_sc1), unless a flag forces one.  Only the speed depends on
+        // the choice.
         int sc1 = forced_store(flags);
         if (sc1 < 0)
-            sc1 = dir == KVCOPY_D2H;
+            sc1 = default_sc1(dir, grid);
         e = launch_copy(recs, (uint32_t)n_chunks, grid, dir, pipelined, sc1 != 0, pace_on,
                         pace_period, stream, start, stop);
     }
@@ -440,7 +441,7 @@ int run_inline(Staging *st, const uint64_t *src, const uint64_t *dst, const uint
     const int forced = forced_store(o.flags);
     if (!(o.flags & KVCOPY_F_PER_CHUNK) && forced < 0 && pipeline_pays(dir, grid, w.n_chunks))
         return kNotInline;
-    const bool sc1 = forced < 0 ? dir == KVCOPY_D2H : forced == 1;
+    const bool sc1 = forced < 0 ? default_sc1(dir, grid) : forced == 1;
     const hipError_t e = launch_copy_inline(w, grid, dir, sc1, stream, o.ev_begin, o.ev_end);
     return e == hipSuccess ? KVCOPY_OK : hip_fail(e);
 }
