@@ -1,8 +1,10 @@
 """Minimal ctypes access to the HIP runtime for timing and baselines.
 
 Used by bench.py and the tests for events on a given stream and for the
-plain DMA baselines (contiguous ceilings, one hipMemcpyAsync per fragment,
-one hipMemcpyBatchAsync per list).  In a process that has imported torch,
+baselines that use the runtime's own copies (contiguous ceilings, one
+hipMemcpyAsync per fragment, one hipMemcpyBatchAsync per list; kernel
+traces show the runtime carrying the contiguous and per-fragment copies
+out as its own blit kernel).  In a process that has imported torch,
 the HIP runtime already loaded is torch's own copy, and this module (like
 libkvcopy.so) binds to it.
 """
