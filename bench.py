@@ -1286,29 +1286,24 @@ def d2d_distinct(c: Ctx, args):
     nb = len(wl.batches)
     if args.no_events:
         # profiler runs: the fastest mode of the timed runs over the rotation
-        # (each batch sorted by destination, one workgroup per chunk, records
+        # (the library's destination order, one workgroup per chunk, records
         # uploaded, sc1 stores), timed by the kernel trace (its kernel,
         # kvcopy_d2d_wg_sc1_kernel, runs nowhere else in a profiled D2D leg),
         # parity-checked
         K = c.K
-        fl = K.F_WG_PER_CHUNK | K.F_DESC_UPLOAD | K.F_STORE_SC1
+        fl = K.F_WG_PER_CHUNK | K.F_DESC_UPLOAD | K.F_DST_ORDER | K.F_STORE_SC1
         calls = max(4 * nb, args.steps)
-        srt = []
-        for i in range(nb):
-            s_, d_ = r.addrs[i]
-            o = c.np.argsort(d_, kind="stable")
-            srt.append((s_[o], d_[o], wl.batches[i].size[o]))
         r.fill()
         for i in range(nb):
-            K.kvcopy_batch(*srt[i], W.D2D, 0, c.sA.cuda_stream, flags=fl)
+            r.submit(i, 0, c.sA, flags=fl)
         hiprt.stream_sync(c.sA)
         c.verify(wl, r, list(range(nb)), "d2d distinct calls, workgroup per chunk")
         for i in range(calls):
-            K.kvcopy_batch(*srt[i % nb], W.D2D, 0, c.sA.cuda_stream, flags=fl)
+            r.submit(i % nb, 0, c.sA, flags=fl)
         hiprt.stream_sync(c.sA)
         r.free()
-        return {"calls": calls, "mode": "each batch sorted by destination; KVCOPY_F_WG_PER_CHUNK | "
-                "KVCOPY_F_DESC_UPLOAD | KVCOPY_F_STORE_SC1",
+        return {"calls": calls, "mode": "KVCOPY_F_WG_PER_CHUNK | KVCOPY_F_DESC_UPLOAD | "
+                "KVCOPY_F_DST_ORDER | KVCOPY_F_STORE_SC1",
                 "timed_by": "the kernel trace (kvcopy_d2d_wg_sc1_kernel)"}
     calls = max(4 * nb, args.steps)
 
@@ -1359,6 +1354,8 @@ def d2d_distinct(c: Ctx, args):
                     (K.F_DESC_UPLOAD | K.F_STORE_SC1, True),
                 "wg_per_chunk_records_in_device_memory": (WG, False),
                 "wg_per_chunk_destination_order_records_in_device_memory": (WG | K.F_DST_ORDER, False),
+                "wg_per_chunk_destination_order_records_in_device_memory_sc1_stores":
+                    (WG | K.F_DST_ORDER | K.F_STORE_SC1, False),
                 "wg_per_chunk_sorted_by_destination_records_in_device_memory": (WG, True),
                 "wg_per_chunk_sorted_by_destination_records_in_device_memory_sc1_stores":
                     (WG | K.F_STORE_SC1, True)}
@@ -1397,6 +1394,8 @@ def d2d_distinct(c: Ctx, args):
     for name, fl, srt in (("list_order_default", 0, False),
                           ("wg_per_chunk_destination_order_records_uploaded",
                            WG | K.F_DST_ORDER, False),
+                          ("wg_per_chunk_destination_order_records_uploaded_sc1_stores",
+                           WG | K.F_DST_ORDER | K.F_STORE_SC1, False),
                           ("wg_per_chunk_sorted_by_destination_records_uploaded", WG, True),
                           ("wg_per_chunk_sorted_by_destination_records_uploaded_sc1_stores",
                            WG | K.F_STORE_SC1, True)):

@@ -86,12 +86,20 @@ uint64_t build_worklist(const uint64_t *src, const uint64_t *dst, const uint64_t
                         bool merge, uint32_t chunk, ChunkRec *out);
 
 // KVCOPY_F_DST_ORDER: writes in[0..n) to out in order of destination
-// region -- a stable counting sort of the records by (dst >> 26) & 15, so
-// the records of one 64 MiB destination region (and of regions 1 GiB
-// apart) are consecutive, in list order within the region.
-constexpr uint32_t kDstRegionShift = 26;
-constexpr uint32_t kDstBuckets = 16;
-void order_by_dst(const ChunkRec *in, uint64_t n, ChunkRec *out);
+// region, a stable counting sort of the records (list order kept within a
+// region).  Up to kDstFineMax records the key is the 4 MiB region,
+// (dst >> 22) & 255; beyond, the 64 MiB region, (dst >> 26) & 15.  Regions
+// 1 GiB apart share a key.  idx and keys are scratch of
+// order_scratch_words(n) entries each (none beyond kDstFineMax; keys are
+// read only as the first n bytes); out may be written with non-temporal
+// stores (finish_records before the GPU reads it).
+constexpr uint32_t kDstFineShift = 22;
+constexpr uint32_t kDstFineBuckets = 256;
+constexpr uint32_t kDstCoarseShift = 26;
+constexpr uint32_t kDstCoarseBuckets = 16;
+constexpr uint64_t kDstFineMax = 1ull << 17;
+uint64_t order_scratch_words(uint64_t n);
+void order_by_dst(const ChunkRec *in, uint64_t n, ChunkRec *out, uint32_t *idx, uint8_t *keys);
 
 // True when KVCOPY_VALIDATE=1 in the environment; any value other than
 // unset, "0" or "1" makes *bad true (strict parsing).

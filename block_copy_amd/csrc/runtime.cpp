@@ -80,6 +80,8 @@ struct Staging {
     uint32_t *claims = nullptr;
     int clock_khz = 0;             // wall-clock rate (hipDeviceAttributeWallClockRate), 0 = not read yet
     std::vector<ChunkRec> order_tmp;   // KVCOPY_F_DST_ORDER: the worklist in list order
+    std::vector<uint32_t> order_idx;   // and the sort's scratch (order_by_dst)
+    std::vector<uint8_t> order_keys;
     // KVCOPY_F_DESC_UPLOAD: the worklist copies run on a stream of the
     // library's own (default priority), created on first use; the caller's
     // stream waits for each copy through `up_done` before its kernel.
@@ -287,6 +289,15 @@ int run_locked(Staging *st, int device, const uint64_t *src, const uint64_t *dst
                 break;
             hint = n_chunks;   // plan again with room for every record
         }
+        const uint64_t words = order_scratch_words(n_chunks);
+        try {
+            if (st->order_idx.size() < words) {
+                st->order_idx.resize(words);
+                st->order_keys.resize(words);
+            }
+        } catch (...) {
+            return KVCOPY_ENOMEM;
+        }
         const uint64_t need = (n_chunks * sizeof(ChunkRec) + kAlign - 1) / kAlign * kAlign;
         if (4 * need > st->ring.capacity() || (upload && st->dev == nullptr) ||
             (dynamic && st->claims == nullptr)) {
@@ -296,7 +307,8 @@ int run_locked(Staging *st, int device, const uint64_t *src, const uint64_t *dst
         if ((rc = st->ring.reserve(need, &off)) != KVCOPY_OK)
             return rc;
         host = reinterpret_cast<ChunkRec *>(st->host + off);
-        order_by_dst(st->order_tmp.data(), n_chunks, host);
+        order_by_dst(st->order_tmp.data(), n_chunks, host, st->order_idx.data(),
+                     st->order_keys.data());
     } else {
         for (int pass = 0; pass < 2; ++pass) {
             const uint64_t room = hint ? hint : 1;

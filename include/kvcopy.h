@@ -139,15 +139,16 @@ enum {
  * kvcopy_batch_pair takes KVCOPY_F_STORE_NT (its default is sc1). */
 #define KVCOPY_F_STORE_SC1 0x80u
 #define KVCOPY_F_STORE_NT 0x100u
-/* Destination order: the worklist handed to the kernel is ordered by 64 MiB
- * destination region ((dst >> 26) mod 16; list order within a region)
- * instead of list order, so that the chunks in flight at any moment write a
- * narrow band of memory.  It costs two more passes over the records on the
- * host.  Results do not depend on it.  Meant for D2D gathers of many random
- * blocks: measured on MI355X, calls of 65,536 random 4 KiB blocks between
- * two 1 GiB pools run 3-5% faster on the GPU (101.6-103.8 against 106-107
- * us), at 66-70 us more host time per call; a caller's list sorted by
- * destination with KVCOPY_F_WG_PER_CHUNK does better (below). */
+/* Destination order: the worklist handed to the kernel is ordered by
+ * destination region instead of list order, so that the chunks in flight at
+ * any moment write a narrow band of memory: by 4 MiB region
+ * ((dst >> 22) mod 256) for up to 131,072 records, by 64 MiB region
+ * ((dst >> 26) mod 16) for longer worklists; list order within a region.
+ * It costs the host a counting sort of the records (on the MI355X host
+ * about 90 us for 65,536 records, on top of the planning).  Results do not
+ * depend on it.  Meant for D2D gathers of many random blocks with
+ * KVCOPY_F_WG_PER_CHUNK (below), where the kernel then runs as fast as on a
+ * list sorted by destination; with the per-chunk loop it gains 3-5%. */
 #define KVCOPY_F_DST_ORDER 0x200u
 /* Tail-bounded policy ([PF] "Proposed direction": a tail-bounded policy
  * beside the throughput-oriented one, for transfers that share the GPU with
@@ -175,12 +176,13 @@ enum {
  * sorted by destination) the workgroups that the dispatcher starts together
  * read and write whole blocks of a narrow band of memory: measured on
  * MI355X for D2D calls of 65,536 random 4 KiB blocks between two 1 GiB pools,
- * cycling over 8 distinct batches, with the records in device memory,
- * 95.6 us per kernel sorted by destination (5.6 TB/s of HBM traffic, 70% of
- * 8 TB/s) against 102.7 us for one wavefront per chunk, and 105.2 against
- * 107.9 us in list order.  Takes the store forms above (default as for the
- * per-chunk loop); with another loop flag, pacing or KVCOPY_F_TAIL_BOUNDED:
- * KVCOPY_EINVAL. */
+ * cycling over 8 distinct batches, with the records in device memory and
+ * sc1 stores, 92.3-92.6 us per kernel with KVCOPY_F_DST_ORDER (5.8 TB/s of
+ * HBM traffic, 73% of 8 TB/s) and 93.1 us on a list sorted by destination,
+ * against 98.0 us for one wavefront per chunk on the sorted list, and 103.4
+ * against 107.6 us in list order.  Takes the store forms above (default as
+ * for the per-chunk loop); with another loop flag, pacing or
+ * KVCOPY_F_TAIL_BOUNDED: KVCOPY_EINVAL. */
 #define KVCOPY_F_WG_PER_CHUNK 0x800u
 
 /*
