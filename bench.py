@@ -1285,11 +1285,12 @@ def d2d_distinct(c: Ctx, args):
     r = c.Resident(wl)
     nb = len(wl.batches)
     if args.no_events:
-        # profiler runs: the fastest mode of the timed runs over the rotation
-        # (the library's destination order, one workgroup per chunk, records
-        # uploaded, sc1 stores), timed by the kernel trace (its kernel,
-        # kvcopy_d2d_wg_sc1_kernel, runs nowhere else in a profiled D2D leg),
-        # parity-checked
+        # profiler runs: the library's own fast mode for an unsorted list
+        # (one workgroup per chunk, records uploaded and grouped by
+        # destination region on the GPU, sc1 stores), timed by the kernel
+        # trace (its kernels, kvcopy_order_count_kernel,
+        # kvcopy_order_place_kernel and kvcopy_d2d_wg_sc1_kernel, run nowhere
+        # else in a profiled D2D leg), parity-checked
         K = c.K
         fl = K.F_WG_PER_CHUNK | K.F_DESC_UPLOAD | K.F_DST_ORDER | K.F_STORE_SC1
         calls = max(4 * nb, args.steps)

@@ -28,7 +28,7 @@ ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 ARCH = "gfx950"
 
 HOST_SOURCES = ["plan.cpp", "runtime.cpp", "jobs.cpp", "autotune.cpp"]
-HIP_SOURCES = ["kvcopy_kernel.hip", "device_batch.hip"]
+HIP_SOURCES = ["kvcopy_kernel.hip", "device_batch.hip", "order_kernel.hip"]
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
     # Keep the compiler away from packed fp32 instructions on this target.

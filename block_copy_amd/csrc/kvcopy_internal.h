@@ -85,21 +85,31 @@ bool planner_vector_path(const uint64_t *src, const uint64_t *dst, const uint64_
 uint64_t build_worklist(const uint64_t *src, const uint64_t *dst, const uint64_t *size, uint64_t n,
                         bool merge, uint32_t chunk, ChunkRec *out);
 
-// KVCOPY_F_DST_ORDER: writes in[0..n) to out in order of destination
-// region, a stable counting sort of the records (list order kept within a
-// region).  Up to kDstFineMax records the key is the 4 MiB region,
-// (dst >> 22) & 255; beyond, the 64 MiB region, (dst >> 26) & 15.  Regions
-// 1 GiB apart share a key.  idx and keys are scratch of
-// order_scratch_words(n) entries each (none beyond kDstFineMax; keys are
-// read only as the first n bytes); out may be written with non-temporal
-// stores (finish_records before the GPU reads it).
-constexpr uint32_t kDstFineShift = 22;
-constexpr uint32_t kDstFineBuckets = 256;
-constexpr uint32_t kDstCoarseShift = 26;
-constexpr uint32_t kDstCoarseBuckets = 16;
-constexpr uint64_t kDstFineMax = 1ull << 17;
-uint64_t order_scratch_words(uint64_t n);
-void order_by_dst(const ChunkRec *in, uint64_t n, ChunkRec *out, uint32_t *idx, uint8_t *keys);
+// KVCOPY_F_DST_ORDER without an upload: writes in[0..n) to out in order of
+// destination region -- a stable counting sort of the records by
+// (dst >> 26) & 15, so the records of one 64 MiB destination region (and of
+// regions 1 GiB apart) are consecutive, in list order within the region.
+constexpr uint32_t kDstRegionShift = 26;
+constexpr uint32_t kDstBuckets = 16;
+void order_by_dst(const ChunkRec *in, uint64_t n, ChunkRec *out);
+
+// KVCOPY_F_DST_ORDER with KVCOPY_F_DESC_UPLOAD: grouping by 4 MiB region
+// made on the GPU (order_kernel.hip), for any worklist length.  in[0..n)
+// are the uploaded records in list order, out[0..n) receives them grouped
+// by (dst >> kOrderShift) & (kOrderKeys - 1) in key order (no set order
+// within a key);
+// header is kOrderHeaderBytes of zeroed device memory (256 counters, then
+// 256 cursors) that the two kernels use and leave dirty.  Two launches on
+// `stream` (the library's upload stream); `start` (may be null) is bound to
+// the first one's start.
+constexpr uint32_t kOrderShift = 22;
+constexpr uint32_t kOrderKeys = 256;
+constexpr uint32_t kOrderThreads = 256;
+constexpr uint32_t kOrderPerWG = 1024;   // records per workgroup (then grid-stride)
+constexpr uint32_t kOrderMaxGrid = 1024;
+constexpr uint64_t kOrderHeaderBytes = 2 * 256 * sizeof(uint32_t);
+hipError_t launch_order(const ChunkRec *in, uint32_t n, ChunkRec *out, uint32_t *header,
+                        hipStream_t stream, hipEvent_t start);
 
 // True when KVCOPY_VALIDATE=1 in the environment; any value other than
 // unset, "0" or "1" makes *bad true (strict parsing).

@@ -381,157 +381,36 @@ uint64_t build_worklist(const uint64_t *src, const uint64_t *dst, const uint64_t
     return w;
 }
 
-// Destination order for D2D gathers of random blocks: with the worklist in
-// list order, the chunks that the GPU has in flight at any moment write all
-// over HBM; grouped by destination region, the workgroups that the
-// dispatcher starts together write into a narrow band of rows.  Measured on
-// MI355X with one workgroup per chunk (65,536 random 4 KiB blocks between two
-// 1 GiB pools, calls over 8 distinct batches, records in device memory):
-// regions of 64 KiB to 4 MiB and a full sort by destination all ran the
-// kernel in 93.5-93.8 us, 16 MiB regions in 95.0, 64 MiB in 98-99, list
-// order in 103.7.  So lists of up to kDstFineMax records are ordered by
-// 4 MiB region, 256 buckets.  A scatter into 256 output streams runs several
-// times slower than into 16 (each stream's next line misses in the cache),
-// so the fine order sorts record indices instead (a 4-byte scatter that
-// stays in the cache) and then reads the records in that order, writing the
-// output sequentially with non-temporal stores: on the MI355X host
-// (AMD EPYC), 88 us for 65,536 records against 82-108 for the 16-bucket
-// scatter.  Beyond kDstFineMax the index sort's reads leave the cache (950
-// against 350 us at 262,144 records) and the kernel's gain does not repay
-// it, so longer lists keep 64 MiB regions, 16 buckets, scattered directly
-// with ordinary (cached) stores: non-temporal stores scattered over the
-// streams each flush a partly filled write-combining buffer, which measured
-// 20 times slower.
-namespace {
-
-template <uint32_t Shift, uint32_t Buckets>
-inline uint32_t dst_key(const ChunkRec &r)
+// Destination order for D2D gathers of random blocks, made on the host
+// when the worklist is read in place from the ring (with an upload the GPU
+// groups it, order_kernel.hip): with the worklist in list order, the
+// chunks that the GPU has in flight at any moment write all over HBM;
+// grouped by destination region, the wavefronts that the dispatcher starts
+// together write into a narrow band of rows.  Measured on MI355X with one
+// wavefront per chunk (65,536 random 4 KiB blocks between two 1 GiB pools,
+// calls over 8 distinct batches): regions of 1, 4, 16 and 64 MiB and a full
+// sort by destination all gave 100.8-103 us against 107 us in list order,
+// so the regions are 64 MiB, 16 of them: a stable counting sort with 16
+// output streams, which the host's prefetchers follow (a 4 MiB grouping,
+// 256 streams, cost 20 us more per 65,536 records on the MI355X host for no
+// gain with this loop).  The records are written with ordinary (cached)
+// stores: non-temporal stores scattered over the streams each flush a partly
+// filled write-combining buffer, which measured 20 times slower.
+void order_by_dst(const ChunkRec *in, uint64_t n, ChunkRec *out)
 {
-    return (uint32_t)(r.dst >> Shift) & (Buckets - 1);
-}
-
-void order_coarse(const ChunkRec *in, uint64_t n, ChunkRec *out)
-{
-    uint64_t at[kDstCoarseBuckets] = {};
+    uint64_t at[kDstBuckets] = {};
     for (uint64_t i = 0; i < n; ++i)
-        ++at[dst_key<kDstCoarseShift, kDstCoarseBuckets>(in[i])];
+        ++at[(in[i].dst >> kDstRegionShift) & (kDstBuckets - 1)];
     uint64_t acc = 0;
-    for (uint32_t b = 0; b < kDstCoarseBuckets; ++b) {
+    for (uint32_t b = 0; b < kDstBuckets; ++b) {
         const uint64_t c = at[b];
         at[b] = acc;
         acc += c;
     }
     for (uint64_t i = 0; i < n; ++i) {
         const ChunkRec &r = in[i];
-        out[at[dst_key<kDstCoarseShift, kDstCoarseBuckets>(r)]++] = r;
+        out[at[(r.dst >> kDstRegionShift) & (kDstBuckets - 1)]++] = r;
     }
-}
-
-// How far ahead the gather prefetches records; idx has this many entries of
-// padding past n.
-constexpr uint32_t kGatherAhead = 16;
-
-inline void stream_rec(long long *o, const ChunkRec &r)
-{
-    const long long *q = reinterpret_cast<const long long *>(&r);
-    _mm_stream_si64(o, q[0]);
-    _mm_stream_si64(o + 1, q[1]);
-    _mm_stream_si64(o + 2, q[2]);
-}
-
-// out[k] = in[idx[k]] for k < n, non-temporal stores; four records (96
-// bytes) per three 32-byte stores once out is 32-byte aligned.
-__attribute__((target("avx2"))) void gather_avx2(const ChunkRec *in, const uint32_t *idx,
-                                                 uint64_t n, ChunkRec *out)
-{
-    long long *o = reinterpret_cast<long long *>(out);
-    uint64_t k = 0;
-    for (; k < n && (reinterpret_cast<uintptr_t>(o) & 31) != 0; ++k, o += 3)
-        stream_rec(o, in[idx[k]]);
-    for (; k + 4 <= n; k += 4, o += 12) {
-        for (uint32_t j = 0; j < 4; ++j) {
-            const char *p = reinterpret_cast<const char *>(in + idx[k + kGatherAhead + j]);
-            _mm_prefetch(p, _MM_HINT_T0);
-            _mm_prefetch(p + sizeof(ChunkRec) - 1, _MM_HINT_T0);
-        }
-        const long long *a = reinterpret_cast<const long long *>(in + idx[k]);
-        const long long *b = reinterpret_cast<const long long *>(in + idx[k + 1]);
-        const long long *c = reinterpret_cast<const long long *>(in + idx[k + 2]);
-        const long long *d = reinterpret_cast<const long long *>(in + idx[k + 3]);
-        _mm256_stream_si256(reinterpret_cast<__m256i *>(o), _mm256_set_epi64x(b[0], a[2], a[1], a[0]));
-        _mm256_stream_si256(reinterpret_cast<__m256i *>(o + 4),
-                            _mm256_set_epi64x(c[1], c[0], b[2], b[1]));
-        _mm256_stream_si256(reinterpret_cast<__m256i *>(o + 8),
-                            _mm256_set_epi64x(d[2], d[1], d[0], c[2]));
-    }
-    for (; k < n; ++k, o += 3)
-        stream_rec(o, in[idx[k]]);
-}
-
-void gather_plain(const ChunkRec *in, const uint32_t *idx, uint64_t n, ChunkRec *out)
-{
-    long long *o = reinterpret_cast<long long *>(out);
-    for (uint64_t k = 0; k < n; ++k, o += 3) {
-        _mm_prefetch(reinterpret_cast<const char *>(in + idx[k + kGatherAhead]), _MM_HINT_T0);
-        stream_rec(o, in[idx[k]]);
-    }
-}
-
-void order_fine(const ChunkRec *in, uint64_t n, ChunkRec *out, uint32_t *idx, uint8_t *keys)
-{
-    static_assert(kDstFineBuckets <= 256, "keys are bytes");
-    // four count tables, so that increments of one bucket in a row do not
-    // wait on each other
-    uint32_t h[4][kDstFineBuckets] = {};
-    uint64_t i = 0;
-    for (; i + 4 <= n; i += 4) {
-        const uint32_t k0 = dst_key<kDstFineShift, kDstFineBuckets>(in[i]);
-        const uint32_t k1 = dst_key<kDstFineShift, kDstFineBuckets>(in[i + 1]);
-        const uint32_t k2 = dst_key<kDstFineShift, kDstFineBuckets>(in[i + 2]);
-        const uint32_t k3 = dst_key<kDstFineShift, kDstFineBuckets>(in[i + 3]);
-        keys[i] = (uint8_t)k0;
-        keys[i + 1] = (uint8_t)k1;
-        keys[i + 2] = (uint8_t)k2;
-        keys[i + 3] = (uint8_t)k3;
-        ++h[0][k0];
-        ++h[1][k1];
-        ++h[2][k2];
-        ++h[3][k3];
-    }
-    for (; i < n; ++i) {
-        const uint32_t k = dst_key<kDstFineShift, kDstFineBuckets>(in[i]);
-        keys[i] = (uint8_t)k;
-        ++h[0][k];
-    }
-    uint32_t at[kDstFineBuckets];
-    uint32_t acc = 0;
-    for (uint32_t b = 0; b < kDstFineBuckets; ++b) {
-        at[b] = acc;
-        acc += h[0][b] + h[1][b] + h[2][b] + h[3][b];
-    }
-    for (i = 0; i < n; ++i)
-        idx[at[keys[i]]++] = (uint32_t)i;
-    for (uint32_t j = 0; j < kGatherAhead; ++j)
-        idx[n + j] = 0;   // the prefetches past the end read record 0
-    if (have_avx2())
-        gather_avx2(in, idx, n, out);
-    else
-        gather_plain(in, idx, n, out);
-}
-
-}  // namespace
-
-uint64_t order_scratch_words(uint64_t n)
-{
-    return n <= kDstFineMax ? n + kGatherAhead : 0;
-}
-
-void order_by_dst(const ChunkRec *in, uint64_t n, ChunkRec *out, uint32_t *idx, uint8_t *keys)
-{
-    if (n <= kDstFineMax)
-        order_fine(in, n, out, idx, keys);
-    else
-        order_coarse(in, n, out);
 }
 
 uint64_t chunk_prefix(const uint64_t *size, uint64_t m, uint32_t chunk, uint64_t *begin)

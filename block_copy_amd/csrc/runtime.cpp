@@ -71,7 +71,7 @@ struct Staging {
     std::mutex mu;             // held for a whole call: planning is host-side and short
     int tuned[3] = {-2, -2, -2};   // kvcopy_autotune's cap per direction (-2: not tuned)
     uint8_t *host = nullptr;   // pinned, mapped (device address == host address)
-    uint8_t *dev = nullptr;    // device twin, allocated on first KVCOPY_F_DESC_UPLOAD
+    uint8_t *dev = nullptr;    // device twin (two halves), allocated on first KVCOPY_F_DESC_UPLOAD
     // KVCOPY_F_DYNAMIC: one pair of claim counters (next chunk, wavefronts
     // done) per 256-byte granule of the ring, in device memory, allocated on
     // first use and zeroed once.  A call uses the pair of its region's first
@@ -80,8 +80,6 @@ struct Staging {
     uint32_t *claims = nullptr;
     int clock_khz = 0;             // wall-clock rate (hipDeviceAttributeWallClockRate), 0 = not read yet
     std::vector<ChunkRec> order_tmp;   // KVCOPY_F_DST_ORDER: the worklist in list order
-    std::vector<uint32_t> order_idx;   // and the sort's scratch (order_by_dst)
-    std::vector<uint8_t> order_keys;
     // KVCOPY_F_DESC_UPLOAD: the worklist copies run on a stream of the
     // library's own (default priority), created on first use; the caller's
     // stream waits for each copy through `up_done` before its kernel.
@@ -147,7 +145,9 @@ int grow(Staging *st, uint64_t need, bool want_dev, bool want_claims)
     }
     st->ring.reset(cap);
     if (want_dev && st->dev == nullptr) {
-        e = hipMalloc((void **)&st->dev, cap);
+        // two halves: the uploaded regions, and at the same offsets in the
+        // second half their destination-ordered copies (launch_order)
+        e = hipMalloc((void **)&st->dev, 2 * cap);
         if (e != hipSuccess) {
             st->dev = nullptr;
             return e == hipErrorOutOfMemory ? KVCOPY_ENOMEM : hip_fail(e);
@@ -260,13 +260,18 @@ int run_locked(Staging *st, int device, const uint64_t *src, const uint64_t *dst
     const bool dynamic = (flags & KVCOPY_F_DYNAMIC) != 0;
     const bool merge = !(flags & KVCOPY_F_NO_COALESCE);
     const bool dst_order = (flags & KVCOPY_F_DST_ORDER) != 0;
+    // Destination order of an uploaded worklist is made on the GPU
+    // (launch_order): the region starts with the order kernels' zeroed
+    // header, and the records follow it.
+    const bool gpu_order = dst_order && upload;
+    const uint64_t head = gpu_order ? kOrderHeaderBytes : 0;
     uint32_t pace_on = 0, pace_period = 0;
     int rc = pace_ticks(st, device, o, &pace_on, &pace_period);
     if (rc != KVCOPY_OK)
         return rc;
     uint64_t off = 0, n_chunks = 0;
     ChunkRec *host = nullptr;
-    if (dst_order) {
+    if (dst_order && !upload) {
         // Plan in list order into host memory of the library's own, then
         // place the records into the ring in destination order.
         std::vector<ChunkRec> &tmp = st->order_tmp;
@@ -289,15 +294,6 @@ int run_locked(Staging *st, int device, const uint64_t *src, const uint64_t *dst
                 break;
             hint = n_chunks;   // plan again with room for every record
         }
-        const uint64_t words = order_scratch_words(n_chunks);
-        try {
-            if (st->order_idx.size() < words) {
-                st->order_idx.resize(words);
-                st->order_keys.resize(words);
-            }
-        } catch (...) {
-            return KVCOPY_ENOMEM;
-        }
         const uint64_t need = (n_chunks * sizeof(ChunkRec) + kAlign - 1) / kAlign * kAlign;
         if (4 * need > st->ring.capacity() || (upload && st->dev == nullptr) ||
             (dynamic && st->claims == nullptr)) {
@@ -307,12 +303,11 @@ int run_locked(Staging *st, int device, const uint64_t *src, const uint64_t *dst
         if ((rc = st->ring.reserve(need, &off)) != KVCOPY_OK)
             return rc;
         host = reinterpret_cast<ChunkRec *>(st->host + off);
-        order_by_dst(st->order_tmp.data(), n_chunks, host, st->order_idx.data(),
-                     st->order_keys.data());
+        order_by_dst(st->order_tmp.data(), n_chunks, host);
     } else {
         for (int pass = 0; pass < 2; ++pass) {
             const uint64_t room = hint ? hint : 1;
-            const uint64_t need = (room * sizeof(ChunkRec) + kAlign - 1) / kAlign * kAlign;
+            const uint64_t need = (head + room * sizeof(ChunkRec) + kAlign - 1) / kAlign * kAlign;
             if (4 * need > st->ring.capacity() || (upload && st->dev == nullptr) ||
                 (dynamic && st->claims == nullptr)) {
                 if ((rc = grow(st, need, upload, dynamic)) != KVCOPY_OK)
@@ -320,7 +315,7 @@ int run_locked(Staging *st, int device, const uint64_t *src, const uint64_t *dst
             }
             if ((rc = st->ring.reserve(need, &off)) != KVCOPY_OK)
                 return rc;
-            host = reinterpret_cast<ChunkRec *>(st->host + off);
+            host = reinterpret_cast<ChunkRec *>(st->host + off + head);
             if ((rc = build_checked(src, dst, sizes, n, merge, chunk, host, room, &n_chunks,
                                     true)) != KVCOPY_OK)
                 return rc;   // nothing committed: the region stays free
@@ -333,7 +328,9 @@ int run_locked(Staging *st, int device, const uint64_t *src, const uint64_t *dst
             hint = n_chunks;   // plan again into a region of the exact size
         }
     }
-    const uint64_t used = (n_chunks * sizeof(ChunkRec) + kAlign - 1) / kAlign * kAlign;
+    const uint64_t used = (head + n_chunks * sizeof(ChunkRec) + kAlign - 1) / kAlign * kAlign;
+    if (gpu_order)
+        memset(st->host + off, 0, head);
     finish_records();   // the streamed records reach memory before the launch is queued
 
     const ChunkRec *recs = host;   // read in place: mapped at the same address on the device
@@ -357,13 +354,26 @@ int run_locked(Staging *st, int device, const uint64_t *src, const uint64_t *dst
             st->up_stream = us;   // both or neither
             st->up_done = ue;
         }
-        ChunkRec *dev = reinterpret_cast<ChunkRec *>(st->dev + off);
-        if ((e = hipMemcpyAsync(dev, host, n_chunks * sizeof(ChunkRec), hipMemcpyHostToDevice,
-                                st->up_stream)) != hipSuccess ||
-            (e = hipEventRecord(st->up_done, st->up_stream)) != hipSuccess ||
+        if ((e = hipMemcpyAsync(st->dev + off, st->host + off, head + n_chunks * sizeof(ChunkRec),
+                                hipMemcpyHostToDevice, st->up_stream)) != hipSuccess)
+            return hip_fail(e);
+        recs = reinterpret_cast<const ChunkRec *>(st->dev + off + head);
+        if (gpu_order) {
+            // The order kernels follow the copy on the same stream, so in a
+            // train of calls they too overlap the previous call's kernel.
+            // Their output goes to the second half of the device twin, at the
+            // region's offset there.
+            ChunkRec *ordered =
+                reinterpret_cast<ChunkRec *>(st->dev + st->ring.capacity() + off + head);
+            if ((e = launch_order(recs, (uint32_t)n_chunks, ordered,
+                                  reinterpret_cast<uint32_t *>(st->dev + off), st->up_stream,
+                                  nullptr)) != hipSuccess)
+                return hip_fail(e);
+            recs = ordered;
+        }
+        if ((e = hipEventRecord(st->up_done, st->up_stream)) != hipSuccess ||
             (e = hipStreamWaitEvent(stream, st->up_done, 0)) != hipSuccess)
             return hip_fail(e);
-        recs = dev;
     }
     if (max_wgs == KVCOPY_WGS_AUTO)
         max_wgs = resolve_auto(st, dir);

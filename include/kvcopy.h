@@ -141,14 +141,23 @@ enum {
 #define KVCOPY_F_STORE_NT 0x100u
 /* Destination order: the worklist handed to the kernel is ordered by
  * destination region instead of list order, so that the chunks in flight at
- * any moment write a narrow band of memory: by 4 MiB region
- * ((dst >> 22) mod 256) for up to 131,072 records, by 64 MiB region
- * ((dst >> 26) mod 16) for longer worklists; list order within a region.
- * It costs the host a counting sort of the records (on the MI355X host
- * about 90 us for 65,536 records, on top of the planning).  Results do not
- * depend on it.  Meant for D2D gathers of many random blocks with
- * KVCOPY_F_WG_PER_CHUNK (below), where the kernel then runs as fast as on a
- * list sorted by destination; with the per-chunk loop it gains 3-5%. */
+ * any moment write a narrow band of memory.  Results do not depend on it.
+ * Meant for D2D gathers of many random blocks.
+ *   - With KVCOPY_F_DESC_UPLOAD the worklist is uploaded in list order and
+ *     grouped on the GPU by 4 MiB region ((dst >> 22) mod 256; no set order
+ *     within a region) by two small kernels that follow the upload on the
+ *     library's stream, outside kernel_begin / kernel_end, so in a train of
+ *     calls they run while the previous call's copy does.  Measured on
+ *     MI355X with KVCOPY_F_WG_PER_CHUNK (below), D2D calls of 65,536 random
+ *     4 KiB blocks between two 1 GiB pools: 95.8-96.0 us per copy kernel
+ *     with sc1 stores (70% of 8 TB/s of HBM traffic; 93.1 on a list sorted
+ *     by destination, 103.5 in list order), and back to back from C 96.2-
+ *     96.7 us per call, the GPU's pace (60-65 us of host time per call).
+ *   - Otherwise the host groups the records by 64 MiB region
+ *     ((dst >> 26) mod 16; list order within a region), a counting sort
+ *     that costs about 60 us of host time per 65,536 records.  With the
+ *     per-chunk loop, reading the records in place, the kernel gains 2-5%
+ *     (101.6-104.8 against 107.0-107.6 us for the calls above). */
 #define KVCOPY_F_DST_ORDER 0x200u
 /* Tail-bounded policy ([PF] "Proposed direction": a tail-bounded policy
  * beside the throughput-oriented one, for transfers that share the GPU with
@@ -291,7 +300,8 @@ typedef struct {
     uint32_t chunk_bytes;   /* 0 = default; else a multiple of 16, <= KVCOPY_CHUNK_MAX */
     uint32_t flags;         /* KVCOPY_F_* */
     uint32_t reserved;
-    hipEvent_t kernel_begin; /* if non-NULL: bound to the copy kernel's start (hipExtLaunchKernel) */
+    hipEvent_t kernel_begin; /* if non-NULL: bound to the copy kernel's start (hipExtLaunchKernel;
+                              * not the upload or the order kernels before it) */
     hipEvent_t kernel_end;   /* if non-NULL: bound to the copy kernel's completion */
     /* Time-sliced issue ([PF] "Proposed direction": a tail-bounded policy
      * that trades transfer speed for co-running kernels' latency).  When

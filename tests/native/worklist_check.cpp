@@ -289,57 +289,31 @@ int main(int argc, char **argv)
                 return 1;
             }
         }
-    // Destination order: a permutation of the records, grouped by
-    // destination region in key order, list order kept within a region;
-    // 4 MiB regions (256 keys) up to kDstFineMax records, 64 MiB regions (16
-    // keys) beyond.  Each record carries its list position in `reserved`
-    // (the sort moves whole records).  The output starts 8 bytes past a
-    // 32-byte boundary on odd trials, and nothing past it is written.
-    std::vector<uint64_t> sizes_to_try;
-    for (int trial = 0; trial < 200; ++trial)
-        sizes_to_try.push_back(rng() % 3000);
-    for (uint64_t n : {kDstFineMax - 1, kDstFineMax, kDstFineMax + 1, kDstFineMax + 4099})
-        sizes_to_try.push_back(n);
-    for (size_t trial = 0; trial < sizes_to_try.size(); ++trial) {
-        const uint64_t n = sizes_to_try[trial];
-        const bool fine = n <= kDstFineMax;
-        const uint32_t shift = fine ? kDstFineShift : kDstCoarseShift;
-        const uint32_t buckets = fine ? kDstFineBuckets : kDstCoarseBuckets;
-        std::vector<ChunkRec> in(n);
+    // Destination order (host): a permutation of the records, grouped by
+    // 64 MiB destination region in key order, list order kept within a
+    // region.  Each record carries its list position in `reserved` (the sort
+    // moves whole records); nothing past the output is written.
+    for (int trial = 0; trial < 204; ++trial) {
+        const uint64_t n = trial < 200 ? rng() % 3000 : 70000 + rng() % 70000;
+        std::vector<ChunkRec> in(n), out(n + 1);
         for (uint64_t i = 0; i < n; ++i)
             in[i] = ChunkRec{rng() & ~7ull, (rng() % (3ull << 30)) & ~7ull,
                              (uint32_t)(8 * (1 + rng() % 2048)), (uint32_t)i};
-        const uint64_t words = order_scratch_words(n);
-        if (words != (fine ? n + 16 : 0)) {
-            printf("order_scratch_words(%llu) = %llu\n", (unsigned long long)n,
-                   (unsigned long long)words);
-            return 1;
-        }
-        std::vector<uint32_t> idx(words);
-        std::vector<uint8_t> keys(words);
-        const size_t lead = (trial & 1) ? 8 : 0;   // bytes before the output in `raw`
-        std::vector<unsigned char> raw(32 + lead + (n + 1) * sizeof(ChunkRec));
-        unsigned char *base = raw.data() + (32 - (reinterpret_cast<uintptr_t>(raw.data()) & 31));
-        ChunkRec *out = reinterpret_cast<ChunkRec *>(base + lead);
-        memset(base, 0x5A, lead + (n + 1) * sizeof(ChunkRec));
-        order_by_dst(in.data(), n, out, idx.data(), keys.data());
-        finish_records();
+        memset(out.data(), 0x5A, out.size() * sizeof(ChunkRec));
+        order_by_dst(in.data(), n, out.data());
         std::vector<int> seen(n, 0);
         for (uint64_t k = 0; k < n; ++k) {
-            ChunkRec r;
-            memcpy(&r, out + k, sizeof r);
-            const uint64_t i = r.reserved;
-            if (i >= n || seen[i]++ || memcmp(&r, &in[i], sizeof(ChunkRec)) != 0) {
+            const uint64_t i = out[k].reserved;
+            if (i >= n || seen[i]++ || memcmp(&out[k], &in[i], sizeof(ChunkRec)) != 0) {
                 printf("order_by_dst: n %llu slot %llu is not a distinct input record\n",
                        (unsigned long long)n, (unsigned long long)k);
                 return 1;
             }
             if (k > 0) {
-                ChunkRec p;
-                memcpy(&p, out + k - 1, sizeof p);
-                const uint32_t b = (uint32_t)((r.dst >> shift) & (buckets - 1));
-                const uint32_t bp = (uint32_t)((p.dst >> shift) & (buckets - 1));
-                if (bp > b || (bp == b && p.reserved > r.reserved)) {
+                const uint32_t b = (uint32_t)((out[k].dst >> kDstRegionShift) & (kDstBuckets - 1));
+                const uint32_t bp =
+                    (uint32_t)((out[k - 1].dst >> kDstRegionShift) & (kDstBuckets - 1));
+                if (bp > b || (bp == b && out[k - 1].reserved > out[k].reserved)) {
                     printf("order_by_dst: n %llu slots %llu-%llu out of order\n",
                            (unsigned long long)n, (unsigned long long)k - 1,
                            (unsigned long long)k);
@@ -347,15 +321,10 @@ int main(int argc, char **argv)
                 }
             }
         }
-        const unsigned char *tail = reinterpret_cast<const unsigned char *>(out + n);
+        const unsigned char *tail = reinterpret_cast<const unsigned char *>(out.data() + n);
         for (size_t b = 0; b < sizeof(ChunkRec); ++b)
             if (tail[b] != 0x5A) {
                 printf("order_by_dst wrote past its output (n %llu)\n", (unsigned long long)n);
-                return 1;
-            }
-        for (size_t b = 0; b < lead; ++b)
-            if (base[b] != 0x5A) {
-                printf("order_by_dst wrote before its output (n %llu)\n", (unsigned long long)n);
                 return 1;
             }
     }

@@ -252,18 +252,22 @@ def test_wg_per_chunk_d2d_large(K):
     res.free()
 
 
-@pytest.mark.parametrize("loop", ["per_chunk", "wg"])
+@pytest.mark.parametrize("loop", ["per_chunk", "wg", "per_chunk_dst_order", "wg_dst_order"])
 def test_upload_train_wraps_the_ring(K, loop):
     """48 uploaded calls back to back on one stream, cycling over 8 batches
     of 16,384 random 4 KiB blocks (393 KiB of worklist each: the 16 MiB
     staging ring and its device twin wrap), so each call's worklist copy,
     on the library's upload stream, runs while earlier kernels still read
-    their own regions.  The pools' sources are never written, so the final
-    images are those of the 8 batches applied once, in order."""
+    their own regions; with destination order each call also runs the two
+    order kernels on its region's header and ordered copy.  The pools'
+    sources are never written, so the final images are those of the 8
+    batches applied once, in order."""
     from block_copy_amd.harness import Resident
     wl = W.d2d_rotation(n=16384, pool_blocks=65536)
     res = Resident(wl)
-    fl = K.F_DESC_UPLOAD | (K.F_WG_PER_CHUNK if loop == "wg" else 0)
+    fl = K.F_DESC_UPLOAD | (K.F_WG_PER_CHUNK if loop.startswith("wg") else 0)
+    if loop.endswith("dst_order"):
+        fl |= K.F_DST_ORDER
     st = torch.cuda.Stream()
     for sentinel in (W.SENTINEL_A, W.SENTINEL_B):
         _say("upload train", loop, "sentinel", hex(sentinel))

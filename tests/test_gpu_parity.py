@@ -588,6 +588,54 @@ def test_destination_order(K, max_wgs):
         res.free()
 
 
+@pytest.mark.parametrize("loop", ["per_chunk", "pipeline", "dynamic", "wg"])
+def test_destination_order_on_the_gpu(K, loop):
+    """KVCOPY_F_DST_ORDER | KVCOPY_F_DESC_UPLOAD: the worklist is uploaded in
+    list order and grouped by destination region by two kernels on the
+    call's stream before the copy.  Record counts around the order kernels'
+    workgroup share (1,024 records) and thread count (256), the D2D block
+    gather, an irregular misaligned batch with multi-chunk ranges and zero
+    sizes, and H2D and D2H batches; each loop reads the ordered copy."""
+    from block_copy_amd.harness import Resident
+    extra = {"per_chunk": 0, "pipeline": K.F_PIPELINE, "dynamic": K.F_DYNAMIC,
+             "wg": K.F_WG_PER_CHUNK}[loop]
+    fl = K.F_DST_ORDER | K.F_DESC_UPLOAD | extra
+    cases = [(W.d2d_blocks(seed=30 + i, n=n, pool_blocks=8192, block=64), 0)
+             for i, n in enumerate((1, 2, 255, 256, 257, 1023, 1024, 1025, 4097))]
+    cases += [(W.d2d_blocks(seed=41), 0),
+              (W.irregular(seed=42, n=900, max_size=80 * 1024, dir_=W.D2D, misalign=True,
+                           zero_frac=0.05), 4096),
+              (W.kv_blocks(seed=43, directions="h2d", n=4096, pool_blocks=16384), 0),
+              (W.irregular(seed=44, n=700, dir_=W.D2H, src_where="device", dst_where="host",
+                           misalign=True, zero_frac=0.05), 0)]
+    for wl, chunk in cases:
+        res = Resident(wl)
+        for sentinel in (W.SENTINEL_A, W.SENTINEL_B):
+            for max_wgs in (8, 0):
+                _say("gpu destination order", loop, wl.name, "n", wl.batches[0].n, "max_wgs",
+                     max_wgs, "sentinel", hex(sentinel))
+                res.fill(sentinel)
+                _run(res, [0], max_wgs, flags=fl, chunk_bytes=chunk)
+                _check(res, [0], f"gpu dst order {loop} {wl.name} n={wl.batches[0].n} "
+                       f"max_wgs={max_wgs}", sentinel)
+        res.free()
+
+
+def test_destination_order_on_the_gpu_grid_stride(K):
+    """More records than the order kernels' largest grid covers in one pass
+    (1,024 workgroups x 1,024 records): 1,200,000 blocks of 64 bytes, so
+    each order workgroup strides over the worklist twice."""
+    from block_copy_amd.harness import Resident
+    wl = W.d2d_blocks(seed=45, n=1_200_000, pool_blocks=1_400_000, block=64)
+    res = Resident(wl)
+    for loop_flag in (0, K.F_WG_PER_CHUNK):
+        _say("gpu destination order, 1,200,000 records, loop flag", hex(loop_flag))
+        res.fill(W.SENTINEL_A)
+        _run(res, [0], 0, flags=K.F_DST_ORDER | K.F_DESC_UPLOAD | loop_flag)
+        _check(res, [0], f"gpu dst order 1.2M records loop={hex(loop_flag)}", W.SENTINEL_A)
+    res.free()
+
+
 def test_tail_bounded_preset(K):
     """KVCOPY_F_TAIL_BOUNDED (sc1 stores, time-sliced issue, at most 4
     workgroups): the KV burst on two streams, an irregular D2H batch, and

@@ -42,7 +42,7 @@ def test_header_symbols_are_exported(K):
         assert hasattr(K.lib, name)
 
 
-@pytest.mark.parametrize("src", ["kvcopy_kernel.hip", "device_batch.hip"])
+@pytest.mark.parametrize("src", ["kvcopy_kernel.hip", "device_batch.hip", "order_kernel.hip"])
 def test_kernels_have_no_scratch_or_spills(K, src):
     """No copy kernel may use private (scratch) memory or spill registers;
     every direction of every loop has its own symbol."""
@@ -66,8 +66,10 @@ def test_kernels_have_no_scratch_or_spills(K, src):
                 for v in ("", "_sc1", "_pipe", "_dyn", "_inline", "_inline_sc1", "_wg",
                           "_wg_sc1")} | {
                     "kvcopy_pair_kernel", "kvcopy_pair_nt_kernel"}
-    else:
+    elif src == "device_batch.hip":
         want = {"kvcopy_device_plan_kernel", "kvcopy_device_copy_kernel"}
+    else:
+        want = {"kvcopy_order_count_kernel", "kvcopy_order_place_kernel"}
     assert names == want, names
 
 
