@@ -11,7 +11,9 @@
 // link once, as part of the kernel's own traffic, with no separate copy and
 // no copy-engine latency in front of the kernel.  (KVCOPY_F_DESC_UPLOAD
 // instead copies it into a device twin of the ring with hipMemcpyAsync on a
-// stream of the library's own, which the caller's stream waits for.)
+// stream of the library's own, which the caller's stream waits for; with
+// KVCOPY_F_DST_ORDER two order kernels follow that copy on the same stream
+// and group the records by destination region into the twin's second half.)
 //
 // The vLLM PR #42212 report, section "review highlights", points out that
 // descriptor buffers must be pinned for the transfer to be asynchronous, and
