@@ -337,7 +337,10 @@ def test_ring_growth_with_calls_in_flight(K):
 
 
 def test_threads_share_the_library(K):
-    """Four host threads, each with its own stream and arenas, submit at once."""
+    """Four host threads, each with its own stream and arenas, submit at once,
+    cycling through the worklist's routes: read in place, uploaded, grouped
+    by destination on the host, and uploaded and grouped on the GPU (the
+    order kernels of all threads share the library's upload stream)."""
     import threading
     from block_copy_amd.harness import Resident
     wls = [W.irregular(seed=90 + t, n=400, max_size=16384, dir_=d, src_where=sw, dst_where=dw)
@@ -348,8 +351,9 @@ def test_threads_share_the_library(K):
 
     def worker(t):
         try:
-            for i in range(30):
-                rs[t].submit(0, [0, 8, 32][i % 3], streams[t])
+            routes = [0, K.F_DESC_UPLOAD, K.F_DST_ORDER, K.F_DST_ORDER | K.F_DESC_UPLOAD]
+            for i in range(32):
+                rs[t].submit(0, [0, 8, 32][i % 3], streams[t], flags=routes[(i + t) % 4])
         except Exception as e:   # noqa: BLE001 - reported below
             errors.append(e)
 
