@@ -94,8 +94,11 @@ enum {
  * host link once, as part of the kernel's own loads); KVCOPY_F_DESC_UPLOAD
  * first copies it into device memory with hipMemcpyAsync on a stream of the
  * library's own (one per device, default priority, created on first use),
- * and `stream` waits for that copy before the kernel: in a train of calls
- * the copy overlaps the previous call's kernel. */
+ * and `stream` waits for that copy (and, with KVCOPY_F_DST_ORDER, the two
+ * order kernels that follow it there) before the kernel: in a train of
+ * calls they overlap the previous call's kernel.  The library's device copy
+ * of its staging ring (two halves, the second for ordered worklists) is
+ * allocated on the first such call. */
 #define KVCOPY_F_VALIDATE 0x1u    /* check the overlap rule (O(n log n)); also on when KVCOPY_VALIDATE=1 */
 #define KVCOPY_F_NO_COALESCE 0x2u /* skip merging of adjacent ranges (for measurement only) */
 #define KVCOPY_F_DESC_UPLOAD 0x8u /* upload the worklist to device memory before the kernel */
