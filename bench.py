@@ -1432,6 +1432,13 @@ def d2d_distinct(c: Ctx, args):
         u = statistics.median(v)
         out[name] = {"kernel_us_p50": round(u, 2), "hbm_GBps_kernel": round(gbs(hbm, u / 1e6), 1),
                      "frac_hbm_peak_kernel": round(gbs(hbm, u / 1e6) / HBM_PEAK_GBS, 4)}
+        fl = variants[name][0]
+        if fl & K.F_DST_ORDER and fl & K.F_DESC_UPLOAD:
+            # the kernel events bracket the copy kernel; the grouping runs
+            # before it, on the library's upload stream (its kernels are in
+            # the D2D kernel trace), and is inside the back-to-back figures
+            out[name]["events_cover"] = ("the copy kernel; the order kernels run before it on the "
+                                         "library's upload stream")
     log(f"  d2d distinct calls: {out} (bit-exact)")
     return out
 
