@@ -101,7 +101,7 @@ void order_by_dst(const ChunkRec *in, uint64_t n, ChunkRec *out);
 // header is kOrderHeaderBytes of zeroed device memory (256 counters, then
 // 256 cursors) that the two kernels use and leave dirty.  Two launches on
 // `stream` (the library's upload stream); `start` (may be null) is bound to
-// the first one's start.
+// the first one's start.  n == 0 launches nothing.
 constexpr uint32_t kOrderShift = 22;
 constexpr uint32_t kOrderKeys = 256;
 constexpr uint32_t kOrderThreads = 256;

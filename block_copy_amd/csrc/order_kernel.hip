@@ -134,6 +134,8 @@ __global__ __launch_bounds__(kOrderThreads) void kvcopy_order_place_kernel(
 hipError_t launch_order(const ChunkRec *in, uint32_t n, ChunkRec *out, uint32_t *header,
                         hipStream_t stream, hipEvent_t start)
 {
+    if (n == 0)   // nothing to order (the kernels load record n - 1 past the end of a pass)
+        return hipSuccess;
     uint64_t blocks = ((uint64_t)n + kOrderPerWG - 1) / kOrderPerWG;
     const uint32_t grid = (uint32_t)(blocks < kOrderMaxGrid ? (blocks ? blocks : 1) : kOrderMaxGrid);
     uint32_t *counts = header, *cursors = header + kOrderKeys;
