@@ -329,3 +329,49 @@ def test_latency_tool_is_built_and_checks_its_arguments(K):
     assert os.access(exe, os.X_OK)
     r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
     assert r.returncode == 1 and "usage" in r.stderr
+
+
+def test_binding_matches_the_compiled_header(K, tmp_path):
+    """Every constant and struct layout the Python binding restates equals
+    what a C compiler reads from include/kvcopy.h (the argument marshalling
+    depends on them)."""
+    import ctypes
+    consts = {"H2D": "KVCOPY_H2D", "D2H": "KVCOPY_D2H", "D2D": "KVCOPY_D2D", "OK": "KVCOPY_OK",
+              "EINVAL": "KVCOPY_EINVAL", "EALIGN": "KVCOPY_EALIGN",
+              "EOVERLAP": "KVCOPY_EOVERLAP", "ENOMEM": "KVCOPY_ENOMEM", "EHIP": "KVCOPY_EHIP",
+              "WGS_ALL": "KVCOPY_WGS_ALL", "WGS_AUTO": "KVCOPY_WGS_AUTO",
+              "CHUNK_DEFAULT": "KVCOPY_CHUNK_DEFAULT", "CHUNK_MAX": "KVCOPY_CHUNK_MAX",
+              "OPTS_V1_SIZE": "KVCOPY_OPTS_V1_SIZE",
+              "DEVICE_BAD_ALIGN": "KVCOPY_DEVICE_BAD_ALIGN",
+              "DEVICE_TOO_MANY_CHUNKS": "KVCOPY_DEVICE_TOO_MANY_CHUNKS",
+              "NOALLOC_MAX_N": "KVCOPY_NOALLOC_MAX_N"}
+    hdr = open(os.path.join(ROOT, "include", "kvcopy.h")).read()
+    flags = re.findall(r"#define (KVCOPY_F_(\w+)) 0x", hdr)
+    assert len(flags) >= 11
+    for macro, short in flags:
+        consts["F_" + short] = macro
+    src = ["#include <stdio.h>", "#include <stddef.h>", '#include "kvcopy.h"', "int main(void) {"]
+    for name, macro in consts.items():
+        src.append(f'    printf("{name} %lld\\n", (long long)({macro}));')
+    for struct, fields in (("kvcopy_opts_t", K.Opts._fields_), ("kvcopy_plan_t", K._Plan._fields_)):
+        src.append(f'    printf("sizeof {struct} %zu\\n", sizeof({struct}));')
+        for f, _ in fields:
+            src.append(f'    printf("offsetof {struct} {f} %zu\\n", offsetof({struct}, {f}));')
+    src += ["    return 0;", "}"]
+    c = tmp_path / "consts.c"
+    c.write_text("\n".join(src) + "\n")
+    exe = tmp_path / "consts"
+    subprocess.run(["gcc", "-std=c11", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include",
+                    "-I" + os.path.join(ROOT, "include"), str(c), "-o", str(exe)],
+                   check=True, capture_output=True)
+    got = {}
+    for line in subprocess.run([str(exe)], check=True, capture_output=True,
+                               text=True).stdout.splitlines():
+        key, val = line.rsplit(" ", 1)
+        got[key] = int(val)
+    for name in consts:
+        assert getattr(K, name) == got[name], name
+    for struct, cls in (("kvcopy_opts_t", K.Opts), ("kvcopy_plan_t", K._Plan)):
+        assert ctypes.sizeof(cls) == got[f"sizeof {struct}"], struct
+        for f, _ in cls._fields_:
+            assert getattr(cls, f).offset == got[f"offsetof {struct} {f}"], (struct, f)
