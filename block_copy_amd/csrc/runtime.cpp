@@ -118,6 +118,14 @@ int grow(Staging *st, uint64_t need, bool want_dev, bool want_claims)
     int rc = st->ring.drain();
     if (rc != KVCOPY_OK)
         return rc;
+    // Work on the upload stream belongs to committed regions (drained above)
+    // except after a call that failed between its upload and its kernel: let
+    // that finish too before the buffers it uses are freed.
+    if (st->up_stream != nullptr) {
+        const hipError_t se = hipStreamSynchronize(st->up_stream);
+        if (se != hipSuccess)
+            return hip_fail(se);
+    }
     if (resize) {
         if (st->host)
             (void)hipHostFree(st->host);
