@@ -315,6 +315,21 @@ def test_ring_regions_outlive_their_kernels(K):
     assert r.returncode == 0, r.stdout + r.stderr
 
 
+def test_ring_growth_with_gpu_order_in_flight(K):
+    """The ring grows while uploaded worklists and their order kernels are
+    still queued: see tests/growth_scenario.py (a fresh process, so that the
+    ring starts at 16 MiB and must grow)."""
+    import os
+    import subprocess
+    import sys
+    here = os.path.dirname(os.path.abspath(__file__))
+    _say("growth scenario in a fresh process")
+    r = subprocess.run([sys.executable, os.path.join(here, "growth_scenario.py")],
+                       capture_output=True, text=True, timeout=240)
+    print(r.stdout + r.stderr, flush=True)
+    assert r.returncode == 0, r.stdout + r.stderr
+
+
 def test_ring_growth_with_calls_in_flight(K):
     """A call whose worklist needs more than a quarter of the ring grows it
     while earlier calls are still queued."""
