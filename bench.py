@@ -365,6 +365,27 @@ def parse_wgs(text):
     return vals
 
 
+def pcie_link():
+    """The GPU's negotiated PCIe link as sysfs reports it ({"speed": "32.0 GT/s
+    PCIe", "width": 16} for PCIe 5.0 x16), or None when it cannot be read or
+    more than one AMD GPU is visible (the card would be ambiguous)."""
+    import glob
+    found = []
+    for d in sorted(glob.glob("/sys/class/drm/card*/device")):
+        try:
+            with open(os.path.join(d, "vendor")) as f:
+                if f.read().strip() != "0x1002":
+                    continue
+            with open(os.path.join(d, "current_link_speed")) as f:
+                speed = f.read().strip()
+            with open(os.path.join(d, "current_link_width")) as f:
+                width = int(f.read().strip())
+        except (OSError, ValueError):
+            continue
+        found.append({"speed": speed, "width": width})
+    return found[0] if len(found) == 1 else None
+
+
 def kernel_name(dir_, spec="auto"):
     """The per-chunk copy kernel's symbol for a direction under --store
     (the library stores D2H in the sc1 form on grids of three or more
@@ -554,7 +575,8 @@ def bench_kv(c: Ctx, args):
         "frac_of_measured_ceiling": round(ach[dom] / meas_ceil, 4) if meas_ceil else None,
         "other_kernel": {"kernel": kernel_name(1 - dom, args.store),
                          "achieved": round(ach[1 - dom], 3),
-                         "kernel_ms": round(kern_ms[1 - dom], 4)}}
+                         "kernel_ms": round(kern_ms[1 - dom], 4)},
+        "link": pcie_link()}
     # the step against the link's measured two-direction ceiling: contiguous
     # hipMemcpyAsync H2D and D2H of 64 MiB each, concurrent on two streams
     both_ceil = extras.get("contiguous_memcpy_ceiling_GBps", {}).get("both")
@@ -912,7 +934,7 @@ def bench_pair(c: Ctx, args):
         "peak": 2 * PCIE_PEAK_GBS, "unit": "GB/s", "frac": round(ach / (2 * PCIE_PEAK_GBS), 4),
         "traffic": measured_traffic("kvcopy_pair_kernel", COUNTERS_PAIR, alg_fetch, alg_write),
         "kernel_ms": round(kern_ms, 4), "algorithmic_bytes_per_launch": alg_fetch,
-        "peak_note": "both directions of PCIe 5.0 x16 (64 GB/s each)",
+        "peak_note": "both directions of PCIe 5.0 x16 (64 GB/s each)", "link": pcie_link(),
         "measured_ceiling": meas_ceil,
         "frac_of_measured_ceiling": round(ach / meas_ceil, 4) if meas_ceil else None}
     line["cpu_baseline"] = cpu_baseline_record(
