@@ -58,6 +58,7 @@ DEFAULT_MAX_WGS = 64
 # default grid for H2D and D2H.
 ONE_WAY_MAX_WGS = 128
 REC_BYTES = 24            # one worklist record per chunk
+LINK_SETTLE_STEPS = 700   # untimed headline steps (about 1 s) before any host-link figure
 DIR_NAMES = ("h2d", "d2h", "d2d")
 COUNTERS_KV = os.path.join(ROOT, "profiles", "counters_kv_bidirectional.json")
 COUNTERS_D2D = os.path.join(ROOT, "profiles", "counters_d2d_blocks.json")
@@ -437,9 +438,21 @@ def bench_kv(c: Ctx, args):
         return max_wgs[j] if isinstance(max_wgs, list) else max_wgs
 
     extras = {}
+    # Before any figure is taken, the headline's own step runs untimed for
+    # about a second (LINK_SETTLE_STEPS).  Measured on MI355X, the start of a
+    # process can find the host link slow for a second or so, for the
+    # runtime's contiguous copies as much as for the kernel: in one process
+    # of nine the contiguous pair read 87.8 GB/s (96.4-96.7 in the others),
+    # each direction alone 54 GB/s and the 20-step headline 85.1, while the
+    # 30 windows that followed it read 96.5 at the median.  Settling first
+    # puts the ceilings, the per-direction legs and the headline on the same
+    # steady link.  The headline then takes its own --warmup steps as asked.
+    c.run_steps(res, [0, 1], [hA, hB], LINK_SETTLE_STEPS, max_wgs, joined=True)
+    for st in (hA, hB):
+        hiprt.stream_sync(st)
     # The host link's contiguous ceilings (DMA, no copy kernel) and, in the
-    # full run, each direction alone come first: they are part of the report,
-    # and they leave the link in steady use before the headline's own warm-up
+    # full run, each direction alone come next: they are part of the report,
+    # and they keep the link in steady use before the headline's own warm-up
     # (measured on MI355X, bidirectional traffic in the first quarter second
     # of a process runs at 51-69 GB/s).
     extras["contiguous_memcpy_ceiling_GBps"] = ceilings(c)
