@@ -889,7 +889,8 @@ def bench_pair(c: Ctx, args):
     step_bytes = wl.nbytes
     g = args.max_wgs if args.max_wgs is not None else K.WGS_AUTO
     log(f"pair: {sum(b.n for b in wl.batches)} descriptors in one call, max_wgs={g}")
-    for _ in range(args.warmup):
+    # settle the host link first, as the headline does (LINK_SETTLE_STEPS)
+    for _ in range(max(args.warmup, LINK_SETTLE_STEPS)):
         c.pair_step(res, c.sA, g)
     torch.cuda.synchronize()
     use_ev = not args.no_events
