@@ -58,7 +58,8 @@ DEFAULT_MAX_WGS = 64
 # default grid for H2D and D2H.
 ONE_WAY_MAX_WGS = 128
 REC_BYTES = 24            # one worklist record per chunk
-LINK_SETTLE_STEPS = 700   # untimed headline steps (about 1 s) before any host-link figure
+LINK_SETTLE_STEPS = 700   # untimed headline steps (about 1 s) before any host-link figure,
+LINK_SETTLE_SECONDS = 1.5  # or this long, whichever ends first (small caps run slow steps)
 DIR_NAMES = ("h2d", "d2h", "d2d")
 COUNTERS_KV = os.path.join(ROOT, "profiles", "counters_kv_bidirectional.json")
 COUNTERS_D2D = os.path.join(ROOT, "profiles", "counters_d2d_blocks.json")
@@ -447,9 +448,12 @@ def bench_kv(c: Ctx, args):
     # 30 windows that followed it read 96.5 at the median.  Settling first
     # puts the ceilings, the per-direction legs and the headline on the same
     # steady link.  The headline then takes its own --warmup steps as asked.
-    c.run_steps(res, [0, 1], [hA, hB], LINK_SETTLE_STEPS, max_wgs, joined=True)
-    for st in (hA, hB):
-        hiprt.stream_sync(st)
+    t_settle, done = time.perf_counter(), 0
+    while done < LINK_SETTLE_STEPS and time.perf_counter() - t_settle < LINK_SETTLE_SECONDS:
+        c.run_steps(res, [0, 1], [hA, hB], 50, max_wgs, joined=True)
+        for st in (hA, hB):
+            hiprt.stream_sync(st)
+        done += 50
     # The host link's contiguous ceilings (DMA, no copy kernel) and, in the
     # full run, each direction alone come next: they are part of the report,
     # and they keep the link in steady use before the headline's own warm-up
@@ -889,8 +893,14 @@ def bench_pair(c: Ctx, args):
     step_bytes = wl.nbytes
     g = args.max_wgs if args.max_wgs is not None else K.WGS_AUTO
     log(f"pair: {sum(b.n for b in wl.batches)} descriptors in one call, max_wgs={g}")
-    # settle the host link first, as the headline does (LINK_SETTLE_STEPS)
-    for _ in range(max(args.warmup, LINK_SETTLE_STEPS)):
+    # settle the host link first, as the headline does, then the --warmup steps
+    t_settle, done = time.perf_counter(), 0
+    while done < LINK_SETTLE_STEPS and time.perf_counter() - t_settle < LINK_SETTLE_SECONDS:
+        for _ in range(50):
+            c.pair_step(res, c.sA, g)
+        hiprt.stream_sync(c.sA)
+        done += 50
+    for _ in range(args.warmup):
         c.pair_step(res, c.sA, g)
     torch.cuda.synchronize()
     use_ev = not args.no_events
